@@ -1,0 +1,432 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test ties one step of the oracle to a closed form, an invariant, an
+exact brute-force computation (tests/exact.py) or an independent library
+routine (torch CPU conversions and eager ops), chosen so that a plausible
+mistake -- a dropped term, a wrong rounding point, swapped gate/up halves, a
+sum in place of a mean, a multiply in place of a divide -- fails one of them.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from tests import exact
+from workloads import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32_of(bits):
+    return oracle.bf16_to_f32(bits)
+
+
+def bf16_t(bits) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+ALL_BF16 = np.arange(65536, dtype=np.uint16)
+FINITE_BF16 = ALL_BF16[np.isfinite(oracle.bf16_to_f32(ALL_BF16))]
+
+
+# ------------------------------------------------------------------ formats
+
+def test_bf16_rounding_matches_torch_cast():
+    """bf16 rounding of binary32 values == torch's fp32->bf16 cast, bitwise,
+    over every top half combined with low halves around the tie point."""
+    hi = np.arange(65536, dtype=np.uint32) << 16
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], dtype=np.uint32)
+    u = (hi[:, None] | lows[None, :]).reshape(-1)
+    f = u.view(np.float32)
+    ref = bits_of(torch.from_numpy(f.copy()).to(torch.bfloat16))
+    lib = oracle._lib()
+    got = np.array([lib.aarms_oracle_bf16_from_f64(float(v)) for v in f], dtype=np.uint16)
+    nan = np.isnan(f)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(f32_of(got[nan])))
+
+
+def test_bf16_rounding_of_binary64_exact():
+    """Values between binary32 points (the SiLU path rounds binary64 directly):
+    brute-force nearest-even search with exact rationals."""
+    rng = np.random.default_rng(7)
+    vals = list(rng.standard_normal(400) * np.exp2(rng.integers(-140, 120, 400)))
+    # exact bf16 midpoints and their binary64 neighbours
+    for b in [0x3F80, 0x0001, 0x0080, 0x7F7E, 0x3F81, 0x00FF]:
+        a, c = exact.bf16_value(b), exact.bf16_value(b + 1)
+        m = (a + c) / 2
+        vals += [m, np.nextafter(m, 0), np.nextafter(m, np.inf), -m]
+    vals += [float.fromhex("0x1.FEp127") * (1 + 2.0 ** -9), float.fromhex("0x1.FEp127") * (1 + 2.0 ** -8.5), 2.0 ** -134, 2.0 ** -134 * 1.0001]
+    for v in vals:
+        assert oracle.bf16_from_f64(v) == exact.round_to_bf16(Fraction(float(v))), v
+
+
+def test_e4m3_decode_matches_torch():
+    table = oracle.e4m3_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(table), nan)
+    assert np.array_equal(table[~nan], ref[~nan])
+    assert table[0x7E] == 448.0 and np.nanmax(table) == 448.0
+    assert set(np.flatnonzero(nan)) == {0x7F, 0xFF}
+
+
+def test_e4m3_encode_exhaustive_vs_bruteforce():
+    """Every binary32 value on a fine grid in [-448, 448] (all bf16 values
+    there, plus every E4M3 midpoint and its neighbours): oracle encode ==
+    exact nearest-even search == torch's cast."""
+    v = oracle.bf16_to_f32(FINITE_BF16).astype(np.float64)
+    v = v[np.abs(v) <= 448]
+    grid = np.array(sorted(set(oracle.e4m3_table()[:0x7F])))
+    mids = (grid[1:] + grid[:-1]) / 2
+    mids = np.concatenate([mids, -mids])
+    extra = np.concatenate([mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                            np.nextafter(mids.astype(np.float32), np.float32(-np.inf))])
+    v = np.concatenate([v, extra.astype(np.float64)])
+    lib = oracle._lib()
+    got = np.array([lib.aarms_oracle_e4m3_from_f64(float(x)) for x in v], dtype=np.uint8)
+    ref_t = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref_t)
+    sample = np.random.default_rng(3).choice(len(v), 3000, replace=False)
+    for i in list(sample) + list(range(len(v) - len(extra), len(v))):
+        assert got[i] == exact.round_to_e4m3(Fraction(float(v[i]))), v[i]
+
+
+# ------------------------------------------------------------------ residual add
+
+def test_residual_add_matches_torch_and_exact():
+    rng = np.random.default_rng(11)
+    n = 200_000
+    x = gen.bf16_bits_from_f32((rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32))
+    r = gen.bf16_bits_from_f32((rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32))
+    got = oracle.residual_add(x, r)
+    ref = bits_of(bf16_t(x) + bf16_t(r))
+    assert np.array_equal(got, ref)
+    # closed form: the binary32 sum of two bf16 rounds to the correctly
+    # rounded bf16 sum (checked exactly on a sample)
+    for i in rng.choice(n, 2000, replace=False):
+        s = Fraction(float(f32_of(x[i]))) + Fraction(float(f32_of(r[i])))
+        assert got[i] == exact.round_to_bf16(s)
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+def _norm(x, res, w, eps):
+    out, res_out, rs = oracle.fused_add_rmsnorm(x, res, w, eps)
+    return out, res_out, rs
+
+
+def test_rmsnorm_constant_row_gives_weight_times_sign():
+    """x = c, residual = 0: mean = c^2 exactly, and t rounds to sign(c) when
+    c^2 >= 512*eps, so out = w * sign(c) bit-exactly."""
+    H = 1536
+    w = gen.normal_bf16((H,), 0, 3, mean=1.0, std=0.1)
+    cs = [1.0, -1.0, 0.5, 3.0, -0.0625, 100.0, 2.0 ** -20]
+    for eps in [1e-6, 1e-5, 0.0]:
+        for c in cs:
+            if eps and c * c < 512 * eps:
+                continue
+            x = np.full((2, H), oracle.bf16_from_f64(c), np.uint16)
+            z = np.zeros((2, H), np.uint16)
+            out, _, _ = _norm(x, z, w, eps)
+            want = w if c > 0 else (w ^ 0x8000)
+            assert np.array_equal(out[0], want) and np.array_equal(out[1], want), (c, eps)
+    # c = 0 with eps > 0: out = 0 (signs follow w)
+    out, _, _ = _norm(np.zeros((1, H), np.uint16), np.zeros((1, H), np.uint16), w, 1e-6)
+    assert np.all(f32_of(out) == 0)
+
+
+def test_rmsnorm_scale_invariance():
+    """eps = 0, x scaled by 2^k: every step scales exactly, output bitwise equal."""
+    x = gen.normal_bf16((8, 1536), 5, 1)
+    w = gen.normal_bf16((1536,), 5, 3, mean=1.0, std=0.1)
+    z = np.zeros_like(x)
+    base, _, _ = _norm(x, z, w, 0.0)
+    for k in [-12, -3, -1, 1, 4, 9]:
+        xs = gen.bf16_bits_from_f32(f32_of(x) * np.float32(2.0 ** k))
+        out, _, _ = _norm(xs, z, w, 0.0)
+        assert np.array_equal(out, base), k
+
+
+def test_rmsnorm_unit_rms_and_weight_one():
+    """w = 1: out is the normalized row; its RMS is 1 within 1e-3 (a sum in
+    place of the mean, or a missing rsqrt, fails this)."""
+    for H in [64, 100, 1536, 16384]:
+        x = gen.normal_bf16((16, H), 2, 1, std=3.0)
+        r = gen.normal_bf16((16, H), 2, 2)
+        w = np.full(H, oracle.bf16_from_f64(1.0), np.uint16)
+        out, res_out, _ = _norm(x, r, w, 1e-6)
+        t = f32_of(out).astype(np.float64)
+        rms = np.sqrt((t ** 2).mean(axis=1))
+        assert np.all(np.abs(rms - 1) < 1e-3), (H, rms)
+        # w = 0 gives zeros
+        out0, _, _ = _norm(x, r, np.zeros(H, np.uint16), 1e-6)
+        assert np.all(f32_of(out0) == 0)
+
+
+def test_rmsnorm_matches_torch_eager_eight_ops():
+    """torch CPU eager, the eight operations as the pages list them, on the
+    residual sum.  torch sums in its own order, so the only differences
+    allowed are at rounding knife-edges, inside the admissible window."""
+    T, H, eps = 256, 1536, 1e-6
+    x = gen.normal_bf16((T, H), 9, 1)
+    res = gen.normal_bf16((T, H), 9, 2)
+    w = gen.normal_bf16((H,), 9, 3, mean=1.0, std=0.1)
+    out, res_out, rs = _norm(x, res, w, eps)
+    hs = bf16_t(res_out)
+    h = hs.to(torch.float32)                                  # cast to float
+    var = h.pow(2).mean(-1, keepdim=True)                     # square, mean
+    hn = h * torch.rsqrt(var + eps)                           # add eps, rsqrt, multiply
+    ref = bits_of(bf16_t(w) * hn.to(torch.bfloat16))          # cast back, weight
+    diff = np.flatnonzero(ref.reshape(-1) != out.reshape(-1))
+    assert len(diff) < 0.005 * out.size
+    _, rs_exact = oracle.rms_scale(res_out, eps)
+    lo, hi = oracle.rms_window(rs_exact, 2.0 ** -18)
+    alt_lo = oracle.rmsnorm_apply(res_out, w, lo).reshape(-1)
+    alt_hi = oracle.rmsnorm_apply(res_out, w, hi).reshape(-1)
+    r = ref.reshape(-1)
+    assert np.all((r[diff] == alt_lo[diff]) | (r[diff] == alt_hi[diff]))
+    # the rounding points: rounding t before the weight (the pages' order)
+    # differs from a single rounding of w*h*rs on a sizeable fraction
+    one_round = bits_of((bf16_t(w).float() * hn).to(torch.bfloat16))
+    assert (one_round != out).mean() > 0.05
+
+
+def test_rms_scale_brute_force_exact():
+    """Tiny rows: mean by exact rationals, rsqrt to 60 digits, each rounded to
+    binary32 by nearest-value search."""
+    rng = np.random.default_rng(1)
+    for H in [1, 2, 3, 5, 8]:
+        for _ in range(40):
+            r = gen.bf16_bits_from_f32((rng.standard_normal((1, H)) * np.exp2(rng.integers(-20, 20))).astype(np.float32))
+            eps = float(np.float32([0.0, 1e-6, 1e-5, 0.25][rng.integers(4)]))
+            rs, _ = oracle.rms_scale(r, eps)
+            hs = [Fraction(float(v)) for v in f32_of(r[0])]
+            m = exact.round_to_f32(sum(h * h for h in hs) / H)
+            v = np.float32(np.float32(m) + np.float32(eps))
+            if v == 0:
+                continue
+            want = exact.round_to_f32(exact.rsqrt_exact(Fraction(float(v))))
+            assert rs[0] == np.float32(want), (H, r, eps)
+
+
+# ------------------------------------------------------------------ SiLU
+
+@pytest.fixture(scope="module")
+def silu_table():
+    return oracle.silu_table()
+
+
+def test_silu_table_exhaustive_vs_60_digit(silu_table):
+    """All 65,536 gates: the oracle's bf16(silu(g)) equals the correctly
+    rounded value of silu computed to 60 digits.  Also checks that no gate's
+    exact silu lies close enough to a bf16 midpoint for the oracle's binary64
+    evaluation to matter (distance > 2^-40 relative) where the oracle uses it
+    (|g| >= 2^-24; below that the value is g/2 up to a tie-breaking term).
+
+    Outside [-200, 100] the exact value needs no evaluation: for g > 100,
+    silu(g) = g(1 - d) with 0 < d < e^-100, which rounds to g; for g < -200,
+    -e^-199 < silu(g) < 0, below half the smallest bf16 subnormal: -0."""
+    closest = Fraction(1)
+    for g in FINITE_BF16:
+        gv = exact.bf16_value(int(g))
+        if gv == 0:
+            assert silu_table[g] == g  # silu(+-0) = +-0
+            continue
+        if gv > 100:
+            assert silu_table[g] == g
+            continue
+        if gv < -200:
+            assert silu_table[g] == 0x8000
+            continue
+        s = exact.silu_exact(gv)
+        want = exact.round_to_bf16(s)
+        assert silu_table[g] == want, hex(g)
+        if abs(gv) < 2.0 ** -24 or abs(s) < Fraction(1, 2 ** 120):
+            continue
+        # relative distance of the exact value to the nearest bf16 midpoint
+        v = Fraction(exact.bf16_value(want & 0x7FFF))
+        nb = exact.bf16_value((want & 0x7FFF) + 1) if abs(s) >= v else exact.bf16_value((want & 0x7FFF) - 1)
+        mid = (v + Fraction(nb)) / 2
+        closest = min(closest, abs(abs(s) - mid) / abs(s))
+    assert closest > Fraction(1, 2 ** 40), float(closest)
+
+
+def test_silu_special_values(silu_table):
+    assert silu_table[0x0000] == 0x0000 and silu_table[0x8000] == 0x8000
+    assert silu_table[0x7F80] == 0x7F80              # +inf
+    assert silu_table[0xFF80] == 0x8000              # -inf -> -0
+    assert np.isnan(f32_of(silu_table[0x7FC0]))
+    g = f32_of(ALL_BF16)
+    big = np.isfinite(g) & (g >= 8)
+    assert np.array_equal(silu_table[big], ALL_BF16[big])   # silu(g) rounds to g
+    # silu(-g) = silu(g) - g: check on the exact values for a sample
+    for gb in [0x3F80, 0x4000, 0x3E00, 0x40A0, 0x3C00]:
+        gv = exact.bf16_value(gb)
+        assert abs(exact.silu_exact(-gv) - (exact.silu_exact(gv) - Fraction(gv))) < Fraction(1, 10 ** 50)
+
+
+def test_silu_vs_torch_differs_only_where_float_cannot_see(silu_table):
+    """torch CPU F.silu on bf16 (binary32 math, one rounding) agrees with the
+    oracle on every gate except two known classes, where the 60-digit pin
+    above shows the oracle is the correctly rounded one:
+      * |g| < 2^-24: binary32 returns g/2 exactly, an exact tie for odd
+        subnormal results, and ties-to-even ignores the g^2/4 term;
+      * g < -88: binary32 exp(-g) overflows and the quotient becomes -0,
+        while the exact value is a bf16 subnormal.
+    Any other difference must sit at a knife-edge (within 2^-18 relative of a
+    bf16 midpoint)."""
+    g = bf16_t(FINITE_BF16)
+    ref = bits_of(F.silu(g))
+    got = silu_table[FINITE_BF16]
+    gv = f32_of(FINITE_BF16)
+    bad = np.flatnonzero(ref != got)
+    tiny = np.abs(gv[bad]) < 2.0 ** -24
+    overflow = gv[bad] < -88
+    assert 0 < tiny.sum() <= 254 and 0 < overflow.sum() <= 20
+    for i in bad[tiny]:
+        # torch's value is the even neighbour of the tie at g/2
+        assert ref[i] == oracle.bf16_from_f64(float(gv[i]) / 2)
+    assert np.all(f32_of(ref[bad[overflow]]) == 0)
+    for i in bad[~tiny & ~overflow]:
+        s = exact.silu_exact(float(gv[i]))
+        a, b = Fraction(exact.bf16_value(int(got[i]))), Fraction(exact.bf16_value(int(ref[i])))
+        assert abs(s - (a + b) / 2) / abs(s) < Fraction(1, 2 ** 18), hex(FINITE_BF16[i])
+
+
+# ------------------------------------------------------------------ SwiGLU
+
+def test_swiglu_layout_and_product():
+    """gate is the first half of each row, up the second; y = bf16(a * u)
+    with a = bf16(silu(gate)): compared with torch's bf16 multiply of the
+    table value and up."""
+    tab = oracle.silu_table()
+    gu = gen.normal_bf16((64, 2 * 320), 4, 4, std=3.0)
+    y = oracle.swiglu(gu)
+    g, u = gu[:, :320], gu[:, 320:]
+    ref = bits_of(bf16_t(tab[g]) * bf16_t(u))
+    assert np.array_equal(y, ref)
+    swapped = bits_of(bf16_t(tab[u]) * bf16_t(g))
+    assert (swapped != y).mean() > 0.5
+
+
+def test_swiglu_product_special_cases():
+    tab = oracle.silu_table()
+    n = FINITE_BF16.size
+    one = np.full(n, oracle.bf16_from_f64(1.0), np.uint16)
+    gu = np.concatenate([FINITE_BF16, one])[None, :]
+    assert np.array_equal(oracle.swiglu(gu)[0], tab[FINITE_BF16])
+    zero = np.zeros(n, np.uint16)
+    y0 = oracle.swiglu(np.concatenate([FINITE_BF16, zero])[None, :])[0]
+    assert np.all(f32_of(y0[np.isfinite(f32_of(tab[FINITE_BF16]))]) == 0)
+    four = np.full(n, oracle.bf16_from_f64(4.0), np.uint16)
+    y4 = oracle.swiglu(np.concatenate([FINITE_BF16, four])[None, :])[0]
+    a = f32_of(tab[FINITE_BF16])
+    ok = np.isfinite(a) & (np.abs(a) < 1e37) & ((np.abs(a) > 1e-37) | (a == 0))
+    with np.errstate(over="ignore"):
+        assert np.array_equal(f32_of(y4)[ok], (a * 4)[ok])
+
+
+# ------------------------------------------------------------------ FP8
+
+@pytest.mark.parametrize("scale", [0.05, 1.0, 0.1, 3.0e-3, 17.5])
+def test_static_quant_exhaustive_vs_torch(scale):
+    """Every bf16 y: oracle == torch clamp(y.float() / scale).to(e4m3fn)."""
+    y = ALL_BF16
+    q = oracle.quant_fp8_static(y, scale)
+    yf = torch.from_numpy(oracle.bf16_to_f32(y).copy())
+    z = torch.clamp(yf / torch.tensor(scale, dtype=torch.float32), -448.0, 448.0)
+    ref = z.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    nan = np.isnan(oracle.bf16_to_f32(y))
+    assert np.array_equal(q[~nan], ref[~nan])
+    assert np.all(np.isin(q[nan], [0x7F, 0xFF]))
+
+
+def test_static_quant_saturation_and_ties():
+    y = FINITE_BF16
+    yf = f32_of(y)
+    q = oracle.quant_fp8_static(y, 0.05)
+    assert np.all(q[yf >= 22.4] == 0x7E) and np.all(q[yf <= -22.4] == 0xFE)
+    inf = np.array([0x7F80, 0xFF80], np.uint16)
+    assert list(oracle.quant_fp8_static(inf, 0.05)) == [0x7E, 0xFE]
+    # exact ties: y / 0.05 in binary32 lands on an E4M3 midpoint; the result
+    # must be the even code (checked with exact rationals)
+    with np.errstate(over="ignore"):
+        z = (yf / np.float32(0.05)).astype(np.float32)
+    grid = np.array(sorted(set(oracle.e4m3_table()[:0x7F])))
+    mids = (grid[1:] + grid[:-1]) / 2
+    ties = np.flatnonzero(np.isin(np.abs(z.astype(np.float64)), mids))
+    assert len(ties) > 10
+    for i in ties:
+        assert q[i] == exact.round_to_e4m3(Fraction(float(z[i])))
+        assert q[i] % 2 == 0
+
+
+def test_per_row_quant_invariants():
+    y = gen.normal_bf16((64, 4096), 6, 1, outlier_frac=0.001)
+    y[3] = 0                                    # all-zero row
+    y[4] = oracle.bf16_from_f64(1e-3)           # tiny row with one outlier
+    y[4, 17] = oracle.bf16_from_f64(37.5)
+    q, s = oracle.quant_fp8_per_row(y)
+    dec = oracle.e4m3_table()
+    qa = np.abs(dec[q])
+    amax = np.abs(f32_of(y)).max(axis=1)
+    for i in range(64):
+        if i == 3:
+            assert s[i] == 0 and np.all(qa[i] == 0)
+            continue
+        assert qa[i].max() == 448.0                  # max |q| = 448 exactly
+        assert s[i] == np.float32(amax[i]) / np.float32(448)
+        assert abs(float(s[i]) * 448 - amax[i]) <= np.spacing(np.float32(amax[i]))
+    assert q[4, 17] == 0x7E
+    # torch: s = amax / 448, q = clamp(y / s).to(e4m3fn)
+    yt = torch.from_numpy(f32_of(y).copy())
+    st = yt.abs().amax(dim=1, keepdim=True) / 448.0
+    z = torch.where(st == 0, yt, yt / torch.where(st == 0, torch.ones_like(st), st))
+    ref = torch.clamp(z, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+    assert np.array_equal(s, st.squeeze(1).numpy())
+
+
+def test_norm_quant_is_composition():
+    x = gen.normal_bf16((32, 2048), 8, 1, outlier_frac=0.001)
+    r = gen.normal_bf16((32, 2048), 8, 2, outlier_frac=0.001)
+    w = gen.normal_bf16((2048,), 8, 3, mean=1.0, std=0.1)
+    q, s, res_out, y, rs = oracle.fused_add_rmsnorm_quant_fp8(x, r, w, 1e-5)
+    out, res_out2, _ = _norm(x, r, w, 1e-5)
+    q2, s2 = oracle.quant_fp8_per_row(out)
+    assert np.array_equal(y, out) and np.array_equal(res_out, res_out2)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+# ------------------------------------------------------------------ the pages' shapes
+
+def test_golden_workload_shapes_from_pages():
+    """Shapes and byte counts the first page prints, against the workloads."""
+    with open(os.path.join(GOLDEN, "pages_workloads.json")) as f:
+        gold = json.load(f)
+    from workloads import configs as C
+    q = gold["qwen2.5-1.5b"]
+    assert C.NORM_PREFILL4096.hidden == q["hidden"]
+    assert C.SWIGLU_PREFILL4096.inter == q["intermediate"]
+    assert C.DECODE_GRAPH.layers == q["layers"]
+    tune = gold["rmsnorm_tuning"]
+    # "every version moves the same 25 MB" at 4,096 rows of 1,536 fp16:
+    # one read and one write of the rows
+    moved = tune["rows"][-1] * tune["hidden"] * 2 * 2
+    assert round(moved / 1e6) == tune["megabytes_moved_at_4096_rows"]
+    prefill = gold["prefill_intermediate"]
+    assert prefill["rows"] * prefill["cols"] == 2048 * C.SWIGLU_PREFILL4096.inter
