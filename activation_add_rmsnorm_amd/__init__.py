@@ -1,0 +1,222 @@
+"""Python binding of libaarms.so: fused residual-add + RMSNorm, SwiGLU and
+their FP8 (E4M3) epilogues on MI355X (gfx950).
+
+Argument marshalling only.  Every step of every op runs in the HIP kernels of
+libaarms.so (see include/aarms.h for the arithmetic, layouts and errors);
+PyTorch supplies device memory and the current stream.  There is no CPU or
+PyTorch fallback: if the library cannot be loaded or built, every call raises.
+
+bf16 tensors are ``torch.bfloat16``; FP8 tensors are ``torch.float8_e4m3fn``
+(OCP E4M3FN) or ``torch.uint8`` holding the same codes.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "AarmsError", "load", "lib_path",
+    "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "swiglu", "swiglu_quant_fp8",
+    "variant_count", "variant_name", "pick_variant",
+    "OP_NORM", "OP_SWIGLU",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libaarms.so")
+_LOCK = threading.Lock()
+_LIB = None
+
+OP_NORM = 0
+OP_SWIGLU = 1
+FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+class AarmsError(RuntimeError):
+    """A libaarms entry point returned an error code."""
+
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s (status %d)" % (what, _status_string(status), status))
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libaarms.so, building it with hipcc first if it is not there."""
+    global _LIB
+    with _LOCK:
+        if _LIB is not None:
+            return _LIB
+        if not os.path.exists(_LIB_PATH):
+            from . import _build
+            _build.build()
+        lib = C.CDLL(_LIB_PATH)
+        vp, i64, f32, i32 = C.c_void_p, C.c_int64, C.c_float, C.c_int
+        sigs = {
+            "fused_add_rmsnorm": [vp, vp, vp, vp, vp, i64, i64, f32, vp],
+            "fused_add_rmsnorm_ex": [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "fused_add_rmsnorm_quant_fp8": [vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
+            "fused_add_rmsnorm_quant_fp8_ex": [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "swiglu": [vp, vp, i64, i64, vp],
+            "swiglu_ex": [vp, vp, i64, i64, i32, vp],
+            "swiglu_quant_fp8": [vp, vp, vp, i64, i64, vp],
+            "swiglu_quant_fp8_ex": [vp, vp, vp, i64, i64, i32, vp],
+            "aarms_variant_count": [i32],
+            "aarms_pick_variant": [i32, i64, i64],
+        }
+        for name, args in sigs.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = C.c_int
+        lib.aarms_status_string.argtypes = [C.c_int]
+        lib.aarms_status_string.restype = C.c_char_p
+        lib.aarms_variant_name.argtypes = [C.c_int, C.c_int]
+        lib.aarms_variant_name.restype = C.c_char_p
+        _LIB = lib
+        return lib
+
+
+def _status_string(status: int) -> str:
+    s = load().aarms_status_string(int(status))
+    return s.decode() if s else "?"
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise AarmsError(status, what)
+
+
+def _require(t: torch.Tensor, name: str, dtypes, shape) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU (got %s); there is no CPU path" % (name, t.device))
+    if t.dtype not in dtypes:
+        raise TypeError("%s must have dtype %s, got %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _same_device(*ts: torch.Tensor) -> None:
+    d = ts[0].device
+    for t in ts[1:]:
+        if t.device != d:
+            raise ValueError("all tensors must be on the same device")
+
+
+def fused_add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor, eps: float,
+                      out: torch.Tensor | None = None, residual_out: torch.Tensor | None = None,
+                      variant: int = -1):
+    """Residual add + RMSNorm in one kernel.  Returns (out, residual_out).
+
+    x, residual: bf16 [T, H]; weight: bf16 [H].  out=x and/or
+    residual_out=residual run in place."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(residual, "residual", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    if out is None:
+        out = torch.empty_like(x)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _require(out, "out", (torch.bfloat16,), (T, H))
+    _require(residual_out, "residual_out", (torch.bfloat16,), (T, H))
+    _same_device(x, residual, weight, out, residual_out)
+    lib = load()
+    _check(lib.fused_add_rmsnorm_ex(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
+                                    residual.data_ptr(), weight.data_ptr(), T, H, float(eps),
+                                    int(variant), _stream(x.device)), "fused_add_rmsnorm")
+    return out, residual_out
+
+
+def fused_add_rmsnorm_quant_fp8(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor,
+                                eps: float, out: torch.Tensor | None = None,
+                                scale_out: torch.Tensor | None = None,
+                                residual_out: torch.Tensor | None = None, variant: int = -1):
+    """fused_add_rmsnorm with a dynamic per-token E4M3 epilogue.
+    Returns (q [T, H] fp8, scale [T] fp32, residual_out [T, H] bf16)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(residual, "residual", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((T,), dtype=torch.float32, device=x.device)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _require(out, "out", FP8_DTYPES, (T, H))
+    _require(scale_out, "scale_out", (torch.float32,), (T,))
+    _require(residual_out, "residual_out", (torch.bfloat16,), (T, H))
+    _same_device(x, residual, weight, out, scale_out, residual_out)
+    lib = load()
+    _check(lib.fused_add_rmsnorm_quant_fp8_ex(out.data_ptr(), scale_out.data_ptr(),
+                                              residual_out.data_ptr(), x.data_ptr(),
+                                              residual.data_ptr(), weight.data_ptr(), T, H,
+                                              float(eps), int(variant), _stream(x.device)),
+           "fused_add_rmsnorm_quant_fp8")
+    return out, scale_out, residual_out
+
+
+def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None, variant: int = -1):
+    """silu(gate) * up with gate_up = [gate | up] of shape [T, 2N]; returns bf16 [T, N]."""
+    if gate_up.dim() != 2 or gate_up.shape[1] % 2:
+        raise ValueError("gate_up must be [tokens, 2 * inter]")
+    T, N = gate_up.shape[0], gate_up.shape[1] // 2
+    _require(gate_up, "gate_up", (torch.bfloat16,), (T, 2 * N))
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=gate_up.device)
+    _require(out, "out", (torch.bfloat16,), (T, N))
+    _same_device(gate_up, out)
+    lib = load()
+    _check(lib.swiglu_ex(out.data_ptr(), gate_up.data_ptr(), T, N, int(variant),
+                         _stream(gate_up.device)), "swiglu")
+    return out
+
+
+def swiglu_quant_fp8(gate_up: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None,
+                     variant: int = -1):
+    """swiglu with a static per-tensor E4M3 epilogue; scale is a 1-element
+    fp32 GPU tensor read by the kernel.  Returns fp8 [T, N]."""
+    if gate_up.dim() != 2 or gate_up.shape[1] % 2:
+        raise ValueError("gate_up must be [tokens, 2 * inter]")
+    T, N = gate_up.shape[0], gate_up.shape[1] // 2
+    _require(gate_up, "gate_up", (torch.bfloat16,), (T, 2 * N))
+    _require(scale, "scale", (torch.float32,), (1,))
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float8_e4m3fn, device=gate_up.device)
+    _require(out, "out", FP8_DTYPES, (T, N))
+    _same_device(gate_up, scale, out)
+    lib = load()
+    _check(lib.swiglu_quant_fp8_ex(out.data_ptr(), gate_up.data_ptr(), scale.data_ptr(), T, N,
+                                   int(variant), _stream(gate_up.device)), "swiglu_quant_fp8")
+    return out
+
+
+def variant_count(op: int) -> int:
+    return int(load().aarms_variant_count(int(op)))
+
+
+def variant_name(op: int, variant: int) -> str | None:
+    s = load().aarms_variant_name(int(op), int(variant))
+    return s.decode() if s else None
+
+
+def pick_variant(op: int, tokens: int, width: int) -> int:
+    return int(load().aarms_pick_variant(int(op), int(tokens), int(width)))

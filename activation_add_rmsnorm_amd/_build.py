@@ -1,0 +1,85 @@
+"""Build libaarms.so in-tree with hipcc for gfx950.
+
+Flags:
+  -ffp-contract=off    no implicit fused multiply-add: every fma in the kernels
+                       is written out, so the rounding points are the ones in
+                       the source;
+  -fhip-fp32-correctly-rounded-divide-sqrt
+                       IEEE binary32 division (per-row scale and reciprocal);
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                       no packed binary32 instructions.
+No fast-math, no denormal flushing (binary32 and binary64 denormals are kept).
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG, "libaarms.so")
+ARCH = os.environ.get("AARMS_OFFLOAD_ARCH", "gfx950")
+
+HIP_SOURCES = ["norm.hip", "swiglu.hip"]
+HOST_SOURCES = ["capi.cpp"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+          "-ffp-contract=off", "-I", INCLUDE, "-I", CSRC]
+DEVICE = ["-x", "hip", "--offload-arch=" + ARCH, "-fhip-fp32-correctly-rounded-divide-sqrt",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if c and (os.path.isabs(c) and os.path.exists(c) or not os.path.isabs(c)):
+            return c
+    return "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libaarms.so; returns its path."""
+    hipcc = _hipcc()
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    jobs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        jobs.append([hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        jobs.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    procs = []
+    for cmd in jobs:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    failed = False
+    for cmd, pr in procs:
+        out, _ = pr.communicate()
+        text = out.decode(errors="replace")
+        # hipcc's host pass does not know the packed-fp32 feature; that warning is expected
+        text = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l
+                         and "is not a recognized feature" not in l)
+        if text.strip():
+            print(text, file=sys.stderr)
+        if pr.returncode != 0:
+            failed = True
+            print("FAILED: " + " ".join(cmd), file=sys.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed")
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    link = [hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs]
+    subprocess.run(link, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

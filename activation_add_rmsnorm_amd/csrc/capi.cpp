@@ -1,0 +1,289 @@
+// capi.cpp -- the extern "C" entry points of libaarms.so (include/aarms.h):
+// argument validation, variant choice and kernel launch.  Validation runs
+// entirely on the host before any HIP call, so every error path can be
+// exercised without a GPU.
+
+#include "aarms.h"
+#include "launch.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+using namespace aarms;
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void *p, uint64_t bytes) { return {(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Row-width checks shared by all ops.
+int check_width(int64_t tokens, int64_t width, int64_t max_width)
+{
+    if (tokens < 0 || width <= 0 || width % 8 != 0) return AARMS_ERR_BAD_SHAPE;
+    if (max_width > 0 && width > max_width) return AARMS_ERR_UNSUPPORTED_SHAPE;
+    if (tokens > 0 && width > AARMS_MAX_ELEMENTS / tokens) return AARMS_ERR_UNSUPPORTED_SHAPE;
+    if (tokens > INT32_MAX) return AARMS_ERR_UNSUPPORTED_SHAPE;
+    return AARMS_OK;
+}
+
+int check_eps(float eps)
+{
+    return (std::isfinite(eps) && eps >= 0.0f) ? AARMS_OK : AARMS_ERR_BAD_EPS;
+}
+
+// An output must not overlap any other argument, except when it is exactly
+// the named in-place partner.
+struct Arg {
+    Range r;
+    const void *ptr;
+};
+
+int check_outputs(const Arg *outs, const int *partner, int n_out, const Arg *ins, int n_in)
+{
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_out; ++j)
+            if (i != j && overlap(outs[i].r, outs[j].r)) return AARMS_ERR_ALIAS;
+        for (int j = 0; j < n_in; ++j) {
+            if (!overlap(outs[i].r, ins[j].r)) continue;
+            const bool in_place = partner[i] == j && outs[i].ptr == ins[j].ptr &&
+                                  outs[i].r.hi == ins[j].r.hi;
+            if (!in_place) return AARMS_ERR_ALIAS;
+        }
+    }
+    return AARMS_OK;
+}
+
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int norm_capacity(const NormVariant *v) { return v->waves_per_row * 64 * v->vecs_per_lane * 8; }
+
+int pick_norm(int64_t tokens, int64_t hidden)
+{
+    (void)tokens;
+    if (hidden <= 0 || hidden > AARMS_MAX_HIDDEN) return -1;
+    // Narrow rows: one wave per row with as few vectors per lane as fit.
+    // Wide rows: the fewest waves per row that fit with 8 vectors per lane
+    // (4, 8 or 16 waves), so that a row's reduction crosses few waves.
+    const int n = norm_variant_count();
+    if (hidden <= 4096) {
+        for (int i = 0; i < n; ++i) {
+            const NormVariant *v = norm_variant(i);
+            if (v->waves_per_row == 1 && norm_capacity(v) >= hidden) return i;
+        }
+    }
+    for (int w : {2, 4, 8, 16}) {
+        int best = -1;
+        for (int i = 0; i < n; ++i) {
+            const NormVariant *v = norm_variant(i);
+            if (v->waves_per_row != w || norm_capacity(v) < hidden) continue;
+            if (best < 0 || v->vecs_per_lane < norm_variant(best)->vecs_per_lane) best = i;
+        }
+        if (best >= 0) return best;
+    }
+    return -1;
+}
+
+int pick_swiglu(int64_t tokens, int64_t inter)
+{
+    (void)tokens;
+    (void)inter;
+    return 1;  // 2 jobs per lane, one block per 512 jobs
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? AARMS_OK : AARMS_ERR_HIP; }
+
+int norm_common(void *out, float *scale_out, void *residual_out, const void *x,
+                const void *residual, const void *weight, int64_t tokens, int64_t hidden,
+                float eps, bool quant, int variant, hipStream_t stream)
+{
+    int st = check_width(tokens, hidden, AARMS_MAX_HIDDEN);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    if (variant < -1 || variant >= norm_variant_count()) return AARMS_ERR_BAD_VARIANT;
+    if (tokens == 0) return AARMS_OK;
+    if (!out || !residual_out || !x || !residual || !weight || (quant && !scale_out))
+        return AARMS_ERR_NULL_POINTER;
+    if (!aligned(out, 16) || !aligned(residual_out, 16) || !aligned(x, 16) ||
+        !aligned(residual, 16) || !aligned(weight, 16) || (quant && !aligned(scale_out, 4)))
+        return AARMS_ERR_MISALIGNED;
+    const uint64_t elems = (uint64_t)tokens * (uint64_t)hidden;
+    const Arg ins[3] = {{span(x, 2 * elems), x},
+                        {span(residual, 2 * elems), residual},
+                        {span(weight, 2 * (uint64_t)hidden), weight}};
+    if (!quant) {
+        const Arg outs[2] = {{span(out, 2 * elems), out}, {span(residual_out, 2 * elems), residual_out}};
+        const int partner[2] = {0, 1};  // out == x, residual_out == residual
+        if ((st = check_outputs(outs, partner, 2, ins, 3))) return st;
+    } else {
+        const Arg outs[3] = {{span(out, elems), out},
+                             {span(residual_out, 2 * elems), residual_out},
+                             {span(scale_out, 4 * (uint64_t)tokens), scale_out}};
+        const int partner[3] = {-1, 1, -1};  // residual_out == residual only
+        if ((st = check_outputs(outs, partner, 3, ins, 3))) return st;
+    }
+    if (variant == -1) variant = pick_norm(tokens, hidden);
+    const NormVariant *v = norm_variant(variant);
+    if (!v || norm_capacity(v) < hidden) return AARMS_ERR_BAD_VARIANT;
+    NormParams p;
+    p.out = out;
+    p.residual_out = residual_out;
+    p.x = x;
+    p.residual = residual;
+    p.weight = weight;
+    p.scale_out = scale_out;
+    p.tokens = tokens;
+    p.hidden = (int32_t)hidden;
+    p.eps = eps;
+    return launch_status(launch_norm(p, quant, variant, stream));
+}
+
+int swiglu_common(void *out, const void *gate_up, const float *scale, int64_t tokens,
+                  int64_t inter, bool quant, int variant, hipStream_t stream)
+{
+    int st = check_width(tokens, inter, 0);
+    if (st) return st;
+    if (tokens > 0 && 2 * inter > AARMS_MAX_ELEMENTS / tokens) return AARMS_ERR_UNSUPPORTED_SHAPE;
+    if (variant < -1 || variant >= swiglu_variant_count()) return AARMS_ERR_BAD_VARIANT;
+    if (tokens == 0) return AARMS_OK;
+    if (!out || !gate_up || (quant && !scale)) return AARMS_ERR_NULL_POINTER;
+    if (!aligned(out, 16) || !aligned(gate_up, 16) || (quant && !aligned(scale, 4)))
+        return AARMS_ERR_MISALIGNED;
+    const uint64_t elems = (uint64_t)tokens * (uint64_t)inter;
+    const Arg outs[1] = {{span(out, quant ? elems : 2 * elems), out}};
+    const Arg ins[2] = {{span(gate_up, 4 * elems), gate_up}, {span(scale, quant ? 4 : 0), scale}};
+    const int partner[1] = {-1};
+    if ((st = check_outputs(outs, partner, 1, ins, quant ? 2 : 1))) return st;
+    if (variant == -1) variant = pick_swiglu(tokens, inter);
+    SwigluParams p;
+    p.out = out;
+    p.gate_up = gate_up;
+    p.scale = scale;
+    p.vecs_per_row = (uint32_t)(inter / 8);
+    p.jobs = (uint64_t)tokens * p.vecs_per_row;
+    p.inv_vecs_per_row = 1.0 / (double)p.vecs_per_row;
+    p.inter = inter;
+    return launch_status(launch_swiglu(p, quant, variant, device_cus(), stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fused_add_rmsnorm(void *out, void *residual_out, const void *x, const void *residual,
+                      const void *weight, int64_t num_tokens, int64_t hidden, float eps,
+                      hipStream_t stream)
+{
+    return norm_common(out, nullptr, residual_out, x, residual, weight, num_tokens, hidden, eps,
+                       false, -1, stream);
+}
+
+int fused_add_rmsnorm_ex(void *out, void *residual_out, const void *x, const void *residual,
+                         const void *weight, int64_t num_tokens, int64_t hidden, float eps,
+                         int variant, hipStream_t stream)
+{
+    return norm_common(out, nullptr, residual_out, x, residual, weight, num_tokens, hidden, eps,
+                       false, variant, stream);
+}
+
+int fused_add_rmsnorm_quant_fp8(void *out_fp8, float *scale_out, void *residual_out,
+                                const void *x, const void *residual, const void *weight,
+                                int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream)
+{
+    return norm_common(out_fp8, scale_out, residual_out, x, residual, weight, num_tokens, hidden,
+                       eps, true, -1, stream);
+}
+
+int fused_add_rmsnorm_quant_fp8_ex(void *out_fp8, float *scale_out, void *residual_out,
+                                   const void *x, const void *residual, const void *weight,
+                                   int64_t num_tokens, int64_t hidden, float eps, int variant,
+                                   hipStream_t stream)
+{
+    return norm_common(out_fp8, scale_out, residual_out, x, residual, weight, num_tokens, hidden,
+                       eps, true, variant, stream);
+}
+
+int swiglu(void *out, const void *gate_up, int64_t num_tokens, int64_t inter, hipStream_t stream)
+{
+    return swiglu_common(out, gate_up, nullptr, num_tokens, inter, false, -1, stream);
+}
+
+int swiglu_ex(void *out, const void *gate_up, int64_t num_tokens, int64_t inter, int variant,
+              hipStream_t stream)
+{
+    return swiglu_common(out, gate_up, nullptr, num_tokens, inter, false, variant, stream);
+}
+
+int swiglu_quant_fp8(void *out_fp8, const void *gate_up, const float *scale, int64_t num_tokens,
+                     int64_t inter, hipStream_t stream)
+{
+    return swiglu_common(out_fp8, gate_up, scale, num_tokens, inter, true, -1, stream);
+}
+
+int swiglu_quant_fp8_ex(void *out_fp8, const void *gate_up, const float *scale,
+                        int64_t num_tokens, int64_t inter, int variant, hipStream_t stream)
+{
+    return swiglu_common(out_fp8, gate_up, scale, num_tokens, inter, true, variant, stream);
+}
+
+const char *aarms_status_string(int status)
+{
+    switch (status) {
+    case AARMS_OK: return "ok";
+    case AARMS_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case AARMS_ERR_BAD_SHAPE: return "bad shape: negative size, zero width or width not a multiple of 8";
+    case AARMS_ERR_UNSUPPORTED_SHAPE: return "unsupported shape: width or element count beyond the limits";
+    case AARMS_ERR_MISALIGNED: return "misaligned pointer: tensors need 16 bytes, scales 4";
+    case AARMS_ERR_ALIAS: return "an output overlaps another argument";
+    case AARMS_ERR_BAD_EPS: return "eps must be finite and >= 0";
+    case AARMS_ERR_HIP: return "the HIP runtime refused the launch";
+    case AARMS_ERR_BAD_VARIANT: return "unknown kernel variant, or too narrow for the row";
+    default: return "unknown status";
+    }
+}
+
+int aarms_variant_count(int op)
+{
+    return op == 0 ? norm_variant_count() : op == 1 ? swiglu_variant_count() : 0;
+}
+
+const char *aarms_variant_name(int op, int variant)
+{
+    if (op == 0) {
+        const NormVariant *v = norm_variant(variant);
+        return v ? v->name : nullptr;
+    }
+    if (op == 1) {
+        const SwigluVariant *v = swiglu_variant(variant);
+        return v ? v->name : nullptr;
+    }
+    return nullptr;
+}
+
+int aarms_pick_variant(int op, int64_t num_tokens, int64_t width)
+{
+    if (op == 0) return pick_norm(num_tokens, width);
+    if (op == 1) return (width > 0 && width % 8 == 0) ? pick_swiglu(num_tokens, width) : -1;
+    return -1;
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+// device.h -- gfx950 device helpers shared by the norm and SwiGLU kernels:
+// bf16 / E4M3 packing, wave and block reductions, the SiLU evaluation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aarms {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// A 16-byte vector holds 8 bf16 values: element 2e is the low half of word
+// e, element 2e+1 the high half.  Widening bf16 -> binary32 is exact.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two binary32 -> one word of two bf16, round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    bf16x2 r = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Saturate to the E4M3 range, keeping NaN: the conversion below turns
+// anything beyond 464 into NaN, and v_med3_f32 drops a NaN operand.
+__device__ __forceinline__ float clamp_e4m3(float z)
+{
+    float c = __builtin_amdgcn_fmed3f(z, -448.0f, 448.0f);
+    return (z != z) ? z : c;
+}
+
+// Four binary32 already inside [-448, 448] (or NaN) -> four OCP E4M3 bytes,
+// round to nearest even (v_cvt_pk_fp8_f32), first value in the lowest byte.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d)
+{
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+    return (uint32_t)v;
+}
+
+// ---------------------------------------------------------------- y / scale
+//
+// q = e4m3(clamp(binary32(y / s), -448, 448)).  A scale of exactly zero is
+// treated as one.  For a scale in [2^-126, 2^118] (the usual case):
+//   - y is first clamped to +-lim, lim = binary32(448 s), with the
+//     NaN-propagating v_maximum3/v_minimum3: a NaN stays NaN, an infinity or
+//     any |y| beyond lim gives a quotient that rounds to +-448, and no
+//     quotient can overflow binary32;
+//   - the quotient is y * inv (inv = binary32(1/s)), within an ulp, plus one
+//     correction step from the exact remainder q0 s - y (one fma), which
+//     rounds it to the nearest binary32 quotient.
+// Outside that range, or for a negative scale, the IEEE division is used (a
+// uniform branch).
+struct E4m3Scale {
+    float s, inv, lim;
+};
+
+__device__ __forceinline__ E4m3Scale make_e4m3_scale(float s)
+{
+    E4m3Scale q;
+    q.s = (s == 0.0f) ? 1.0f : s;
+    q.inv = 1.0f / q.s;
+    q.lim = __builtin_fabsf(448.0f * q.s);
+    return q;
+}
+
+__device__ __forceinline__ bool e4m3_scale_is_fast(const E4m3Scale &q)
+{
+    return q.s >= 0x1p-126f && q.s <= 0x1p118f;
+}
+
+template <bool FAST>
+__device__ __forceinline__ float e4m3_quotient(float y, const E4m3Scale &q)
+{
+    if constexpr (FAST) {
+        const float yc = __builtin_elementwise_minimum(__builtin_elementwise_maximum(y, -q.lim), q.lim);
+        const float q0 = yc * q.inv;
+        // rem = q0 s - y is exact; z = q0 - rem * inv.  Written this way round
+        // (rather than y - q0 s) so that a zero quotient keeps the sign of y.
+        const float rem = __builtin_fmaf(q0, q.s, -yc);
+        return __builtin_fmaf(rem, -q.inv, q0);
+    } else {
+        return clamp_e4m3(y / q.s);
+    }
+}
+
+// Butterfly sums and maxima over the 64 lanes of a wave.  Every lane ends
+// with the same bits: each step combines the same two operands on both
+// partner lanes, and IEEE addition is commutative.
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// ---------------------------------------------------------------- SiLU
+//
+// bf16(silu(g)) must be the correctly rounded value.  The fast form below,
+// g * rcp(1 + 2^(-g*log2 e)) with the hardware exp2 and reciprocal, has a
+// relative error below 2^-19 for g >= -16 (about 31 units of binary32
+// rounding: the rounding of -g*log2 e amplified by |g|*ln 2, the exp2, the
+// add, the reciprocal and the product).  Its bf16 rounding is therefore
+// right unless the binary32 result lies within SILU_EDGE units of a bf16
+// midpoint (the low 16 bits near 0x8000), or g < -16.  Those lanes -- about
+// one element in 200 for normally distributed gates -- are recomputed by
+// silu_exact().  (Measured over all 65,536 gates on gfx950 the fast form is
+// within 14 units for g in [-16, -8) and within 4 for |g| <= 4, so the
+// window has a wide margin; its only misroundings are exact ties.)
+
+constexpr float SILU_FAST_MIN = -16.0f;
+constexpr uint32_t SILU_EDGE = 48;
+// g < -16 (or g is a negative NaN) exactly when the bit pattern of g, read
+// as unsigned, exceeds that of -16.0; integer compares cannot be upset by a
+// signalling NaN the way a floating-point minimum can.
+constexpr uint32_t SILU_FAST_MIN_BITS = 0xC1800000u;
+
+__device__ __forceinline__ float silu_fast(float g)
+{
+    float e = __builtin_amdgcn_exp2f(g * -1.44269502162933349609375f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Knife-edge key of a binary32 result s: with l = the low 16 bits of s (its
+// position between two bf16 values, 0x8000 being the rounding midpoint),
+// key = ((l + SILU_EDGE - 0x8000) mod 2^16) << 16, which is at most
+// SILU_EDGE_KEY_MAX exactly when |l - 0x8000| <= SILU_EDGE.  One
+// v_lshl_add_u32.
+constexpr uint32_t SILU_EDGE_KEY_MAX = (2u * SILU_EDGE) << 16;
+
+__device__ __forceinline__ uint32_t silu_edge_key(float s)
+{
+    return (__float_as_uint(s) << 16) + ((SILU_EDGE - 0x8000u) << 16);
+}
+
+// The binary32 neighbour of f in direction dir (+1 up, -1 down); f != 0.
+__device__ __forceinline__ float step_f32(float f, int dir)
+{
+    uint32_t b = __float_as_uint(f);
+    bool up_in_magnitude = (dir > 0) == !(b >> 31);
+    return __uint_as_float(up_in_magnitude ? b + 1u : b - 1u);
+}
+
+// Correctly rounded bf16(silu(g)), returned as a binary32 value on the bf16
+// grid (so that a later round-to-nearest-even leaves it unchanged).
+//  - |g| < 2^-24: silu(g) = g/2 + g^2/4 - ...; the binary64 value is g/2 and
+//    the positive g^2/4 decides a tie (odd subnormal results).
+//  - otherwise silu is evaluated in binary64 (error a few units of 2^-53).
+// The binary64 value x goes to binary32 first; that rounding can only change
+// the bf16 result when it lands exactly on a bf16 midpoint, and then the
+// value is stepped one binary32 unit back toward x.
+__device__ __attribute__((noinline)) float silu_exact(float g)
+{
+    if (g != g) return g;
+    if (g == -__builtin_inff()) return -0.0f;
+    double x;
+    int dir_if_exact;
+    if (__builtin_fabsf(g) < 0x1p-24f) {
+        x = 0.5 * (double)g;
+        dir_if_exact = +1;
+    } else {
+        double gd = (double)g;
+        x = gd / (1.0 + exp(-gd));
+        dir_if_exact = 0;
+    }
+    float f = (float)x;
+    if ((__float_as_uint(f) & 0xFFFFu) == 0x8000u) {
+        double back = (double)f;
+        if (x > back) f = step_f32(f, +1);
+        else if (x < back) f = step_f32(f, -1);
+        else if (dir_if_exact != 0) f = step_f32(f, dir_if_exact);
+    }
+    return f;
+}
+
+}  // namespace aarms

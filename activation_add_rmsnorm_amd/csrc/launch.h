@@ -1,0 +1,55 @@
+// launch.h -- internal interface between the C ABI (capi.cpp) and the kernel
+// translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace aarms {
+
+struct NormParams {
+    void *out;               // bf16 [T,H], or fp8 [T,H] when quantising
+    void *residual_out;      // bf16 [T,H]
+    const void *x;           // bf16 [T,H]
+    const void *residual;    // bf16 [T,H]
+    const void *weight;      // bf16 [H]
+    float *scale_out;        // fp32 [T] when quantising, else null
+    int64_t tokens;
+    int32_t hidden;
+    float eps;
+};
+
+struct SwigluParams {
+    void *out;               // bf16 [T,N], or fp8 [T,N] when quantising
+    const void *gate_up;     // bf16 [T,2N]
+    const float *scale;      // fp32 [1] when quantising, else null
+    uint64_t jobs;           // T * N / 8: one job = 8 adjacent outputs
+    uint32_t vecs_per_row;   // N / 8
+    double inv_vecs_per_row; // 1 / (N / 8), for the job -> row division
+    int64_t inter;           // N
+};
+
+// Norm variants: (waves per row, 16-byte vectors per lane).  A row of H
+// elements needs waves * 64 * vectors * 8 >= H.
+struct NormVariant {
+    int waves_per_row;
+    int vecs_per_lane;
+    const char *name;
+};
+
+struct SwigluVariant {
+    int jobs_per_lane;       // jobs in flight per lane and loop trip
+    int blocks_per_cu;       // 0: one block per 256*jobs_per_lane jobs; else a grid-stride grid
+    const char *name;
+};
+
+int norm_variant_count();
+const NormVariant *norm_variant(int id);
+int swiglu_variant_count();
+const SwigluVariant *swiglu_variant(int id);
+
+hipError_t launch_norm(const NormParams &p, bool quant, int variant, hipStream_t stream);
+hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, int num_cus,
+                         hipStream_t stream);
+
+}  // namespace aarms

@@ -1,0 +1,398 @@
+#!/usr/bin/env python3
+"""Throughput of the fused add-RMSNorm + SwiGLU(+FP8) kernels on one MI355X.
+
+One step = one pass of the Qwen2.5-1.5B-shaped prefill layer's memory-bound
+ops over 4,096 tokens: fused_add_rmsnorm on bf16 [4096, 1536] followed by
+swiglu on bf16 gate_up [4096, 17920] -> [4096, 8960].  ``value`` is the
+effective HBM bandwidth of the step: the algorithmic bytes (every input read
+once, every output written once, the weight once) divided by the wall time of
+K back-to-back steps with the inputs already resident in HBM.  Three buffer
+sets are rotated so that every step reads HBM rather than the 256 MB
+last-level cache.
+
+The same run also measures, as supplementary figures, the static-FP8 SwiGLU
+on Llama-70B's [8192, 57344] gate_up, the dynamic-FP8 norm on Llama-405B's
+[2048, 16384] rows, the 16-token norm, and the 28-layer decode chain under a
+HIP graph; and it times the CPU oracle on the host's cores on the headline
+workload (a baseline, not a target).
+
+Prints exactly one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s (10^9 B/s)
+METRIC = "effective HBM GB/s and % of MI355X peak, fused add-RMSNorm + SwiGLU(+fp8)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- bytes
+
+def norm_bytes(T, H, quant=False):
+    """x, residual read; residual_out written; out written (bf16 or fp8);
+    weight read once; per-token scales written."""
+    io = T * H * 2 * 3 + (T * H * (1 if quant else 2))
+    return io + H * 2 + (T * 4 if quant else 0)
+
+
+def swiglu_bytes(T, N, quant=False):
+    return T * 2 * N * 2 + T * N * (1 if quant else 2) + (4 if quant else 0)
+
+
+# ----------------------------------------------------------------- timing
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+
+    def region(self, fn, reps):
+        t = self.torch
+        t.cuda.synchronize()
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(i)
+        b.record()
+        t.cuda.synchronize()
+        return a.elapsed_time(b) / reps  # ms per rep
+
+
+def traffic_from_profiles(kernel_key: str, src_hash: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*counters*.md")):
+        txt = open(path).read()
+        if ("kernel_sources_sha256: " + src_hash) not in txt:
+            continue
+        for line in txt.splitlines():
+            if line.startswith("traffic_bytes_per_launch[" + kernel_key + "]:"):
+                return float(line.split(":", 1)[1].split()[0])
+    return None
+
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "activation_add_rmsnorm_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the kernels are row-independent and this build "
+              "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import activation_add_rmsnorm_amd as A
+    from workloads import configs as W
+
+    lib = A.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    timer = Timer(torch)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ------------------------------------------------------------ headline
+    wn, ws = W.NORM_PREFILL4096, W.SWIGLU_PREFILL4096
+    T, H, N = wn.tokens, wn.hidden, ws.inter
+    nd = W.norm_inputs(wn)
+    gd = W.swiglu_inputs(ws)
+    x0, r0, w0, gu0 = to_dev(nd["x"]), to_dev(nd["residual"]), to_dev(nd["weight"]), to_dev(gd["gate_up"])
+    step_bytes_norm = norm_bytes(T, H)
+    step_bytes_swiglu = swiglu_bytes(T, N)
+    step_bytes = step_bytes_norm + step_bytes_swiglu
+    n_sets = max(2, int(np.ceil(2 * 256e6 / step_bytes)) + 0)
+    sets = []
+    for _ in range(n_sets):
+        s = dict(x=x0.clone(), r=r0.clone(), w=w0.clone(), gu=gu0.clone(),
+                 out=torch.empty_like(x0), ro=torch.empty_like(r0),
+                 y=torch.empty((T, N), dtype=torch.bfloat16, device=dev))
+        s["p_norm"] = (s["out"].data_ptr(), s["ro"].data_ptr(), s["x"].data_ptr(), s["r"].data_ptr(),
+                       s["w"].data_ptr())
+        s["p_sw"] = (s["y"].data_ptr(), s["gu"].data_ptr())
+        sets.append(s)
+    eps = wn.eps
+
+    def norm_call(s):
+        st = lib.fused_add_rmsnorm(*s["p_norm"], T, H, eps, sp)
+        if st:
+            raise A.AarmsError(st, "fused_add_rmsnorm")
+
+    def swiglu_call(s):
+        st = lib.swiglu(*s["p_sw"], T, N, sp)
+        if st:
+            raise A.AarmsError(st, "swiglu")
+
+    def step(i):
+        s = sets[i % n_sets]
+        norm_call(s)
+        swiglu_call(s)
+
+    K, Wu = args.steps, args.warmup
+    for i in range(Wu):
+        step(i)
+    ms_step = timer.region(step, K)
+
+    # per-kernel durations with HIP events on the launch stream, same rotation
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        s = sets[i % n_sets]
+        ev[i][0].record()
+        norm_call(s)
+        ev[i][1].record()
+        swiglu_call(s)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    norm_us = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
+    swiglu_us = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
+
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    src_hash = kernel_sources_hash()
+    roof = {
+        "bound": "hbm",
+        "kernel": "swiglu [4096,17920]->[4096,8960]",
+        "achieved": round(step_bytes_swiglu / (swiglu_us * 1e-6) / 1e9, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+    }
+    roof["frac"] = round(roof["achieved"] / HBM_PEAK_GBS, 4)
+    roof["traffic"] = traffic_from_profiles("swiglu_qwen_prefill4096", src_hash)
+    roof["bytes_per_launch"] = step_bytes_swiglu
+    roof["avg_launch_us"] = round(swiglu_us, 2)
+
+    extra = {
+        "norm_4096x1536": {"bytes": step_bytes_norm, "avg_launch_us": round(norm_us, 2),
+                           "GB/s": round(step_bytes_norm / (norm_us * 1e-6) / 1e9, 1)},
+        "swiglu_4096x17920": {"bytes": step_bytes_swiglu, "avg_launch_us": round(swiglu_us, 2),
+                              "GB/s": roof["achieved"]},
+        "buffer_sets_rotated": n_sets,
+    }
+    for s in sets:
+        for k in list(s):
+            s[k] = None
+    del sets
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ supplementary
+    configs = {}
+    if not args.no_extra:
+        configs = supplementary(args, torch, np, A, lib, W, dev, sp, timer, to_dev)
+
+    # ------------------------------------------------------------ cpu baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, W, nd, gd, step_bytes, args.cpu_seconds)
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wu,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normals, Qwen2.5-1.5B prefill-layer shapes; no weights)",
+        "config": {
+            "workload": "qwen1.5b_prefill4096: fused_add_rmsnorm bf16 [4096,1536] eps 1e-6 + "
+                        "swiglu bf16 gate_up [4096,17920] -> [4096,8960]",
+            "bytes_per_step": step_bytes,
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": extra,
+        "configs": configs,
+        "device": torch.cuda.get_device_name(dev),
+        "kernel_sources_sha256": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def supplementary(args, torch, np, A, lib, W, dev, sp, timer, to_dev):
+    out = {}
+    reps = max(20, args.steps // 2)
+
+    # static-FP8 SwiGLU, Llama-70B MLP: [8192, 57344] -> e4m3 [8192, 28672]
+    wl = W.SWIGLU_FP8_LLAMA70B
+    T, N = wl.tokens, wl.inter
+    g = torch.Generator(device=dev).manual_seed(0)
+    gu = (torch.randn((T, 2 * N), generator=g, device=dev, dtype=torch.float32) * wl.gate_up_std).to(torch.bfloat16)
+    sets = [(gu if i == 0 else gu.clone(), torch.empty((T, N), dtype=torch.uint8, device=dev)) for i in range(2)]
+    scale = torch.tensor([wl.scale], dtype=torch.float32, device=dev)
+    ptr = [(o.data_ptr(), a.data_ptr(), scale.data_ptr()) for a, o in sets]
+
+    def call4(i):
+        st = lib.swiglu_quant_fp8(*ptr[i % 2], T, N, sp)
+        if st:
+            raise A.AarmsError(st, "swiglu_quant_fp8")
+
+    for i in range(5):
+        call4(i)
+    ms = timer.region(call4, reps)
+    b = swiglu_bytes(T, N, quant=True)
+    out["llama70b_swiglu_fp8_8192x57344"] = {"bytes": b, "avg_launch_us": round(ms * 1e3, 2),
+                                              "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                                              "pct_of_hbm_peak": round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                                              "inputs": "torch.randn on device, seed 0, std 2"}
+    del sets, gu, ptr
+    torch.cuda.empty_cache()
+
+    # dynamic-FP8 norm, Llama-405B: [2048, 16384]
+    wl = W.NORM_FP8_LLAMA405B
+    T, H = wl.tokens, wl.hidden
+    d = W.norm_inputs(wl)
+    x0, r0, w0 = to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["weight"])
+    b = norm_bytes(T, H, quant=True)
+    n_sets = int(np.ceil(2 * 256e6 / b))
+    sets = []
+    for i in range(n_sets):
+        s = dict(x=x0.clone(), r=r0.clone(), q=torch.empty((T, H), dtype=torch.uint8, device=dev),
+                 s=torch.empty((T,), dtype=torch.float32, device=dev), ro=torch.empty_like(r0))
+        s["p"] = (s["q"].data_ptr(), s["s"].data_ptr(), s["ro"].data_ptr(), s["x"].data_ptr(),
+                  s["r"].data_ptr(), w0.data_ptr())
+        sets.append(s)
+
+    def call5(i):
+        st = lib.fused_add_rmsnorm_quant_fp8(*sets[i % n_sets]["p"], T, H, wl.eps, sp)
+        if st:
+            raise A.AarmsError(st, "fused_add_rmsnorm_quant_fp8")
+
+    for i in range(5):
+        call5(i)
+    ms = timer.region(call5, reps)
+    out["llama405b_norm_fp8_2048x16384"] = {"bytes": b, "avg_launch_us": round(ms * 1e3, 2),
+                                             "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                                             "pct_of_hbm_peak": round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                                             "buffer_sets_rotated": n_sets}
+    del sets
+    torch.cuda.empty_cache()
+
+    # 16-token norm (launch-bound)
+    wl = W.NORM_DECODE16
+    d = W.norm_inputs(wl)
+    x, r, w = to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["weight"])
+    o, ro = torch.empty_like(x), torch.empty_like(r)
+    p = (o.data_ptr(), ro.data_ptr(), x.data_ptr(), r.data_ptr(), w.data_ptr())
+
+    def call1(i):
+        lib.fused_add_rmsnorm(*p, wl.tokens, wl.hidden, wl.eps, sp)
+
+    for i in range(10):
+        call1(i)
+    ms = timer.region(call1, reps)
+    out["qwen1.5b_norm_16x1536"] = {"bytes": norm_bytes(16, 1536), "avg_launch_us": round(ms * 1e3, 2)}
+
+    # decode chain under a HIP graph, per token count
+    out["qwen1.5b_decode_28layers_graph"] = decode_graph(torch, np, A, W, dev, to_dev, timer)
+    return out
+
+
+def decode_graph(torch, np, A, W, dev, to_dev, timer):
+    wl = W.DECODE_GRAPH
+    res = {}
+    for T in wl.tokens:
+        H, N, L = wl.hidden, wl.inter, wl.layers
+        host = [W.decode_layer_inputs(wl, T, l) for l in range(L)]
+        r = to_dev(W.decode_residual(wl, T))
+        bufs = []
+        for h in host:
+            bufs.append(dict(x1=to_dev(h["x1"]), x2=to_dev(h["x2"]), w1=to_dev(h["w1"]), w2=to_dev(h["w2"]),
+                             gu=to_dev(h["gate_up"]), o1=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+                             o2=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+                             y=torch.empty((T, N), dtype=torch.bfloat16, device=dev)))
+
+        def chain():
+            for b in bufs:
+                A.fused_add_rmsnorm(b["x1"], r, b["w1"], wl.eps, out=b["o1"], residual_out=r)
+                A.fused_add_rmsnorm(b["x2"], r, b["w2"], wl.eps, out=b["o2"], residual_out=r)
+                A.swiglu(b["gu"], out=b["y"])
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            chain()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            chain()
+        for _ in range(5):
+            g.replay()
+        reps = 50
+        ms_graph = timer.region(lambda i: g.replay(), reps)
+        ms_eager = timer.region(lambda i: chain(), 10)
+        byts = L * (2 * norm_bytes(T, H) + swiglu_bytes(T, N))
+        res["T=%d" % T] = {"us_per_replay": round(ms_graph * 1e3, 1),
+                           "us_per_node": round(ms_graph * 1e3 / (3 * L), 2),
+                           "us_eager_python": round(ms_eager * 1e3, 1),
+                           "bytes": byts, "GB/s": round(byts / (ms_graph * 1e-3) / 1e9, 1)}
+        del g, bufs
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(np, W, nd, gd, step_bytes, seconds):
+    """The oracle as it stands, on the headline workload, repeated for a
+    bounded time on the host's cores."""
+    import oracle
+    wl = W.NORM_PREFILL4096
+    oracle.fused_add_rmsnorm(nd["x"][:8], nd["residual"][:8], nd["weight"], wl.eps)  # warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.fused_add_rmsnorm(nd["x"], nd["residual"], nd["weight"], wl.eps)
+        oracle.swiglu(gd["gate_up"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or el > 30:
+            break
+    return {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": "%d full passes of the headline workload (norm [4096,1536] + "
+                                        "swiglu [4096,17920]) in %.1f s" % (reps, el)}
+
+
+if __name__ == "__main__":
+    main()

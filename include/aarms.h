@@ -1,0 +1,179 @@
+/*
+ * aarms.h -- C ABI of libaarms.so: fused residual-add + RMSNorm, SwiGLU, and
+ * their FP8 (E4M3) epilogues, as hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * Data formats
+ *   bf16  : 16-bit bit pattern (the top half of an IEEE binary32), passed as
+ *           uint16 storage.
+ *   fp8   : one byte, OCP E4M3FN (exponent bias 7, 3 mantissa bits, no
+ *           infinities, 0x7F/0xFF are NaN, largest finite 448).
+ *   All tensors are dense and row-major; a "row" is one token.
+ *
+ * Conventions common to every entry point
+ *   - Every pointer is a device pointer.  The caller allocates, owns and frees
+ *     all memory; the library never allocates, frees or synchronizes, and
+ *     keeps no pointer after it returns.
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs
+ *     asynchronously; every entry point may be captured into a hipGraph.
+ *   - num_tokens == 0 is a no-op that returns AARMS_OK without checking the
+ *     pointers.
+ *   - Arguments are validated before anything is enqueued; on any error code
+ *     nothing has been launched.  No C++ exception crosses this interface.
+ *   - Tensor pointers must be 16-byte aligned; fp32 scale pointers 4-byte
+ *     aligned.
+ *   - Outputs may not overlap any other argument, except the in-place pairs
+ *     each entry point names.  Inputs may overlap each other.
+ *   - Results are deterministic: the same inputs give the same bits on every
+ *     run (reductions use a fixed order).
+ *
+ * Arithmetic (identical across entry points; the oracle-parity tests pin it)
+ *   - Residual add: r = bf16(f32(x) + f32(residual)), one binary32 add.
+ *   - RMSNorm: h = f32(r); mean of h^2 accumulated in binary64 and rounded
+ *     once to binary32; v = binary32(mean + eps); rs = binary32(1/sqrt(v))
+ *     from binary64; t = bf16(f32(h * rs)); y = bf16(f32(w) * f32(t)).
+ *   - SiLU: a = bf16(silu(gate)) correctly rounded (silu(g) = g/(1+e^-g));
+ *     y = bf16(f32(a) * f32(up)).
+ *   - FP8: q = e4m3(clamp(f32(y) / scale, -448, 448)), the quotient rounded
+ *     once to binary32, then round-to-nearest-even to E4M3.  NaN stays NaN,
+ *     infinities saturate.  A scale of exactly zero is treated as one.
+ */
+#ifndef AARMS_H
+#define AARMS_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum aarms_status {
+    AARMS_OK = 0,
+    AARMS_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                 */
+    AARMS_ERR_BAD_SHAPE = 2,         /* negative size, zero width, width % 8 != 0  */
+    AARMS_ERR_UNSUPPORTED_SHAPE = 3, /* width or element count beyond the limits   */
+    AARMS_ERR_MISALIGNED = 4,        /* pointer alignment not met                  */
+    AARMS_ERR_ALIAS = 5,             /* an output overlaps another argument        */
+    AARMS_ERR_BAD_EPS = 6,           /* eps negative, NaN or infinite              */
+    AARMS_ERR_HIP = 7,               /* the HIP runtime refused the launch         */
+    AARMS_ERR_BAD_VARIANT = 8        /* *_ex: unknown variant, or too narrow for H */
+};
+
+/* Limits. */
+#define AARMS_MAX_HIDDEN 65536            /* norms: row width kept in registers    */
+#define AARMS_MAX_ELEMENTS (1LL << 40)    /* tokens x width, per tensor            */
+
+/*
+ * fused_add_rmsnorm -- residual add followed by RMSNorm in one pass.
+ *
+ * TensorRT-LLM's RMSNorm "adds the residual and normalizes in one kernel";
+ * the norm itself is the eight operations of Hugging Face's RMSNorm (cast to
+ * float, square, mean, add epsilon, reciprocal square root, multiply, cast
+ * back, multiply by the weight): "TensorRT-LLM: Compiling Inference Engines
+ * Ahead of Time", section "Fusing operations, measured".
+ *
+ *   out          [num_tokens, hidden] bf16   written: the normalized, weighted row
+ *   residual_out [num_tokens, hidden] bf16   written: x + residual (the updated
+ *                                            residual stream)
+ *   x            [num_tokens, hidden] bf16   read
+ *   residual     [num_tokens, hidden] bf16   read
+ *   weight       [hidden]             bf16   read
+ *   hidden       > 0, multiple of 8, <= AARMS_MAX_HIDDEN
+ *   eps          >= 0 and finite, added to the binary32 mean
+ * In place: out == x and/or residual_out == residual are allowed.
+ */
+int fused_add_rmsnorm(void *out, void *residual_out,
+                      const void *x, const void *residual, const void *weight,
+                      int64_t num_tokens, int64_t hidden, float eps,
+                      hipStream_t stream);
+
+/*
+ * fused_add_rmsnorm_quant_fp8 -- fused_add_rmsnorm whose bf16 output is
+ * quantised to E4M3 with a dynamic per-token scale, in the same pass.
+ *
+ * The fused RMSNorm + FP8 quant is one of vLLM's fusion passes, and the
+ * format is FP8 E4M3 with per-tensor or finer scaling: "Introduction to
+ * torch.compile and How It Works with vLLM", section 4; "TensorRT-LLM"
+ * walkthrough, Part V (quantization deep dive).
+ *
+ *   out_fp8      [num_tokens, hidden] fp8    written: e4m3(clamp(y / s_row))
+ *   scale_out    [num_tokens]         fp32   written: s_row = binary32(max_j |y_j| / 448)
+ *                                            (0 for an all-zero row, whose codes are zeros)
+ *   residual_out [num_tokens, hidden] bf16   written: x + residual
+ *   x, residual, weight, hidden, eps         as for fused_add_rmsnorm
+ * y is the bf16 value fused_add_rmsnorm would write to `out`; every non-zero
+ * row has max |q| = 448.  In place: residual_out == residual is allowed.
+ */
+int fused_add_rmsnorm_quant_fp8(void *out_fp8, float *scale_out, void *residual_out,
+                                const void *x, const void *residual, const void *weight,
+                                int64_t num_tokens, int64_t hidden, float eps,
+                                hipStream_t stream);
+
+/*
+ * swiglu -- silu(gate) * up over a concatenated gate_up projection output.
+ *
+ * TensorRT-LLM's gated MLP runs one gate_up_proj matmul followed by a fused
+ * swiglu; the activation reads the two halves of each row, gate first, and
+ * rounds the SiLU to the storage type before the product: first page,
+ * section "Fusing operations, measured" (the swiglu kernel).
+ *
+ *   out      [num_tokens, inter]     bf16   written
+ *   gate_up  [num_tokens, 2 * inter] bf16   read; gate = columns [0, inter),
+ *                                           up = columns [inter, 2*inter)
+ *   inter    > 0, multiple of 8
+ * No in-place form: out may not overlap gate_up.
+ */
+int swiglu(void *out, const void *gate_up, int64_t num_tokens, int64_t inter,
+           hipStream_t stream);
+
+/*
+ * swiglu_quant_fp8 -- swiglu whose bf16 output is quantised to E4M3 with a
+ * given per-tensor scale, in the same pass (vLLM's SiLU-and-mul + quant
+ * fusion: "Introduction to torch.compile and How It Works with vLLM",
+ * sections 3 and 4).
+ *
+ *   out_fp8  [num_tokens, inter]     fp8    written: e4m3(clamp(y / *scale))
+ *   gate_up  [num_tokens, 2 * inter] bf16   read, as for swiglu
+ *   scale    [1] fp32, device memory,       read by the kernel (so it may be
+ *            changed between graph replays); must be positive and finite,
+ *            except that exactly zero is treated as one
+ *   inter    > 0, multiple of 8
+ */
+int swiglu_quant_fp8(void *out_fp8, const void *gate_up, const float *scale,
+                     int64_t num_tokens, int64_t inter, hipStream_t stream);
+
+/* Human-readable name of a return code (static storage, never NULL). */
+const char *aarms_status_string(int status);
+
+/*
+ * Kernel variants, for tuning sweeps.  The plain entry points pick a variant
+ * from (num_tokens, width); the *_ex forms take it explicitly.  A variant id
+ * is an index into the op's table; aarms_variant_name() describes it
+ * (static storage) and returns NULL past the end.  ops: 0 = fused_add_rmsnorm
+ * and fused_add_rmsnorm_quant_fp8, 1 = swiglu and swiglu_quant_fp8.
+ * aarms_pick_variant() returns the id the plain entry point would use, or -1
+ * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
+ */
+int aarms_variant_count(int op);
+const char *aarms_variant_name(int op, int variant);
+int aarms_pick_variant(int op, int64_t num_tokens, int64_t width);
+
+int fused_add_rmsnorm_ex(void *out, void *residual_out,
+                         const void *x, const void *residual, const void *weight,
+                         int64_t num_tokens, int64_t hidden, float eps,
+                         int variant, hipStream_t stream);
+int fused_add_rmsnorm_quant_fp8_ex(void *out_fp8, float *scale_out, void *residual_out,
+                                   const void *x, const void *residual, const void *weight,
+                                   int64_t num_tokens, int64_t hidden, float eps,
+                                   int variant, hipStream_t stream);
+int swiglu_ex(void *out, const void *gate_up, int64_t num_tokens, int64_t inter,
+              int variant, hipStream_t stream);
+int swiglu_quant_fp8_ex(void *out_fp8, const void *gate_up, const float *scale,
+                        int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AARMS_H */

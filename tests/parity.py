@@ -1,0 +1,155 @@
+"""Comparison of GPU results with the oracle (numpy only, no GPU calls).
+
+The reading of "within 1 bf16 ulp / 1 E4M3 ulp" used here: the pages leave
+the order of the row reduction open and say a fused kernel's results may
+differ from the unfused ones in the last bits for that reason.  So a GPU norm
+output is correct when it equals the oracle's value for *some* per-row
+multiplier rho within relative distance DELTA of the exact 1/sqrt(mean+eps)
+(the "admissible" values; one or two per element).  Outside such knife-edges
+the admissible set is the single nominal value, so these checks demand
+bit-exactness there.  The residual output has no freedom at all.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+# Relative window for the row multiplier.  A binary64 accumulation over any
+# order, one rounding to binary32 for the mean, one for mean + eps and one for
+# the reciprocal square root stay far inside 2^-18.
+DELTA = 2.0 ** -18
+
+
+# ----------------------------------------------------------------- tensors
+
+def to_gpu_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(device)
+
+
+def from_gpu_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    if t.dtype == torch.uint8:
+        return t.numpy()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError(t.dtype)
+
+
+# ----------------------------------------------------------------- ulps
+
+def bf16_ordered(b: np.ndarray) -> np.ndarray:
+    b = b.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def e4m3_ordered(q: np.ndarray) -> np.ndarray:
+    q = q.astype(np.int64)
+    mag = q & 0x7F
+    return np.where(q & 0x80, -mag, mag)
+
+
+def bf16_ulps(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    return np.abs(bf16_ordered(a) - bf16_ordered(b))
+
+
+def e4m3_ulps(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    return np.abs(e4m3_ordered(a) - e4m3_ordered(b))
+
+
+def same_bf16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Bitwise equal, with every NaN equal to every NaN."""
+    fa, fb = oracle.bf16_to_f32(a), oracle.bf16_to_f32(b)
+    return (a == b) | (np.isnan(fa) & np.isnan(fb))
+
+
+# ----------------------------------------------------------------- norm
+
+class NormReport(dict):
+    pass
+
+
+def norm_admissible(res_out: np.ndarray, weight: np.ndarray, eps: float):
+    """Nominal oracle output and the two window-end alternatives."""
+    rs, rs_exact = oracle.rms_scale(res_out, eps)
+    lo, hi = oracle.rms_window(rs_exact, DELTA)
+    nominal = oracle.rmsnorm_apply(res_out, weight, rs)
+    alt_lo = oracle.rmsnorm_apply(res_out, weight, lo)
+    alt_hi = oracle.rmsnorm_apply(res_out, weight, hi)
+    return nominal, alt_lo, alt_hi
+
+
+def check_norm(x, residual, weight, eps, out_gpu, res_out_gpu) -> NormReport:
+    """Assert the GPU's fused_add_rmsnorm results; return statistics."""
+    res_out = oracle.residual_add(x, residual)
+    bad_res = ~same_bf16(res_out_gpu, res_out)
+    assert not bad_res.any(), "residual_out differs at %d positions, first %s" % (
+        bad_res.sum(), np.argwhere(bad_res)[:5].tolist())
+    nominal, alt_lo, alt_hi = norm_admissible(res_out, weight, eps)
+    exact = same_bf16(out_gpu, nominal)
+    admissible = exact | same_bf16(out_gpu, alt_lo) | same_bf16(out_gpu, alt_hi)
+    bad = ~admissible
+    assert not bad.any(), "out outside the admissible set at %d positions, first %s: gpu %s oracle %s" % (
+        bad.sum(), np.argwhere(bad)[:5].tolist(), out_gpu[bad][:5], nominal[bad][:5])
+    finite = np.isfinite(oracle.bf16_to_f32(nominal))
+    ulps = bf16_ulps(out_gpu[finite], nominal[finite])
+    return NormReport(elements=int(out_gpu.size), not_nominal=int((~exact).sum()),
+                      max_ulps_vs_nominal=int(ulps.max()) if ulps.size else 0)
+
+
+def check_norm_fp8(x, residual, weight, eps, q_gpu, s_gpu, res_out_gpu) -> NormReport:
+    """Assert fused_add_rmsnorm_quant_fp8 results.
+
+    Bit-exact is expected; the stated tolerances (scales within 1e-6
+    relative, codes within 1 E4M3 ulp) are applied against admissible values
+    where the norm output itself sits on a knife-edge."""
+    q_o, s_o, res_o, y_o, _ = oracle.fused_add_rmsnorm_quant_fp8(x, residual, weight, eps)
+    bad_res = ~same_bf16(res_out_gpu, res_o)
+    assert not bad_res.any(), "residual_out differs at %d positions" % bad_res.sum()
+    rows_s = np.flatnonzero(s_gpu.view(np.uint32) != s_o.view(np.uint32))
+    rows_q = np.flatnonzero((q_gpu != q_o).any(axis=1))
+    rows = np.union1d(rows_s, rows_q)
+    if len(rows):
+        _, lo, hi = norm_admissible(res_o[rows], weight, eps)
+        ylo, yhi = oracle.bf16_to_f32(lo), oracle.bf16_to_f32(hi)
+        amax_lo = np.minimum(np.abs(ylo), np.abs(yhi)).max(axis=1)
+        amax_hi = np.maximum(np.abs(ylo), np.abs(yhi)).max(axis=1)
+        s_lo = (amax_lo.astype(np.float32) / np.float32(448)).astype(np.float32)
+        s_hi = (amax_hi.astype(np.float32) / np.float32(448)).astype(np.float32)
+        sg = s_gpu[rows]
+        ok_s = (sg >= s_lo * (1 - 1e-6)) & (sg <= s_hi * (1 + 1e-6))
+        assert ok_s.all(), "scale outside tolerance in rows %s" % rows[~ok_s][:5].tolist()
+        for k, r in enumerate(rows):
+            cand = [oracle.quant_fp8_static(lo[k], float(sg[k])), oracle.quant_fp8_static(hi[k], float(sg[k]))]
+            d = np.minimum(e4m3_ulps(q_gpu[r], cand[0]), e4m3_ulps(q_gpu[r], cand[1]))
+            assert d.max() <= 1, "row %d: code off by %d e4m3 ulps" % (r, d.max())
+    return NormReport(rows=int(q_gpu.shape[0]), rows_not_nominal=int(len(rows)),
+                      codes_not_nominal=int((q_gpu != q_o).sum()),
+                      scales_not_nominal=int(len(rows_s)))
+
+
+# ----------------------------------------------------------------- swiglu
+
+def check_swiglu(gate_up, y_gpu):
+    y_o = oracle.swiglu(gate_up)
+    bad = ~same_bf16(y_gpu, y_o)
+    assert not bad.any(), "swiglu differs at %d positions, first %s: gpu %s oracle %s" % (
+        bad.sum(), np.argwhere(bad)[:5].tolist(), y_gpu[bad][:5], y_o[bad][:5])
+
+
+def check_swiglu_fp8(gate_up, scale, q_gpu):
+    q_o = oracle.swiglu_quant_fp8(gate_up, scale)
+    nan_o = np.isin(q_o, [0x7F, 0xFF])
+    nan_g = np.isin(q_gpu, [0x7F, 0xFF])
+    assert np.array_equal(nan_o, nan_g), "NaN codes differ at %d positions" % (nan_o != nan_g).sum()
+    bad = (q_gpu != q_o) & ~nan_o
+    assert not bad.any(), "swiglu_quant_fp8 differs at %d positions, first %s: gpu %s oracle %s" % (
+        bad.sum(), np.argwhere(bad)[:5].tolist(), q_gpu[bad][:5], q_o[bad][:5])

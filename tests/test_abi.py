@@ -1,0 +1,192 @@
+"""The C ABI without a GPU: libaarms.so loads, exports every function that
+include/aarms.h declares, and rejects bad arguments before any HIP call.
+
+Only error paths are called here (validation returns before anything is
+enqueued), plus the variant tables; no kernel is launched.  Pointer values
+are plain integers that are never dereferenced.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import activation_add_rmsnorm_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aarms.h")
+
+OK, NULLP, SHAPE, UNSUP, MISAL, ALIAS, EPS, HIP, VARIANT = range(9)
+MAX_HIDDEN = 65536
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_four_ops():
+    fns = declared_functions()
+    for name in ["fused_add_rmsnorm", "swiglu", "swiglu_quant_fp8", "fused_add_rmsnorm_quant_fp8",
+                 "aarms_status_string"]:
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = A.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", A.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+
+
+def test_status_strings():
+    lib = A.load()
+    for s in range(9):
+        txt = lib.aarms_status_string(s)
+        assert txt and txt != b"unknown status"
+    assert lib.aarms_status_string(99) == b"unknown status"
+
+
+# ----------------------------------------------------------------- norms
+
+P = 0x10000  # an aligned fake device address; buffers are placed far apart
+BIG = 1 << 32
+
+
+def norm(lib, out=P, res_out=P + BIG, x=P + 2 * BIG, res=P + 3 * BIG, w=P + 4 * BIG,
+         T=4, H=1536, eps=1e-6):
+    return lib.fused_add_rmsnorm(out, res_out, x, res, w, T, H, eps, None)
+
+
+def normq(lib, out=P, scale=P + BIG, res_out=P + 2 * BIG, x=P + 3 * BIG, res=P + 4 * BIG,
+          w=P + 5 * BIG, T=4, H=1536, eps=1e-6):
+    return lib.fused_add_rmsnorm_quant_fp8(out, scale, res_out, x, res, w, T, H, eps, None)
+
+
+def test_norm_shape_errors():
+    lib = A.load()
+    assert norm(lib, T=-1) == SHAPE
+    assert norm(lib, H=0) == SHAPE
+    assert norm(lib, H=-8) == SHAPE
+    assert norm(lib, H=12) == SHAPE
+    assert norm(lib, H=MAX_HIDDEN + 8) == UNSUP
+    assert norm(lib, T=1 << 31, H=8) == UNSUP
+    assert norm(lib, T=1 << 30, H=4096) == UNSUP          # beyond 2^40 elements
+    assert normq(lib, H=20) == SHAPE
+
+
+def test_norm_zero_tokens_is_a_noop():
+    lib = A.load()
+    assert norm(lib, T=0, out=0, res_out=0, x=0, res=0, w=0) == OK
+    assert normq(lib, T=0, out=0, scale=0, res_out=0, x=0, res=0, w=0) == OK
+    assert norm(lib, T=0, H=12) == SHAPE                    # the shape is still checked
+
+
+def test_norm_eps_errors():
+    lib = A.load()
+    for eps in [-1e-6, float("nan"), float("inf"), -float("inf")]:
+        assert norm(lib, eps=eps) == EPS
+        assert normq(lib, eps=eps) == EPS
+
+
+def test_norm_null_and_alignment():
+    lib = A.load()
+    for k in ["out", "res_out", "x", "res", "w"]:
+        assert norm(lib, **{k: 0}) == NULLP
+        assert norm(lib, **{k: P + 8 + {"out": 0, "res_out": 1, "x": 2, "res": 3, "w": 4}[k] * BIG}) == MISAL
+    assert normq(lib, scale=0) == NULLP
+    assert normq(lib, scale=P + BIG + 2) == MISAL
+
+
+def test_norm_aliasing_rules():
+    """Calls that pass the aliasing rules are stopped before launch by a
+    variant too narrow for the row (checked last)."""
+    lib = A.load()
+    T, H = 4, 1536
+    n = T * H * 2
+    x = P + 2 * BIG
+    res = P + 3 * BIG
+    w = P + 4 * BIG
+    narrow = 0                                  # one wave, one vector per lane: 512 wide
+    assert A.variant_name(A.OP_NORM, narrow) == "wave/row x1 vec"
+    # exact in-place pairs are allowed
+    assert lib.fused_add_rmsnorm_ex(x, res, x, res, w, T, H, 1e-6, narrow, None) == VARIANT
+    # out overlapping residual_out
+    assert norm(lib, out=P, res_out=P + 16) == ALIAS
+    # out == residual (not an allowed pair)
+    assert norm(lib, out=res) == ALIAS
+    # partial overlap with x
+    assert norm(lib, out=x + 16) == ALIAS
+    # residual_out overlapping the weight
+    assert norm(lib, res_out=w - 16) == ALIAS
+    # adjacent, non-overlapping buffers are fine
+    assert lib.fused_add_rmsnorm_ex(P, P + n, P + 2 * n, P + 3 * n, P + 4 * n, T, H, 1e-6,
+                                    narrow, None) == VARIANT
+    # quant: out_fp8 may not alias x; residual_out may alias residual
+    assert normq(lib, out=P + 3 * BIG) == ALIAS
+    assert lib.fused_add_rmsnorm_quant_fp8_ex(P, P + BIG, P + 4 * BIG, P + 3 * BIG, P + 4 * BIG,
+                                              P + 5 * BIG, T, H, 1e-6, narrow, None) == VARIANT
+    # scale_out overlapping out
+    assert normq(lib, scale=P + 64) == ALIAS
+
+
+def test_norm_variant_checks():
+    lib = A.load()
+    n = A.variant_count(A.OP_NORM)
+    assert n >= 10
+    args = (P, P + BIG, P + 2 * BIG, P + 3 * BIG, P + 4 * BIG)
+    assert lib.fused_add_rmsnorm_ex(*args, 4, 1536, 1e-6, n, None) == VARIANT
+    assert lib.fused_add_rmsnorm_ex(*args, 4, 1536, 1e-6, -2, None) == VARIANT
+    # a variant too narrow for the row is refused before launch
+    narrow = [i for i in range(n) if "wave/row x1" in A.variant_name(A.OP_NORM, i)][0]
+    assert lib.fused_add_rmsnorm_ex(*args, 4, 1536, 1e-6, narrow, None) == VARIANT
+    assert A.variant_name(A.OP_NORM, n) is None
+
+
+# ----------------------------------------------------------------- swiglu
+
+def sw(lib, out=P, gu=P + BIG, T=4, N=8960):
+    return lib.swiglu(out, gu, T, N, None)
+
+
+def swq(lib, out=P, gu=P + BIG, scale=P + 2 * BIG, T=4, N=8960):
+    return lib.swiglu_quant_fp8(out, gu, scale, T, N, None)
+
+
+def test_swiglu_errors():
+    lib = A.load()
+    assert sw(lib, T=-1) == SHAPE
+    assert sw(lib, N=0) == SHAPE
+    assert sw(lib, N=12) == SHAPE
+    assert sw(lib, T=1 << 20, N=1 << 20) == UNSUP
+    assert sw(lib, T=0, out=0, gu=0) == OK
+    assert sw(lib, out=0) == NULLP
+    assert sw(lib, gu=0) == NULLP
+    assert sw(lib, out=P + 2) == MISAL
+    assert sw(lib, gu=P + BIG + 8) == MISAL
+    assert sw(lib, out=P + BIG) == ALIAS                       # in place is not allowed
+    assert sw(lib, out=P + BIG + 4 * 8960 * 4 - 16) == ALIAS   # tail overlap
+    assert swq(lib, scale=0) == NULLP
+    assert swq(lib, scale=P + 2 * BIG + 2) == MISAL
+    assert swq(lib, scale=P + 4) == ALIAS                      # scale inside out
+    assert swq(lib, T=0, out=0, gu=0, scale=0) == OK
+    n = A.variant_count(A.OP_SWIGLU)
+    assert lib.swiglu_ex(P, P + BIG, 4, 8960, n, None) == VARIANT
+
+
+def test_pick_variant_ranges():
+    for H in [8, 512, 520, 1536, 4096, 4104, 8192, 16384, 32768, 65536]:
+        v = A.pick_variant(A.OP_NORM, 16, H)
+        assert v >= 0, H
+    assert A.pick_variant(A.OP_NORM, 16, MAX_HIDDEN + 8) == -1
+    assert A.pick_variant(A.OP_SWIGLU, 16, 8960) >= 0
+    assert A.pick_variant(A.OP_SWIGLU, 16, 12) == -1
