@@ -68,7 +68,7 @@ def load():
             "swiglu_quant_fp8": [vp, vp, vp, i64, i64, vp],
             "swiglu_quant_fp8_ex": [vp, vp, vp, i64, i64, i32, vp],
             "aarms_variant_count": [i32],
-            "aarms_pick_variant": [i32, i64, i64],
+            "aarms_pick_variant": [i32, i64, i64, i32],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -218,5 +218,5 @@ def variant_name(op: int, variant: int) -> str | None:
     return s.decode() if s else None
 
 
-def pick_variant(op: int, tokens: int, width: int) -> int:
-    return int(load().aarms_pick_variant(int(op), int(tokens), int(width)))
+def pick_variant(op: int, tokens: int, width: int, quant: bool = False) -> int:
+    return int(load().aarms_pick_variant(int(op), int(tokens), int(width), int(bool(quant))))

@@ -6,7 +6,6 @@
 #include "aarms.h"
 #include "launch.h"
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -59,31 +58,17 @@ int check_outputs(const Arg *outs, const int *partner, int n_out, const Arg *ins
     return AARMS_OK;
 }
 
-int device_cus()
-{
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64) {
-        int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-        n = 256;
-    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-
 int norm_capacity(const NormVariant *v) { return v->waves_per_row * 64 * v->vecs_per_lane * 8; }
 
-int pick_norm(int64_t tokens, int64_t hidden)
+int pick_norm(int64_t tokens, int64_t hidden, bool quant)
 {
     (void)tokens;
     if (hidden <= 0 || hidden > AARMS_MAX_HIDDEN) return -1;
     // Narrow rows: one wave per row with as few vectors per lane as fit.
     // Wide rows: the fewest waves per row that fit with 8 vectors per lane
-    // (4, 8 or 16 waves), so that a row's reduction crosses few waves.
+    // (the FP8 form, which keeps the row in registers through two
+    // reductions, prefers 4 vectors per lane: twice the waves, half the
+    // registers each).
     const int n = norm_variant_count();
     if (hidden <= 4096) {
         for (int i = 0; i < n; ++i) {
@@ -91,23 +76,31 @@ int pick_norm(int64_t tokens, int64_t hidden)
             if (v->waves_per_row == 1 && norm_capacity(v) >= hidden) return i;
         }
     }
-    for (int w : {2, 4, 8, 16}) {
-        int best = -1;
-        for (int i = 0; i < n; ++i) {
-            const NormVariant *v = norm_variant(i);
-            if (v->waves_per_row != w || norm_capacity(v) < hidden) continue;
-            if (best < 0 || v->vecs_per_lane < norm_variant(best)->vecs_per_lane) best = i;
+    const int max_vecs = quant ? 4 : 8;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int w : {2, 4, 8, 16}) {
+            int best = -1;
+            for (int i = 0; i < n; ++i) {
+                const NormVariant *v = norm_variant(i);
+                if (v->waves_per_row != w || norm_capacity(v) < hidden) continue;
+                if (pass == 0 && v->vecs_per_lane > max_vecs) continue;
+                if (best < 0 || v->vecs_per_lane < norm_variant(best)->vecs_per_lane) best = i;
+            }
+            if (best >= 0) return best;
         }
-        if (best >= 0) return best;
     }
     return -1;
 }
 
-int pick_swiglu(int64_t tokens, int64_t inter)
+int pick_swiglu(int64_t tokens, int64_t inter, bool quant)
 {
     (void)tokens;
     (void)inter;
-    return 1;  // 2 jobs per lane, one block per 512 jobs
+    // bf16 output: one job per lane (the most blocks, each short-lived, so
+    // the blocks in flight stay on one contiguous stretch of memory).  E4M3
+    // output: two jobs per lane, which gives the longer per-job arithmetic
+    // two loads in flight to hide behind.
+    return quant ? 1 : 0;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? AARMS_OK : AARMS_ERR_HIP; }
@@ -141,7 +134,7 @@ int norm_common(void *out, float *scale_out, void *residual_out, const void *x,
         const int partner[3] = {-1, 1, -1};  // residual_out == residual only
         if ((st = check_outputs(outs, partner, 3, ins, 3))) return st;
     }
-    if (variant == -1) variant = pick_norm(tokens, hidden);
+    if (variant == -1) variant = pick_norm(tokens, hidden, quant);
     const NormVariant *v = norm_variant(variant);
     if (!v || norm_capacity(v) < hidden) return AARMS_ERR_BAD_VARIANT;
     NormParams p;
@@ -162,6 +155,7 @@ int swiglu_common(void *out, const void *gate_up, const float *scale, int64_t to
 {
     int st = check_width(tokens, inter, 0);
     if (st) return st;
+    if (inter > (int64_t)1 << 34) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (tokens > 0 && 2 * inter > AARMS_MAX_ELEMENTS / tokens) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (variant < -1 || variant >= swiglu_variant_count()) return AARMS_ERR_BAD_VARIANT;
     if (tokens == 0) return AARMS_OK;
@@ -173,16 +167,15 @@ int swiglu_common(void *out, const void *gate_up, const float *scale, int64_t to
     const Arg ins[2] = {{span(gate_up, 4 * elems), gate_up}, {span(scale, quant ? 4 : 0), scale}};
     const int partner[1] = {-1};
     if ((st = check_outputs(outs, partner, 1, ins, quant ? 2 : 1))) return st;
-    if (variant == -1) variant = pick_swiglu(tokens, inter);
+    if (variant == -1) variant = pick_swiglu(tokens, inter, quant);
     SwigluParams p;
     p.out = out;
     p.gate_up = gate_up;
     p.scale = scale;
-    p.vecs_per_row = (uint32_t)(inter / 8);
-    p.jobs = (uint64_t)tokens * p.vecs_per_row;
-    p.inv_vecs_per_row = 1.0 / (double)p.vecs_per_row;
+    p.tokens = tokens;
     p.inter = inter;
-    return launch_status(launch_swiglu(p, quant, variant, device_cus(), stream));
+    p.vecs_per_row = (uint32_t)(inter / 8);
+    return launch_status(launch_swiglu(p, quant, variant, stream));
 }
 
 }  // namespace
@@ -279,10 +272,10 @@ const char *aarms_variant_name(int op, int variant)
     return nullptr;
 }
 
-int aarms_pick_variant(int op, int64_t num_tokens, int64_t width)
+int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant)
 {
-    if (op == 0) return pick_norm(num_tokens, width);
-    if (op == 1) return (width > 0 && width % 8 == 0) ? pick_swiglu(num_tokens, width) : -1;
+    if (op == 0) return pick_norm(num_tokens, width, quant != 0);
+    if (op == 1) return (width > 0 && width % 8 == 0) ? pick_swiglu(num_tokens, width, quant != 0) : -1;
     return -1;
 }
 

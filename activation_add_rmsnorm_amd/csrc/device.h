@@ -12,6 +12,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Streaming accesses: every tensor except the weight is read or written
+// exactly once, so loads and stores carry the non-temporal hint (the data is
+// not kept in the caches for reuse that will not come).
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T *p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st_stream(T *p, T v) { __builtin_nontemporal_store(v, p); }
+
 // A 16-byte vector holds 8 bf16 values: element 2e is the low half of word
 // e, element 2e+1 the high half.  Widening bf16 -> binary32 is exact.
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -108,19 +116,24 @@ __device__ __forceinline__ float wave_max(float v)
 // ---------------------------------------------------------------- SiLU
 //
 // bf16(silu(g)) must be the correctly rounded value.  The fast form below,
-// g * rcp(1 + 2^(-g*log2 e)) with the hardware exp2 and reciprocal, has a
-// relative error below 2^-19 for g >= -16 (about 31 units of binary32
-// rounding: the rounding of -g*log2 e amplified by |g|*ln 2, the exp2, the
-// add, the reciprocal and the product).  Its bf16 rounding is therefore
-// right unless the binary32 result lies within SILU_EDGE units of a bf16
-// midpoint (the low 16 bits near 0x8000), or g < -16.  Those lanes -- about
-// one element in 200 for normally distributed gates -- are recomputed by
-// silu_exact().  (Measured over all 65,536 gates on gfx950 the fast form is
-// within 14 units for g in [-16, -8) and within 4 for |g| <= 4, so the
-// window has a wide margin; its only misroundings are exact ties.)
+// g * rcp(1 + 2^(-g*log2 e)) with the hardware exp2 and reciprocal, is within
+// a few units of binary32 rounding of silu(g) (analytically below 31 units
+// for g >= -16; measured on gfx950 over all 65,536 gates: within 14 units
+// for g in [-16, -8) and within 4 for |g| <= 4).  Because the gate is a bf16,
+// the fast form is a function of 16 bits and its bf16 rounding can be
+// checked against the correctly rounded value for every input: on gfx950 the
+// only gates it misrounds with g >= -16 are those whose binary32 result is
+// an exact bf16 midpoint (subnormal gates, where silu(g) = g/2 + g^2/4 and
+// binary32 loses the g^2/4).  So a lane is recomputed by silu_exact() when
+// its result lies within SILU_EDGE units of a midpoint (the low 16 bits near
+// 0x8000) or when g < -16; everything else keeps the fast value.  The
+// exhaustive check runs on the shipped kernel through the public API in the
+// GPU parity tests.  A window this narrow is taken by about one element in
+// 20,000-40,000 for normally distributed gates, so the exact path costs
+// almost nothing; a window as wide as the analytic bound would send most
+// waves through it.
 
-constexpr float SILU_FAST_MIN = -16.0f;
-constexpr uint32_t SILU_EDGE = 48;
+constexpr uint32_t SILU_EDGE = 2;
 // g < -16 (or g is a negative NaN) exactly when the bit pattern of g, read
 // as unsigned, exceeds that of -16.0; integer compares cannot be upset by a
 // signalling NaN the way a floating-point minimum can.

@@ -23,11 +23,13 @@ struct SwigluParams {
     void *out;               // bf16 [T,N], or fp8 [T,N] when quantising
     const void *gate_up;     // bf16 [T,2N]
     const float *scale;      // fp32 [1] when quantising, else null
-    uint64_t jobs;           // T * N / 8: one job = 8 adjacent outputs
-    uint32_t vecs_per_row;   // N / 8
-    double inv_vecs_per_row; // 1 / (N / 8), for the job -> row division
+    int64_t tokens;          // T
     int64_t inter;           // N
+    uint32_t vecs_per_row;   // N / 8: one job = 8 adjacent outputs of a row
 };
+
+// Rows per launch along grid y; more rows go to grid z.
+constexpr uint32_t SWIGLU_ROWS_PER_Y = 65535;
 
 // Norm variants: (waves per row, 16-byte vectors per lane).  A row of H
 // elements needs waves * 64 * vectors * 8 >= H.
@@ -38,8 +40,7 @@ struct NormVariant {
 };
 
 struct SwigluVariant {
-    int jobs_per_lane;       // jobs in flight per lane and loop trip
-    int blocks_per_cu;       // 0: one block per 256*jobs_per_lane jobs; else a grid-stride grid
+    int jobs_per_lane;       // a block of 256 lanes covers 256 * jobs_per_lane jobs of one row
     const char *name;
 };
 
@@ -49,7 +50,6 @@ int swiglu_variant_count();
 const SwigluVariant *swiglu_variant(int id);
 
 hipError_t launch_norm(const NormParams &p, bool quant, int variant, hipStream_t stream);
-hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, int num_cus,
-                         hipStream_t stream);
+hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, hipStream_t stream);
 
 }  // namespace aarms

@@ -1,8 +1,8 @@
 // norm.hip -- fused residual add + RMSNorm for gfx950, with a bf16 epilogue
 // or a dynamic per-token E4M3 epilogue.
 //
-// One pass over HBM: x and residual are read once with 16-byte loads, the
-// updated residual and the output are written once, and the row stays in
+// One pass over HBM: x and residual are read once with 16-byte streaming
+// loads, the updated residual and the output are written once, and the row stays in
 // registers between the reduction and the epilogue.  A row is handled by one
 // wave (narrow rows, four rows per 256-thread block) or by a whole block of
 // 2..16 waves (wide rows).  The sum of squares is accumulated per lane in
@@ -39,7 +39,7 @@ __device__ __forceinline__ void quantize_row(const u32x4 (&yv)[VPT], const E4m3S
         u32x2 q;
         q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
         q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
-        *(u32x2 *)(qo + (size_t)v * 8) = q;
+        st_stream((u32x2 *)(qo + (size_t)v * 8), q);
     }
 }
 
@@ -73,8 +73,8 @@ norm_kernel(NormParams p)
     for (int k = 0; k < VPT; ++k) {
         const int v = lane + k * ROW_THREADS;
         const bool ok = v < nvec;
-        xv[k] = ok ? xr[v] : (u32x4)0u;
-        rv[k] = ok ? rr[v] : (u32x4)0u;
+        xv[k] = ok ? ld_stream(xr + v) : (u32x4)0u;
+        rv[k] = ok ? ld_stream(rr + v) : (u32x4)0u;
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -92,7 +92,7 @@ norm_kernel(NormParams p)
         for (int e = 0; e < 4; ++e)
             r[e] = pack_bf16(bf_lo(xv[k][e]) + bf_lo(rv[k][e]), bf_hi(xv[k][e]) + bf_hi(rv[k][e]));
         rv[k] = r;
-        if (v < nvec) ro[v] = r;
+        if (v < nvec) st_stream(ro + v, r);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const double h0 = (double)bf_lo(r[e]);
@@ -128,7 +128,7 @@ norm_kernel(NormParams p)
                 const uint32_t t = pack_bf16(bf_lo(rv[k][e]) * rs, bf_hi(rv[k][e]) * rs);
                 y[e] = pack_bf16(bf_lo(wv[k][e]) * bf_lo(t), bf_hi(wv[k][e]) * bf_hi(t));
             }
-            o[v] = y;
+            st_stream(o + v, y);
         }
     } else {
         // ---- y as above, kept in registers; row amax

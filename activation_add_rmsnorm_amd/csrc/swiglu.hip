@@ -1,13 +1,15 @@
 // swiglu.hip -- silu(gate) * up over a concatenated gate_up row, with a bf16
 // epilogue or a static per-tensor E4M3 epilogue, for gfx950.
 //
-// The output is a flat sequence of jobs; a job is 8 adjacent outputs of one
-// row, fed by one 16-byte load of gate and one of up from the same row of
-// gate_up (gate first, up second: "TensorRT-LLM: Compiling Inference Engines
-// Ahead of Time", section "Fusing operations, measured", the swiglu kernel).
-// Consecutive lanes take consecutive jobs, so every load and store of a wave
-// is one contiguous stretch.  Nothing is kept between jobs: the kernel is a
-// pure stream, bounded by HBM bandwidth and, for the FP8 form, by VALU work.
+// A job is 8 adjacent outputs of one row, fed by one 16-byte load of gate and
+// one of up from the same row of gate_up (gate first, up second:
+// "TensorRT-LLM: Compiling Inference Engines Ahead of Time", section "Fusing
+// operations, measured", the swiglu kernel).  The grid is (column chunk,
+// row): a block of 256 lanes takes 256 * U consecutive jobs of one row, so
+// the row is a per-block scalar, every load and store of a wave is one
+// contiguous stretch, and blocks are dispatched in memory order (one block
+// per chunk, no grid-stride loop: the blocks in flight then cover one
+// contiguous window of HBM).  Nothing is kept between jobs.
 //
 // SiLU is rounded once to bf16 before the product, and that rounding must be
 // the correctly rounded one: the fast hardware exp2/rcp form is used unless
@@ -44,12 +46,18 @@ __device__ __forceinline__ u32x4 swiglu8(u32x4 gv, u32x4 uv)
         gmax = max(gmax, gb[j]);
     }
     if (kmin <= SILU_EDGE_KEY_MAX || gmax > SILU_FAST_MIN_BITS) {
-        // recompute this lane's flagged elements exactly, one at a time
+        // rare: recompute this lane's flagged elements exactly, one at a
+        // time.  The empty asm makes the flag bookkeeping depend on values
+        // produced inside this branch, so it is not hoisted onto the hot path.
         uint32_t redo = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            redo |= (uint32_t)((silu_edge_key(s[j]) <= SILU_EDGE_KEY_MAX) |
-                               (gb[j] > SILU_FAST_MIN_BITS)) << j;
+        for (int j = 0; j < 8; ++j) {
+            float sj = s[j];
+            uint32_t gbj = gb[j];
+            asm volatile("" : "+v"(sj), "+v"(gbj));
+            redo |= (uint32_t)((silu_edge_key(sj) <= SILU_EDGE_KEY_MAX) |
+                               (gbj > SILU_FAST_MIN_BITS)) << j;
+        }
         while (redo) {
             const int j = __builtin_ctz(redo);
             redo &= redo - 1u;
@@ -72,44 +80,41 @@ __device__ __forceinline__ u32x4 swiglu8(u32x4 gv, u32x4 uv)
 
 // MODE 0: bf16 output; 1: E4M3 output, fast quotient; 2: E4M3, IEEE division.
 template <int U, int MODE>
-__device__ __forceinline__ void swiglu_loop(const SwigluParams &p, const E4m3Scale &qs)
+__device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Scale &qs)
 {
-    const uint16_t *gu = (const uint16_t *)p.gate_up;
-    const uint64_t stride = (uint64_t)gridDim.x * 256u * U;
-    for (uint64_t base = (uint64_t)blockIdx.x * 256u * U + threadIdx.x; base < p.jobs;
-         base += stride) {
-        u32x4 gv[U], uv[U];
-        uint64_t job[U];
+    const uint64_t row = (uint64_t)blockIdx.z * SWIGLU_ROWS_PER_Y + blockIdx.y;
+    if (row >= (uint64_t)p.tokens) return;
+    const uint32_t nvec = p.vecs_per_row;
+    const uint32_t c0 = blockIdx.x * (256u * U) + threadIdx.x;
+    const u32x4 *gate = (const u32x4 *)((const uint16_t *)p.gate_up + row * 2u * (uint64_t)p.inter);
+    const u32x4 *up = gate + nvec;
+    const uint64_t job0 = row * nvec;
+    u32x4 gv[U], uv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            job[u] = base + (uint64_t)u * 256u;
-            const bool ok = job[u] < p.jobs;
-            const uint64_t i = ok ? job[u] : 0;
-            // row = i / (N/8): a binary64 estimate is the row or one below it
-            uint64_t row = (uint64_t)((double)i * p.inv_vecs_per_row);
-            if (i - row * p.vecs_per_row >= p.vecs_per_row) ++row;
-            const uint16_t *g = gu + i * 8u + row * (uint64_t)p.inter;
-            gv[u] = ok ? *(const u32x4 *)g : (u32x4)0u;
-            uv[u] = ok ? *(const u32x4 *)(g + p.inter) : (u32x4)0u;
-        }
+    for (int u = 0; u < U; ++u) {
+        const uint32_t c = c0 + 256u * u;
+        const bool ok = c < nvec;
+        gv[u] = ok ? ld_stream(gate + c) : (u32x4)0u;
+        uv[u] = ok ? ld_stream(up + c) : (u32x4)0u;
+    }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (job[u] >= p.jobs) continue;
-            const u32x4 y = swiglu8(gv[u], uv[u]);
-            if constexpr (MODE == 0) {
-                *((u32x4 *)p.out + job[u]) = y;
-            } else {
-                float z[8];
+    for (int u = 0; u < U; ++u) {
+        const uint32_t c = c0 + 256u * u;
+        if (c >= nvec) continue;
+        const u32x4 y = swiglu8(gv[u], uv[u]);
+        if constexpr (MODE == 0) {
+            st_stream((u32x4 *)p.out + job0 + c, y);
+        } else {
+            float z[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    z[2 * e] = e4m3_quotient<MODE == 1>(bf_lo(y[e]), qs);
-                    z[2 * e + 1] = e4m3_quotient<MODE == 1>(bf_hi(y[e]), qs);
-                }
-                u32x2 q;
-                q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
-                q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
-                *((u32x2 *)p.out + job[u]) = q;
+            for (int e = 0; e < 4; ++e) {
+                z[2 * e] = e4m3_quotient<MODE == 1>(bf_lo(y[e]), qs);
+                z[2 * e + 1] = e4m3_quotient<MODE == 1>(bf_hi(y[e]), qs);
             }
+            u32x2 q;
+            q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+            q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
+            st_stream((u32x2 *)p.out + job0 + c, q);
         }
     }
 }
@@ -120,25 +125,20 @@ __global__ void __launch_bounds__(256) swiglu_kernel(SwigluParams p)
     if constexpr (QUANT) {
         const E4m3Scale qs = make_e4m3_scale(*p.scale);
         if (e4m3_scale_is_fast(qs))
-            swiglu_loop<U, 1>(p, qs);
+            swiglu_block<U, 1>(p, qs);
         else
-            swiglu_loop<U, 2>(p, qs);
+            swiglu_block<U, 2>(p, qs);
     } else {
-        swiglu_loop<U, 0>(p, E4m3Scale{});
+        swiglu_block<U, 0>(p, E4m3Scale{});
     }
 }
 
 // ---------------------------------------------------------------- variants
 
 static const SwigluVariant kSwigluVariants[] = {
-    {1, 0, "1 job/lane, one-shot grid"},
-    {2, 0, "2 jobs/lane, one-shot grid"},
-    {4, 0, "4 jobs/lane, one-shot grid"},
-    {1, 8, "1 job/lane, 8 blocks/CU stride"},
-    {2, 8, "2 jobs/lane, 8 blocks/CU stride"},
-    {4, 8, "4 jobs/lane, 8 blocks/CU stride"},
-    {2, 4, "2 jobs/lane, 4 blocks/CU stride"},
-    {4, 4, "4 jobs/lane, 4 blocks/CU stride"},
+    {1, "1 job/lane"},
+    {2, "2 jobs/lane"},
+    {4, "4 jobs/lane"},
 };
 constexpr int kNumSwigluVariants = sizeof(kSwigluVariants) / sizeof(kSwigluVariants[0]);
 
@@ -149,39 +149,34 @@ const SwigluVariant *swiglu_variant(int id)
 }
 
 template <int U, bool Q>
-static hipError_t launch_one(const SwigluParams &p, int blocks_per_cu, int num_cus,
-                             hipStream_t stream)
+static hipError_t launch_one(const SwigluParams &p, hipStream_t stream)
 {
-    const uint64_t per_block = 256u * (uint64_t)U;
-    uint64_t blocks = (p.jobs + per_block - 1) / per_block;
-    if (blocks_per_cu > 0) {
-        const uint64_t cap = (uint64_t)num_cus * (uint64_t)blocks_per_cu;
-        if (blocks > cap) blocks = cap;
-    }
+    const uint32_t per_block = 256u * U;
+    const uint64_t T = (uint64_t)p.tokens;
+    const dim3 grid((p.vecs_per_row + per_block - 1) / per_block,
+                    (unsigned)(T < SWIGLU_ROWS_PER_Y ? T : SWIGLU_ROWS_PER_Y),
+                    (unsigned)((T + SWIGLU_ROWS_PER_Y - 1) / SWIGLU_ROWS_PER_Y));
     SwigluParams copy = p;
     void *args[] = {&copy};
-    return hipLaunchKernel((const void *)&swiglu_kernel<U, Q>, dim3((unsigned)blocks), dim3(256),
-                           args, 0, stream);
+    return hipLaunchKernel((const void *)&swiglu_kernel<U, Q>, grid, dim3(256), args, 0, stream);
 }
 
 template <bool Q>
-static hipError_t dispatch(const SwigluParams &p, int variant, int num_cus, hipStream_t s)
+static hipError_t dispatch(const SwigluParams &p, int variant, hipStream_t s)
 {
     const SwigluVariant *v = swiglu_variant(variant);
     if (!v) return hipErrorInvalidValue;
     switch (v->jobs_per_lane) {
-    case 1: return launch_one<1, Q>(p, v->blocks_per_cu, num_cus, s);
-    case 2: return launch_one<2, Q>(p, v->blocks_per_cu, num_cus, s);
-    case 4: return launch_one<4, Q>(p, v->blocks_per_cu, num_cus, s);
+    case 1: return launch_one<1, Q>(p, s);
+    case 2: return launch_one<2, Q>(p, s);
+    case 4: return launch_one<4, Q>(p, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, int num_cus,
-                         hipStream_t stream)
+hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, hipStream_t stream)
 {
-    return quant ? dispatch<true>(p, variant, num_cus, stream)
-                 : dispatch<false>(p, variant, num_cus, stream);
+    return quant ? dispatch<true>(p, variant, stream) : dispatch<false>(p, variant, stream);
 }
 
 }  // namespace aarms

@@ -164,20 +164,10 @@ def main():
         step(i)
     ms_step = timer.region(step, K)
 
-    # per-kernel durations with HIP events on the launch stream, same rotation
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        s = sets[i % n_sets]
-        ev[i][0].record()
-        norm_call(s)
-        ev[i][1].record()
-        swiglu_call(s)
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    norm_us = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
-    swiglu_us = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
+    # per-kernel durations: each kernel alone, K back-to-back launches over
+    # the same rotation, HIP events on the launch stream at both ends
+    norm_us = timer.region(lambda i: norm_call(sets[i % n_sets]), K) * 1e3
+    swiglu_us = timer.region(lambda i: swiglu_call(sets[i % n_sets]), K) * 1e3
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     src_hash = kernel_sources_hash()

@@ -148,16 +148,17 @@ const char *aarms_status_string(int status);
 
 /*
  * Kernel variants, for tuning sweeps.  The plain entry points pick a variant
- * from (num_tokens, width); the *_ex forms take it explicitly.  A variant id
- * is an index into the op's table; aarms_variant_name() describes it
- * (static storage) and returns NULL past the end.  ops: 0 = fused_add_rmsnorm
- * and fused_add_rmsnorm_quant_fp8, 1 = swiglu and swiglu_quant_fp8.
+ * from (num_tokens, width, output format); the *_ex forms take it
+ * explicitly.  A variant id is an index into the op's table;
+ * aarms_variant_name() describes it (static storage) and returns NULL past
+ * the end.  ops: 0 = fused_add_rmsnorm and fused_add_rmsnorm_quant_fp8,
+ * 1 = swiglu and swiglu_quant_fp8 (quant != 0 selects the FP8 form).
  * aarms_pick_variant() returns the id the plain entry point would use, or -1
  * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
  */
 int aarms_variant_count(int op);
 const char *aarms_variant_name(int op, int variant);
-int aarms_pick_variant(int op, int64_t num_tokens, int64_t width);
+int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant);
 
 int fused_add_rmsnorm_ex(void *out, void *residual_out,
                          const void *x, const void *residual, const void *weight,
