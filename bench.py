@@ -80,6 +80,15 @@ class Timer:
         return a.elapsed_time(b) / reps  # ms per rep
 
 
+MALL_BYTES = 256e6             # MI355X last-level (Infinity) cache
+
+
+def rotation_sets(bytes_per_launch):
+    """Buffer sets to rotate so that one cycle touches >= 2x the LLC."""
+    import math
+    return max(2, math.ceil(2 * MALL_BYTES / bytes_per_launch))
+
+
 def traffic_from_profiles(kernel_key: str, src_hash: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel sources; else None."""
@@ -132,32 +141,36 @@ def main():
     step_bytes_norm = norm_bytes(T, H)
     step_bytes_swiglu = swiglu_bytes(T, N)
     step_bytes = step_bytes_norm + step_bytes_swiglu
-    n_sets = max(2, int(np.ceil(2 * 256e6 / step_bytes)) + 0)
-    sets = []
-    for _ in range(n_sets):
-        s = dict(x=x0.clone(), r=r0.clone(), w=w0.clone(), gu=gu0.clone(),
-                 out=torch.empty_like(x0), ro=torch.empty_like(r0),
-                 y=torch.empty((T, N), dtype=torch.bfloat16, device=dev))
-        s["p_norm"] = (s["out"].data_ptr(), s["ro"].data_ptr(), s["x"].data_ptr(), s["r"].data_ptr(),
-                       s["w"].data_ptr())
-        s["p_sw"] = (s["y"].data_ptr(), s["gu"].data_ptr())
-        sets.append(s)
+    # Separate rotation pools for the two ops, each cycling through at least
+    # twice the 256 MB last-level cache, so that every launch -- in the step
+    # loop and in the per-kernel loops -- reads HBM.
+    n_norm = rotation_sets(step_bytes_norm)
+    n_sw = rotation_sets(step_bytes_swiglu)
+    norm_sets, sw_sets = [], []
+    for _ in range(n_norm):
+        s = dict(x=x0.clone(), r=r0.clone(), out=torch.empty_like(x0), ro=torch.empty_like(r0))
+        s["p"] = (s["out"].data_ptr(), s["ro"].data_ptr(), s["x"].data_ptr(), s["r"].data_ptr(),
+                  w0.data_ptr())
+        norm_sets.append(s)
+    for _ in range(n_sw):
+        s = dict(gu=gu0.clone(), y=torch.empty((T, N), dtype=torch.bfloat16, device=dev))
+        s["p"] = (s["y"].data_ptr(), s["gu"].data_ptr())
+        sw_sets.append(s)
     eps = wn.eps
 
-    def norm_call(s):
-        st = lib.fused_add_rmsnorm(*s["p_norm"], T, H, eps, sp)
+    def norm_call(i):
+        st = lib.fused_add_rmsnorm(*norm_sets[i % n_norm]["p"], T, H, eps, sp)
         if st:
             raise A.AarmsError(st, "fused_add_rmsnorm")
 
-    def swiglu_call(s):
-        st = lib.swiglu(*s["p_sw"], T, N, sp)
+    def swiglu_call(i):
+        st = lib.swiglu(*sw_sets[i % n_sw]["p"], T, N, sp)
         if st:
             raise A.AarmsError(st, "swiglu")
 
     def step(i):
-        s = sets[i % n_sets]
-        norm_call(s)
-        swiglu_call(s)
+        norm_call(i)
+        swiglu_call(i)
 
     K, Wu = args.steps, args.warmup
     for i in range(Wu):
@@ -166,8 +179,8 @@ def main():
 
     # per-kernel durations: each kernel alone, K back-to-back launches over
     # the same rotation, HIP events on the launch stream at both ends
-    norm_us = timer.region(lambda i: norm_call(sets[i % n_sets]), K) * 1e3
-    swiglu_us = timer.region(lambda i: swiglu_call(sets[i % n_sets]), K) * 1e3
+    norm_us = timer.region(norm_call, K) * 1e3
+    swiglu_us = timer.region(swiglu_call, K) * 1e3
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     src_hash = kernel_sources_hash()
@@ -188,12 +201,9 @@ def main():
                            "GB/s": round(step_bytes_norm / (norm_us * 1e-6) / 1e9, 1)},
         "swiglu_4096x17920": {"bytes": step_bytes_swiglu, "avg_launch_us": round(swiglu_us, 2),
                               "GB/s": roof["achieved"]},
-        "buffer_sets_rotated": n_sets,
+        "buffer_sets_rotated": {"norm": n_norm, "swiglu": n_sw},
     }
-    for s in sets:
-        for k in list(s):
-            s[k] = None
-    del sets
+    del norm_sets, sw_sets, x0, r0, gu0
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ supplementary
@@ -251,12 +261,13 @@ def supplementary(args, torch, np, A, lib, W, dev, sp, timer, to_dev):
     T, N = wl.tokens, wl.inter
     g = torch.Generator(device=dev).manual_seed(0)
     gu = (torch.randn((T, 2 * N), generator=g, device=dev, dtype=torch.float32) * wl.gate_up_std).to(torch.bfloat16)
-    sets = [(gu if i == 0 else gu.clone(), torch.empty((T, N), dtype=torch.uint8, device=dev)) for i in range(2)]
+    n4 = rotation_sets(swiglu_bytes(T, N, quant=True))
+    sets = [(gu if i == 0 else gu.clone(), torch.empty((T, N), dtype=torch.uint8, device=dev)) for i in range(n4)]
     scale = torch.tensor([wl.scale], dtype=torch.float32, device=dev)
     ptr = [(o.data_ptr(), a.data_ptr(), scale.data_ptr()) for a, o in sets]
 
     def call4(i):
-        st = lib.swiglu_quant_fp8(*ptr[i % 2], T, N, sp)
+        st = lib.swiglu_quant_fp8(*ptr[i % n4], T, N, sp)
         if st:
             raise A.AarmsError(st, "swiglu_quant_fp8")
 
@@ -277,7 +288,7 @@ def supplementary(args, torch, np, A, lib, W, dev, sp, timer, to_dev):
     d = W.norm_inputs(wl)
     x0, r0, w0 = to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["weight"])
     b = norm_bytes(T, H, quant=True)
-    n_sets = int(np.ceil(2 * 256e6 / b))
+    n_sets = rotation_sets(b)
     sets = []
     for i in range(n_sets):
         s = dict(x=x0.clone(), r=r0.clone(), q=torch.empty((T, H), dtype=torch.uint8, device=dev),
