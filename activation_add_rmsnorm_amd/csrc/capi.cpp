@@ -6,6 +6,7 @@
 #include "aarms.h"
 #include "launch.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -58,6 +59,24 @@ int check_outputs(const Arg *outs, const int *partner, int n_out, const Arg *ins
     return AARMS_OK;
 }
 
+// Compute units of the current device, cached per device (the grid of the
+// persistent variants is sized from it).
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 int norm_capacity(const NormVariant *v) { return v->waves_per_row * 64 * v->vecs_per_lane * 8; }
 
 int pick_norm(int64_t tokens, int64_t hidden, bool quant)
@@ -73,7 +92,7 @@ int pick_norm(int64_t tokens, int64_t hidden, bool quant)
     if (hidden <= 4096) {
         for (int i = 0; i < n; ++i) {
             const NormVariant *v = norm_variant(i);
-            if (v->waves_per_row == 1 && norm_capacity(v) >= hidden) return i;
+            if (v->blocks_per_cu == 0 && v->waves_per_row == 1 && norm_capacity(v) >= hidden) return i;
         }
     }
     const int max_vecs = quant ? 4 : 8;
@@ -82,7 +101,7 @@ int pick_norm(int64_t tokens, int64_t hidden, bool quant)
             int best = -1;
             for (int i = 0; i < n; ++i) {
                 const NormVariant *v = norm_variant(i);
-                if (v->waves_per_row != w || norm_capacity(v) < hidden) continue;
+                if (v->blocks_per_cu != 0 || v->waves_per_row != w || norm_capacity(v) < hidden) continue;
                 if (pass == 0 && v->vecs_per_lane > max_vecs) continue;
                 if (best < 0 || v->vecs_per_lane < norm_variant(best)->vecs_per_lane) best = i;
             }
@@ -147,7 +166,7 @@ int norm_common(void *out, float *scale_out, void *residual_out, const void *x,
     p.tokens = tokens;
     p.hidden = (int32_t)hidden;
     p.eps = eps;
-    return launch_status(launch_norm(p, quant, variant, stream));
+    return launch_status(launch_norm(p, quant, variant, device_cus(), stream));
 }
 
 int swiglu_common(void *out, const void *gate_up, const float *scale, int64_t tokens,

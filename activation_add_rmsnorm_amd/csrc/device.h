@@ -81,11 +81,15 @@ __device__ __forceinline__ bool e4m3_scale_is_fast(const E4m3Scale &q)
     return q.s >= 0x1p-126f && q.s <= 0x1p118f;
 }
 
-template <bool FAST>
+// CLAMP = false is for per-token scales s = binary32(amax / 448), where every
+// |y| <= amax gives |y / s| <= 448 (1 + 2^-24) and the input clamp is moot.
+template <bool FAST, bool CLAMP = true>
 __device__ __forceinline__ float e4m3_quotient(float y, const E4m3Scale &q)
 {
     if constexpr (FAST) {
-        const float yc = __builtin_elementwise_minimum(__builtin_elementwise_maximum(y, -q.lim), q.lim);
+        float yc = y;
+        if constexpr (CLAMP)
+            yc = __builtin_elementwise_minimum(__builtin_elementwise_maximum(y, -q.lim), q.lim);
         const float q0 = yc * q.inv;
         // rem = q0 s - y is exact; z = q0 - rem * inv.  Written this way round
         // (rather than y - q0 s) so that a zero quotient keeps the sign of y.

@@ -36,6 +36,8 @@ constexpr uint32_t SWIGLU_ROWS_PER_Y = 65535;
 struct NormVariant {
     int waves_per_row;
     int vecs_per_lane;
+    int blocks_per_cu;       // 0: one block per row (or row quartet); else a persistent,
+                             // software-pipelined grid of this many blocks per CU
     const char *name;
 };
 
@@ -49,7 +51,8 @@ const NormVariant *norm_variant(int id);
 int swiglu_variant_count();
 const SwigluVariant *swiglu_variant(int id);
 
-hipError_t launch_norm(const NormParams &p, bool quant, int variant, hipStream_t stream);
+hipError_t launch_norm(const NormParams &p, bool quant, int variant, int num_cus,
+                       hipStream_t stream);
 hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, hipStream_t stream);
 
 }  // namespace aarms

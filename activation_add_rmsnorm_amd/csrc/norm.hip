@@ -20,10 +20,10 @@
 
 namespace aarms {
 
-// q = e4m3(clamp(y / s)) for this lane's slices of the row, stored as 8-byte
-// groups.
+// q = e4m3(clamp(y / s)) for this lane's slices of the row (y as binary32
+// values of bf16), stored as 8-byte groups.
 template <int WPR, int VPT, bool FAST>
-__device__ __forceinline__ void quantize_row(const u32x4 (&yv)[VPT], const E4m3Scale &qs,
+__device__ __forceinline__ void quantize_row(const float (&yf)[VPT][8], const E4m3Scale &qs,
                                              uint8_t *qo, int lane, int nvec)
 {
 #pragma unroll
@@ -32,10 +32,7 @@ __device__ __forceinline__ void quantize_row(const u32x4 (&yv)[VPT], const E4m3S
         if (v >= nvec) continue;
         float z[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            z[2 * e] = e4m3_quotient<FAST>(bf_lo(yv[k][e]), qs);
-            z[2 * e + 1] = e4m3_quotient<FAST>(bf_hi(yv[k][e]), qs);
-        }
+        for (int j = 0; j < 8; ++j) z[j] = e4m3_quotient<FAST, false>(yf[k][j], qs);
         u32x2 q;
         q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
         q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
@@ -43,50 +40,58 @@ __device__ __forceinline__ void quantize_row(const u32x4 (&yv)[VPT], const E4m3S
     }
 }
 
-template <int WPR, int VPT, bool QUANT>
-__global__ void __launch_bounds__(WPR == 1 ? 256 : WPR * 64)
-norm_kernel(NormParams p)
+template <int WPR, int VPT>
+__device__ __forceinline__ void load_row(const NormParams &p, int64_t row, int lane, int nvec,
+                                         u32x4 (&xv)[VPT], u32x4 (&rv)[VPT])
 {
-    constexpr int ROW_THREADS = WPR * 64;
-    constexpr int ROWS_PER_BLOCK = (WPR == 1) ? 4 : 1;
-    __shared__ double part_sum[WPR];
-    __shared__ float part_max[WPR];
-
-    const int tid = threadIdx.x;
-    const int lane = tid % ROW_THREADS;
-    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + tid / ROW_THREADS;
-    // WPR == 1: the test is per wave (no block barrier follows); WPR > 1:
-    // one row per block, so the whole block leaves together.
-    if (row >= p.tokens) return;
-
-    const int H = p.hidden;
-    const int nvec = H >> 3;
-    const size_t base = (size_t)row * (size_t)H;
+    const size_t base = (size_t)row * (size_t)p.hidden;
     const u32x4 *xr = (const u32x4 *)((const uint16_t *)p.x + base);
     const u32x4 *rr = (const u32x4 *)((const uint16_t *)p.residual + base);
-    const u32x4 *wr = (const u32x4 *)p.weight;
-    u32x4 *ro = (u32x4 *)((uint16_t *)p.residual_out + base);
-
-    // ---- load the row slice (all loads in flight before any use)
-    u32x4 xv[VPT], rv[VPT], wv[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const int v = lane + k * ROW_THREADS;
+        const int v = lane + k * WPR * 64;
         const bool ok = v < nvec;
         xv[k] = ok ? ld_stream(xr + v) : (u32x4)0u;
         rv[k] = ok ? ld_stream(rr + v) : (u32x4)0u;
     }
+}
+
+template <int WPR, int VPT>
+__device__ __forceinline__ void load_weight(const NormParams &p, int lane, int nvec, u32x4 (&wv)[VPT])
+{
+    const u32x4 *wr = (const u32x4 *)p.weight;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const int v = lane + k * ROW_THREADS;
+        const int v = lane + k * WPR * 64;
         wv[k] = (v < nvec) ? wr[v] : (u32x4)0u;
     }
+}
 
-    // ---- residual add (binary32, one rounding), store, sum of squares
-    double acc = 0.0;
+// Everything after the row's loads: residual add and store, sum of squares,
+// the row reduction (through psum when the row spans several waves), the
+// normalization and the epilogue.  With W_LATE the weight is loaded here,
+// after the first pass, so that its registers are not live while the row
+// loads are in flight.
+template <int WPR, int VPT, bool QUANT, bool W_LATE>
+__device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int lane, int nvec,
+                                           const u32x4 (&xv)[VPT], u32x4 (&rv)[VPT],
+                                           u32x4 (&wv)[VPT], double *psum, float *pmax)
+{
+    const size_t base = (size_t)row * (size_t)p.hidden;
+    u32x4 *ro = (u32x4 *)((uint16_t *)p.residual_out + base);
+
+    // ---- residual add (binary32, one rounding), store, sum of squares.
+    // With few vectors per lane the FP8 form keeps h = f32(r) for the
+    // epilogue (fewer instructions); otherwise the packed words are kept
+    // (fewer registers, so more rows in flight) and widened again.
+    constexpr bool KEEP = QUANT && VPT <= 2;
+    // four independent binary64 chains (one per word of a vector), summed in
+    // a fixed order at the end: a quarter of the dependent-FMA latency
+    double acc4[4] = {0.0, 0.0, 0.0, 0.0};
+    float hf[QUANT ? VPT : 1][8];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const int v = lane + k * ROW_THREADS;
+        const int v = lane + k * WPR * 64;
         u32x4 r;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -95,23 +100,32 @@ norm_kernel(NormParams p)
         if (v < nvec) st_stream(ro + v, r);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const double h0 = (double)bf_lo(r[e]);
-            const double h1 = (double)bf_hi(r[e]);
-            acc = __builtin_fma(h0, h0, acc);
-            acc = __builtin_fma(h1, h1, acc);
+            const float h0 = bf_lo(r[e]), h1 = bf_hi(r[e]);
+            if constexpr (KEEP) {
+                hf[k][2 * e] = h0;
+                hf[k][2 * e + 1] = h1;
+            }
+            acc4[e] = __builtin_fma((double)h0, (double)h0, acc4[e]);
+            acc4[e] = __builtin_fma((double)h1, (double)h1, acc4[e]);
         }
+    }
+    double acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    if constexpr (W_LATE) {
+        // keep the scheduler from hoisting these loads back to the top
+        __builtin_amdgcn_sched_barrier(0);
+        load_weight<WPR, VPT>(p, lane, nvec, wv);
     }
     acc = wave_sum(acc);
     if constexpr (WPR > 1) {
-        if ((lane & 63) == 0) part_sum[lane >> 6] = acc;
+        if ((lane & 63) == 0) psum[lane >> 6] = acc;
         __syncthreads();
-        acc = part_sum[0];
+        acc = psum[0];
 #pragma unroll
-        for (int i = 1; i < WPR; ++i) acc += part_sum[i];
+        for (int i = 1; i < WPR; ++i) acc += psum[i];
     }
 
     // ---- mean (rounded once to binary32), + eps, reciprocal square root
-    const float mean = (float)(acc / (double)H);
+    const float mean = (float)(acc / (double)p.hidden);
     const float var = mean + p.eps;
     const float rs = (float)(1.0 / sqrt((double)var));
 
@@ -120,7 +134,7 @@ norm_kernel(NormParams p)
         u32x4 *o = (u32x4 *)((uint16_t *)p.out + base);
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int v = lane + k * ROW_THREADS;
+            const int v = lane + k * WPR * 64;
             if (v >= nvec) continue;
             u32x4 y;
 #pragma unroll
@@ -131,26 +145,29 @@ norm_kernel(NormParams p)
             st_stream(o + v, y);
         }
     } else {
-        // ---- y as above, kept in registers; row amax
+        // ---- y as above, kept as binary32 values of bf16; row amax.  Slices
+        // past the row end hold w = 0, so y = 0 there.
         float amax = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            u32x4 y;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t t = pack_bf16(bf_lo(rv[k][e]) * rs, bf_hi(rv[k][e]) * rs);
-                y[e] = pack_bf16(bf_lo(wv[k][e]) * bf_lo(t), bf_hi(wv[k][e]) * bf_hi(t));
-                amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf_lo(y[e])), __builtin_fabsf(bf_hi(y[e]))));
+                const float h0 = KEEP ? hf[k][2 * e] : bf_lo(rv[k][e]);
+                const float h1 = KEEP ? hf[k][2 * e + 1] : bf_hi(rv[k][e]);
+                const uint32_t t = pack_bf16(h0 * rs, h1 * rs);
+                const uint32_t y = pack_bf16(bf_lo(wv[k][e]) * bf_lo(t), bf_hi(wv[k][e]) * bf_hi(t));
+                hf[k][2 * e] = bf_lo(y);
+                hf[k][2 * e + 1] = bf_hi(y);
+                amax = fmaxf(amax, fmaxf(__builtin_fabsf(hf[k][2 * e]), __builtin_fabsf(hf[k][2 * e + 1])));
             }
-            rv[k] = y;   // slices past the row end hold w = 0, so y = 0
         }
         amax = wave_max(amax);
         if constexpr (WPR > 1) {
-            if ((lane & 63) == 0) part_max[lane >> 6] = amax;
+            if ((lane & 63) == 0) pmax[lane >> 6] = amax;
             __syncthreads();
-            amax = part_max[0];
+            amax = pmax[0];
 #pragma unroll
-            for (int i = 1; i < WPR; ++i) amax = fmaxf(amax, part_max[i]);
+            for (int i = 1; i < WPR; ++i) amax = fmaxf(amax, pmax[i]);
         }
         // ---- per-token scale, then q = e4m3(clamp(y / s))
         const float s = amax / 448.0f;
@@ -158,22 +175,114 @@ norm_kernel(NormParams p)
         const E4m3Scale qs = make_e4m3_scale(s);
         uint8_t *qo = (uint8_t *)p.out + base;
         if (e4m3_scale_is_fast(qs))
-            quantize_row<WPR, VPT, true>(rv, qs, qo, lane, nvec);
+            quantize_row<WPR, VPT, true>(hf, qs, qo, lane, nvec);
         else
-            quantize_row<WPR, VPT, false>(rv, qs, qo, lane, nvec);
+            quantize_row<WPR, VPT, false>(hf, qs, qo, lane, nvec);
+    }
+}
+
+// One row per block (WPR > 1) or per wave (WPR == 1, four rows per block);
+// one block per row or row quartet.
+template <int WPR, int VPT, bool QUANT>
+__global__ void __launch_bounds__(WPR == 1 ? 256 : WPR * 64)
+norm_kernel(NormParams p)
+{
+    constexpr int ROW_THREADS = WPR * 64;
+    constexpr int ROWS_PER_BLOCK = (WPR == 1) ? 4 : 1;
+    __shared__ double psum[WPR];
+    __shared__ float pmax[WPR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % ROW_THREADS;
+    // the row is uniform over the wave (WPR == 1) or the block, and is made a
+    // scalar so that row addresses are scalar bases plus one lane offset
+    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK +
+                        (WPR == 1 ? __builtin_amdgcn_readfirstlane(tid / ROW_THREADS) : 0);
+    // WPR == 1: the test is per wave (no block barrier follows); WPR > 1:
+    // one row per block, so the whole block leaves together.
+    if (row >= p.tokens) return;
+    const int nvec = p.hidden >> 3;
+
+    // all loads of the row slice in flight before any use
+    u32x4 xv[VPT], rv[VPT], wv[VPT];
+    load_row<WPR, VPT>(p, row, lane, nvec, xv, rv);
+    constexpr bool W_LATE = WPR > 1;
+    if constexpr (!W_LATE) load_weight<WPR, VPT>(p, lane, nvec, wv);
+    finish_row<WPR, VPT, QUANT, W_LATE>(p, row, lane, nvec, xv, rv, wv, psum, pmax);
+}
+
+// Persistent and software-pipelined: a fixed grid of blocks walks the rows
+// (row, row + G, row + 2G, ...); the weight is loaded once per block, and the
+// next row's x and residual are loaded before the current row is processed,
+// so their latency hides behind its reductions and stores.  The blocks in
+// flight always cover a window of G consecutive rows.
+template <int WPR, int VPT, bool QUANT>
+__global__ void __launch_bounds__(WPR == 1 ? 256 : WPR * 64)
+norm_kernel_pipelined(NormParams p)
+{
+    constexpr int ROW_THREADS = WPR * 64;
+    constexpr int ROWS_PER_BLOCK = (WPR == 1) ? 4 : 1;
+    // the bf16 form has one barrier per row, so a fast wave could write the
+    // next row's partial sums while a slow one still reads these: two sets
+    __shared__ double psum[2][WPR];
+    __shared__ float pmax[WPR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % ROW_THREADS;
+    const int64_t step = (int64_t)gridDim.x * ROWS_PER_BLOCK;
+    int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK +
+                  (WPR == 1 ? __builtin_amdgcn_readfirstlane(tid / ROW_THREADS) : 0);
+    // uniform per block for WPR > 1, per wave for WPR == 1
+    if (row >= p.tokens) return;
+    const int nvec = p.hidden >> 3;
+
+    u32x4 wv[VPT];
+    load_weight<WPR, VPT>(p, lane, nvec, wv);
+    u32x4 xa[VPT], ra[VPT];
+    load_row<WPR, VPT>(p, row, lane, nvec, xa, ra);
+    int par = 0;
+    while (true) {
+        const int64_t next = row + step;
+        const bool more = next < p.tokens;
+        u32x4 xb[VPT], rb[VPT];
+        if (more) {
+            load_row<WPR, VPT>(p, next, lane, nvec, xb, rb);
+        } else {
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) xb[k] = rb[k] = (u32x4)0u;
+        }
+        finish_row<WPR, VPT, QUANT, false>(p, row, lane, nvec, xa, ra, wv, psum[par], pmax);
+        if (!more) break;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            xa[k] = xb[k];
+            ra[k] = rb[k];
+        }
+        row = next;
+        par ^= 1;
     }
 }
 
 // ---------------------------------------------------------------- variants
 
 static const NormVariant kNormVariants[] = {
-    {1, 1, "wave/row x1 vec"},   {1, 2, "wave/row x2 vec"},   {1, 3, "wave/row x3 vec"},
-    {1, 4, "wave/row x4 vec"},   {1, 6, "wave/row x6 vec"},   {1, 8, "wave/row x8 vec"},
-    {2, 2, "2 waves/row x2 vec"}, {2, 4, "2 waves/row x4 vec"}, {2, 8, "2 waves/row x8 vec"},
-    {4, 1, "4 waves/row x1 vec"}, {4, 2, "4 waves/row x2 vec"}, {4, 4, "4 waves/row x4 vec"},
-    {4, 8, "4 waves/row x8 vec"}, {8, 1, "8 waves/row x1 vec"}, {8, 2, "8 waves/row x2 vec"},
-    {8, 4, "8 waves/row x4 vec"}, {8, 8, "8 waves/row x8 vec"}, {16, 1, "16 waves/row x1 vec"},
-    {16, 2, "16 waves/row x2 vec"}, {16, 4, "16 waves/row x4 vec"}, {16, 8, "16 waves/row x8 vec"},
+    {1, 1, 0, "wave/row x1 vec"},   {1, 2, 0, "wave/row x2 vec"},   {1, 3, 0, "wave/row x3 vec"},
+    {1, 4, 0, "wave/row x4 vec"},   {1, 6, 0, "wave/row x6 vec"},   {1, 8, 0, "wave/row x8 vec"},
+    {2, 2, 0, "2 waves/row x2 vec"}, {2, 4, 0, "2 waves/row x4 vec"}, {2, 8, 0, "2 waves/row x8 vec"},
+    {4, 1, 0, "4 waves/row x1 vec"}, {4, 2, 0, "4 waves/row x2 vec"}, {4, 4, 0, "4 waves/row x4 vec"},
+    {4, 8, 0, "4 waves/row x8 vec"}, {8, 1, 0, "8 waves/row x1 vec"}, {8, 2, 0, "8 waves/row x2 vec"},
+    {8, 4, 0, "8 waves/row x4 vec"}, {8, 8, 0, "8 waves/row x8 vec"}, {16, 1, 0, "16 waves/row x1 vec"},
+    {16, 2, 0, "16 waves/row x2 vec"}, {16, 4, 0, "16 waves/row x4 vec"}, {16, 8, 0, "16 waves/row x8 vec"},
+    // persistent, software-pipelined (blocks per CU)
+    {1, 3, 4, "wave/row x3 vec, pipelined 4 blocks/CU"},
+    {1, 3, 8, "wave/row x3 vec, pipelined 8 blocks/CU"},
+    {1, 4, 4, "wave/row x4 vec, pipelined 4 blocks/CU"},
+    {8, 4, 2, "8 waves/row x4 vec, pipelined 2 blocks/CU"},
+    {16, 2, 1, "16 waves/row x2 vec, pipelined 1 block/CU"},
+    {8, 2, 2, "8 waves/row x2 vec, pipelined 2 blocks/CU"},
+    {4, 4, 4, "4 waves/row x4 vec, pipelined 4 blocks/CU"},
+    {16, 4, 1, "16 waves/row x4 vec, pipelined 1 block/CU"},
+    {16, 8, 1, "16 waves/row x8 vec, pipelined 1 block/CU"},
 };
 constexpr int kNumNormVariants = sizeof(kNormVariants) / sizeof(kNormVariants[0]);
 
@@ -183,50 +292,62 @@ const NormVariant *norm_variant(int id)
     return (id >= 0 && id < kNumNormVariants) ? &kNormVariants[id] : nullptr;
 }
 
-template <int WPR, int VPT, bool Q>
-static hipError_t launch_one(const NormParams &p, hipStream_t stream)
+template <int WPR, int VPT, bool Q, bool PIPE>
+static hipError_t launch_one(const NormParams &p, int blocks_per_cu, int num_cus,
+                             hipStream_t stream)
 {
     constexpr int threads = (WPR == 1) ? 256 : WPR * 64;
     constexpr int rows_per_block = (WPR == 1) ? 4 : 1;
-    const dim3 grid((unsigned)((p.tokens + rows_per_block - 1) / rows_per_block));
+    int64_t blocks = (p.tokens + rows_per_block - 1) / rows_per_block;
+    if (PIPE) {
+        const int64_t cap = (int64_t)num_cus * blocks_per_cu;
+        if (blocks > cap) blocks = cap;
+    }
     NormParams copy = p;
     void *args[] = {&copy};
-    return hipLaunchKernel((const void *)&norm_kernel<WPR, VPT, Q>, grid, dim3(threads), args, 0,
-                           stream);
+    const void *fn = PIPE ? (const void *)&norm_kernel_pipelined<WPR, VPT, Q>
+                          : (const void *)&norm_kernel<WPR, VPT, Q>;
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
 }
 
 template <bool Q>
-static hipError_t dispatch(const NormParams &p, int variant, hipStream_t s)
+static hipError_t dispatch(const NormParams &p, int variant, int num_cus, hipStream_t s)
 {
-    switch (variant) {
-    case 0: return launch_one<1, 1, Q>(p, s);
-    case 1: return launch_one<1, 2, Q>(p, s);
-    case 2: return launch_one<1, 3, Q>(p, s);
-    case 3: return launch_one<1, 4, Q>(p, s);
-    case 4: return launch_one<1, 6, Q>(p, s);
-    case 5: return launch_one<1, 8, Q>(p, s);
-    case 6: return launch_one<2, 2, Q>(p, s);
-    case 7: return launch_one<2, 4, Q>(p, s);
-    case 8: return launch_one<2, 8, Q>(p, s);
-    case 9: return launch_one<4, 1, Q>(p, s);
-    case 10: return launch_one<4, 2, Q>(p, s);
-    case 11: return launch_one<4, 4, Q>(p, s);
-    case 12: return launch_one<4, 8, Q>(p, s);
-    case 13: return launch_one<8, 1, Q>(p, s);
-    case 14: return launch_one<8, 2, Q>(p, s);
-    case 15: return launch_one<8, 4, Q>(p, s);
-    case 16: return launch_one<8, 8, Q>(p, s);
-    case 17: return launch_one<16, 1, Q>(p, s);
-    case 18: return launch_one<16, 2, Q>(p, s);
-    case 19: return launch_one<16, 4, Q>(p, s);
-    case 20: return launch_one<16, 8, Q>(p, s);
-    default: return hipErrorInvalidValue;
-    }
+    const NormVariant *v = norm_variant(variant);
+    if (!v) return hipErrorInvalidValue;
+    const int b = v->blocks_per_cu;
+#define AARMS_NORM_CASE(W, V)                                                              \
+    if (v->waves_per_row == W && v->vecs_per_lane == V)                                    \
+        return b ? launch_one<W, V, Q, true>(p, b, num_cus, s) : launch_one<W, V, Q, false>(p, 0, num_cus, s);
+    AARMS_NORM_CASE(1, 1)
+    AARMS_NORM_CASE(1, 2)
+    AARMS_NORM_CASE(1, 3)
+    AARMS_NORM_CASE(1, 4)
+    AARMS_NORM_CASE(1, 6)
+    AARMS_NORM_CASE(1, 8)
+    AARMS_NORM_CASE(2, 2)
+    AARMS_NORM_CASE(2, 4)
+    AARMS_NORM_CASE(2, 8)
+    AARMS_NORM_CASE(4, 1)
+    AARMS_NORM_CASE(4, 2)
+    AARMS_NORM_CASE(4, 4)
+    AARMS_NORM_CASE(4, 8)
+    AARMS_NORM_CASE(8, 1)
+    AARMS_NORM_CASE(8, 2)
+    AARMS_NORM_CASE(8, 4)
+    AARMS_NORM_CASE(8, 8)
+    AARMS_NORM_CASE(16, 1)
+    AARMS_NORM_CASE(16, 2)
+    AARMS_NORM_CASE(16, 4)
+    AARMS_NORM_CASE(16, 8)
+#undef AARMS_NORM_CASE
+    return hipErrorInvalidValue;
 }
 
-hipError_t launch_norm(const NormParams &p, bool quant, int variant, hipStream_t stream)
+hipError_t launch_norm(const NormParams &p, bool quant, int variant, int num_cus, hipStream_t stream)
 {
-    return quant ? dispatch<true>(p, variant, stream) : dispatch<false>(p, variant, stream);
+    return quant ? dispatch<true>(p, variant, num_cus, stream)
+                 : dispatch<false>(p, variant, num_cus, stream);
 }
 
 }  // namespace aarms

@@ -116,6 +116,27 @@ def test_norm_every_variant(H):
         P.check_norm_fp8(x, r, w, 1e-5, q, s, res_q)
 
 
+def test_norm_pipelined_variants_walk_several_rows():
+    """Persistent variants: T larger than the grid covers, so every block
+    walks at least two rows (and some a third), through the public API."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for v in range(A.variant_count(A.OP_NORM)):
+        name = A.variant_name(A.OP_NORM, v)
+        if "pipelined" not in name:
+            continue
+        w = 1 if name.startswith("wave/row") else int(name.split()[0])
+        vec = int(name.split("x")[-1].split()[0])
+        bpc = int(name.split("pipelined")[1].split()[0])
+        rows_per_block = 4 if w == 1 else 1
+        H = min(w * 64 * vec * 8, 16384) if w > 1 else 1536
+        T = 2 * cus * bpc * rows_per_block + 37
+        x, r, wt = norm_case(T, H, seed=v)
+        out, res_out = run_norm(x, r, wt, 1e-5, variant=v)
+        P.check_norm(x, r, wt, 1e-5, out, res_out)
+        q, s, res_q = run_norm_fp8(x, r, wt, 1e-5, variant=v)
+        P.check_norm_fp8(x, r, wt, 1e-5, q, s, res_q)
+
+
 def test_norm_decode16_full():
     wl = W.NORM_DECODE16
     d = W.norm_inputs(wl)
