@@ -79,35 +79,43 @@ int device_cus()
 
 int norm_capacity(const NormVariant *v) { return v->waves_per_row * 64 * v->vecs_per_lane * 8; }
 
+// One-shot variant with `waves` waves per row that fits the row with the
+// fewest vectors per lane, if that is at most max_vecs; else -1.
+static int norm_fit(int waves, int64_t hidden, int max_vecs)
+{
+    int best = -1;
+    for (int i = 0; i < norm_variant_count(); ++i) {
+        const NormVariant *v = norm_variant(i);
+        if (v->blocks_per_cu != 0 || v->waves_per_row != waves || norm_capacity(v) < hidden) continue;
+        if (v->vecs_per_lane > max_vecs) continue;
+        if (best < 0 || v->vecs_per_lane < norm_variant(best)->vecs_per_lane) best = i;
+    }
+    return best;
+}
+
+// Below this many rows a narrow-row launch is latency-bound (a few waves per
+// CU at most) and splitting each row over four waves shortens every row's
+// dependent chain of loads and reductions; from here on one wave per row
+// wins (measured on MI355X, 256 CUs, rows of 1,536).
+constexpr int64_t kNarrowMultiWaveTokens = 1024;
+
 int pick_norm(int64_t tokens, int64_t hidden, bool quant)
 {
-    (void)tokens;
+    (void)quant;
     if (hidden <= 0 || hidden > AARMS_MAX_HIDDEN) return -1;
-    // Narrow rows: one wave per row with as few vectors per lane as fit.
-    // Wide rows: the fewest waves per row that fit with 8 vectors per lane
-    // (the FP8 form, which keeps the row in registers through two
-    // reductions, prefers 4 vectors per lane: twice the waves, half the
-    // registers each).
-    const int n = norm_variant_count();
+    // Narrow rows: one wave per row with as few vectors per lane as fit (four
+    // waves per row for small batches).  Wide rows: the fewest waves per row
+    // that fit with at most 2 vectors per lane (the row's loads spread over
+    // many short slices, few registers per wave), else 4, else 8.
     if (hidden <= 4096) {
-        for (int i = 0; i < n; ++i) {
-            const NormVariant *v = norm_variant(i);
-            if (v->blocks_per_cu == 0 && v->waves_per_row == 1 && norm_capacity(v) >= hidden) return i;
-        }
+        const int i = norm_fit(tokens < kNarrowMultiWaveTokens ? 4 : 1, hidden, 8);
+        if (i >= 0) return i;
     }
-    const int max_vecs = quant ? 4 : 8;
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int max_vecs : {2, 4, 8})
         for (int w : {2, 4, 8, 16}) {
-            int best = -1;
-            for (int i = 0; i < n; ++i) {
-                const NormVariant *v = norm_variant(i);
-                if (v->blocks_per_cu != 0 || v->waves_per_row != w || norm_capacity(v) < hidden) continue;
-                if (pass == 0 && v->vecs_per_lane > max_vecs) continue;
-                if (best < 0 || v->vecs_per_lane < norm_variant(best)->vecs_per_lane) best = i;
-            }
-            if (best >= 0) return best;
+            const int i = norm_fit(w, hidden, max_vecs);
+            if (i >= 0) return i;
         }
-    }
     return -1;
 }
 

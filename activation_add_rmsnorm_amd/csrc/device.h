@@ -100,21 +100,88 @@ __device__ __forceinline__ float e4m3_quotient(float y, const E4m3Scale &q)
     }
 }
 
-// Butterfly sums and maxima over the 64 lanes of a wave.  Every lane ends
-// with the same bits: each step combines the same two operands on both
-// partner lanes, and IEEE addition is commutative.
+// Butterfly sums and maxima over the 64 lanes of a wave, entirely in VALU
+// lane permutations (no LDS round trips, which dominate a lone row's latency).
+// Each step combines v with its value on a partner lane, and every
+// permutation used is an involution that pairs lanes: lane ^ 1 and lane ^ 2
+// (DPP quad_perm), 7 - lane within 8 (row_half_mirror, pairs the two
+// quads), 15 - lane within 16 (row_mirror, pairs the two halves of a
+// row), then the two 16-lane rows of each 32-lane half and the two halves
+// (v_permlane16_swap / v_permlane32_swap, which hand every lane both
+// operands in the same order).  So every lane ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // row_half_mirror
+constexpr int DPP_MIRROR = 0x140;      // row_mirror
+
+// (a, b) with a = the value of the lower 16-lane row (32-lane half) of each
+// pair and b = the upper one, on every lane of the pair.
+template <int SPAN>
+__device__ __forceinline__ void swap_pair_u32(uint32_t v, uint32_t &a, uint32_t &b)
+{
+    if constexpr (SPAN == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        a = r[0];
+        b = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        a = r[0];
+        b = r[1];
+    }
+}
+
+template <int SPAN>
+__device__ __forceinline__ double swap_sum_f64(double v)
+{
+    const uint64_t bits = __builtin_bit_cast(uint64_t, v);
+    uint32_t alo, blo, ahi, bhi;
+    swap_pair_u32<SPAN>((uint32_t)bits, alo, blo);
+    swap_pair_u32<SPAN>((uint32_t)(bits >> 32), ahi, bhi);
+    const double a = __builtin_bit_cast(double, ((uint64_t)ahi << 32) | alo);
+    const double b = __builtin_bit_cast(double, ((uint64_t)bhi << 32) | blo);
+    return a + b;
+}
+
 __device__ __forceinline__ double wave_sum(double v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+    v += dpp_f64<DPP_XOR1>(v);
+    v += dpp_f64<DPP_XOR2>(v);
+    v += dpp_f64<DPP_HALF_MIRROR>(v);
+    v += dpp_f64<DPP_MIRROR>(v);
+    v = swap_sum_f64<16>(v);
+    return swap_sum_f64<32>(v);
+}
+
+template <int SPAN>
+__device__ __forceinline__ float swap_max_f32(float v)
+{
+    uint32_t a, b;
+    swap_pair_u32<SPAN>(__float_as_uint(v), a, b);
+    return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
 
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_MIRROR>(__float_as_uint(v))));
+    v = swap_max_f32<16>(v);
+    return swap_max_f32<32>(v);
 }
 
 // ---------------------------------------------------------------- SiLU
