@@ -1,4 +1,6 @@
-"""Build libaarms.so in-tree with hipcc for gfx950.
+"""Build libaarms.so (the library) and libaarms_ceiling.so (a plain streaming
+kernel that bench.py times beside the library kernels) in-tree with hipcc for
+gfx950.
 
 Flags:
   -ffp-contract=off    no implicit fused multiply-add: every fma in the kernels
@@ -22,10 +24,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libaarms.so")
+CEILING_PATH = os.path.join(PKG, "libaarms_ceiling.so")
 ARCH = os.environ.get("AARMS_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["norm.hip", "swiglu.hip"]
 HOST_SOURCES = ["capi.cpp"]
+CEILING_SOURCES = ["ceiling.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
           "-ffp-contract=off", "-I", INCLUDE, "-I", CSRC]
@@ -40,21 +44,7 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libaarms.so; returns its path."""
-    hipcc = _hipcc()
-    objdir = os.path.join(ROOT, "_build")
-    os.makedirs(objdir, exist_ok=True)
-    objs = []
-    jobs = []
-    for src in HIP_SOURCES:
-        obj = os.path.join(objdir, src + ".o")
-        jobs.append([hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
-        objs.append(obj)
-    for src in HOST_SOURCES:
-        obj = os.path.join(objdir, src + ".o")
-        jobs.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
-        objs.append(obj)
+def _run(jobs, verbose):
     procs = []
     for cmd in jobs:
         if verbose:
@@ -74,10 +64,30 @@ def build(verbose: bool = False) -> str:
             print("FAILED: " + " ".join(cmd), file=sys.stderr)
     if failed:
         raise RuntimeError("hipcc failed")
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    link = [hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs]
-    subprocess.run(link, check=True)
-    os.replace(tmp, LIB_PATH)
+
+
+def _link(hipcc, objs, path):
+    tmp = path + ".tmp%d" % os.getpid()
+    subprocess.run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs], check=True)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libaarms.so and libaarms_ceiling.so;
+    returns the path of libaarms.so."""
+    hipcc = _hipcc()
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+
+    def obj(src):
+        return os.path.join(objdir, src + ".o")
+
+    jobs = [[hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, s), "-o", obj(s)]
+            for s in HIP_SOURCES + CEILING_SOURCES]
+    jobs += [[hipcc, *COMMON, "-c", os.path.join(CSRC, s), "-o", obj(s)] for s in HOST_SOURCES]
+    _run(jobs, verbose)
+    _link(hipcc, [obj(s) for s in HIP_SOURCES + HOST_SOURCES], LIB_PATH)
+    _link(hipcc, [obj(s) for s in CEILING_SOURCES], CEILING_PATH)
     return LIB_PATH
 
 

@@ -10,6 +10,12 @@ K back-to-back steps with the inputs already resident in HBM.  Three buffer
 sets are rotated so that every step reads HBM rather than the 256 MB
 last-level cache.
 
+Beside every kernel the same rotation of buffers is also streamed by a plain
+copy-like kernel (libaarms_ceiling.so) that reads and writes exactly the same
+bytes with no arithmetic: its time is what a launch of that size and
+read/write mix can reach on this device, and ``of_stream_ceiling`` is the
+kernel's time measured against it.
+
 The same run also measures, as supplementary figures, the static-FP8 SwiGLU
 on Llama-70B's [8192, 57344] gate_up, the dynamic-FP8 norm on Llama-405B's
 [2048, 16384] rows, the 16-token norm, and the 28-layer decode chain under a
@@ -40,7 +46,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -80,6 +86,22 @@ class Timer:
         return a.elapsed_time(b) / reps  # ms per rep
 
 
+    def warm(self, fn, seconds=0.1):
+        """Launch fn until about `seconds` of device time have passed: after
+        the host has left the GPU idle (input generation) its clocks take some
+        tens of milliseconds of load to settle."""
+        t = self.torch
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            for _ in range(20):
+                fn(n)
+                n += 1
+            t.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return n
+
+
 MALL_BYTES = 256e6             # MI355X last-level (Infinity) cache
 
 
@@ -100,6 +122,24 @@ def traffic_from_profiles(kernel_key: str, src_hash: str):
             if line.startswith("traffic_bytes_per_launch[" + kernel_key + "]:"):
                 return float(line.split(":", 1)[1].split()[0])
     return None
+
+
+def load_ceiling():
+    """libaarms_ceiling.so: the plain streaming kernel (built with the library)."""
+    import ctypes as C
+    from activation_add_rmsnorm_amd import _build
+    if not os.path.exists(_build.CEILING_PATH):
+        _build.build()
+    lib = C.CDLL(_build.CEILING_PATH)
+    vp, i32, i64 = C.c_void_p, C.c_int, C.c_int64
+    lib.aarms_stream_ceiling.argtypes = [vp, i32, vp, i32, vp, vp, i64, vp]
+    return lib
+
+
+def ceiling_entry(kernel_us, ceiling_us, nbytes):
+    return {"stream_ceiling_us": round(ceiling_us, 2),
+            "stream_ceiling_GB/s": round(nbytes / (ceiling_us * 1e-6) / 1e9, 1),
+            "of_stream_ceiling": round(ceiling_us / kernel_us, 3)}
 
 
 def kernel_sources_hash():
@@ -123,6 +163,7 @@ def main():
     from workloads import configs as W
 
     lib = A.load()
+    clib = load_ceiling()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -172,6 +213,20 @@ def main():
         norm_call(i)
         swiglu_call(i)
 
+    def stream(*a):
+        st = clib.aarms_stream_ceiling(*a, sp)
+        if st:
+            raise RuntimeError("aarms_stream_ceiling: %d" % st)
+
+    def norm_ceiling(i):
+        s = norm_sets[i % n_norm]
+        stream(s["ro"].data_ptr(), 16, s["out"].data_ptr(), 16, s["x"].data_ptr(), s["r"].data_ptr(), T * H // 8)
+
+    def swiglu_ceiling(i):
+        s = sw_sets[i % n_sw]
+        gu = s["gu"].data_ptr()
+        stream(s["y"].data_ptr(), 16, None, 0, gu, gu + T * N * 2, T * N // 8)
+
     K, Wu = args.steps, args.warmup
     for i in range(Wu):
         step(i)
@@ -181,6 +236,10 @@ def main():
     # the same rotation, HIP events on the launch stream at both ends
     norm_us = timer.region(norm_call, K) * 1e3
     swiglu_us = timer.region(swiglu_call, K) * 1e3
+    timer.warm(norm_ceiling, 0.02)
+    norm_ceil_us = timer.region(norm_ceiling, K) * 1e3
+    timer.warm(swiglu_ceiling, 0.02)
+    swiglu_ceil_us = timer.region(swiglu_ceiling, K) * 1e3
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     src_hash = kernel_sources_hash()
@@ -195,12 +254,15 @@ def main():
     roof["traffic"] = traffic_from_profiles("swiglu_qwen_prefill4096", src_hash)
     roof["bytes_per_launch"] = step_bytes_swiglu
     roof["avg_launch_us"] = round(swiglu_us, 2)
+    roof.update(ceiling_entry(swiglu_us, swiglu_ceil_us, step_bytes_swiglu))
 
     extra = {
         "norm_4096x1536": {"bytes": step_bytes_norm, "avg_launch_us": round(norm_us, 2),
-                           "GB/s": round(step_bytes_norm / (norm_us * 1e-6) / 1e9, 1)},
+                           "GB/s": round(step_bytes_norm / (norm_us * 1e-6) / 1e9, 1),
+                           **ceiling_entry(norm_us, norm_ceil_us, step_bytes_norm)},
         "swiglu_4096x17920": {"bytes": step_bytes_swiglu, "avg_launch_us": round(swiglu_us, 2),
-                              "GB/s": roof["achieved"]},
+                              "GB/s": roof["achieved"],
+                              **ceiling_entry(swiglu_us, swiglu_ceil_us, step_bytes_swiglu)},
         "buffer_sets_rotated": {"norm": n_norm, "swiglu": n_sw},
     }
     del norm_sets, sw_sets, x0, r0, gu0
@@ -209,7 +271,7 @@ def main():
     # ------------------------------------------------------------ supplementary
     configs = {}
     if not args.no_extra:
-        configs = supplementary(args, torch, np, A, lib, W, dev, sp, timer, to_dev)
+        configs = supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev)
 
     # ------------------------------------------------------------ cpu baseline
     cpu = None
@@ -252,9 +314,14 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def supplementary(args, torch, np, A, lib, W, dev, sp, timer, to_dev):
+def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
     out = {}
     reps = max(20, args.steps // 2)
+
+    def stream(*a):
+        st = clib.aarms_stream_ceiling(*a, sp)
+        if st:
+            raise RuntimeError("aarms_stream_ceiling: %d" % st)
 
     # static-FP8 SwiGLU, Llama-70B MLP: [8192, 57344] -> e4m3 [8192, 28672]
     wl = W.SWIGLU_FP8_LLAMA70B
@@ -271,13 +338,19 @@ def supplementary(args, torch, np, A, lib, W, dev, sp, timer, to_dev):
         if st:
             raise A.AarmsError(st, "swiglu_quant_fp8")
 
-    for i in range(5):
-        call4(i)
+    def ceil4(i):
+        o, a, _ = ptr[i % n4]
+        stream(o, 8, None, 0, a, a + T * N * 2, T * N // 8)
+
+    timer.warm(call4)
     ms = timer.region(call4, reps)
+    timer.warm(ceil4)
+    ms_c = timer.region(ceil4, reps)
     b = swiglu_bytes(T, N, quant=True)
     out["llama70b_swiglu_fp8_8192x57344"] = {"bytes": b, "avg_launch_us": round(ms * 1e3, 2),
                                               "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
                                               "pct_of_hbm_peak": round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                                              **ceiling_entry(ms * 1e3, ms_c * 1e3, b),
                                               "inputs": "torch.randn on device, seed 0, std 2"}
     del sets, gu, ptr
     torch.cuda.empty_cache()
@@ -302,12 +375,18 @@ def supplementary(args, torch, np, A, lib, W, dev, sp, timer, to_dev):
         if st:
             raise A.AarmsError(st, "fused_add_rmsnorm_quant_fp8")
 
-    for i in range(5):
-        call5(i)
+    def ceil5(i):
+        s = sets[i % n_sets]
+        stream(s["ro"].data_ptr(), 16, s["q"].data_ptr(), 8, s["x"].data_ptr(), s["r"].data_ptr(), T * H // 8)
+
+    timer.warm(call5)
     ms = timer.region(call5, reps)
+    timer.warm(ceil5)
+    ms_c = timer.region(ceil5, reps)
     out["llama405b_norm_fp8_2048x16384"] = {"bytes": b, "avg_launch_us": round(ms * 1e3, 2),
                                              "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
                                              "pct_of_hbm_peak": round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                                             **ceiling_entry(ms * 1e3, ms_c * 1e3, b),
                                              "buffer_sets_rotated": n_sets}
     del sets
     torch.cuda.empty_cache()
@@ -322,8 +401,7 @@ def supplementary(args, torch, np, A, lib, W, dev, sp, timer, to_dev):
     def call1(i):
         lib.fused_add_rmsnorm(*p, wl.tokens, wl.hidden, wl.eps, sp)
 
-    for i in range(10):
-        call1(i)
+    timer.warm(call1, 0.02)
     ms = timer.region(call1, reps)
     out["qwen1.5b_norm_16x1536"] = {"bytes": norm_bytes(16, 1536), "avg_launch_us": round(ms * 1e3, 2)}
 
@@ -361,8 +439,7 @@ def decode_graph(torch, np, A, W, dev, to_dev, timer):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             chain()
-        for _ in range(5):
-            g.replay()
+        timer.warm(lambda i: g.replay(), 0.05)
         reps = 50
         ms_graph = timer.region(lambda i: g.replay(), reps)
         ms_eager = timer.region(lambda i: chain(), 10)

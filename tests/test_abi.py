@@ -190,3 +190,22 @@ def test_pick_variant_ranges():
     assert A.pick_variant(A.OP_NORM, 16, MAX_HIDDEN + 8) == -1
     assert A.pick_variant(A.OP_SWIGLU, 16, 8960) >= 0
     assert A.pick_variant(A.OP_SWIGLU, 16, 12) == -1
+
+
+def test_ceiling_library_rejects_bad_arguments():
+    # the streaming reference kernel bench.py times beside each op: only its
+    # argument checks run here (they return before any HIP call)
+    from activation_add_rmsnorm_amd import _build
+    if not os.path.exists(_build.CEILING_PATH):
+        _build.build()
+    lib = C.CDLL(_build.CEILING_PATH)
+    vp, i32, i64 = C.c_void_p, C.c_int, C.c_int64
+    f = lib.aarms_stream_ceiling
+    f.argtypes = [vp, i32, vp, i32, vp, vp, i64, vp]
+    P = 1 << 40
+    assert f(P, 16, P + (1 << 30), 16, P + (2 << 30), P + (3 << 30), 0, None) == 0   # empty: no launch
+    assert f(P, 16, P, 16, P, P, -1, None) == -1
+    assert f(P, 12, None, 0, P, P, 8, None) == -1                                     # bad width
+    assert f(P, 16, None, 8, P, P, 8, None) == -1                                     # out1 missing
+    assert f(P, 16, None, 0, P + 8, P, 8, None) == -1                                 # misaligned
+    assert f(P, 16, None, 0, P, P, (2**31) * 256, None) == -1                         # grid too large
