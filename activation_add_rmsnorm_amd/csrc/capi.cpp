@@ -119,15 +119,32 @@ int pick_norm(int64_t tokens, int64_t hidden, bool quant)
     return -1;
 }
 
+// Launch-bound below about two million outputs (a decode batch): half jobs
+// (4 outputs per lane) halve every lane's dependent chain of loads and SiLU
+// arithmetic.  Measured on MI355X over T x 8,960 and T x 28,672.
+constexpr int64_t kSwigluHalfJobOutputs = (int64_t)1 << 21;
+constexpr int64_t kSwigluFp8TwoJobOutputs = (int64_t)1 << 22;
+
+static int swiglu_find(int jobs_per_lane, int job_outputs)
+{
+    for (int i = 0; i < swiglu_variant_count(); ++i) {
+        const SwigluVariant *v = swiglu_variant(i);
+        if (v->jobs_per_lane == jobs_per_lane && v->job_outputs == job_outputs) return i;
+    }
+    return -1;
+}
+
 int pick_swiglu(int64_t tokens, int64_t inter, bool quant)
 {
-    (void)tokens;
-    (void)inter;
+    if (tokens < 0 || inter <= 0) return -1;
+    // tokens * inter against the thresholds, without forming the product
+    if (tokens <= kSwigluHalfJobOutputs / inter) return swiglu_find(1, 4);
     // bf16 output: one job per lane (the most blocks, each short-lived, so
     // the blocks in flight stay on one contiguous stretch of memory).  E4M3
-    // output: two jobs per lane, which gives the longer per-job arithmetic
-    // two loads in flight to hide behind.
-    return quant ? 1 : 0;
+    // output, from about four million outputs: two jobs per lane, which
+    // gives the longer per-job arithmetic two loads in flight to hide behind.
+    if (quant && tokens > kSwigluFp8TwoJobOutputs / inter) return swiglu_find(2, 8);
+    return swiglu_find(1, 8);
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? AARMS_OK : AARMS_ERR_HIP; }
@@ -182,7 +199,7 @@ int swiglu_common(void *out, const void *gate_up, const float *scale, int64_t to
 {
     int st = check_width(tokens, inter, 0);
     if (st) return st;
-    if (inter > (int64_t)1 << 34) return AARMS_ERR_UNSUPPORTED_SHAPE;
+    if (inter > AARMS_MAX_INTER) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (tokens > 0 && 2 * inter > AARMS_MAX_ELEMENTS / tokens) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (variant < -1 || variant >= swiglu_variant_count()) return AARMS_ERR_BAD_VARIANT;
     if (tokens == 0) return AARMS_OK;

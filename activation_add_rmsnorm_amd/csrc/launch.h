@@ -43,6 +43,7 @@ struct NormVariant {
 
 struct SwigluVariant {
     int jobs_per_lane;       // a block of 256 lanes covers 256 * jobs_per_lane jobs of one row
+    int job_outputs;         // outputs per job: 8 (16-byte loads) or 4 (8-byte loads)
     const char *name;
 };
 

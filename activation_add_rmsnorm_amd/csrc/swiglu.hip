@@ -4,7 +4,9 @@
 // A job is 8 adjacent outputs of one row, fed by one 16-byte load of gate and
 // one of up from the same row of gate_up (gate first, up second:
 // "TensorRT-LLM: Compiling Inference Engines Ahead of Time", section "Fusing
-// operations, measured", the swiglu kernel).  The grid is (column chunk,
+// operations, measured", the swiglu kernel), or 4 outputs fed by 8-byte
+// loads (twice the lanes, half the dependent arithmetic per lane: for
+// launch-bound decode batches).  The grid is (column chunk,
 // row): a block of 256 lanes takes 256 * U consecutive jobs of one row, so
 // the row is a per-block scalar, every load and store of a wave is one
 // contiguous stretch, and blocks are dispatched in memory order (one block
@@ -23,14 +25,29 @@
 
 namespace aarms {
 
-// 8 outputs of one job: a = bf16(silu(g)), y = bf16(a * u).  Returns the 8
-// bf16 results as 4 packed words.
-__device__ __forceinline__ u32x4 swiglu8(u32x4 gv, u32x4 uv)
+template <int W>
+struct Words;
+template <>
+struct Words<4> {
+    typedef u32x4 T;   // 8 bf16
+    typedef u32x2 Q;   // 8 E4M3 codes
+};
+template <>
+struct Words<2> {
+    typedef u32x2 T;   // 4 bf16
+    typedef uint32_t Q;  // 4 E4M3 codes
+};
+
+// 2W outputs of one job: a = bf16(silu(g)), y = bf16(a * u).  Returns the
+// bf16 results as W packed words.
+template <int W>
+__device__ __forceinline__ typename Words<W>::T swiglu_job(typename Words<W>::T gv, typename Words<W>::T uv)
 {
-    uint32_t gb[8];
-    float g[8], s[8];
+    constexpr int E = 2 * W;
+    uint32_t gb[E];
+    float g[E], s[E];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < W; ++e) {
         gb[2 * e] = gv[e] << 16;
         gb[2 * e + 1] = gv[e] & 0xFFFF0000u;
         g[2 * e] = __uint_as_float(gb[2 * e]);
@@ -40,7 +57,7 @@ __device__ __forceinline__ u32x4 swiglu8(u32x4 gv, u32x4 uv)
     // bit pattern (above SILU_FAST_MIN_BITS means g < -16)
     uint32_t kmin = 0xFFFFFFFFu, gmax = 0u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < E; ++j) {
         s[j] = silu_fast(g[j]);
         kmin = min(kmin, silu_edge_key(s[j]));
         gmax = max(gmax, gb[j]);
@@ -51,7 +68,7 @@ __device__ __forceinline__ u32x4 swiglu8(u32x4 gv, u32x4 uv)
         // produced inside this branch, so it is not hoisted onto the hot path.
         uint32_t redo = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < E; ++j) {
             float sj = s[j];
             uint32_t gbj = gb[j];
             asm volatile("" : "+v"(sj), "+v"(gbj));
@@ -63,15 +80,15 @@ __device__ __forceinline__ u32x4 swiglu8(u32x4 gv, u32x4 uv)
             redo &= redo - 1u;
             float gj = g[0];
 #pragma unroll
-            for (int t = 1; t < 8; ++t) gj = (j == t) ? g[t] : gj;
+            for (int t = 1; t < E; ++t) gj = (j == t) ? g[t] : gj;
             const float r = silu_exact(gj);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) s[t] = (j == t) ? r : s[t];
+            for (int t = 0; t < E; ++t) s[t] = (j == t) ? r : s[t];
         }
     }
-    u32x4 y;
+    typename Words<W>::T y;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < W; ++e) {
         const uint32_t a = pack_bf16(s[2 * e], s[2 * e + 1]);
         y[e] = pack_bf16(bf_lo(a) * bf_lo(uv[e]), bf_hi(a) * bf_hi(uv[e]));
     }
@@ -79,66 +96,72 @@ __device__ __forceinline__ u32x4 swiglu8(u32x4 gv, u32x4 uv)
 }
 
 // MODE 0: bf16 output; 1: E4M3 output, fast quotient; 2: E4M3, IEEE division.
-template <int U, int MODE>
+template <int U, int W, int MODE>
 __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Scale &qs)
 {
+    typedef typename Words<W>::T V;
     const uint64_t row = (uint64_t)blockIdx.z * SWIGLU_ROWS_PER_Y + blockIdx.y;
     if (row >= (uint64_t)p.tokens) return;
-    const uint32_t nvec = p.vecs_per_row;
+    const uint32_t njobs = p.vecs_per_row * (4 / W);
     const uint32_t c0 = blockIdx.x * (256u * U) + threadIdx.x;
-    const u32x4 *gate = (const u32x4 *)((const uint16_t *)p.gate_up + row * 2u * (uint64_t)p.inter);
-    const u32x4 *up = gate + nvec;
-    const uint64_t job0 = row * nvec;
-    u32x4 gv[U], uv[U];
+    const V *gate = (const V *)((const uint16_t *)p.gate_up + row * 2u * (uint64_t)p.inter);
+    const V *up = gate + njobs;
+    const uint64_t job0 = row * njobs;
+    V gv[U], uv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t c = c0 + 256u * u;
-        const bool ok = c < nvec;
-        gv[u] = ok ? ld_stream(gate + c) : (u32x4)0u;
-        uv[u] = ok ? ld_stream(up + c) : (u32x4)0u;
+        const bool ok = c < njobs;
+        gv[u] = ok ? ld_stream(gate + c) : (V)0u;
+        uv[u] = ok ? ld_stream(up + c) : (V)0u;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t c = c0 + 256u * u;
-        if (c >= nvec) continue;
-        const u32x4 y = swiglu8(gv[u], uv[u]);
+        if (c >= njobs) continue;
+        const V y = swiglu_job<W>(gv[u], uv[u]);
         if constexpr (MODE == 0) {
-            st_stream((u32x4 *)p.out + job0 + c, y);
+            st_stream((V *)p.out + job0 + c, y);
         } else {
-            float z[8];
+            float z[2 * W];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < W; ++e) {
                 z[2 * e] = e4m3_quotient<MODE == 1>(bf_lo(y[e]), qs);
                 z[2 * e + 1] = e4m3_quotient<MODE == 1>(bf_hi(y[e]), qs);
             }
-            u32x2 q;
-            q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
-            q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
-            st_stream((u32x2 *)p.out + job0 + c, q);
+            typename Words<W>::Q q;
+            if constexpr (W == 4) {
+                q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+                q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
+            } else {
+                q = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+            }
+            st_stream((typename Words<W>::Q *)p.out + job0 + c, q);
         }
     }
 }
 
-template <int U, bool QUANT>
+template <int U, int W, bool QUANT>
 __global__ void __launch_bounds__(256) swiglu_kernel(SwigluParams p)
 {
     if constexpr (QUANT) {
         const E4m3Scale qs = make_e4m3_scale(*p.scale);
         if (e4m3_scale_is_fast(qs))
-            swiglu_block<U, 1>(p, qs);
+            swiglu_block<U, W, 1>(p, qs);
         else
-            swiglu_block<U, 2>(p, qs);
+            swiglu_block<U, W, 2>(p, qs);
     } else {
-        swiglu_block<U, 0>(p, E4m3Scale{});
+        swiglu_block<U, W, 0>(p, E4m3Scale{});
     }
 }
 
 // ---------------------------------------------------------------- variants
 
 static const SwigluVariant kSwigluVariants[] = {
-    {1, "1 job/lane"},
-    {2, "2 jobs/lane"},
-    {4, "4 jobs/lane"},
+    {1, 8, "1 job/lane"},
+    {2, 8, "2 jobs/lane"},
+    {4, 8, "4 jobs/lane"},
+    {1, 4, "1 half job/lane"},
 };
 constexpr int kNumSwigluVariants = sizeof(kSwigluVariants) / sizeof(kSwigluVariants[0]);
 
@@ -148,17 +171,18 @@ const SwigluVariant *swiglu_variant(int id)
     return (id >= 0 && id < kNumSwigluVariants) ? &kSwigluVariants[id] : nullptr;
 }
 
-template <int U, bool Q>
+template <int U, int W, bool Q>
 static hipError_t launch_one(const SwigluParams &p, hipStream_t stream)
 {
     const uint32_t per_block = 256u * U;
+    const uint32_t njobs = p.vecs_per_row * (4 / W);
     const uint64_t T = (uint64_t)p.tokens;
-    const dim3 grid((p.vecs_per_row + per_block - 1) / per_block,
+    const dim3 grid((njobs + per_block - 1) / per_block,
                     (unsigned)(T < SWIGLU_ROWS_PER_Y ? T : SWIGLU_ROWS_PER_Y),
                     (unsigned)((T + SWIGLU_ROWS_PER_Y - 1) / SWIGLU_ROWS_PER_Y));
     SwigluParams copy = p;
     void *args[] = {&copy};
-    return hipLaunchKernel((const void *)&swiglu_kernel<U, Q>, grid, dim3(256), args, 0, stream);
+    return hipLaunchKernel((const void *)&swiglu_kernel<U, W, Q>, grid, dim3(256), args, 0, stream);
 }
 
 template <bool Q>
@@ -166,12 +190,16 @@ static hipError_t dispatch(const SwigluParams &p, int variant, hipStream_t s)
 {
     const SwigluVariant *v = swiglu_variant(variant);
     if (!v) return hipErrorInvalidValue;
-    switch (v->jobs_per_lane) {
-    case 1: return launch_one<1, Q>(p, s);
-    case 2: return launch_one<2, Q>(p, s);
-    case 4: return launch_one<4, Q>(p, s);
-    default: return hipErrorInvalidValue;
+    if (v->job_outputs == 8) {
+        switch (v->jobs_per_lane) {
+        case 1: return launch_one<1, 4, Q>(p, s);
+        case 2: return launch_one<2, 4, Q>(p, s);
+        case 4: return launch_one<4, 4, Q>(p, s);
+        default: return hipErrorInvalidValue;
+        }
     }
+    if (v->job_outputs == 4 && v->jobs_per_lane == 1) return launch_one<1, 2, Q>(p, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, hipStream_t stream)

@@ -63,6 +63,7 @@ enum aarms_status {
 /* Limits. */
 #define AARMS_MAX_HIDDEN 65536            /* norms: row width kept in registers    */
 #define AARMS_MAX_ELEMENTS (1LL << 40)    /* tokens x width, per tensor            */
+#define AARMS_MAX_INTER (1LL << 33)       /* swiglu: output row width              */
 
 /*
  * fused_add_rmsnorm -- residual add followed by RMSNorm in one pass.
@@ -121,7 +122,7 @@ int fused_add_rmsnorm_quant_fp8(void *out_fp8, float *scale_out, void *residual_
  *   out      [num_tokens, inter]     bf16   written
  *   gate_up  [num_tokens, 2 * inter] bf16   read; gate = columns [0, inter),
  *                                           up = columns [inter, 2*inter)
- *   inter    > 0, multiple of 8
+ *   inter    > 0, multiple of 8, at most AARMS_MAX_INTER
  * No in-place form: out may not overlap gate_up.
  */
 int swiglu(void *out, const void *gate_up, int64_t num_tokens, int64_t inter,
@@ -138,7 +139,7 @@ int swiglu(void *out, const void *gate_up, int64_t num_tokens, int64_t inter,
  *   scale    [1] fp32, device memory,       read by the kernel (so it may be
  *            changed between graph replays); must be positive and finite,
  *            except that exactly zero is treated as one
- *   inter    > 0, multiple of 8
+ *   inter    > 0, multiple of 8, at most AARMS_MAX_INTER
  */
 int swiglu_quant_fp8(void *out_fp8, const void *gate_up, const float *scale,
                      int64_t num_tokens, int64_t inter, hipStream_t stream);

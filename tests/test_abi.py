@@ -183,6 +183,13 @@ def test_swiglu_errors():
     assert lib.swiglu_ex(P, P + BIG, 4, 8960, n, None) == VARIANT
 
 
+def test_swiglu_width_limit():
+    lib = A.load()
+    P = 1 << 40
+    assert lib.swiglu(P, P + (1 << 45), 1, (1 << 33) + 8, None) == UNSUP
+    assert lib.swiglu_quant_fp8(P, P + (1 << 45), P - 64, 1, (1 << 33) + 8, None) == UNSUP
+
+
 def test_pick_variant_ranges():
     for H in [8, 512, 520, 1536, 4096, 4104, 8192, 16384, 32768, 65536]:
         v = A.pick_variant(A.OP_NORM, 16, H)

@@ -97,7 +97,8 @@ def test_native_library_is_loaded():
 # ------------------------------------------------------------------ norm
 
 @pytest.mark.parametrize("T,H", [(1, 8), (3, 24), (16, 1536), (5, 520), (257, 1536), (7, 4104),
-                                 (33, 8192), (4, 16384), (3, 16392), (2, 40000), (1, 65536)])
+                                 (33, 8192), (4, 16384), (3, 16392), (2, 40000), (1, 65536),
+                                 (1023, 1536), (1024, 1536)])
 def test_norm_shapes_default_variant(T, H):
     x, r, w = norm_case(T, H, seed=T + H)
     out, res_out = run_norm(x, r, w, 1e-6)
@@ -223,14 +224,18 @@ def test_norm_fp8_ragged_and_tiny():
 
 # ------------------------------------------------------------------ swiglu
 
-def test_swiglu_silu_table_exhaustive():
+@pytest.mark.parametrize("variant", [-1, 0, 1, 2, 3])
+def test_swiglu_silu_table_exhaustive(variant):
     """One row: gate = every bf16 pattern, up = 1, so the output is the
     GPU's bf16(silu(g)) for all 65,536 gates: it must equal the oracle's
-    correctly rounded table everywhere (NaN positions as NaN)."""
+    correctly rounded table everywhere (NaN positions as NaN), in every
+    kernel variant."""
+    if variant >= A.variant_count(A.OP_SWIGLU):
+        pytest.skip("no such variant")
     g = np.arange(65536, dtype=np.uint16)
     one = np.full(65536, oracle.bf16_from_f64(1.0), np.uint16)
     gu = np.concatenate([g, one])[None, :]
-    y = run_swiglu(gu)[0]
+    y = run_swiglu(gu, variant=variant)[0]
     tab = oracle.silu_table()
     bad = ~P.same_bf16(y, tab)
     assert not bad.any(), "gates %s: gpu %s oracle %s" % (
@@ -279,6 +284,14 @@ def test_swiglu_fp8_dynamic_scales():
         s = float(np.float32(a) / np.float32(448))
         q = run_swiglu_fp8(gu, s)
         P.check_swiglu_fp8(gu, s, q)
+
+
+def test_swiglu_fp8_every_y_every_variant():
+    gu = _all_y_rows()
+    for v in range(A.variant_count(A.OP_SWIGLU)):
+        for scale in (0.05, 2.0 ** -126):
+            q = run_swiglu_fp8(gu, scale, variant=v)
+            P.check_swiglu_fp8(gu, scale, q)
 
 
 def test_swiglu_fp8_zero_scale_is_one():
