@@ -60,6 +60,7 @@ def _lib():
                 "aarms_oracle_rmsnorm_apply": (None, [u16p, u16p, f32p, i64, i64, u16p]),
                 "aarms_oracle_rms_window": (None, [f64p, i64, f64, f32p, f32p]),
                 "aarms_oracle_fused_add_rmsnorm": (None, [u16p, u16p, u16p, i64, i64, f32, u16p, u16p, f32p]),
+                "aarms_oracle_rmsnorm": (None, [u16p, u16p, i64, i64, f32, u16p, f32p]),
                 "aarms_oracle_quant_fp8_static": (None, [u16p, i64, f32, u8p]),
                 "aarms_oracle_quant_fp8_per_row": (None, [u16p, i64, i64, u8p, f32p]),
                 "aarms_oracle_fused_add_rmsnorm_quant_fp8": (
@@ -67,6 +68,7 @@ def _lib():
                 "aarms_oracle_silu_bf16": (C.c_uint16, [C.c_uint16]),
                 "aarms_oracle_swiglu": (None, [u16p, i64, i64, u16p]),
                 "aarms_oracle_swiglu_quant_fp8": (None, [u16p, i64, i64, f32, u8p]),
+                "aarms_oracle_swiglu_quant_fp8_per_row": (None, [u16p, i64, i64, u16p, u8p, f32p]),
                 "aarms_oracle_num_threads": (C.c_int, []),
             }
             for name, (res, args) in sig.items():
@@ -168,6 +170,18 @@ def fused_add_rmsnorm(x, residual, weight, eps: float):
     return out, res_out, rs
 
 
+def rmsnorm(x, weight, eps: float):
+    """RMSNorm without the residual add.  Returns (out, rs)."""
+    x, weight = _u16(x), _u16(weight)
+    T, H = _rows(x)
+    if weight.shape != (H,):
+        raise ValueError("shape mismatch")
+    out = np.empty_like(x)
+    rs = np.empty(T, np.float32)
+    _lib().aarms_oracle_rmsnorm(x, weight, T, H, float(eps), out, rs)
+    return out, rs
+
+
 # ---------------------------------------------------------------- fp8
 
 def quant_fp8_static(y, scale: float) -> np.ndarray:
@@ -204,6 +218,27 @@ def fused_add_rmsnorm_quant_fp8(x, residual, weight, eps: float):
     return q, s, res_out, y, rs
 
 
+def fused_add_rmsnorm_quant_fp8_static(x, residual, weight, eps: float, scale: float):
+    """The norm with its bf16 output quantised with a given per-tensor scale.
+    Returns (q, residual_out, y, rs)."""
+    out, res_out, rs = fused_add_rmsnorm(x, residual, weight, eps)
+    return quant_fp8_static(out, scale), res_out, out, rs
+
+
+def rmsnorm_quant_fp8(x, weight, eps: float):
+    """RMSNorm (no residual add), quantised per token.  Returns (q, s, y, rs)."""
+    out, rs = rmsnorm(x, weight, eps)
+    q, s = quant_fp8_per_row(out)
+    return q, s, out, rs
+
+
+def rmsnorm_quant_fp8_static(x, weight, eps: float, scale: float):
+    """RMSNorm (no residual add), quantised with a per-tensor scale.
+    Returns (q, y, rs)."""
+    out, rs = rmsnorm(x, weight, eps)
+    return quant_fp8_static(out, scale), out, rs
+
+
 # ---------------------------------------------------------------- swiglu
 
 def silu_bf16(g_bits) -> np.ndarray:
@@ -236,6 +271,20 @@ def swiglu_quant_fp8(gate_up, scale: float) -> np.ndarray:
     q = np.empty((T, W // 2), np.uint8)
     _lib().aarms_oracle_swiglu_quant_fp8(gu, T, W // 2, float(np.float32(scale)), q)
     return q
+
+
+def swiglu_quant_fp8_dynamic(gate_up):
+    """SwiGLU quantised per token.  Returns (q, s, y); y is the bf16 SwiGLU
+    output before quantisation."""
+    gu = _u16(gate_up)
+    T, W = _rows(gu)
+    if W % 2:
+        raise ValueError("gate_up width must be even")
+    y = np.empty((T, W // 2), np.uint16)
+    q = np.empty((T, W // 2), np.uint8)
+    s = np.empty(T, np.float32)
+    _lib().aarms_oracle_swiglu_quant_fp8_per_row(gu, T, W // 2, y, q, s)
+    return q, s, y
 
 
 def num_threads() -> int:

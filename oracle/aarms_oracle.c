@@ -214,6 +214,15 @@ void aarms_oracle_fused_add_rmsnorm(const uint16_t *x, const uint16_t *res, cons
     aarms_oracle_rmsnorm_apply(res_out, w, rs, T, H, out);
 }
 
+/* rmsnorm without the residual add (the form of the first page's own Metal
+ * norm, same section): out = RMSNorm(x) * w on x as given. */
+void aarms_oracle_rmsnorm(const uint16_t *x, const uint16_t *w, int64_t T, int64_t H, float eps,
+                          uint16_t *out, float *rs)
+{
+    aarms_oracle_rms_scale(x, T, H, eps, rs, 0);
+    aarms_oracle_rmsnorm_apply(x, w, rs, T, H, out);
+}
+
 /* ------------------------------------------------------------------ */
 /* FP8 quantisation                                                    */
 /* ------------------------------------------------------------------ */
@@ -307,6 +316,15 @@ void aarms_oracle_swiglu_quant_fp8(const uint16_t *gu, int64_t T, int64_t N, flo
             uint16_t y = swiglu_one(gu[row * 2 * N + j], gu[row * 2 * N + N + j]);
             q[row * N + j] = quant_e4m3(aarms_oracle_bf16_to_f32(y), scale);
         }
+}
+
+/* SwiGLU output (bf16) quantised with a per-token scale:
+ * s[row] = f32(max_j |y_j| / 448), q = e4m3(clamp(y / s)). */
+void aarms_oracle_swiglu_quant_fp8_per_row(const uint16_t *gu, int64_t T, int64_t N,
+                                           uint16_t *y_scratch, uint8_t *q, float *s)
+{
+    aarms_oracle_swiglu(gu, T, N, y_scratch);
+    aarms_oracle_quant_fp8_per_row(y_scratch, T, N, q, s);
 }
 
 int aarms_oracle_num_threads(void)

@@ -412,6 +412,124 @@ def test_norm_quant_is_composition():
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
 
 
+# ------------------------------------------------------------------ the rest of the quant matrix
+#
+# RMSNorm without the residual add (the first page's Metal norm), the norm
+# with a per-tensor (static) E4M3 scale, and SwiGLU with a per-token
+# (dynamic) scale: the same steps as above, composed differently.
+
+def test_plain_rmsnorm_constant_row_and_signed_zero():
+    H = 1536
+    w = gen.normal_bf16((H,), 10, 3, mean=1.0, std=0.1)
+    for eps in [1e-6, 1e-5, 0.0]:
+        for c in [1.0, -1.0, 0.5, 3.0, -0.0625, 100.0, 2.0 ** -20]:
+            if eps and c * c < 512 * eps:
+                continue
+            x = np.full((2, H), oracle.bf16_from_f64(c), np.uint16)
+            out, _ = oracle.rmsnorm(x, w, eps)
+            want = w if c > 0 else (w ^ 0x8000)
+            assert np.array_equal(out[0], want) and np.array_equal(out[1], want), (c, eps)
+    # no add in front: a -0 input reaches the multiply as -0, so out = w * -0
+    # (a residual add of +0 would have turned it into +0)
+    x = gen.normal_bf16((1, H), 10, 1)
+    x[0, :7] = 0x8000
+    out, _ = oracle.rmsnorm(x, w, 1e-6)
+    want = np.where(f32_of(w[:7]) > 0, 0x8000, 0x0000).astype(np.uint16)
+    assert np.array_equal(out[0, :7], want)
+
+
+def test_plain_rmsnorm_scale_invariance():
+    x = gen.normal_bf16((8, 2048), 11, 1)
+    w = gen.normal_bf16((2048,), 11, 3, mean=1.0, std=0.1)
+    base, _ = oracle.rmsnorm(x, w, 0.0)
+    for k in [-9, -2, 1, 5]:
+        xs = gen.bf16_bits_from_f32(f32_of(x) * np.float32(2.0 ** k))
+        out, _ = oracle.rmsnorm(xs, w, 0.0)
+        assert np.array_equal(out, base), k
+
+
+def test_plain_rmsnorm_matches_torch_eager_eight_ops():
+    """torch CPU eager on x itself (no residual): equal except at knife-edges,
+    which lie inside the admissible window."""
+    T, H, eps = 256, 1536, 1e-6
+    x = gen.normal_bf16((T, H), 12, 1, std=2.0)
+    w = gen.normal_bf16((H,), 12, 3, mean=1.0, std=0.1)
+    out, rs = oracle.rmsnorm(x, w, eps)
+    h = bf16_t(x).to(torch.float32)
+    hn = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + eps)
+    ref = bits_of(bf16_t(w) * hn.to(torch.bfloat16))
+    diff = np.flatnonzero(ref.reshape(-1) != out.reshape(-1))
+    assert len(diff) < 0.005 * out.size
+    _, rs_exact = oracle.rms_scale(x, eps)
+    lo, hi = oracle.rms_window(rs_exact, 2.0 ** -18)
+    alt_lo = oracle.rmsnorm_apply(x, w, lo).reshape(-1)
+    alt_hi = oracle.rmsnorm_apply(x, w, hi).reshape(-1)
+    r = ref.reshape(-1)
+    assert np.all((r[diff] == alt_lo[diff]) | (r[diff] == alt_hi[diff]))
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.0125, 1.0])
+def test_static_norm_quant_vs_torch(scale):
+    """Per-tensor E4M3 on the norm output: the codes are torch's
+    clamp(y / scale).to(e4m3fn) of the bf16 norm output, with and without
+    the residual add."""
+    x = gen.normal_bf16((32, 2048), 13, 1, outlier_frac=0.001)
+    r = gen.normal_bf16((32, 2048), 13, 2, outlier_frac=0.001)
+    w = gen.normal_bf16((2048,), 13, 3, mean=1.0, std=0.1)
+    q, res_out, y, _ = oracle.fused_add_rmsnorm_quant_fp8_static(x, r, w, 1e-5, scale)
+    out, res_out2, _ = _norm(x, r, w, 1e-5)
+    assert np.array_equal(y, out) and np.array_equal(res_out, res_out2)
+    q2, y2, _ = oracle.rmsnorm_quant_fp8_static(x, w, 1e-5, scale)
+    assert np.array_equal(y2, oracle.rmsnorm(x, w, 1e-5)[0])
+    for qq, yy in ((q, y), (q2, y2)):
+        z = torch.clamp(torch.from_numpy(f32_of(yy).copy()) / torch.tensor(scale, dtype=torch.float32), -448, 448)
+        assert np.array_equal(qq, z.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    # saturation reached: with scale 0.0125 the largest |y| (about 4) lands
+    # beyond 448 and must give the largest code, not NaN
+    if scale == 0.0125:
+        big = np.abs(f32_of(y)) >= 448 * 0.0125
+        assert big.any() and np.all((q[big] & 0x7F) == 0x7E)
+
+
+def test_dynamic_norm_quant_without_residual():
+    x = gen.normal_bf16((32, 4096), 14, 1, outlier_frac=0.001)
+    w = gen.normal_bf16((4096,), 14, 3, mean=1.0, std=0.1)
+    q, s, y, _ = oracle.rmsnorm_quant_fp8(x, w, 1e-5)
+    assert np.array_equal(y, oracle.rmsnorm(x, w, 1e-5)[0])
+    amax = np.abs(f32_of(y)).max(axis=1)
+    assert np.array_equal(s, (amax / np.float32(448)).astype(np.float32))
+    assert np.all(np.abs(oracle.e4m3_table()[q]).max(axis=1) == 448.0)
+
+
+def test_dynamic_swiglu_quant_invariants_and_torch():
+    """Per-token E4M3 on the SwiGLU output: s = f32(max|y| / 448), every
+    non-zero row reaches 448 exactly, an all-zero row gives s = 0 and zero
+    codes, and the codes are torch's conversion of clamp(y / s)."""
+    T, N = 64, 4096
+    gu = gen.normal_bf16((T, 2 * N), 15, 4, std=2.0)
+    gu[5, :N] = 0                                  # gate 0: silu = 0, y = +-0
+    gu[6, :N] = oracle.bf16_from_f64(0.01)         # small row with one large output
+    gu[6, 100] = oracle.bf16_from_f64(12.0)
+    gu[6, N + 100] = oracle.bf16_from_f64(5.0)
+    q, s, y = oracle.swiglu_quant_fp8_dynamic(gu)
+    assert np.array_equal(y, oracle.swiglu(gu))
+    yf = f32_of(y)
+    amax = np.abs(yf).max(axis=1)
+    qa = np.abs(oracle.e4m3_table()[q])
+    for i in range(T):
+        if i == 5:
+            assert s[i] == 0 and np.all(qa[i] == 0)
+            continue
+        assert s[i] == np.float32(amax[i]) / np.float32(448)
+        assert qa[i].max() == 448.0
+    assert q[6, 100] == 0x7E
+    yt = torch.from_numpy(yf.copy())
+    st = yt.abs().amax(dim=1, keepdim=True) / 448.0
+    z = torch.where(st == 0, yt, yt / torch.where(st == 0, torch.ones_like(st), st))
+    ref = torch.clamp(z, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+
+
 # ------------------------------------------------------------------ the pages' shapes
 
 def test_golden_workload_shapes_from_pages():
