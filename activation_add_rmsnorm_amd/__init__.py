@@ -20,9 +20,11 @@ import torch
 
 __all__ = [
     "AarmsError", "load", "lib_path",
-    "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "swiglu", "swiglu_quant_fp8",
+    "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_static",
+    "rmsnorm", "rmsnorm_quant_fp8", "rmsnorm_quant_fp8_static",
+    "swiglu", "swiglu_quant_fp8", "swiglu_quant_fp8_dynamic",
     "variant_count", "variant_name", "pick_variant",
-    "OP_NORM", "OP_SWIGLU",
+    "OP_NORM", "OP_SWIGLU", "OP_SWIGLU_DYNAMIC",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +34,7 @@ _LIB = None
 
 OP_NORM = 0
 OP_SWIGLU = 1
+OP_SWIGLU_DYNAMIC = 2
 FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
 
 
@@ -67,6 +70,11 @@ def load():
             "swiglu_ex": [vp, vp, i64, i64, i32, vp],
             "swiglu_quant_fp8": [vp, vp, vp, i64, i64, vp],
             "swiglu_quant_fp8_ex": [vp, vp, vp, i64, i64, i32, vp],
+            "fused_add_rmsnorm_quant_fp8_static_ex": [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "rmsnorm_ex": [vp, vp, vp, i64, i64, f32, i32, vp],
+            "rmsnorm_quant_fp8_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "rmsnorm_quant_fp8_static_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "swiglu_quant_fp8_dynamic_ex": [vp, vp, vp, i64, i64, i32, vp],
             "aarms_variant_count": [i32],
             "aarms_pick_variant": [i32, i64, i64, i32],
         }
@@ -174,6 +182,98 @@ def fused_add_rmsnorm_quant_fp8(x: torch.Tensor, residual: torch.Tensor, weight:
     return out, scale_out, residual_out
 
 
+def fused_add_rmsnorm_quant_fp8_static(x: torch.Tensor, residual: torch.Tensor,
+                                       weight: torch.Tensor, scale: torch.Tensor, eps: float,
+                                       out: torch.Tensor | None = None,
+                                       residual_out: torch.Tensor | None = None, variant: int = -1):
+    """fused_add_rmsnorm with a static per-tensor E4M3 epilogue; scale is a
+    1-element fp32 GPU tensor read by the kernel.
+    Returns (q [T, H] fp8, residual_out [T, H] bf16)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(residual, "residual", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    _require(scale, "scale", (torch.float32,), (1,))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=x.device)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _require(out, "out", FP8_DTYPES, (T, H))
+    _require(residual_out, "residual_out", (torch.bfloat16,), (T, H))
+    _same_device(x, residual, weight, scale, out, residual_out)
+    lib = load()
+    _check(lib.fused_add_rmsnorm_quant_fp8_static_ex(out.data_ptr(), residual_out.data_ptr(),
+                                                     x.data_ptr(), residual.data_ptr(),
+                                                     weight.data_ptr(), scale.data_ptr(), T, H,
+                                                     float(eps), int(variant), _stream(x.device)),
+           "fused_add_rmsnorm_quant_fp8_static")
+    return out, residual_out
+
+
+def rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, out: torch.Tensor | None = None,
+            variant: int = -1):
+    """RMSNorm without the residual add.  x: bf16 [T, H]; out=x runs in place."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    if out is None:
+        out = torch.empty_like(x)
+    _require(out, "out", (torch.bfloat16,), (T, H))
+    _same_device(x, weight, out)
+    lib = load()
+    _check(lib.rmsnorm_ex(out.data_ptr(), x.data_ptr(), weight.data_ptr(), T, H, float(eps),
+                          int(variant), _stream(x.device)), "rmsnorm")
+    return out
+
+
+def rmsnorm_quant_fp8(x: torch.Tensor, weight: torch.Tensor, eps: float,
+                      out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
+                      variant: int = -1):
+    """rmsnorm with a dynamic per-token E4M3 epilogue.
+    Returns (q [T, H] fp8, scale [T] fp32)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _require(out, "out", FP8_DTYPES, (T, H))
+    _require(scale_out, "scale_out", (torch.float32,), (T,))
+    _same_device(x, weight, out, scale_out)
+    lib = load()
+    _check(lib.rmsnorm_quant_fp8_ex(out.data_ptr(), scale_out.data_ptr(), x.data_ptr(),
+                                    weight.data_ptr(), T, H, float(eps), int(variant),
+                                    _stream(x.device)), "rmsnorm_quant_fp8")
+    return out, scale_out
+
+
+def rmsnorm_quant_fp8_static(x: torch.Tensor, weight: torch.Tensor, scale: torch.Tensor, eps: float,
+                             out: torch.Tensor | None = None, variant: int = -1):
+    """rmsnorm with a static per-tensor E4M3 epilogue.  Returns q [T, H] fp8."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    _require(scale, "scale", (torch.float32,), (1,))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=x.device)
+    _require(out, "out", FP8_DTYPES, (T, H))
+    _same_device(x, weight, scale, out)
+    lib = load()
+    _check(lib.rmsnorm_quant_fp8_static_ex(out.data_ptr(), x.data_ptr(), weight.data_ptr(),
+                                           scale.data_ptr(), T, H, float(eps), int(variant),
+                                           _stream(x.device)), "rmsnorm_quant_fp8_static")
+    return out
+
+
 def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None, variant: int = -1):
     """silu(gate) * up with gate_up = [gate | up] of shape [T, 2N]; returns bf16 [T, N]."""
     if gate_up.dim() != 2 or gate_up.shape[1] % 2:
@@ -207,6 +307,28 @@ def swiglu_quant_fp8(gate_up: torch.Tensor, scale: torch.Tensor, out: torch.Tens
     _check(lib.swiglu_quant_fp8_ex(out.data_ptr(), gate_up.data_ptr(), scale.data_ptr(), T, N,
                                    int(variant), _stream(gate_up.device)), "swiglu_quant_fp8")
     return out
+
+
+def swiglu_quant_fp8_dynamic(gate_up: torch.Tensor, out: torch.Tensor | None = None,
+                             scale_out: torch.Tensor | None = None, variant: int = -1):
+    """swiglu with a dynamic per-token E4M3 epilogue.
+    Returns (q [T, N] fp8, scale [T] fp32)."""
+    if gate_up.dim() != 2 or gate_up.shape[1] % 2:
+        raise ValueError("gate_up must be [tokens, 2 * inter]")
+    T, N = gate_up.shape[0], gate_up.shape[1] // 2
+    _require(gate_up, "gate_up", (torch.bfloat16,), (T, 2 * N))
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float8_e4m3fn, device=gate_up.device)
+    if scale_out is None:
+        scale_out = torch.empty((T,), dtype=torch.float32, device=gate_up.device)
+    _require(out, "out", FP8_DTYPES, (T, N))
+    _require(scale_out, "scale_out", (torch.float32,), (T,))
+    _same_device(gate_up, out, scale_out)
+    lib = load()
+    _check(lib.swiglu_quant_fp8_dynamic_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(),
+                                           T, N, int(variant), _stream(gate_up.device)),
+           "swiglu_quant_fp8_dynamic")
+    return out, scale_out
 
 
 def variant_count(op: int) -> int:

@@ -147,51 +147,89 @@ int pick_swiglu(int64_t tokens, int64_t inter, bool quant)
     return swiglu_find(1, 8);
 }
 
+int rowq_capacity(const SwigluRowVariant *v) { return v->waves_per_row * 64 * v->jobs_per_lane * 8; }
+
+// Per-token FP8 SwiGLU: the fewest waves per row (one, else 4, 8, 16) that
+// hold the row with at most 4 jobs per lane, the fewest jobs for that count;
+// else the widest variant.
+int pick_swiglu_rowq(int64_t tokens, int64_t inter)
+{
+    if (tokens < 0 || inter <= 0 || inter > AARMS_MAX_INTER_PER_TOKEN) return -1;
+    for (int max_jobs : {4, 8})
+        for (int w : {1, 4, 8, 16}) {
+            int best = -1;
+            for (int i = 0; i < swiglu_row_variant_count(); ++i) {
+                const SwigluRowVariant *v = swiglu_row_variant(i);
+                if (v->waves_per_row != w || v->jobs_per_lane > max_jobs || rowq_capacity(v) < inter) continue;
+                if (best < 0 || v->jobs_per_lane < swiglu_row_variant(best)->jobs_per_lane) best = i;
+            }
+            if (best >= 0) return best;
+        }
+    return -1;
+}
+
 int launch_status(hipError_t e) { return e == hipSuccess ? AARMS_OK : AARMS_ERR_HIP; }
 
-int norm_common(void *out, float *scale_out, void *residual_out, const void *x,
-                const void *residual, const void *weight, int64_t tokens, int64_t hidden,
-                float eps, bool quant, int variant, hipStream_t stream)
+// All norm forms: epi = NORM_EPI_*, res = with the residual add in front
+// (residual and residual_out), scale_out for the dynamic E4M3 form, scale_in
+// for the static one.
+int norm_common(void *out, float *scale_out, const float *scale_in, void *residual_out,
+                const void *x, const void *residual, const void *weight, int64_t tokens,
+                int64_t hidden, float eps, int epi, bool res, int variant, hipStream_t stream)
 {
+    const bool dyn = epi == NORM_EPI_FP8_DYNAMIC, stat = epi == NORM_EPI_FP8_STATIC;
     int st = check_width(tokens, hidden, AARMS_MAX_HIDDEN);
     if (st) return st;
     if ((st = check_eps(eps))) return st;
     if (variant < -1 || variant >= norm_variant_count()) return AARMS_ERR_BAD_VARIANT;
     if (tokens == 0) return AARMS_OK;
-    if (!out || !residual_out || !x || !residual || !weight || (quant && !scale_out))
+    if (!out || !x || !weight || (res && (!residual_out || !residual)) || (dyn && !scale_out) ||
+        (stat && !scale_in))
         return AARMS_ERR_NULL_POINTER;
-    if (!aligned(out, 16) || !aligned(residual_out, 16) || !aligned(x, 16) ||
-        !aligned(residual, 16) || !aligned(weight, 16) || (quant && !aligned(scale_out, 4)))
+    if (!aligned(out, 16) || !aligned(x, 16) || !aligned(weight, 16) ||
+        (res && (!aligned(residual_out, 16) || !aligned(residual, 16))) ||
+        (dyn && !aligned(scale_out, 4)) || (stat && !aligned(scale_in, 4)))
         return AARMS_ERR_MISALIGNED;
     const uint64_t elems = (uint64_t)tokens * (uint64_t)hidden;
-    const Arg ins[3] = {{span(x, 2 * elems), x},
-                        {span(residual, 2 * elems), residual},
-                        {span(weight, 2 * (uint64_t)hidden), weight}};
-    if (!quant) {
-        const Arg outs[2] = {{span(out, 2 * elems), out}, {span(residual_out, 2 * elems), residual_out}};
-        const int partner[2] = {0, 1};  // out == x, residual_out == residual
-        if ((st = check_outputs(outs, partner, 2, ins, 3))) return st;
-    } else {
-        const Arg outs[3] = {{span(out, elems), out},
-                             {span(residual_out, 2 * elems), residual_out},
-                             {span(scale_out, 4 * (uint64_t)tokens), scale_out}};
-        const int partner[3] = {-1, 1, -1};  // residual_out == residual only
-        if ((st = check_outputs(outs, partner, 3, ins, 3))) return st;
+    // inputs: x, weight, then residual and scale_in when present
+    Arg ins[4];
+    int n_in = 0;
+    ins[n_in++] = {span(x, 2 * elems), x};
+    ins[n_in++] = {span(weight, 2 * (uint64_t)hidden), weight};
+    const int res_idx = res ? n_in : -1;
+    if (res) ins[n_in++] = {span(residual, 2 * elems), residual};
+    if (stat) ins[n_in++] = {span(scale_in, 4), scale_in};
+    // outputs: out (may be x itself in the bf16 form), residual_out (may be
+    // the residual itself), scale_out
+    Arg outs[3];
+    int partner[3];
+    int n_out = 0;
+    partner[n_out] = (epi == NORM_EPI_BF16) ? 0 : -1;
+    outs[n_out++] = {span(out, epi == NORM_EPI_BF16 ? 2 * elems : elems), out};
+    if (res) {
+        partner[n_out] = res_idx;
+        outs[n_out++] = {span(residual_out, 2 * elems), residual_out};
     }
-    if (variant == -1) variant = pick_norm(tokens, hidden, quant);
+    if (dyn) {
+        partner[n_out] = -1;
+        outs[n_out++] = {span(scale_out, 4 * (uint64_t)tokens), scale_out};
+    }
+    if ((st = check_outputs(outs, partner, n_out, ins, n_in))) return st;
+    if (variant == -1) variant = pick_norm(tokens, hidden, epi != NORM_EPI_BF16);
     const NormVariant *v = norm_variant(variant);
     if (!v || norm_capacity(v) < hidden) return AARMS_ERR_BAD_VARIANT;
     NormParams p;
     p.out = out;
-    p.residual_out = residual_out;
+    p.residual_out = res ? residual_out : nullptr;
     p.x = x;
-    p.residual = residual;
+    p.residual = res ? residual : nullptr;
     p.weight = weight;
-    p.scale_out = scale_out;
+    p.scale_out = dyn ? scale_out : nullptr;
+    p.scale_in = stat ? scale_in : nullptr;
     p.tokens = tokens;
     p.hidden = (int32_t)hidden;
     p.eps = eps;
-    return launch_status(launch_norm(p, quant, variant, device_cus(), stream));
+    return launch_status(launch_norm(p, epi, res, variant, device_cus(), stream));
 }
 
 int swiglu_common(void *out, const void *gate_up, const float *scale, int64_t tokens,
@@ -216,10 +254,40 @@ int swiglu_common(void *out, const void *gate_up, const float *scale, int64_t to
     p.out = out;
     p.gate_up = gate_up;
     p.scale = scale;
+    p.scale_out = nullptr;
     p.tokens = tokens;
     p.inter = inter;
     p.vecs_per_row = (uint32_t)(inter / 8);
     return launch_status(launch_swiglu(p, quant, variant, stream));
+}
+
+int swiglu_rowq_common(void *out, float *scale_out, const void *gate_up, int64_t tokens,
+                       int64_t inter, int variant, hipStream_t stream)
+{
+    int st = check_width(tokens, inter, AARMS_MAX_INTER_PER_TOKEN);
+    if (st) return st;
+    if (tokens > 0 && 2 * inter > AARMS_MAX_ELEMENTS / tokens) return AARMS_ERR_UNSUPPORTED_SHAPE;
+    if (variant < -1 || variant >= swiglu_row_variant_count()) return AARMS_ERR_BAD_VARIANT;
+    if (tokens == 0) return AARMS_OK;
+    if (!out || !scale_out || !gate_up) return AARMS_ERR_NULL_POINTER;
+    if (!aligned(out, 16) || !aligned(gate_up, 16) || !aligned(scale_out, 4)) return AARMS_ERR_MISALIGNED;
+    const uint64_t elems = (uint64_t)tokens * (uint64_t)inter;
+    const Arg outs[2] = {{span(out, elems), out}, {span(scale_out, 4 * (uint64_t)tokens), scale_out}};
+    const Arg ins[1] = {{span(gate_up, 4 * elems), gate_up}};
+    const int partner[2] = {-1, -1};
+    if ((st = check_outputs(outs, partner, 2, ins, 1))) return st;
+    if (variant == -1) variant = pick_swiglu_rowq(tokens, inter);
+    const SwigluRowVariant *v = swiglu_row_variant(variant);
+    if (!v || rowq_capacity(v) < inter) return AARMS_ERR_BAD_VARIANT;
+    SwigluParams p;
+    p.out = out;
+    p.gate_up = gate_up;
+    p.scale = nullptr;
+    p.scale_out = scale_out;
+    p.tokens = tokens;
+    p.inter = inter;
+    p.vecs_per_row = (uint32_t)(inter / 8);
+    return launch_status(launch_swiglu_rowq(p, variant, stream));
 }
 
 }  // namespace
@@ -230,24 +298,24 @@ int fused_add_rmsnorm(void *out, void *residual_out, const void *x, const void *
                       const void *weight, int64_t num_tokens, int64_t hidden, float eps,
                       hipStream_t stream)
 {
-    return norm_common(out, nullptr, residual_out, x, residual, weight, num_tokens, hidden, eps,
-                       false, -1, stream);
+    return norm_common(out, nullptr, nullptr, residual_out, x, residual, weight, num_tokens, hidden,
+                       eps, NORM_EPI_BF16, true, -1, stream);
 }
 
 int fused_add_rmsnorm_ex(void *out, void *residual_out, const void *x, const void *residual,
                          const void *weight, int64_t num_tokens, int64_t hidden, float eps,
                          int variant, hipStream_t stream)
 {
-    return norm_common(out, nullptr, residual_out, x, residual, weight, num_tokens, hidden, eps,
-                       false, variant, stream);
+    return norm_common(out, nullptr, nullptr, residual_out, x, residual, weight, num_tokens, hidden,
+                       eps, NORM_EPI_BF16, true, variant, stream);
 }
 
 int fused_add_rmsnorm_quant_fp8(void *out_fp8, float *scale_out, void *residual_out,
                                 const void *x, const void *residual, const void *weight,
                                 int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream)
 {
-    return norm_common(out_fp8, scale_out, residual_out, x, residual, weight, num_tokens, hidden,
-                       eps, true, -1, stream);
+    return norm_common(out_fp8, scale_out, nullptr, residual_out, x, residual, weight, num_tokens,
+                       hidden, eps, NORM_EPI_FP8_DYNAMIC, true, -1, stream);
 }
 
 int fused_add_rmsnorm_quant_fp8_ex(void *out_fp8, float *scale_out, void *residual_out,
@@ -255,8 +323,70 @@ int fused_add_rmsnorm_quant_fp8_ex(void *out_fp8, float *scale_out, void *residu
                                    int64_t num_tokens, int64_t hidden, float eps, int variant,
                                    hipStream_t stream)
 {
-    return norm_common(out_fp8, scale_out, residual_out, x, residual, weight, num_tokens, hidden,
-                       eps, true, variant, stream);
+    return norm_common(out_fp8, scale_out, nullptr, residual_out, x, residual, weight, num_tokens,
+                       hidden, eps, NORM_EPI_FP8_DYNAMIC, true, variant, stream);
+}
+
+int fused_add_rmsnorm_quant_fp8_static(void *out_fp8, void *residual_out, const void *x,
+                                       const void *residual, const void *weight, const float *scale,
+                                       int64_t num_tokens, int64_t hidden, float eps,
+                                       hipStream_t stream)
+{
+    return norm_common(out_fp8, nullptr, scale, residual_out, x, residual, weight, num_tokens,
+                       hidden, eps, NORM_EPI_FP8_STATIC, true, -1, stream);
+}
+
+int fused_add_rmsnorm_quant_fp8_static_ex(void *out_fp8, void *residual_out, const void *x,
+                                          const void *residual, const void *weight,
+                                          const float *scale, int64_t num_tokens, int64_t hidden,
+                                          float eps, int variant, hipStream_t stream)
+{
+    return norm_common(out_fp8, nullptr, scale, residual_out, x, residual, weight, num_tokens,
+                       hidden, eps, NORM_EPI_FP8_STATIC, true, variant, stream);
+}
+
+int rmsnorm(void *out, const void *x, const void *weight, int64_t num_tokens, int64_t hidden,
+            float eps, hipStream_t stream)
+{
+    return norm_common(out, nullptr, nullptr, nullptr, x, nullptr, weight, num_tokens, hidden, eps,
+                       NORM_EPI_BF16, false, -1, stream);
+}
+
+int rmsnorm_ex(void *out, const void *x, const void *weight, int64_t num_tokens, int64_t hidden,
+               float eps, int variant, hipStream_t stream)
+{
+    return norm_common(out, nullptr, nullptr, nullptr, x, nullptr, weight, num_tokens, hidden, eps,
+                       NORM_EPI_BF16, false, variant, stream);
+}
+
+int rmsnorm_quant_fp8(void *out_fp8, float *scale_out, const void *x, const void *weight,
+                      int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream)
+{
+    return norm_common(out_fp8, scale_out, nullptr, nullptr, x, nullptr, weight, num_tokens, hidden,
+                       eps, NORM_EPI_FP8_DYNAMIC, false, -1, stream);
+}
+
+int rmsnorm_quant_fp8_ex(void *out_fp8, float *scale_out, const void *x, const void *weight,
+                         int64_t num_tokens, int64_t hidden, float eps, int variant,
+                         hipStream_t stream)
+{
+    return norm_common(out_fp8, scale_out, nullptr, nullptr, x, nullptr, weight, num_tokens, hidden,
+                       eps, NORM_EPI_FP8_DYNAMIC, false, variant, stream);
+}
+
+int rmsnorm_quant_fp8_static(void *out_fp8, const void *x, const void *weight, const float *scale,
+                             int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream)
+{
+    return norm_common(out_fp8, nullptr, scale, nullptr, x, nullptr, weight, num_tokens, hidden,
+                       eps, NORM_EPI_FP8_STATIC, false, -1, stream);
+}
+
+int rmsnorm_quant_fp8_static_ex(void *out_fp8, const void *x, const void *weight,
+                                const float *scale, int64_t num_tokens, int64_t hidden, float eps,
+                                int variant, hipStream_t stream)
+{
+    return norm_common(out_fp8, nullptr, scale, nullptr, x, nullptr, weight, num_tokens, hidden,
+                       eps, NORM_EPI_FP8_STATIC, false, variant, stream);
 }
 
 int swiglu(void *out, const void *gate_up, int64_t num_tokens, int64_t inter, hipStream_t stream)
@@ -282,6 +412,18 @@ int swiglu_quant_fp8_ex(void *out_fp8, const void *gate_up, const float *scale,
     return swiglu_common(out_fp8, gate_up, scale, num_tokens, inter, true, variant, stream);
 }
 
+int swiglu_quant_fp8_dynamic(void *out_fp8, float *scale_out, const void *gate_up,
+                             int64_t num_tokens, int64_t inter, hipStream_t stream)
+{
+    return swiglu_rowq_common(out_fp8, scale_out, gate_up, num_tokens, inter, -1, stream);
+}
+
+int swiglu_quant_fp8_dynamic_ex(void *out_fp8, float *scale_out, const void *gate_up,
+                                int64_t num_tokens, int64_t inter, int variant, hipStream_t stream)
+{
+    return swiglu_rowq_common(out_fp8, scale_out, gate_up, num_tokens, inter, variant, stream);
+}
+
 const char *aarms_status_string(int status)
 {
     switch (status) {
@@ -300,7 +442,9 @@ const char *aarms_status_string(int status)
 
 int aarms_variant_count(int op)
 {
-    return op == 0 ? norm_variant_count() : op == 1 ? swiglu_variant_count() : 0;
+    return op == 0 ? norm_variant_count()
+         : op == 1 ? swiglu_variant_count()
+         : op == 2 ? swiglu_row_variant_count() : 0;
 }
 
 const char *aarms_variant_name(int op, int variant)
@@ -313,6 +457,10 @@ const char *aarms_variant_name(int op, int variant)
         const SwigluVariant *v = swiglu_variant(variant);
         return v ? v->name : nullptr;
     }
+    if (op == 2) {
+        const SwigluRowVariant *v = swiglu_row_variant(variant);
+        return v ? v->name : nullptr;
+    }
     return nullptr;
 }
 
@@ -320,6 +468,7 @@ int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant)
 {
     if (op == 0) return pick_norm(num_tokens, width, quant != 0);
     if (op == 1) return (width > 0 && width % 8 == 0) ? pick_swiglu(num_tokens, width, quant != 0) : -1;
+    if (op == 2) return (width > 0 && width % 8 == 0) ? pick_swiglu_rowq(num_tokens, width) : -1;
     return -1;
 }
 

@@ -7,13 +7,21 @@
 
 namespace aarms {
 
+// Norm epilogues.
+enum NormEpilogue : int {
+    NORM_EPI_BF16 = 0,        // bf16 out
+    NORM_EPI_FP8_DYNAMIC = 1, // E4M3 out, per-token scale written to scale_out
+    NORM_EPI_FP8_STATIC = 2,  // E4M3 out, per-tensor scale read from scale_in
+};
+
 struct NormParams {
     void *out;               // bf16 [T,H], or fp8 [T,H] when quantising
-    void *residual_out;      // bf16 [T,H]
+    void *residual_out;      // bf16 [T,H] (with the residual add), else null
     const void *x;           // bf16 [T,H]
-    const void *residual;    // bf16 [T,H]
+    const void *residual;    // bf16 [T,H] (with the residual add), else null
     const void *weight;      // bf16 [H]
-    float *scale_out;        // fp32 [T] when quantising, else null
+    float *scale_out;        // fp32 [T], dynamic FP8 only
+    const float *scale_in;   // fp32 [1], static FP8 only
     int64_t tokens;
     int32_t hidden;
     float eps;
@@ -22,7 +30,8 @@ struct NormParams {
 struct SwigluParams {
     void *out;               // bf16 [T,N], or fp8 [T,N] when quantising
     const void *gate_up;     // bf16 [T,2N]
-    const float *scale;      // fp32 [1] when quantising, else null
+    const float *scale;      // fp32 [1], static FP8 only
+    float *scale_out;        // fp32 [T], per-token FP8 only
     int64_t tokens;          // T
     int64_t inter;           // N
     uint32_t vecs_per_row;   // N / 8: one job = 8 adjacent outputs of a row
@@ -47,13 +56,24 @@ struct SwigluVariant {
     const char *name;
 };
 
+// Per-token FP8 SwiGLU variants: (waves per row, 8-output jobs per lane).
+// A row of N outputs needs waves * 64 * jobs * 8 >= N.
+struct SwigluRowVariant {
+    int waves_per_row;
+    int jobs_per_lane;
+    const char *name;
+};
+
 int norm_variant_count();
 const NormVariant *norm_variant(int id);
 int swiglu_variant_count();
 const SwigluVariant *swiglu_variant(int id);
 
-hipError_t launch_norm(const NormParams &p, bool quant, int variant, int num_cus,
+hipError_t launch_norm(const NormParams &p, int epi, bool residual, int variant, int num_cus,
                        hipStream_t stream);
+int swiglu_row_variant_count();
+const SwigluRowVariant *swiglu_row_variant(int id);
 hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, hipStream_t stream);
+hipError_t launch_swiglu_rowq(const SwigluParams &p, int variant, hipStream_t stream);
 
 }  // namespace aarms

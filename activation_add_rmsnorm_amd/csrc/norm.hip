@@ -1,9 +1,10 @@
-// norm.hip -- fused residual add + RMSNorm for gfx950, with a bf16 epilogue
-// or a dynamic per-token E4M3 epilogue.
+// norm.hip -- RMSNorm for gfx950, with or without the residual add in front,
+// and with a bf16 epilogue, a dynamic per-token E4M3 epilogue or a static
+// per-tensor E4M3 epilogue.
 //
-// One pass over HBM: x and residual are read once with 16-byte streaming
-// loads, the updated residual and the output are written once, and the row stays in
-// registers between the reduction and the epilogue.  A row is handled by one
+// One pass over HBM: x (and the residual) are read once with 16-byte
+// streaming loads, the updated residual and the output are written once, and
+// the row stays in registers between the reduction and the epilogue.  A row is handled by one
 // wave (narrow rows, four rows per 256-thread block) or by a whole block of
 // 2..16 waves (wide rows).  The sum of squares is accumulated per lane in
 // binary64, reduced with a wave butterfly and, across waves, through LDS in
@@ -11,9 +12,11 @@
 //
 // The arithmetic follows the eight-operation RMSNorm with the residual add
 // in front ("TensorRT-LLM: Compiling Inference Engines Ahead of Time",
-// section "Fusing operations, measured"); the FP8 epilogue follows vLLM's
-// RMSNorm + quant fusion ("Introduction to torch.compile and How It Works
-// with vLLM", section 4).
+// section "Fusing operations, measured"; the same page's own Metal norm has
+// no add); the FP8 epilogues follow vLLM's RMSNorm + quant fusion
+// ("Introduction to torch.compile and How It Works with vLLM", section 4)
+// with the per-token or per-tensor scaling of the TensorRT-LLM walkthrough's
+// quantization deep dive (Part V).
 
 #include "device.h"
 #include "launch.h"
@@ -22,7 +25,7 @@ namespace aarms {
 
 // q = e4m3(clamp(y / s)) for this lane's slices of the row (y as binary32
 // values of bf16), stored as 8-byte groups.
-template <int WPR, int VPT, bool FAST>
+template <int WPR, int VPT, bool FAST, bool CLAMP>
 __device__ __forceinline__ void quantize_row(const float (&yf)[VPT][8], const E4m3Scale &qs,
                                              uint8_t *qo, int lane, int nvec)
 {
@@ -32,7 +35,7 @@ __device__ __forceinline__ void quantize_row(const float (&yf)[VPT][8], const E4
         if (v >= nvec) continue;
         float z[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) z[j] = e4m3_quotient<FAST, false>(yf[k][j], qs);
+        for (int j = 0; j < 8; ++j) z[j] = e4m3_quotient<FAST, CLAMP>(yf[k][j], qs);
         u32x2 q;
         q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
         q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
@@ -40,7 +43,8 @@ __device__ __forceinline__ void quantize_row(const float (&yf)[VPT][8], const E4
     }
 }
 
-template <int WPR, int VPT>
+// x into xv and, with RES, the residual into rv.
+template <int WPR, int VPT, bool RES>
 __device__ __forceinline__ void load_row(const NormParams &p, int64_t row, int lane, int nvec,
                                          u32x4 (&xv)[VPT], u32x4 (&rv)[VPT])
 {
@@ -52,7 +56,38 @@ __device__ __forceinline__ void load_row(const NormParams &p, int64_t row, int l
         const int v = lane + k * WPR * 64;
         const bool ok = v < nvec;
         xv[k] = ok ? ld_stream(xr + v) : (u32x4)0u;
-        rv[k] = ok ? ld_stream(rr + v) : (u32x4)0u;
+        if constexpr (RES) rv[k] = ok ? ld_stream(rr + v) : (u32x4)0u;
+    }
+}
+
+// y = bf16(w * bf16(h * rs)) for the two bf16 of one word of the row.
+__device__ __forceinline__ uint32_t norm_word(uint32_t r, uint32_t w, float rs)
+{
+    const uint32_t t = pack_bf16(bf_lo(r) * rs, bf_hi(r) * rs);
+    return pack_bf16(bf_lo(w) * bf_lo(t), bf_hi(w) * bf_hi(t));
+}
+
+// Static per-tensor E4M3 epilogue: q = e4m3(clamp(y / s)) straight from the
+// row, 8 bytes per 16-byte slice.
+template <int WPR, int VPT, bool FAST>
+__device__ __forceinline__ void store_static_fp8(const u32x4 (&rv)[VPT], const u32x4 (&wv)[VPT], float rs,
+                                                 const E4m3Scale &qs, uint8_t *qo, int lane, int nvec)
+{
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int v = lane + k * WPR * 64;
+        if (v >= nvec) continue;
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t y = norm_word(rv[k][e], wv[k][e], rs);
+            z[2 * e] = e4m3_quotient<FAST, true>(bf_lo(y), qs);
+            z[2 * e + 1] = e4m3_quotient<FAST, true>(bf_hi(y), qs);
+        }
+        u32x2 q;
+        q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+        q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
+        st_stream((u32x2 *)(qo + (size_t)v * 8), q);
     }
 }
 
@@ -67,16 +102,17 @@ __device__ __forceinline__ void load_weight(const NormParams &p, int lane, int n
     }
 }
 
-// Everything after the row's loads: residual add and store, sum of squares,
-// the row reduction (through psum when the row spans several waves), the
-// normalization and the epilogue.  With W_LATE the weight is loaded here,
-// after the first pass, so that its registers are not live while the row
-// loads are in flight.
-template <int WPR, int VPT, bool QUANT, bool W_LATE>
+// Everything after the row's loads: residual add and store (RES), sum of
+// squares, the row reduction (through psum when the row spans several
+// waves), the normalization and the epilogue.  With W_LATE the weight is
+// loaded here, after the first pass, so that its registers are not live
+// while the row loads are in flight.
+template <int WPR, int VPT, int EPI, bool RES, bool W_LATE>
 __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int lane, int nvec,
                                            const u32x4 (&xv)[VPT], u32x4 (&rv)[VPT],
                                            u32x4 (&wv)[VPT], double *psum, float *pmax)
 {
+    constexpr bool QUANT = EPI == NORM_EPI_FP8_DYNAMIC;
     const size_t base = (size_t)row * (size_t)p.hidden;
     u32x4 *ro = (u32x4 *)((uint16_t *)p.residual_out + base);
 
@@ -93,11 +129,15 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
     for (int k = 0; k < VPT; ++k) {
         const int v = lane + k * WPR * 64;
         u32x4 r;
+        if constexpr (RES) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            r[e] = pack_bf16(bf_lo(xv[k][e]) + bf_lo(rv[k][e]), bf_hi(xv[k][e]) + bf_hi(rv[k][e]));
+            for (int e = 0; e < 4; ++e)
+                r[e] = pack_bf16(bf_lo(xv[k][e]) + bf_lo(rv[k][e]), bf_hi(xv[k][e]) + bf_hi(rv[k][e]));
+            if (v < nvec) st_stream(ro + v, r);
+        } else {
+            r = xv[k];
+        }
         rv[k] = r;
-        if (v < nvec) st_stream(ro + v, r);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float h0 = bf_lo(r[e]), h1 = bf_hi(r[e]);
@@ -129,7 +169,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
     const float var = mean + p.eps;
     const float rs = (float)(1.0 / sqrt((double)var));
 
-    if constexpr (!QUANT) {
+    if constexpr (EPI == NORM_EPI_BF16) {
         // ---- t = bf16(h * rs), y = bf16(w * t)
         u32x4 *o = (u32x4 *)((uint16_t *)p.out + base);
 #pragma unroll
@@ -138,12 +178,17 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
             if (v >= nvec) continue;
             u32x4 y;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t t = pack_bf16(bf_lo(rv[k][e]) * rs, bf_hi(rv[k][e]) * rs);
-                y[e] = pack_bf16(bf_lo(wv[k][e]) * bf_lo(t), bf_hi(wv[k][e]) * bf_hi(t));
-            }
+            for (int e = 0; e < 4; ++e) y[e] = norm_word(rv[k][e], wv[k][e], rs);
             st_stream(o + v, y);
         }
+    } else if constexpr (EPI == NORM_EPI_FP8_STATIC) {
+        // ---- y as above, q = e4m3(clamp(y / s)) with the given scale
+        const E4m3Scale qs = make_e4m3_scale(*p.scale_in);
+        uint8_t *qo = (uint8_t *)p.out + base;
+        if (e4m3_scale_is_fast(qs))
+            store_static_fp8<WPR, VPT, true>(rv, wv, rs, qs, qo, lane, nvec);
+        else
+            store_static_fp8<WPR, VPT, false>(rv, wv, rs, qs, qo, lane, nvec);
     } else {
         // ---- y as above, kept as binary32 values of bf16; row amax.  Slices
         // past the row end hold w = 0, so y = 0 there.
@@ -175,15 +220,15 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         const E4m3Scale qs = make_e4m3_scale(s);
         uint8_t *qo = (uint8_t *)p.out + base;
         if (e4m3_scale_is_fast(qs))
-            quantize_row<WPR, VPT, true>(hf, qs, qo, lane, nvec);
+            quantize_row<WPR, VPT, true, false>(hf, qs, qo, lane, nvec);
         else
-            quantize_row<WPR, VPT, false>(hf, qs, qo, lane, nvec);
+            quantize_row<WPR, VPT, false, false>(hf, qs, qo, lane, nvec);
     }
 }
 
 // One row per block (WPR > 1) or per wave (WPR == 1, four rows per block);
 // one block per row or row quartet.
-template <int WPR, int VPT, bool QUANT>
+template <int WPR, int VPT, int EPI, bool RES>
 __global__ void __launch_bounds__(WPR == 1 ? 256 : WPR * 64)
 norm_kernel(NormParams p)
 {
@@ -205,10 +250,10 @@ norm_kernel(NormParams p)
 
     // all loads of the row slice in flight before any use
     u32x4 xv[VPT], rv[VPT], wv[VPT];
-    load_row<WPR, VPT>(p, row, lane, nvec, xv, rv);
+    load_row<WPR, VPT, RES>(p, row, lane, nvec, xv, rv);
     constexpr bool W_LATE = WPR > 1;
     if constexpr (!W_LATE) load_weight<WPR, VPT>(p, lane, nvec, wv);
-    finish_row<WPR, VPT, QUANT, W_LATE>(p, row, lane, nvec, xv, rv, wv, psum, pmax);
+    finish_row<WPR, VPT, EPI, RES, W_LATE>(p, row, lane, nvec, xv, rv, wv, psum, pmax);
 }
 
 // Persistent and software-pipelined: a fixed grid of blocks walks the rows
@@ -216,7 +261,7 @@ norm_kernel(NormParams p)
 // next row's x and residual are loaded before the current row is processed,
 // so their latency hides behind its reductions and stores.  The blocks in
 // flight always cover a window of G consecutive rows.
-template <int WPR, int VPT, bool QUANT>
+template <int WPR, int VPT, int EPI, bool RES>
 __global__ void __launch_bounds__(WPR == 1 ? 256 : WPR * 64)
 norm_kernel_pipelined(NormParams p)
 {
@@ -239,19 +284,19 @@ norm_kernel_pipelined(NormParams p)
     u32x4 wv[VPT];
     load_weight<WPR, VPT>(p, lane, nvec, wv);
     u32x4 xa[VPT], ra[VPT];
-    load_row<WPR, VPT>(p, row, lane, nvec, xa, ra);
+    load_row<WPR, VPT, RES>(p, row, lane, nvec, xa, ra);
     int par = 0;
     while (true) {
         const int64_t next = row + step;
         const bool more = next < p.tokens;
         u32x4 xb[VPT], rb[VPT];
         if (more) {
-            load_row<WPR, VPT>(p, next, lane, nvec, xb, rb);
+            load_row<WPR, VPT, RES>(p, next, lane, nvec, xb, rb);
         } else {
 #pragma unroll
             for (int k = 0; k < VPT; ++k) xb[k] = rb[k] = (u32x4)0u;
         }
-        finish_row<WPR, VPT, QUANT, false>(p, row, lane, nvec, xa, ra, wv, psum[par], pmax);
+        finish_row<WPR, VPT, EPI, RES, false>(p, row, lane, nvec, xa, ra, wv, psum[par], pmax);
         if (!more) break;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
@@ -292,7 +337,7 @@ const NormVariant *norm_variant(int id)
     return (id >= 0 && id < kNumNormVariants) ? &kNormVariants[id] : nullptr;
 }
 
-template <int WPR, int VPT, bool Q, bool PIPE>
+template <int WPR, int VPT, int EPI, bool RES, bool PIPE>
 static hipError_t launch_one(const NormParams &p, int blocks_per_cu, int num_cus,
                              hipStream_t stream)
 {
@@ -305,12 +350,12 @@ static hipError_t launch_one(const NormParams &p, int blocks_per_cu, int num_cus
     }
     NormParams copy = p;
     void *args[] = {&copy};
-    const void *fn = PIPE ? (const void *)&norm_kernel_pipelined<WPR, VPT, Q>
-                          : (const void *)&norm_kernel<WPR, VPT, Q>;
+    const void *fn = PIPE ? (const void *)&norm_kernel_pipelined<WPR, VPT, EPI, RES>
+                          : (const void *)&norm_kernel<WPR, VPT, EPI, RES>;
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
 }
 
-template <bool Q>
+template <int EPI, bool RES>
 static hipError_t dispatch(const NormParams &p, int variant, int num_cus, hipStream_t s)
 {
     const NormVariant *v = norm_variant(variant);
@@ -318,7 +363,8 @@ static hipError_t dispatch(const NormParams &p, int variant, int num_cus, hipStr
     const int b = v->blocks_per_cu;
 #define AARMS_NORM_CASE(W, V)                                                              \
     if (v->waves_per_row == W && v->vecs_per_lane == V)                                    \
-        return b ? launch_one<W, V, Q, true>(p, b, num_cus, s) : launch_one<W, V, Q, false>(p, 0, num_cus, s);
+        return b ? launch_one<W, V, EPI, RES, true>(p, b, num_cus, s)                       \
+                 : launch_one<W, V, EPI, RES, false>(p, 0, num_cus, s);
     AARMS_NORM_CASE(1, 1)
     AARMS_NORM_CASE(1, 2)
     AARMS_NORM_CASE(1, 3)
@@ -344,10 +390,22 @@ static hipError_t dispatch(const NormParams &p, int variant, int num_cus, hipStr
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_norm(const NormParams &p, bool quant, int variant, int num_cus, hipStream_t stream)
+hipError_t launch_norm(const NormParams &p, int epi, bool residual, int variant, int num_cus,
+                       hipStream_t stream)
 {
-    return quant ? dispatch<true>(p, variant, num_cus, stream)
-                 : dispatch<false>(p, variant, num_cus, stream);
+    switch (epi) {
+    case NORM_EPI_BF16:
+        return residual ? dispatch<NORM_EPI_BF16, true>(p, variant, num_cus, stream)
+                        : dispatch<NORM_EPI_BF16, false>(p, variant, num_cus, stream);
+    case NORM_EPI_FP8_DYNAMIC:
+        return residual ? dispatch<NORM_EPI_FP8_DYNAMIC, true>(p, variant, num_cus, stream)
+                        : dispatch<NORM_EPI_FP8_DYNAMIC, false>(p, variant, num_cus, stream);
+    case NORM_EPI_FP8_STATIC:
+        return residual ? dispatch<NORM_EPI_FP8_STATIC, true>(p, variant, num_cus, stream)
+                        : dispatch<NORM_EPI_FP8_STATIC, false>(p, variant, num_cus, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace aarms

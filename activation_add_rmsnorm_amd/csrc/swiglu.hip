@@ -13,6 +13,11 @@
 // per chunk, no grid-stride loop: the blocks in flight then cover one
 // contiguous window of HBM).  Nothing is kept between jobs.
 //
+// The per-token (dynamic) E4M3 form needs the row's amax before any code is
+// written, so there a row belongs to one wave or one block (as in the norm),
+// every job's y stays packed in registers through the amax reduction, and
+// the scale s = amax / 448 is written per row.
+//
 // SiLU is rounded once to bf16 before the product, and that rounding must be
 // the correctly rounded one: the fast hardware exp2/rcp form is used unless
 // its result sits near a bf16 midpoint, in which case that lane recomputes
@@ -153,6 +158,132 @@ __global__ void __launch_bounds__(256) swiglu_kernel(SwigluParams p)
     } else {
         swiglu_block<U, W, 0>(p, E4m3Scale{});
     }
+}
+
+// Per-token E4M3: one row per wave (WPR == 1, four rows per 256-thread
+// block) or per block of WPR waves, JPT jobs per lane.
+template <int WPR, int JPT, bool FAST>
+__device__ __forceinline__ void rowq_store(const u32x4 (&y)[JPT], const E4m3Scale &qs, u32x2 *qo,
+                                           int lane, uint32_t njobs)
+{
+#pragma unroll
+    for (int k = 0; k < JPT; ++k) {
+        const uint32_t v = lane + k * WPR * 64;
+        if (v >= njobs) continue;
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // |y| <= amax, so |y / s| <= 448 (1 + 2^-24): no input clamp needed
+            z[2 * e] = e4m3_quotient<FAST, false>(bf_lo(y[k][e]), qs);
+            z[2 * e + 1] = e4m3_quotient<FAST, false>(bf_hi(y[k][e]), qs);
+        }
+        u32x2 q;
+        q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+        q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
+        st_stream(qo + v, q);
+    }
+}
+
+template <int WPR, int JPT>
+__global__ void __launch_bounds__(WPR == 1 ? 256 : WPR * 64) swiglu_rowq_kernel(SwigluParams p)
+{
+    constexpr int ROW_THREADS = WPR * 64;
+    constexpr int ROWS_PER_BLOCK = (WPR == 1) ? 4 : 1;
+    __shared__ float pmax[WPR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % ROW_THREADS;
+    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK +
+                        (WPR == 1 ? __builtin_amdgcn_readfirstlane(tid / ROW_THREADS) : 0);
+    // uniform per wave (WPR == 1: no block barrier follows) or per block
+    if (row >= p.tokens) return;
+    const uint32_t njobs = p.vecs_per_row;
+    const u32x4 *gate = (const u32x4 *)((const uint16_t *)p.gate_up + (uint64_t)row * 2u * (uint64_t)p.inter);
+    const u32x4 *up = gate + njobs;
+
+    u32x4 y[JPT], uv[JPT];
+#pragma unroll
+    for (int k = 0; k < JPT; ++k) {
+        const uint32_t v = lane + k * ROW_THREADS;
+        const bool ok = v < njobs;
+        y[k] = ok ? ld_stream(gate + v) : (u32x4)0u;
+        uv[k] = ok ? ld_stream(up + v) : (u32x4)0u;
+    }
+    // y in place of the gate; slots past the row end hold gate = up = 0, so
+    // y = 0 there and the amax is unaffected
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < JPT; ++k) {
+        y[k] = swiglu_job<4>(y[k], uv[k]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf_lo(y[k][e])), __builtin_fabsf(bf_hi(y[k][e]))));
+    }
+    amax = wave_max(amax);
+    if constexpr (WPR > 1) {
+        if ((lane & 63) == 0) pmax[lane >> 6] = amax;
+        __syncthreads();
+        amax = pmax[0];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) amax = fmaxf(amax, pmax[i]);
+    }
+    const float s = amax / 448.0f;
+    if (lane == 0) p.scale_out[row] = s;
+    const E4m3Scale qs = make_e4m3_scale(s);
+    u32x2 *qo = (u32x2 *)p.out + (uint64_t)row * njobs;
+    if (e4m3_scale_is_fast(qs))
+        rowq_store<WPR, JPT, true>(y, qs, qo, lane, njobs);
+    else
+        rowq_store<WPR, JPT, false>(y, qs, qo, lane, njobs);
+}
+
+static const SwigluRowVariant kSwigluRowVariants[] = {
+    {1, 1, "wave/row x1 job"},   {1, 2, "wave/row x2 jobs"},   {1, 4, "wave/row x4 jobs"},
+    {4, 2, "4 waves/row x2 jobs"},  {4, 4, "4 waves/row x4 jobs"},
+    {8, 2, "8 waves/row x2 jobs"},  {8, 3, "8 waves/row x3 jobs"},  {8, 4, "8 waves/row x4 jobs"},
+    {16, 2, "16 waves/row x2 jobs"}, {16, 3, "16 waves/row x3 jobs"}, {16, 4, "16 waves/row x4 jobs"},
+    {16, 8, "16 waves/row x8 jobs"},
+};
+constexpr int kNumSwigluRowVariants = sizeof(kSwigluRowVariants) / sizeof(kSwigluRowVariants[0]);
+
+int swiglu_row_variant_count() { return kNumSwigluRowVariants; }
+const SwigluRowVariant *swiglu_row_variant(int id)
+{
+    return (id >= 0 && id < kNumSwigluRowVariants) ? &kSwigluRowVariants[id] : nullptr;
+}
+
+template <int WPR, int JPT>
+static hipError_t launch_rowq(const SwigluParams &p, hipStream_t stream)
+{
+    constexpr int threads = (WPR == 1) ? 256 : WPR * 64;
+    constexpr int rows_per_block = (WPR == 1) ? 4 : 1;
+    const int64_t blocks = (p.tokens + rows_per_block - 1) / rows_per_block;
+    SwigluParams copy = p;
+    void *args[] = {&copy};
+    return hipLaunchKernel((const void *)&swiglu_rowq_kernel<WPR, JPT>, dim3((unsigned)blocks),
+                           dim3(threads), args, 0, stream);
+}
+
+hipError_t launch_swiglu_rowq(const SwigluParams &p, int variant, hipStream_t s)
+{
+    const SwigluRowVariant *v = swiglu_row_variant(variant);
+    if (!v) return hipErrorInvalidValue;
+#define AARMS_ROWQ_CASE(W, J) \
+    if (v->waves_per_row == W && v->jobs_per_lane == J) return launch_rowq<W, J>(p, s);
+    AARMS_ROWQ_CASE(1, 1)
+    AARMS_ROWQ_CASE(1, 2)
+    AARMS_ROWQ_CASE(1, 4)
+    AARMS_ROWQ_CASE(4, 2)
+    AARMS_ROWQ_CASE(4, 4)
+    AARMS_ROWQ_CASE(8, 2)
+    AARMS_ROWQ_CASE(8, 3)
+    AARMS_ROWQ_CASE(8, 4)
+    AARMS_ROWQ_CASE(16, 2)
+    AARMS_ROWQ_CASE(16, 3)
+    AARMS_ROWQ_CASE(16, 4)
+    AARMS_ROWQ_CASE(16, 8)
+#undef AARMS_ROWQ_CASE
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- variants

@@ -64,6 +64,8 @@ enum aarms_status {
 #define AARMS_MAX_HIDDEN 65536            /* norms: row width kept in registers    */
 #define AARMS_MAX_ELEMENTS (1LL << 40)    /* tokens x width, per tensor            */
 #define AARMS_MAX_INTER (1LL << 33)       /* swiglu: output row width              */
+#define AARMS_MAX_INTER_PER_TOKEN 65536   /* swiglu_quant_fp8_dynamic: row kept in
+                                             registers until its amax is known    */
 
 /*
  * fused_add_rmsnorm -- residual add followed by RMSNorm in one pass.
@@ -112,6 +114,48 @@ int fused_add_rmsnorm_quant_fp8(void *out_fp8, float *scale_out, void *residual_
                                 hipStream_t stream);
 
 /*
+ * fused_add_rmsnorm_quant_fp8_static -- fused_add_rmsnorm whose bf16 output
+ * is quantised to E4M3 with a given per-tensor scale, in the same pass
+ * (vLLM's RMSNorm + quant fusion with the per-tensor scaling of the
+ * "TensorRT-LLM" walkthrough, Part V).
+ *
+ *   out_fp8      [num_tokens, hidden] fp8    written: e4m3(clamp(y / *scale, -448, 448))
+ *   residual_out [num_tokens, hidden] bf16   written: x + residual
+ *   scale        [1] fp32, device memory,    read by the kernel; positive and
+ *                finite, except that exactly zero is treated as one
+ *   x, residual, weight, hidden, eps         as for fused_add_rmsnorm
+ * In place: residual_out == residual is allowed.
+ */
+int fused_add_rmsnorm_quant_fp8_static(void *out_fp8, void *residual_out,
+                                       const void *x, const void *residual, const void *weight,
+                                       const float *scale, int64_t num_tokens, int64_t hidden,
+                                       float eps, hipStream_t stream);
+
+/*
+ * rmsnorm -- RMSNorm without the residual add: the form of the first page's
+ * own Metal norm ("TensorRT-LLM: Compiling Inference Engines Ahead of Time",
+ * section "Fusing operations, measured": the laptop fusions have no add).
+ *
+ *   out      [num_tokens, hidden] bf16   written: bf16(w * bf16(x * rs))
+ *   x        [num_tokens, hidden] bf16   read
+ *   weight, hidden, eps                  as for fused_add_rmsnorm
+ * In place: out == x is allowed.
+ */
+int rmsnorm(void *out, const void *x, const void *weight, int64_t num_tokens, int64_t hidden,
+            float eps, hipStream_t stream);
+
+/*
+ * rmsnorm_quant_fp8 / rmsnorm_quant_fp8_static -- rmsnorm with the dynamic
+ * per-token or the static per-tensor E4M3 epilogue of the two
+ * fused_add_rmsnorm_quant_fp8 forms above (same outputs, no residual).
+ * No in-place form.
+ */
+int rmsnorm_quant_fp8(void *out_fp8, float *scale_out, const void *x, const void *weight,
+                      int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream);
+int rmsnorm_quant_fp8_static(void *out_fp8, const void *x, const void *weight, const float *scale,
+                             int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream);
+
+/*
  * swiglu -- silu(gate) * up over a concatenated gate_up projection output.
  *
  * TensorRT-LLM's gated MLP runs one gate_up_proj matmul followed by a fused
@@ -144,6 +188,22 @@ int swiglu(void *out, const void *gate_up, int64_t num_tokens, int64_t inter,
 int swiglu_quant_fp8(void *out_fp8, const void *gate_up, const float *scale,
                      int64_t num_tokens, int64_t inter, hipStream_t stream);
 
+/*
+ * swiglu_quant_fp8_dynamic -- swiglu whose bf16 output is quantised to E4M3
+ * with a dynamic per-token scale, in the same pass (vLLM's SiLU-and-mul +
+ * quant fusion, sections 3 and 4 of its post, with per-token scaling as in
+ * the norm above).
+ *
+ *   out_fp8   [num_tokens, inter]     fp8    written: e4m3(clamp(y / s_row))
+ *   scale_out [num_tokens]            fp32   written: s_row = binary32(max_j |y_j| / 448)
+ *                                            (0 for an all-zero row, whose codes are zeros)
+ *   gate_up   [num_tokens, 2 * inter] bf16   read, as for swiglu
+ *   inter     > 0, multiple of 8, at most AARMS_MAX_INTER_PER_TOKEN
+ * y is the bf16 value swiglu would write.  No in-place form.
+ */
+int swiglu_quant_fp8_dynamic(void *out_fp8, float *scale_out, const void *gate_up,
+                             int64_t num_tokens, int64_t inter, hipStream_t stream);
+
 /* Human-readable name of a return code (static storage, never NULL). */
 const char *aarms_status_string(int status);
 
@@ -152,8 +212,9 @@ const char *aarms_status_string(int status);
  * from (num_tokens, width, output format); the *_ex forms take it
  * explicitly.  A variant id is an index into the op's table;
  * aarms_variant_name() describes it (static storage) and returns NULL past
- * the end.  ops: 0 = fused_add_rmsnorm and fused_add_rmsnorm_quant_fp8,
- * 1 = swiglu and swiglu_quant_fp8 (quant != 0 selects the FP8 form).
+ * the end.  ops: 0 = every norm entry point (quant != 0 for an E4M3 form),
+ * 1 = swiglu and swiglu_quant_fp8 (quant != 0 selects the FP8 form),
+ * 2 = swiglu_quant_fp8_dynamic.
  * aarms_pick_variant() returns the id the plain entry point would use, or -1
  * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
  */
@@ -173,6 +234,20 @@ int swiglu_ex(void *out, const void *gate_up, int64_t num_tokens, int64_t inter,
               int variant, hipStream_t stream);
 int swiglu_quant_fp8_ex(void *out_fp8, const void *gate_up, const float *scale,
                         int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
+int fused_add_rmsnorm_quant_fp8_static_ex(void *out_fp8, void *residual_out,
+                                          const void *x, const void *residual, const void *weight,
+                                          const float *scale, int64_t num_tokens, int64_t hidden,
+                                          float eps, int variant, hipStream_t stream);
+int rmsnorm_ex(void *out, const void *x, const void *weight, int64_t num_tokens, int64_t hidden,
+               float eps, int variant, hipStream_t stream);
+int rmsnorm_quant_fp8_ex(void *out_fp8, float *scale_out, const void *x, const void *weight,
+                         int64_t num_tokens, int64_t hidden, float eps, int variant,
+                         hipStream_t stream);
+int rmsnorm_quant_fp8_static_ex(void *out_fp8, const void *x, const void *weight,
+                                const float *scale, int64_t num_tokens, int64_t hidden, float eps,
+                                int variant, hipStream_t stream);
+int swiglu_quant_fp8_dynamic_ex(void *out_fp8, float *scale_out, const void *gate_up,
+                                int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -105,20 +105,25 @@ def check_norm(x, residual, weight, eps, out_gpu, res_out_gpu) -> NormReport:
                       max_ulps_vs_nominal=int(ulps.max()) if ulps.size else 0)
 
 
-def check_norm_fp8(x, residual, weight, eps, q_gpu, s_gpu, res_out_gpu) -> NormReport:
-    """Assert fused_add_rmsnorm_quant_fp8 results.
+def check_rmsnorm(x, weight, eps, out_gpu) -> NormReport:
+    """Assert the GPU's rmsnorm (no residual add) results."""
+    nominal, alt_lo, alt_hi = norm_admissible(x, weight, eps)
+    exact = same_bf16(out_gpu, nominal)
+    admissible = exact | same_bf16(out_gpu, alt_lo) | same_bf16(out_gpu, alt_hi)
+    bad = ~admissible
+    assert not bad.any(), "out outside the admissible set at %d positions, first %s: gpu %s oracle %s" % (
+        bad.sum(), np.argwhere(bad)[:5].tolist(), out_gpu[bad][:5], nominal[bad][:5])
+    return NormReport(elements=int(out_gpu.size), not_nominal=int((~exact).sum()))
 
-    Bit-exact is expected; the stated tolerances (scales within 1e-6
-    relative, codes within 1 E4M3 ulp) are applied against admissible values
-    where the norm output itself sits on a knife-edge."""
-    q_o, s_o, res_o, y_o, _ = oracle.fused_add_rmsnorm_quant_fp8(x, residual, weight, eps)
-    bad_res = ~same_bf16(res_out_gpu, res_o)
-    assert not bad_res.any(), "residual_out differs at %d positions" % bad_res.sum()
+
+def _check_dynamic_codes(rows_in, weight, eps, q_gpu, s_gpu, q_o, s_o) -> NormReport:
+    """Per-token E4M3 codes and scales of a norm of rows_in (the rows the
+    norm normalizes), against the oracle's q_o, s_o."""
     rows_s = np.flatnonzero(s_gpu.view(np.uint32) != s_o.view(np.uint32))
     rows_q = np.flatnonzero((q_gpu != q_o).any(axis=1))
     rows = np.union1d(rows_s, rows_q)
     if len(rows):
-        _, lo, hi = norm_admissible(res_o[rows], weight, eps)
+        _, lo, hi = norm_admissible(rows_in[rows], weight, eps)
         ylo, yhi = oracle.bf16_to_f32(lo), oracle.bf16_to_f32(hi)
         amax_lo = np.minimum(np.abs(ylo), np.abs(yhi)).max(axis=1)
         amax_hi = np.maximum(np.abs(ylo), np.abs(yhi)).max(axis=1)
@@ -134,6 +139,59 @@ def check_norm_fp8(x, residual, weight, eps, q_gpu, s_gpu, res_out_gpu) -> NormR
     return NormReport(rows=int(q_gpu.shape[0]), rows_not_nominal=int(len(rows)),
                       codes_not_nominal=int((q_gpu != q_o).sum()),
                       scales_not_nominal=int(len(rows_s)))
+
+
+def check_norm_fp8(x, residual, weight, eps, q_gpu, s_gpu, res_out_gpu) -> NormReport:
+    """Assert fused_add_rmsnorm_quant_fp8 results.
+
+    Bit-exact is expected; the stated tolerances (scales within 1e-6
+    relative, codes within 1 E4M3 ulp) are applied against admissible values
+    where the norm output itself sits on a knife-edge."""
+    q_o, s_o, res_o, y_o, _ = oracle.fused_add_rmsnorm_quant_fp8(x, residual, weight, eps)
+    bad_res = ~same_bf16(res_out_gpu, res_o)
+    assert not bad_res.any(), "residual_out differs at %d positions" % bad_res.sum()
+    return _check_dynamic_codes(res_o, weight, eps, q_gpu, s_gpu, q_o, s_o)
+
+
+def check_rmsnorm_fp8(x, weight, eps, q_gpu, s_gpu) -> NormReport:
+    """Assert rmsnorm_quant_fp8 (no residual add, per-token scale) results."""
+    q_o, s_o, _, _ = oracle.rmsnorm_quant_fp8(x, weight, eps)
+    return _check_dynamic_codes(x, weight, eps, q_gpu, s_gpu, q_o, s_o)
+
+
+def _same_codes(a, b):
+    """Equal E4M3 codes, with every NaN code equal to every NaN code."""
+    nan_a, nan_b = np.isin(a, [0x7F, 0xFF]), np.isin(b, [0x7F, 0xFF])
+    return (a == b) | (nan_a & nan_b)
+
+
+def _check_static_codes(rows_in, weight, eps, scale, q_gpu, q_o) -> NormReport:
+    bad = ~_same_codes(q_gpu, q_o)
+    rows = np.flatnonzero(bad.any(axis=1))
+    if len(rows):
+        _, lo, hi = norm_admissible(rows_in[rows], weight, eps)
+        for k, r in enumerate(rows):
+            cand = [oracle.quant_fp8_static(lo[k], scale), oracle.quant_fp8_static(hi[k], scale)]
+            d = np.minimum(e4m3_ulps(q_gpu[r], cand[0]), e4m3_ulps(q_gpu[r], cand[1]))
+            d[_same_codes(q_gpu[r], q_o[r])] = 0
+            assert d.max() <= 1, "row %d: code off by %d e4m3 ulps" % (r, d.max())
+    return NormReport(rows=int(q_gpu.shape[0]), rows_not_nominal=int(len(rows)),
+                      codes_not_nominal=int(bad.sum()))
+
+
+def check_norm_fp8_static(x, residual, weight, eps, scale, q_gpu, res_out_gpu) -> NormReport:
+    """Assert fused_add_rmsnorm_quant_fp8_static results (codes bit-exact
+    except where the norm output sits on a knife-edge, then within 1 E4M3 ulp
+    of an admissible value)."""
+    q_o, res_o, _, _ = oracle.fused_add_rmsnorm_quant_fp8_static(x, residual, weight, eps, scale)
+    bad_res = ~same_bf16(res_out_gpu, res_o)
+    assert not bad_res.any(), "residual_out differs at %d positions" % bad_res.sum()
+    return _check_static_codes(res_o, weight, eps, scale, q_gpu, q_o)
+
+
+def check_rmsnorm_fp8_static(x, weight, eps, scale, q_gpu) -> NormReport:
+    q_o, _, _ = oracle.rmsnorm_quant_fp8_static(x, weight, eps, scale)
+    return _check_static_codes(x, weight, eps, scale, q_gpu, q_o)
 
 
 # ----------------------------------------------------------------- swiglu
@@ -152,4 +210,16 @@ def check_swiglu_fp8(gate_up, scale, q_gpu):
     assert np.array_equal(nan_o, nan_g), "NaN codes differ at %d positions" % (nan_o != nan_g).sum()
     bad = (q_gpu != q_o) & ~nan_o
     assert not bad.any(), "swiglu_quant_fp8 differs at %d positions, first %s: gpu %s oracle %s" % (
+        bad.sum(), np.argwhere(bad)[:5].tolist(), q_gpu[bad][:5], q_o[bad][:5])
+
+
+def check_swiglu_fp8_dynamic(gate_up, q_gpu, s_gpu):
+    """Per-token E4M3 SwiGLU: the SwiGLU output has no knife-edges (its
+    SiLU is correctly rounded), so scales and codes must be bit-exact."""
+    q_o, s_o, _ = oracle.swiglu_quant_fp8_dynamic(gate_up)
+    bad_s = ~((s_gpu.view(np.uint32) == s_o.view(np.uint32)) | (np.isnan(s_gpu) & np.isnan(s_o)))
+    assert not bad_s.any(), "scales differ in %d rows, first %s: gpu %s oracle %s" % (
+        bad_s.sum(), np.flatnonzero(bad_s)[:5].tolist(), s_gpu[bad_s][:5], s_o[bad_s][:5])
+    bad = ~_same_codes(q_gpu, q_o)
+    assert not bad.any(), "codes differ at %d positions, first %s: gpu %s oracle %s" % (
         bad.sum(), np.argwhere(bad)[:5].tolist(), q_gpu[bad][:5], q_o[bad][:5])

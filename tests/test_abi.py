@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_four_ops():
     fns = declared_functions()
     for name in ["fused_add_rmsnorm", "swiglu", "swiglu_quant_fp8", "fused_add_rmsnorm_quant_fp8",
-                 "aarms_status_string"]:
+                 "aarms_status_string", "rmsnorm", "rmsnorm_quant_fp8", "rmsnorm_quant_fp8_static",
+                 "fused_add_rmsnorm_quant_fp8_static", "swiglu_quant_fp8_dynamic"]:
         assert name in fns
 
 
@@ -152,6 +153,69 @@ def test_norm_variant_checks():
     assert A.variant_name(A.OP_NORM, n) is None
 
 
+# ----------------------------------------------------------------- the other norm forms
+
+def rms(lib, out=P, x=P + BIG, w=P + 2 * BIG, T=4, H=1536, eps=1e-6, variant=-1):
+    return lib.rmsnorm_ex(out, x, w, T, H, eps, variant, None)
+
+
+def rmsq(lib, out=P, scale=P + BIG, x=P + 2 * BIG, w=P + 3 * BIG, T=4, H=1536, eps=1e-6, variant=-1):
+    return lib.rmsnorm_quant_fp8_ex(out, scale, x, w, T, H, eps, variant, None)
+
+
+def rmss(lib, out=P, x=P + BIG, w=P + 2 * BIG, scale=P + 3 * BIG, T=4, H=1536, eps=1e-6, variant=-1):
+    return lib.rmsnorm_quant_fp8_static_ex(out, x, w, scale, T, H, eps, variant, None)
+
+
+def norms(lib, out=P, res_out=P + BIG, x=P + 2 * BIG, res=P + 3 * BIG, w=P + 4 * BIG,
+          scale=P + 5 * BIG, T=4, H=1536, eps=1e-6, variant=-1):
+    return lib.fused_add_rmsnorm_quant_fp8_static_ex(out, res_out, x, res, w, scale, T, H, eps,
+                                                     variant, None)
+
+
+def test_other_norm_forms_errors():
+    lib = A.load()
+    narrow = 0
+    for f in (rms, rmsq, rmss, norms):
+        assert f(lib, T=-1) == SHAPE
+        assert f(lib, H=12) == SHAPE
+        assert f(lib, H=MAX_HIDDEN + 8) == UNSUP
+        assert f(lib, eps=float("nan")) == EPS
+        assert f(lib, out=0) == NULLP
+        assert f(lib, out=P + 8) == MISAL
+        assert f(lib, variant=A.variant_count(A.OP_NORM)) == VARIANT
+        assert f(lib, variant=narrow) == VARIANT                # too narrow, stops before launch
+    assert rms(lib, T=0, out=0, x=0, w=0) == OK
+    assert rmsq(lib, T=0, out=0, scale=0, x=0, w=0) == OK
+    assert rmss(lib, T=0, out=0, x=0, w=0, scale=0) == OK
+    assert norms(lib, T=0, out=0, res_out=0, x=0, res=0, w=0, scale=0) == OK
+    assert rmsq(lib, scale=0) == NULLP
+    assert rmsq(lib, scale=P + BIG + 2) == MISAL
+    assert rmss(lib, scale=0) == NULLP
+    assert rmss(lib, scale=P + 3 * BIG + 1) == MISAL
+    assert norms(lib, scale=0) == NULLP
+    assert norms(lib, res=0) == NULLP
+    assert norms(lib, res_out=P + BIG + 8) == MISAL
+
+
+def test_other_norm_forms_aliasing():
+    lib = A.load()
+    x, w = P + BIG, P + 2 * BIG
+    # rmsnorm: out == x in place is allowed (stopped by the narrow variant)
+    assert rms(lib, out=x, variant=0) == VARIANT
+    assert rms(lib, out=x + 16) == ALIAS
+    assert rms(lib, out=w - 16) == ALIAS
+    # FP8 forms: no in-place output
+    assert rmsq(lib, out=P + 2 * BIG) == ALIAS
+    assert rmss(lib, out=P + BIG) == ALIAS
+    assert rmsq(lib, scale=P + 64) == ALIAS                   # scale_out inside out
+    assert rmss(lib, scale=P + 64) == ALIAS                   # scale inside out
+    # static fused form: residual_out == residual allowed, out == x not
+    assert norms(lib, res_out=P + 3 * BIG, variant=0) == VARIANT
+    assert norms(lib, out=P + 2 * BIG) == ALIAS
+    assert norms(lib, res_out=P + 5 * BIG) == ALIAS           # residual_out over the scale
+
+
 # ----------------------------------------------------------------- swiglu
 
 def sw(lib, out=P, gu=P + BIG, T=4, N=8960):
@@ -181,6 +245,34 @@ def test_swiglu_errors():
     assert swq(lib, T=0, out=0, gu=0, scale=0) == OK
     n = A.variant_count(A.OP_SWIGLU)
     assert lib.swiglu_ex(P, P + BIG, 4, 8960, n, None) == VARIANT
+
+
+def swd(lib, out=P, scale=P + BIG, gu=P + 2 * BIG, T=4, N=8960, variant=-1):
+    return lib.swiglu_quant_fp8_dynamic_ex(out, scale, gu, T, N, variant, None)
+
+
+def test_swiglu_dynamic_errors():
+    lib = A.load()
+    assert swd(lib, T=-1) == SHAPE
+    assert swd(lib, N=12) == SHAPE
+    assert swd(lib, N=65536 + 8) == UNSUP                   # row kept in registers
+    assert swd(lib, T=0, out=0, scale=0, gu=0) == OK
+    for k in ("out", "scale", "gu"):
+        assert swd(lib, **{k: 0}) == NULLP
+    assert swd(lib, out=P + 8) == MISAL
+    assert swd(lib, scale=P + BIG + 2) == MISAL
+    assert swd(lib, out=P + 2 * BIG) == ALIAS
+    assert swd(lib, scale=P + 64) == ALIAS
+    n = A.variant_count(A.OP_SWIGLU_DYNAMIC)
+    assert swd(lib, variant=n) == VARIANT
+    assert swd(lib, variant=0) == VARIANT                   # one wave, one job: 512 wide
+    assert A.pick_variant(A.OP_SWIGLU_DYNAMIC, 16, 65544) == -1
+    for N in (8, 2048, 8960, 28672, 65536):
+        v = A.pick_variant(A.OP_SWIGLU_DYNAMIC, 16, N)
+        name = A.variant_name(A.OP_SWIGLU_DYNAMIC, v)
+        waves = 1 if name.startswith("wave/row") else int(name.split()[0])
+        jobs = int(name.split("x")[-1].split()[0])
+        assert waves * 64 * jobs * 8 >= N
 
 
 def test_swiglu_width_limit():

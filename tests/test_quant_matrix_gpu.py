@@ -1,0 +1,247 @@
+"""GPU parity for the rest of the quantisation matrix: RMSNorm without the
+residual add (bf16, per-token E4M3, per-tensor E4M3), the residual-add norm
+with a per-tensor E4M3 scale, and SwiGLU with a per-token E4M3 scale -- the
+HIP kernels through the C ABI against the CPU oracle, to the same bar as the
+other ops (tests/parity.py)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import activation_add_rmsnorm_amd as A
+import oracle
+from tests import parity as P
+from workloads import configs as W
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+SCALES = [0.05, 0.0125, 1.0, 2.0 ** -126, 2.0 ** 120, 0.0]
+
+
+def announce(*what):
+    print("[gpu]", *what, flush=True)
+
+
+def bf16(b):
+    return P.to_gpu_bf16(b, DEV)
+
+
+def bits(t):
+    return P.from_gpu_bits(t)
+
+
+def scale_t(s):
+    return torch.tensor([s], dtype=torch.float32, device=DEV)
+
+
+def norm_case(T, H, seed=0, outliers=0.0, std=1.0):
+    x = gen.normal_bf16((T, H), seed, 1, std=std, outlier_frac=outliers)
+    r = gen.normal_bf16((T, H), seed, 2, outlier_frac=outliers)
+    w = gen.normal_bf16((H,), seed, 3, mean=1.0, std=0.1)
+    return x, r, w
+
+
+def variants_for(op, width):
+    out = []
+    for v in range(A.variant_count(op)):
+        name = A.variant_name(op, v)
+        waves = 1 if name.startswith("wave/row") else int(name.split()[0])
+        per_lane = int(name.split("x")[-1].split()[0])
+        if waves * 64 * per_lane * 8 >= width:
+            out.append(v)
+    return out
+
+
+def run_rms(x, w, eps, variant=-1):
+    announce("rmsnorm", x.shape, "eps", eps, "variant", variant)
+    out = A.rmsnorm(bf16(x), bf16(w), eps, variant=variant)
+    torch.cuda.synchronize()
+    return bits(out)
+
+
+def run_rms_fp8(x, w, eps, variant=-1):
+    announce("rmsnorm_quant_fp8", x.shape, "eps", eps, "variant", variant)
+    q, s = A.rmsnorm_quant_fp8(bf16(x), bf16(w), eps, variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s)
+
+
+def run_rms_static(x, w, eps, scale, variant=-1):
+    announce("rmsnorm_quant_fp8_static", x.shape, "eps", eps, "scale", scale, "variant", variant)
+    q = A.rmsnorm_quant_fp8_static(bf16(x), bf16(w), scale_t(scale), eps, variant=variant)
+    torch.cuda.synchronize()
+    return bits(q)
+
+
+def run_fused_static(x, r, w, eps, scale, variant=-1):
+    announce("fused_add_rmsnorm_quant_fp8_static", x.shape, "eps", eps, "scale", scale, "variant", variant)
+    q, ro = A.fused_add_rmsnorm_quant_fp8_static(bf16(x), bf16(r), bf16(w), scale_t(scale), eps,
+                                                 variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(ro)
+
+
+def run_swiglu_dyn(gu, variant=-1):
+    announce("swiglu_quant_fp8_dynamic", gu.shape, "variant", variant)
+    q, s = A.swiglu_quant_fp8_dynamic(bf16(gu), variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s)
+
+
+# ------------------------------------------------------------------ rmsnorm
+
+@pytest.mark.parametrize("T,H", [(1, 8), (3, 24), (16, 1536), (257, 1536), (4, 16384), (3, 16392),
+                                 (1, 65536), (1023, 1536), (1024, 1536)])
+def test_rmsnorm_shapes_default_variant(T, H):
+    x, _, w = norm_case(T, H, seed=T * 7 + H)
+    announce(P.check_rmsnorm(x, w, 1e-6, run_rms(x, w, 1e-6)))
+
+
+@pytest.mark.parametrize("H", [1536, 16384])
+def test_rmsnorm_forms_every_variant(H):
+    T = 37
+    x, _, w = norm_case(T, H, seed=H + 1, outliers=0.001)
+    for v in variants_for(A.OP_NORM, H):
+        P.check_rmsnorm(x, w, 1e-5, run_rms(x, w, 1e-5, v))
+        q, s = run_rms_fp8(x, w, 1e-5, v)
+        P.check_rmsnorm_fp8(x, w, 1e-5, q, s)
+        P.check_rmsnorm_fp8_static(x, w, 1e-5, 0.0125, run_rms_static(x, w, 1e-5, 0.0125, v))
+
+
+def test_rmsnorm_closed_forms_and_in_place():
+    H = 1536
+    w = gen.normal_bf16((H,), 0, 3, mean=1.0, std=0.1)
+    x = np.full((4, H), oracle.bf16_from_f64(0.75), np.uint16)
+    x[1] ^= 0x8000
+    x[2] = 0
+    x[3] = gen.normal_bf16((H,), 1, 1)
+    x[3, :5] = 0x8000                                  # -0 stays -0: out = w * -0
+    out = run_rms(x, w, 1e-6)
+    assert np.array_equal(out[0], w) and np.array_equal(out[1], w ^ 0x8000)
+    assert np.all(oracle.bf16_to_f32(out[2]) == 0)
+    assert np.all(out[3, :5] == np.where(oracle.bf16_to_f32(w[:5]) > 0, 0x8000, 0))
+    P.check_rmsnorm(x, w, 1e-6, out)
+    # in place
+    xr, _, _ = norm_case(64, H, seed=3)
+    xt = bf16(xr)
+    announce("rmsnorm in place", xr.shape)
+    A.rmsnorm(xt, bf16(w), 1e-6, out=xt)
+    torch.cuda.synchronize()
+    P.check_rmsnorm(xr, w, 1e-6, bits(xt))
+
+
+def test_rmsnorm_prefill4096_full():
+    wl = W.NORM_PREFILL4096
+    d = W.norm_inputs(wl)
+    announce(P.check_rmsnorm(d["x"], d["weight"], wl.eps, run_rms(d["x"], d["weight"], wl.eps)))
+
+
+def test_rmsnorm_fp8_dynamic_edge_rows():
+    H = 16384
+    x, _, w = norm_case(6, H, seed=21)
+    x[0] = 0                                           # all-zero row: s = 0, q = 0
+    x[1] = oracle.bf16_from_f64(0.5)                   # constant row
+    x[2] = oracle.bf16_from_f64(1e-3)
+    x[2, 7] = oracle.bf16_from_f64(300.0)              # one outlier
+    q, s = run_rms_fp8(x, w, 1e-5)
+    P.check_rmsnorm_fp8(x, w, 1e-5, q, s)
+    assert s[0] == 0 and np.all((q[0] & 0x7F) == 0)
+    assert q[2, 7] in (0x7E, 0xFE)
+    dec = oracle.e4m3_table()
+    assert np.all(np.abs(dec[q[1:]]).max(axis=1) == 448.0)
+
+
+# ------------------------------------------------------------------ static norm + fp8
+
+@pytest.mark.parametrize("scale", SCALES)
+def test_static_norm_fp8_scales(scale):
+    """Per-tensor scales on both sides of the fast quotient's range, one that
+    saturates (|y| reaches about 4, 448 * 0.0125 = 5.6 is passed by the
+    outliers), and zero (treated as one)."""
+    x, r, w = norm_case(64, 4096, seed=22, outliers=0.002)
+    q, ro = run_fused_static(x, r, w, 1e-5, scale)
+    announce(P.check_norm_fp8_static(x, r, w, 1e-5, scale, q, ro))
+    q2 = run_rms_static(x, w, 1e-5, scale)
+    announce(P.check_rmsnorm_fp8_static(x, w, 1e-5, scale, q2))
+
+
+def test_static_norm_fp8_every_variant():
+    T, H = 37, 16384
+    x, r, w = norm_case(T, H, seed=23, outliers=0.001)
+    for v in variants_for(A.OP_NORM, H):
+        q, ro = run_fused_static(x, r, w, 1e-5, 0.02, v)
+        P.check_norm_fp8_static(x, r, w, 1e-5, 0.02, q, ro)
+
+
+def test_static_norm_fp8_in_place_residual():
+    x, r, w = norm_case(32, 2048, seed=24)
+    rt = bf16(r)
+    announce("fused_add_rmsnorm_quant_fp8_static residual in place", x.shape)
+    q, ro = A.fused_add_rmsnorm_quant_fp8_static(bf16(x), rt, bf16(w), scale_t(0.05), 1e-5,
+                                                 residual_out=rt)
+    torch.cuda.synchronize()
+    P.check_norm_fp8_static(x, r, w, 1e-5, 0.05, bits(q), bits(rt))
+
+
+def test_static_norm_fp8_llama405b_full():
+    wl = W.NORM_FP8_LLAMA405B
+    d = W.norm_inputs(wl)
+    q, ro = run_fused_static(d["x"], d["residual"], d["weight"], wl.eps, 0.02)
+    announce(P.check_norm_fp8_static(d["x"], d["residual"], d["weight"], wl.eps, 0.02, q, ro))
+
+
+# ------------------------------------------------------------------ per-token swiglu + fp8
+
+@pytest.mark.parametrize("T,N", [(1, 8), (3, 24), (5, 1032), (64, 8960), (7, 28672), (2, 65536)])
+def test_swiglu_dynamic_shapes_every_variant(T, N):
+    gu = gen.normal_bf16((T, 2 * N), T + 3 * N, 4, std=2.0)
+    for v in [-1] + variants_for(A.OP_SWIGLU_DYNAMIC, N):
+        q, s = run_swiglu_dyn(gu, v)
+        P.check_swiglu_fp8_dynamic(gu, q, s)
+
+
+def test_swiglu_dynamic_edge_rows():
+    T, N = 8, 8960
+    gu = gen.normal_bf16((T, 2 * N), 31, 4, std=2.0)
+    gu[0, :N] = 0                                      # gate 0: y = +-0, s = 0, codes zero
+    gu[1, :N] = oracle.bf16_from_f64(0.01)             # small row with one large output
+    gu[1, 100] = oracle.bf16_from_f64(12.0)
+    gu[1, N + 100] = oracle.bf16_from_f64(5.0)
+    gu[2, 17] = 0x7FC0                                 # a NaN gate: its code is NaN, amax ignores it
+    gu[3, N + 5] = 0x7F80                              # an infinite up: s = inf
+    gu[4, :N] = gen.normal_bf16((N,), 32, 1, std=30.0)  # gates past -16 take the exact SiLU
+    q, s = run_swiglu_dyn(gu)
+    P.check_swiglu_fp8_dynamic(gu, q, s)
+    assert s[0] == 0 and np.all((q[0] & 0x7F) == 0)
+    assert q[1, 100] == 0x7E
+    assert q[2, 17] in (0x7F, 0xFF)
+    dec = oracle.e4m3_table()
+    assert np.abs(dec[q[5]]).max() == 448.0
+
+
+def test_swiglu_dynamic_every_y():
+    """gate = 8 (a = 8 exactly) and up = bf16 patterns of one binade range per
+    row, so y = 8u sweeps every significand through the per-token scale."""
+    N = 65536
+    u = np.arange(N, dtype=np.uint16)
+    finite = (u & 0x7F80) != 0x7F80
+    rows = []
+    for hi_exp in (0x3F80, 0x4700, 0x1000):
+        uu = np.where(finite & ((u & 0x7F80) <= hi_exp), u, u & 0x807F)
+        rows.append(np.concatenate([np.full(N, oracle.bf16_from_f64(8.0), np.uint16), uu]))
+    gu = np.stack(rows)
+    q, s = run_swiglu_dyn(gu)
+    P.check_swiglu_fp8_dynamic(gu, q, s)
+
+
+def test_swiglu_dynamic_llama70b_full():
+    wl = W.SWIGLU_FP8_LLAMA70B
+    gu = W.swiglu_inputs(wl)["gate_up"]
+    q, s = run_swiglu_dyn(gu)
+    P.check_swiglu_fp8_dynamic(gu, q, s)
+    dec = oracle.e4m3_table()
+    assert np.all(np.abs(dec[q]).max(axis=1) == 448.0)
