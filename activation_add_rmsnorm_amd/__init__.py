@@ -24,7 +24,7 @@ __all__ = [
     "rmsnorm", "rmsnorm_quant_fp8", "rmsnorm_quant_fp8_static",
     "swiglu", "swiglu_quant_fp8", "swiglu_quant_fp8_dynamic",
     "variant_count", "variant_name", "pick_variant",
-    "OP_NORM", "OP_SWIGLU", "OP_SWIGLU_DYNAMIC",
+    "OP_NORM", "OP_SWIGLU", "OP_SWIGLU_DYNAMIC", "OP_RMSNORM",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +35,7 @@ _LIB = None
 OP_NORM = 0
 OP_SWIGLU = 1
 OP_SWIGLU_DYNAMIC = 2
+OP_RMSNORM = 3
 FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
 
 
@@ -70,7 +71,12 @@ def load():
             "swiglu_ex": [vp, vp, i64, i64, i32, vp],
             "swiglu_quant_fp8": [vp, vp, vp, i64, i64, vp],
             "swiglu_quant_fp8_ex": [vp, vp, vp, i64, i64, i32, vp],
+            "fused_add_rmsnorm_quant_fp8_static": [vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
             "fused_add_rmsnorm_quant_fp8_static_ex": [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "rmsnorm": [vp, vp, vp, i64, i64, f32, vp],
+            "rmsnorm_quant_fp8": [vp, vp, vp, vp, i64, i64, f32, vp],
+            "rmsnorm_quant_fp8_static": [vp, vp, vp, vp, i64, i64, f32, vp],
+            "swiglu_quant_fp8_dynamic": [vp, vp, vp, i64, i64, vp],
             "rmsnorm_ex": [vp, vp, vp, i64, i64, f32, i32, vp],
             "rmsnorm_quant_fp8_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],
             "rmsnorm_quant_fp8_static_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],

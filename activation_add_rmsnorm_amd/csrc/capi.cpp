@@ -99,19 +99,21 @@ static int norm_fit(int waves, int64_t hidden, int max_vecs)
 // wins (measured on MI355X, 256 CUs, rows of 1,536).
 constexpr int64_t kNarrowMultiWaveTokens = 1024;
 
-int pick_norm(int64_t tokens, int64_t hidden, bool quant)
+int pick_norm(int64_t tokens, int64_t hidden, bool quant, bool residual)
 {
     (void)quant;
     if (hidden <= 0 || hidden > AARMS_MAX_HIDDEN) return -1;
     // Narrow rows: one wave per row with as few vectors per lane as fit (four
     // waves per row for small batches).  Wide rows: the fewest waves per row
     // that fit with at most 2 vectors per lane (the row's loads spread over
-    // many short slices, few registers per wave), else 4, else 8.
+    // many short slices, few registers per wave), else 4, else 8.  Without
+    // the residual a slice holds half the data, and 4 vectors per lane (half
+    // the waves per row, twice the rows in flight) come first.
     if (hidden <= 4096) {
         const int i = norm_fit(tokens < kNarrowMultiWaveTokens ? 4 : 1, hidden, 8);
         if (i >= 0) return i;
     }
-    for (int max_vecs : {2, 4, 8})
+    for (int max_vecs : {residual ? 2 : 4, 4, 8})
         for (int w : {2, 4, 8, 16}) {
             const int i = norm_fit(w, hidden, max_vecs);
             if (i >= 0) return i;
@@ -215,7 +217,7 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
         outs[n_out++] = {span(scale_out, 4 * (uint64_t)tokens), scale_out};
     }
     if ((st = check_outputs(outs, partner, n_out, ins, n_in))) return st;
-    if (variant == -1) variant = pick_norm(tokens, hidden, epi != NORM_EPI_BF16);
+    if (variant == -1) variant = pick_norm(tokens, hidden, epi != NORM_EPI_BF16, res);
     const NormVariant *v = norm_variant(variant);
     if (!v || norm_capacity(v) < hidden) return AARMS_ERR_BAD_VARIANT;
     NormParams p;
@@ -442,14 +444,14 @@ const char *aarms_status_string(int status)
 
 int aarms_variant_count(int op)
 {
-    return op == 0 ? norm_variant_count()
+    return (op == 0 || op == 3) ? norm_variant_count()
          : op == 1 ? swiglu_variant_count()
          : op == 2 ? swiglu_row_variant_count() : 0;
 }
 
 const char *aarms_variant_name(int op, int variant)
 {
-    if (op == 0) {
+    if (op == 0 || op == 3) {
         const NormVariant *v = norm_variant(variant);
         return v ? v->name : nullptr;
     }
@@ -466,7 +468,7 @@ const char *aarms_variant_name(int op, int variant)
 
 int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant)
 {
-    if (op == 0) return pick_norm(num_tokens, width, quant != 0);
+    if (op == 0 || op == 3) return pick_norm(num_tokens, width, quant != 0, op == 0);
     if (op == 1) return (width > 0 && width % 8 == 0) ? pick_swiglu(num_tokens, width, quant != 0) : -1;
     if (op == 2) return (width > 0 && width % 8 == 0) ? pick_swiglu_rowq(num_tokens, width) : -1;
     return -1;

@@ -184,6 +184,39 @@ __device__ __forceinline__ float wave_max(float v)
     return swap_max_f32<32>(v);
 }
 
+// Cross-wave combine of a block's per-wave partials in LDS (N <= 16 of them):
+// lane i < N of every wave reads partial i, a 16-lane butterfly (same
+// involutions as above) combines them, and lane 0's value is broadcast.
+// Every wave runs the same steps on the same data, so every lane of the
+// block ends with the same bits; registers hold one partial, not N.
+template <int N>
+__device__ __forceinline__ double block_sum(const double *part, int wave_lane)
+{
+    static_assert(N >= 1 && N <= 16, "up to 16 waves");
+    double v = (wave_lane < N) ? part[wave_lane] : 0.0;
+    v += dpp_f64<DPP_XOR1>(v);
+    v += dpp_f64<DPP_XOR2>(v);
+    v += dpp_f64<DPP_HALF_MIRROR>(v);
+    v += dpp_f64<DPP_MIRROR>(v);
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 0);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 0);
+    return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+// The same for maxima of non-negative values (absent partials read as 0).
+template <int N>
+__device__ __forceinline__ float block_max(const float *part, int wave_lane)
+{
+    static_assert(N >= 1 && N <= 16, "up to 16 waves");
+    float v = (wave_lane < N) ? part[wave_lane] : 0.0f;
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_MIRROR>(__float_as_uint(v))));
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+}
+
 // ---------------------------------------------------------------- SiLU
 //
 // bf16(silu(g)) must be the correctly rounded value.  The fast form below,
@@ -236,8 +269,8 @@ __device__ __forceinline__ float step_f32(float f, int dir)
     return __uint_as_float(up_in_magnitude ? b + 1u : b - 1u);
 }
 
-// Correctly rounded bf16(silu(g)), returned as a binary32 value on the bf16
-// grid (so that a later round-to-nearest-even leaves it unchanged).
+// Correctly rounded bf16(silu(g)), returned as a binary32 value whose
+// round-to-nearest-even to bf16 is that result.
 //  - |g| < 2^-24: silu(g) = g/2 + g^2/4 - ...; the binary64 value is g/2 and
 //    the positive g^2/4 decides a tie (odd subnormal results).
 //  - otherwise silu is evaluated in binary64 (error a few units of 2^-53).

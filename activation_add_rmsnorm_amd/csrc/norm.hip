@@ -159,9 +159,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
     if constexpr (WPR > 1) {
         if ((lane & 63) == 0) psum[lane >> 6] = acc;
         __syncthreads();
-        acc = psum[0];
-#pragma unroll
-        for (int i = 1; i < WPR; ++i) acc += psum[i];
+        acc = block_sum<WPR>(psum, lane & 63);
     }
 
     // ---- mean (rounded once to binary32), + eps, reciprocal square root
@@ -210,9 +208,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         if constexpr (WPR > 1) {
             if ((lane & 63) == 0) pmax[lane >> 6] = amax;
             __syncthreads();
-            amax = pmax[0];
-#pragma unroll
-            for (int i = 1; i < WPR; ++i) amax = fmaxf(amax, pmax[i]);
+            amax = block_max<WPR>(pmax, lane & 63);
         }
         // ---- per-token scale, then q = e4m3(clamp(y / s))
         const float s = amax / 448.0f;
@@ -251,7 +247,10 @@ norm_kernel(NormParams p)
     // all loads of the row slice in flight before any use
     u32x4 xv[VPT], rv[VPT], wv[VPT];
     load_row<WPR, VPT, RES>(p, row, lane, nvec, xv, rv);
-    constexpr bool W_LATE = WPR > 1;
+    // wide rows with the residual load the weight after the first pass (its
+    // registers are not live during the row loads); without the residual
+    // there are registers to spare and the weight is loaded with the row
+    constexpr bool W_LATE = WPR > 1 && RES;
     if constexpr (!W_LATE) load_weight<WPR, VPT>(p, lane, nvec, wv);
     finish_row<WPR, VPT, EPI, RES, W_LATE>(p, row, lane, nvec, xv, rv, wv, psum, pmax);
 }

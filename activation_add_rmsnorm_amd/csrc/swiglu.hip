@@ -44,59 +44,44 @@ struct Words<2> {
 };
 
 // 2W outputs of one job: a = bf16(silu(g)), y = bf16(a * u).  Returns the
-// bf16 results as W packed words.
+// bf16 results as W packed words.  Each word of the gate is turned into its
+// word of a at once (two SiLUs, one pack), so only the packed words stay
+// live; a lane with a flagged element redoes its words in the rare branch.
 template <int W>
 __device__ __forceinline__ typename Words<W>::T swiglu_job(typename Words<W>::T gv, typename Words<W>::T uv)
 {
-    constexpr int E = 2 * W;
-    uint32_t gb[E];
-    float g[E], s[E];
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-        gb[2 * e] = gv[e] << 16;
-        gb[2 * e + 1] = gv[e] & 0xFFFF0000u;
-        g[2 * e] = __uint_as_float(gb[2 * e]);
-        g[2 * e + 1] = __uint_as_float(gb[2 * e + 1]);
-    }
+    uint32_t a[W];
     // running extrema: smallest knife-edge key of the results, largest gate
     // bit pattern (above SILU_FAST_MIN_BITS means g < -16)
     uint32_t kmin = 0xFFFFFFFFu, gmax = 0u;
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-        s[j] = silu_fast(g[j]);
-        kmin = min(kmin, silu_edge_key(s[j]));
-        gmax = max(gmax, gb[j]);
+    for (int e = 0; e < W; ++e) {
+        const uint32_t glo = gv[e] << 16, ghi = gv[e] & 0xFFFF0000u;
+        const float s0 = silu_fast(__uint_as_float(glo)), s1 = silu_fast(__uint_as_float(ghi));
+        kmin = min(kmin, min(silu_edge_key(s0), silu_edge_key(s1)));
+        gmax = max(gmax, max(glo, ghi));
+        a[e] = pack_bf16(s0, s1);
     }
     if (kmin <= SILU_EDGE_KEY_MAX || gmax > SILU_FAST_MIN_BITS) {
-        // rare: recompute this lane's flagged elements exactly, one at a
-        // time.  The empty asm makes the flag bookkeeping depend on values
-        // produced inside this branch, so it is not hoisted onto the hot path.
-        uint32_t redo = 0;
+        // rare: recompute this lane's words, the flagged elements exactly.
+        // The empty asm hides the gate word's earlier uses, so the fast values
+        // are recomputed here instead of being kept live on the hot path.
 #pragma unroll
-        for (int j = 0; j < E; ++j) {
-            float sj = s[j];
-            uint32_t gbj = gb[j];
-            asm volatile("" : "+v"(sj), "+v"(gbj));
-            redo |= (uint32_t)((silu_edge_key(sj) <= SILU_EDGE_KEY_MAX) |
-                               (gbj > SILU_FAST_MIN_BITS)) << j;
-        }
-        while (redo) {
-            const int j = __builtin_ctz(redo);
-            redo &= redo - 1u;
-            float gj = g[0];
-#pragma unroll
-            for (int t = 1; t < E; ++t) gj = (j == t) ? g[t] : gj;
-            const float r = silu_exact(gj);
-#pragma unroll
-            for (int t = 0; t < E; ++t) s[t] = (j == t) ? r : s[t];
+        for (int e = 0; e < W; ++e) {
+            uint32_t w = gv[e];
+            asm volatile("" : "+v"(w));
+            const uint32_t glo = w << 16, ghi = w & 0xFFFF0000u;
+            float s0 = silu_fast(__uint_as_float(glo)), s1 = silu_fast(__uint_as_float(ghi));
+            if (silu_edge_key(s0) <= SILU_EDGE_KEY_MAX || glo > SILU_FAST_MIN_BITS)
+                s0 = silu_exact(__uint_as_float(glo));
+            if (silu_edge_key(s1) <= SILU_EDGE_KEY_MAX || ghi > SILU_FAST_MIN_BITS)
+                s1 = silu_exact(__uint_as_float(ghi));
+            a[e] = pack_bf16(s0, s1);
         }
     }
     typename Words<W>::T y;
 #pragma unroll
-    for (int e = 0; e < W; ++e) {
-        const uint32_t a = pack_bf16(s[2 * e], s[2 * e + 1]);
-        y[e] = pack_bf16(bf_lo(a) * bf_lo(uv[e]), bf_hi(a) * bf_hi(uv[e]));
-    }
+    for (int e = 0; e < W; ++e) y[e] = pack_bf16(bf_lo(a[e]) * bf_lo(uv[e]), bf_hi(a[e]) * bf_hi(uv[e]));
     return y;
 }
 
@@ -223,9 +208,7 @@ __global__ void __launch_bounds__(WPR == 1 ? 256 : WPR * 64) swiglu_rowq_kernel(
     if constexpr (WPR > 1) {
         if ((lane & 63) == 0) pmax[lane >> 6] = amax;
         __syncthreads();
-        amax = pmax[0];
-#pragma unroll
-        for (int i = 1; i < WPR; ++i) amax = fmaxf(amax, pmax[i]);
+        amax = block_max<WPR>(pmax, lane & 63);
     }
     const float s = amax / 448.0f;
     if (lane == 0) p.scale_out[row] = s;

@@ -18,9 +18,12 @@ kernel's time measured against it.
 
 The same run also measures, as supplementary figures, the static-FP8 SwiGLU
 on Llama-70B's [8192, 57344] gate_up, the dynamic-FP8 norm on Llama-405B's
-[2048, 16384] rows, the 16-token norm, and the 28-layer decode chain under a
-HIP graph; and it times the CPU oracle on the host's cores on the headline
-workload (a baseline, not a target).
+[2048, 16384] rows, the 16-token norm, the 28-layer decode chain under a
+HIP graph, and the rest of the quantisation matrix (rmsnorm without the
+residual add, the static-scale FP8 norm, the per-token FP8 norm without the
+residual, the per-token FP8 SwiGLU) at the same shapes; and it times the CPU
+oracle on the host's cores on the headline workload (a baseline, not a
+target).
 
 Prints exactly one JSON line.
 """
@@ -407,6 +410,96 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
 
     # decode chain under a HIP graph, per token count
     out["qwen1.5b_decode_28layers_graph"] = decode_graph(torch, np, A, W, dev, to_dev, timer)
+
+    # the rest of the quantisation matrix, at the same shapes
+    out.update(quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream))
+    return out
+
+
+def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
+    """rmsnorm (no residual add) at the Qwen prefill shape; the static-scale
+    and the no-residual per-token FP8 norms at the Llama-405B shape; the
+    per-token FP8 SwiGLU at the Llama-70B shape.  Each beside its streaming
+    ceiling, on rotated buffer sets."""
+    out = {}
+
+    def measure(key, call, ceil, nbytes, extra=None):
+        timer.warm(call)
+        ms = timer.region(call, reps)
+        timer.warm(ceil)
+        ms_c = timer.region(ceil, reps)
+        e = {"bytes": nbytes, "avg_launch_us": round(ms * 1e3, 2),
+             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+             "pct_of_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+             **ceiling_entry(ms * 1e3, ms_c * 1e3, nbytes)}
+        e.update(extra or {})
+        out[key] = e
+
+    def check(st, what):
+        if st:
+            raise A.AarmsError(st, what)
+
+    # rmsnorm bf16 [4096, 1536]
+    wl = W.NORM_PREFILL4096
+    T, H = wl.tokens, wl.hidden
+    d = W.norm_inputs(wl)
+    x0, w0 = to_dev(d["x"]), to_dev(d["weight"])
+    nb = T * H * 2 * 2 + H * 2
+    ns = rotation_sets(nb)
+    sets = [(x0.clone(), torch.empty_like(x0)) for _ in range(ns)]
+    half = T * H                                      # bytes in half of a bf16 [T, H] tensor
+    measure("qwen1.5b_rmsnorm_4096x1536",
+            lambda i: check(lib.rmsnorm(sets[i % ns][1].data_ptr(), sets[i % ns][0].data_ptr(),
+                                        w0.data_ptr(), T, H, wl.eps, sp), "rmsnorm"),
+            lambda i: stream(sets[i % ns][1].data_ptr(), 16, sets[i % ns][1].data_ptr() + half, 16,
+                             sets[i % ns][0].data_ptr(), sets[i % ns][0].data_ptr() + half, T * H // 16),
+            nb, {"buffer_sets_rotated": ns})
+    del sets
+
+    # static-scale FP8 norms and the per-token FP8 norm without the residual, [2048, 16384]
+    wl = W.NORM_FP8_LLAMA405B
+    T, H = wl.tokens, wl.hidden
+    d = W.norm_inputs(wl)
+    x0, r0, w0 = to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["weight"])
+    scale = torch.tensor([0.02], dtype=torch.float32, device=dev)
+    nb = T * H * 7 + H * 2 + 4
+    ns = rotation_sets(nb)
+    sets = [dict(x=x0.clone(), r=r0.clone(), q=torch.empty((T, H), dtype=torch.uint8, device=dev),
+                 ro=torch.empty_like(r0), s=torch.empty((T,), dtype=torch.float32, device=dev))
+            for _ in range(ns)]
+    P = lambda i, k: sets[i % ns][k].data_ptr()
+    measure("llama405b_norm_fp8_static_2048x16384",
+            lambda i: check(lib.fused_add_rmsnorm_quant_fp8_static(
+                P(i, "q"), P(i, "ro"), P(i, "x"), P(i, "r"), w0.data_ptr(), scale.data_ptr(),
+                T, H, wl.eps, sp), "fused_add_rmsnorm_quant_fp8_static"),
+            lambda i: stream(P(i, "ro"), 16, P(i, "q"), 8, P(i, "x"), P(i, "r"), T * H // 8),
+            nb, {"scale": 0.02, "buffer_sets_rotated": ns})
+    nb = T * H * 3 + H * 2 + T * 4
+    measure("llama405b_rmsnorm_fp8_2048x16384",
+            lambda i: check(lib.rmsnorm_quant_fp8(P(i, "q"), P(i, "s"), P(i, "x"), w0.data_ptr(),
+                                                  T, H, wl.eps, sp), "rmsnorm_quant_fp8"),
+            lambda i: stream(P(i, "q"), 16, None, 0, P(i, "x"), P(i, "x") + T * H, T * H // 16),
+            nb, {"buffer_sets_rotated": ns})
+    del sets, x0, r0
+
+    # per-token FP8 SwiGLU, [8192, 57344] -> e4m3 [8192, 28672]
+    wl = W.SWIGLU_FP8_LLAMA70B
+    T, N = wl.tokens, wl.inter
+    g = torch.Generator(device=dev).manual_seed(0)
+    gu = (torch.randn((T, 2 * N), generator=g, device=dev, dtype=torch.float32) * wl.gate_up_std).to(torch.bfloat16)
+    nb = T * 2 * N * 2 + T * N + T * 4
+    ns = rotation_sets(nb)
+    sets = [(gu if i == 0 else gu.clone(), torch.empty((T, N), dtype=torch.uint8, device=dev),
+             torch.empty((T,), dtype=torch.float32, device=dev)) for i in range(ns)]
+    measure("llama70b_swiglu_fp8_dynamic_8192x57344",
+            lambda i: check(lib.swiglu_quant_fp8_dynamic(sets[i % ns][1].data_ptr(), sets[i % ns][2].data_ptr(),
+                                                         sets[i % ns][0].data_ptr(), T, N, sp),
+                            "swiglu_quant_fp8_dynamic"),
+            lambda i: stream(sets[i % ns][1].data_ptr(), 8, None, 0, sets[i % ns][0].data_ptr(),
+                             sets[i % ns][0].data_ptr() + T * N * 2, T * N // 8),
+            nb, {"inputs": "torch.randn on device, seed 0, std 2", "buffer_sets_rotated": ns})
+    del sets, gu
+    torch.cuda.empty_cache()
     return out
 
 

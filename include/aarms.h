@@ -212,9 +212,10 @@ const char *aarms_status_string(int status);
  * from (num_tokens, width, output format); the *_ex forms take it
  * explicitly.  A variant id is an index into the op's table;
  * aarms_variant_name() describes it (static storage) and returns NULL past
- * the end.  ops: 0 = every norm entry point (quant != 0 for an E4M3 form),
- * 1 = swiglu and swiglu_quant_fp8 (quant != 0 selects the FP8 form),
- * 2 = swiglu_quant_fp8_dynamic.
+ * the end.  ops: 0 = the norms with the residual add (fused_add_rmsnorm*),
+ * 3 = the norms without it (rmsnorm*), both on one variant table (quant != 0
+ * for an E4M3 form); 1 = swiglu and swiglu_quant_fp8 (quant != 0 selects
+ * the FP8 form); 2 = swiglu_quant_fp8_dynamic.
  * aarms_pick_variant() returns the id the plain entry point would use, or -1
  * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
  */

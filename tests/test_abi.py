@@ -308,3 +308,11 @@ def test_ceiling_library_rejects_bad_arguments():
     assert f(P, 16, None, 8, P, P, 8, None) == -1                                     # out1 missing
     assert f(P, 16, None, 0, P + 8, P, 8, None) == -1                                 # misaligned
     assert f(P, 16, None, 0, P, P, (2**31) * 256, None) == -1                         # grid too large
+
+
+def test_binding_types_every_declared_function():
+    # ctypes converts a Python float only through a declared argument type:
+    # every function of the header must have one in the binding
+    lib = A.load()
+    missing = [n for n in declared_functions() if getattr(lib, n).argtypes is None]
+    assert not missing, missing
