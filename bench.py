@@ -548,21 +548,40 @@ def decode_graph(torch, np, A, W, dev, to_dev, timer):
 
 def cpu_baseline(np, W, nd, gd, step_bytes, seconds):
     """The oracle as it stands, on the headline workload, repeated for a
-    bounded time on the host's cores."""
+    bounded time on all of the host's cores, then on one core over a row
+    sample of the same workload."""
     import oracle
     wl = W.NORM_PREFILL4096
     oracle.fused_add_rmsnorm(nd["x"][:8], nd["residual"][:8], nd["weight"], wl.eps)  # warm
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.fused_add_rmsnorm(nd["x"], nd["residual"], nd["weight"], wl.eps)
-        oracle.swiglu(gd["gate_up"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or el > 30:
-            break
-    return {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": "%d full passes of the headline workload (norm [4096,1536] + "
-                                        "swiglu [4096,17920]) in %.1f s" % (reps, el)}
+    cores = oracle.num_threads()
+
+    def timed(rows, budget):
+        x, r, gu = nd["x"][:rows], nd["residual"][:rows], gd["gate_up"][:rows]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.fused_add_rmsnorm(x, r, nd["weight"], wl.eps)
+            oracle.swiglu(gu)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or el > 3 * budget:
+                return reps, el
+
+    T = nd["x"].shape[0]
+    reps, el = timed(T, seconds)
+    out = {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": cores,
+           "kind": "oracle", "sample": "%d full passes of the headline workload (norm [4096,1536] + "
+                                       "swiglu [4096,17920]) in %.1f s" % (reps, el)}
+    # one core, on the first 256 rows of the same tensors (the bytes scale with rows)
+    rows = 256
+    oracle.set_threads(1)
+    try:
+        reps1, el1 = timed(rows, max(1.0, seconds / 5))
+    finally:
+        oracle.set_threads(cores)
+    out["single_core"] = {"value": round(step_bytes * rows / T * reps1 / el1 / 1e9, 3), "unit": "GB/s",
+                          "cores": 1, "sample": "%d passes over the first %d rows of the headline workload "
+                                                "in %.1f s" % (reps1, rows, el1)}
+    return out
 
 
 if __name__ == "__main__":

@@ -70,6 +70,7 @@ def _lib():
                 "aarms_oracle_swiglu_quant_fp8": (None, [u16p, i64, i64, f32, u8p]),
                 "aarms_oracle_swiglu_quant_fp8_per_row": (None, [u16p, i64, i64, u16p, u8p, f32p]),
                 "aarms_oracle_num_threads": (C.c_int, []),
+                "aarms_oracle_set_threads": (None, [C.c_int]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(lib, name)
@@ -285,6 +286,11 @@ def swiglu_quant_fp8_dynamic(gate_up):
     s = np.empty(T, np.float32)
     _lib().aarms_oracle_swiglu_quant_fp8_per_row(gu, T, W // 2, y, q, s)
     return q, s, y
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's OpenMP loops in this process."""
+    _lib().aarms_oracle_set_threads(int(n))
 
 
 def num_threads() -> int:

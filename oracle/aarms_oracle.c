@@ -327,6 +327,16 @@ void aarms_oracle_swiglu_quant_fp8_per_row(const uint16_t *gu, int64_t T, int64_
     aarms_oracle_quant_fp8_per_row(y_scratch, T, N, q, s);
 }
 
+/* Threads for the OpenMP loops above (0 or less: leave as is). */
+void aarms_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int aarms_oracle_num_threads(void)
 {
 #ifdef _OPENMP
