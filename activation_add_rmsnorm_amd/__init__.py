@@ -27,6 +27,18 @@ __all__ = [
     "OP_NORM", "OP_SWIGLU", "OP_SWIGLU_DYNAMIC", "OP_RMSNORM",
 ]
 
+# Variants installed by tuning.tune() / tuning.load(), keyed by (form, width,
+# token bucket); consulted by the entry points below when variant == -1.
+_TUNED: dict = {}
+
+
+def _variant(form: str, tokens: int, width: int, variant: int) -> int:
+    if variant != -1 or not _TUNED:
+        return variant
+    t = max(1, int(tokens))
+    return _TUNED.get((form, int(width), 1 << (t - 1).bit_length()), -1)
+
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libaarms.so")
 _LOCK = threading.Lock()
@@ -151,6 +163,7 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Ten
     _require(residual_out, "residual_out", (torch.bfloat16,), (T, H))
     _same_device(x, residual, weight, out, residual_out)
     lib = load()
+    variant = _variant("fused_add_rmsnorm", T, H, variant)
     _check(lib.fused_add_rmsnorm_ex(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
                                     residual.data_ptr(), weight.data_ptr(), T, H, float(eps),
                                     int(variant), _stream(x.device)), "fused_add_rmsnorm")
@@ -180,6 +193,7 @@ def fused_add_rmsnorm_quant_fp8(x: torch.Tensor, residual: torch.Tensor, weight:
     _require(residual_out, "residual_out", (torch.bfloat16,), (T, H))
     _same_device(x, residual, weight, out, scale_out, residual_out)
     lib = load()
+    variant = _variant("fused_add_rmsnorm_quant_fp8", T, H, variant)
     _check(lib.fused_add_rmsnorm_quant_fp8_ex(out.data_ptr(), scale_out.data_ptr(),
                                               residual_out.data_ptr(), x.data_ptr(),
                                               residual.data_ptr(), weight.data_ptr(), T, H,
@@ -210,6 +224,7 @@ def fused_add_rmsnorm_quant_fp8_static(x: torch.Tensor, residual: torch.Tensor,
     _require(residual_out, "residual_out", (torch.bfloat16,), (T, H))
     _same_device(x, residual, weight, scale, out, residual_out)
     lib = load()
+    variant = _variant("fused_add_rmsnorm_quant_fp8_static", T, H, variant)
     _check(lib.fused_add_rmsnorm_quant_fp8_static_ex(out.data_ptr(), residual_out.data_ptr(),
                                                      x.data_ptr(), residual.data_ptr(),
                                                      weight.data_ptr(), scale.data_ptr(), T, H,
@@ -231,6 +246,7 @@ def rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, out: torch.Tensor
     _require(out, "out", (torch.bfloat16,), (T, H))
     _same_device(x, weight, out)
     lib = load()
+    variant = _variant("rmsnorm", T, H, variant)
     _check(lib.rmsnorm_ex(out.data_ptr(), x.data_ptr(), weight.data_ptr(), T, H, float(eps),
                           int(variant), _stream(x.device)), "rmsnorm")
     return out
@@ -254,6 +270,7 @@ def rmsnorm_quant_fp8(x: torch.Tensor, weight: torch.Tensor, eps: float,
     _require(scale_out, "scale_out", (torch.float32,), (T,))
     _same_device(x, weight, out, scale_out)
     lib = load()
+    variant = _variant("rmsnorm_quant_fp8", T, H, variant)
     _check(lib.rmsnorm_quant_fp8_ex(out.data_ptr(), scale_out.data_ptr(), x.data_ptr(),
                                     weight.data_ptr(), T, H, float(eps), int(variant),
                                     _stream(x.device)), "rmsnorm_quant_fp8")
@@ -274,6 +291,7 @@ def rmsnorm_quant_fp8_static(x: torch.Tensor, weight: torch.Tensor, scale: torch
     _require(out, "out", FP8_DTYPES, (T, H))
     _same_device(x, weight, scale, out)
     lib = load()
+    variant = _variant("rmsnorm_quant_fp8_static", T, H, variant)
     _check(lib.rmsnorm_quant_fp8_static_ex(out.data_ptr(), x.data_ptr(), weight.data_ptr(),
                                            scale.data_ptr(), T, H, float(eps), int(variant),
                                            _stream(x.device)), "rmsnorm_quant_fp8_static")
@@ -291,6 +309,7 @@ def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None, variant: int 
     _require(out, "out", (torch.bfloat16,), (T, N))
     _same_device(gate_up, out)
     lib = load()
+    variant = _variant("swiglu", T, N, variant)
     _check(lib.swiglu_ex(out.data_ptr(), gate_up.data_ptr(), T, N, int(variant),
                          _stream(gate_up.device)), "swiglu")
     return out
@@ -310,6 +329,7 @@ def swiglu_quant_fp8(gate_up: torch.Tensor, scale: torch.Tensor, out: torch.Tens
     _require(out, "out", FP8_DTYPES, (T, N))
     _same_device(gate_up, scale, out)
     lib = load()
+    variant = _variant("swiglu_quant_fp8", T, N, variant)
     _check(lib.swiglu_quant_fp8_ex(out.data_ptr(), gate_up.data_ptr(), scale.data_ptr(), T, N,
                                    int(variant), _stream(gate_up.device)), "swiglu_quant_fp8")
     return out
@@ -331,6 +351,7 @@ def swiglu_quant_fp8_dynamic(gate_up: torch.Tensor, out: torch.Tensor | None = N
     _require(scale_out, "scale_out", (torch.float32,), (T,))
     _same_device(gate_up, out, scale_out)
     lib = load()
+    variant = _variant("swiglu_quant_fp8_dynamic", T, N, variant)
     _check(lib.swiglu_quant_fp8_dynamic_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(),
                                            T, N, int(variant), _stream(gate_up.device)),
            "swiglu_quant_fp8_dynamic")

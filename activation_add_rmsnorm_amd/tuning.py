@@ -1,0 +1,231 @@
+"""Startup variant autotuning, cached per (op form, row width, token bucket).
+
+The plain entry points choose a kernel variant with a fixed heuristic
+(include/aarms.h, aarms_pick_variant).  No variant is fastest for every
+shape; the first page's tuning study finds near-ties among versions flipping
+from run to run and only large gaps stable ("TensorRT-LLM: Compiling
+Inference Engines Ahead of Time", section "Auto-tuning, measured"), and its
+runtime tunes at start-up per shape bucket with a cache saved to a file and
+reloaded (section "Leaving the engine behind").  ``tune()`` times every
+variant that fits one (form, tokens, width) on this device, on rotated
+buffer sets so that each launch reads HBM, and installs the fastest in this
+process's table only when it beats the heuristic's choice by more than
+``margin``, so a near-tie never flips the choice.  The Python entry points
+of this package consult the table when called with ``variant=-1``; the C
+library itself stays stateless.  Tokens are bucketed to the next power of
+two.  ``save()`` / ``load()`` keep the table in a JSON file tied to the
+library build and device, so a stale table is ignored rather than applied.
+
+Each variant's launches are captured once into a HIP graph and the graph is
+replayed between HIP events, so host launch overhead does not hide the
+kernels' own differences at small shapes.  This module allocates its own
+buffers and synchronizes: call it at start-up, not inside a captured graph.
+"""
+
+from __future__ import annotations
+
+import hashlib
+import json
+import math
+import os
+
+import torch
+
+import activation_add_rmsnorm_amd as A
+
+MALL_BYTES = 256e6          # MI355X last-level cache; rotation covers twice this
+
+# form -> (variant table op, quant flag for aarms_pick_variant)
+FORMS = {
+    "fused_add_rmsnorm": (A.OP_NORM, False),
+    "fused_add_rmsnorm_quant_fp8": (A.OP_NORM, True),
+    "fused_add_rmsnorm_quant_fp8_static": (A.OP_NORM, True),
+    "rmsnorm": (A.OP_RMSNORM, False),
+    "rmsnorm_quant_fp8": (A.OP_RMSNORM, True),
+    "rmsnorm_quant_fp8_static": (A.OP_RMSNORM, True),
+    "swiglu": (A.OP_SWIGLU, False),
+    "swiglu_quant_fp8": (A.OP_SWIGLU, True),
+    "swiglu_quant_fp8_dynamic": (A.OP_SWIGLU_DYNAMIC, True),
+}
+
+
+def bucket(tokens: int) -> int:
+    """The power of two at or above tokens (1 for 0 or 1)."""
+    t = max(1, int(tokens))
+    return 1 << (t - 1).bit_length()
+
+
+def _key(form: str, tokens: int, width: int):
+    if form not in FORMS:
+        raise ValueError("unknown form %r" % form)
+    return (form, int(width), bucket(tokens))
+
+
+def set_variant(form: str, tokens: int, width: int, variant: int) -> None:
+    A._TUNED[_key(form, tokens, width)] = int(variant)
+
+
+def variant_for(form: str, tokens: int, width: int) -> int:
+    """The tuned variant for this call, or -1 (the library's heuristic)."""
+    return A._TUNED.get(_key(form, tokens, width), -1)
+
+
+def clear() -> None:
+    A._TUNED.clear()
+
+
+def variants_fitting(form: str, width: int):
+    op, _ = FORMS[form]
+    out = []
+    for v in range(A.variant_count(op)):
+        name = A.variant_name(op, v)
+        if op == A.OP_SWIGLU:
+            out.append(v)                       # any width that is a multiple of 8
+            continue
+        waves = 1 if name.startswith("wave/row") else int(name.split()[0])
+        per_lane = int(name.split("x")[-1].split()[0])
+        if waves * 64 * per_lane * 8 >= width:
+            out.append(v)
+    return out
+
+
+def _buffers(form: str, tokens: int, width: int, device):
+    """One set of inputs and outputs for a launch of `form`, and its bytes."""
+    T, W = int(tokens), int(width)
+    bf = dict(dtype=torch.bfloat16, device=device)
+    f8 = dict(dtype=torch.uint8, device=device)
+    if form.startswith("swiglu"):
+        b = dict(gu=(torch.randn((T, 2 * W), device=device) * 2).to(torch.bfloat16))
+        b["y"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
+        b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
+        nbytes = T * W * 4 + T * W * (1 if "fp8" in form else 2)
+    else:
+        b = dict(x=torch.randn((T, W), device=device).to(torch.bfloat16),
+                 r=torch.randn((T, W), device=device).to(torch.bfloat16))
+        b["o"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
+        b["ro"] = torch.empty((T, W), **bf)
+        b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
+        nbytes = T * W * (2 if form.startswith("rmsnorm") else 6) + T * W * (1 if "fp8" in form else 2)
+    return b, nbytes
+
+
+def _launcher(form: str, b: dict, w, scale, variant: int):
+    if form == "fused_add_rmsnorm":
+        return lambda: A.fused_add_rmsnorm(b["x"], b["r"], w, 1e-6, out=b["o"], residual_out=b["ro"], variant=variant)
+    if form == "fused_add_rmsnorm_quant_fp8":
+        return lambda: A.fused_add_rmsnorm_quant_fp8(b["x"], b["r"], w, 1e-6, out=b["o"], scale_out=b["s"],
+                                                     residual_out=b["ro"], variant=variant)
+    if form == "fused_add_rmsnorm_quant_fp8_static":
+        return lambda: A.fused_add_rmsnorm_quant_fp8_static(b["x"], b["r"], w, scale, 1e-6, out=b["o"],
+                                                            residual_out=b["ro"], variant=variant)
+    if form == "rmsnorm":
+        return lambda: A.rmsnorm(b["x"], w, 1e-6, out=b["o"], variant=variant)
+    if form == "rmsnorm_quant_fp8":
+        return lambda: A.rmsnorm_quant_fp8(b["x"], w, 1e-6, out=b["o"], scale_out=b["s"], variant=variant)
+    if form == "rmsnorm_quant_fp8_static":
+        return lambda: A.rmsnorm_quant_fp8_static(b["x"], w, scale, 1e-6, out=b["o"], variant=variant)
+    if form == "swiglu":
+        return lambda: A.swiglu(b["gu"], out=b["y"], variant=variant)
+    if form == "swiglu_quant_fp8":
+        return lambda: A.swiglu_quant_fp8(b["gu"], scale, out=b["y"], variant=variant)
+    if form == "swiglu_quant_fp8_dynamic":
+        return lambda: A.swiglu_quant_fp8_dynamic(b["gu"], out=b["y"], scale_out=b["s"], variant=variant)
+    raise ValueError(form)
+
+
+def sweep(form: str, tokens: int, width: int, rounds: int = 3, device=None, max_sets: int = 64):
+    """Mean time per launch in microseconds of every fitting variant (the best
+    of `rounds` graph replays each), on rotated buffer sets."""
+    device = torch.device(device or "cuda")
+    first, nbytes = _buffers(form, tokens, width, device)
+    sets = [first]
+    n_sets = min(max_sets, max(2, math.ceil(2 * MALL_BYTES / max(nbytes, 1))))
+    for _ in range(n_sets - 1):
+        sets.append({k: (v.clone() if k in ("x", "r", "gu") else torch.empty_like(v)) for k, v in first.items()})
+    W = int(width)
+    w = (1 + 0.1 * torch.randn((W,), device=device)).to(torch.bfloat16) if not form.startswith("swiglu") else None
+    scale = torch.tensor([0.05], dtype=torch.float32, device=device)
+    # about 2 ms of work per replay, at least 8 launches
+    est_us = max(nbytes / 5e3, 2.0)
+    reps = max(8, min(512, int(2000 / est_us)))
+    times = {}
+    for v in variants_fitting(form, W):
+        calls = [_launcher(form, s, w, scale, v) for s in sets]
+        side = torch.cuda.Stream(device)
+        side.wait_stream(torch.cuda.current_stream(device))
+        with torch.cuda.stream(side):
+            for c in calls:
+                c()
+        torch.cuda.current_stream(device).wait_stream(side)
+        torch.cuda.synchronize(device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                calls[i % len(calls)]()
+        g.replay()
+        torch.cuda.synchronize(device)
+        best = float("inf")
+        for _ in range(rounds):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            e.record()
+            torch.cuda.synchronize(device)
+            best = min(best, a.elapsed_time(e) * 1e3 / reps)
+        times[v] = best
+        del g
+    return times
+
+
+def tune(form: str, tokens: int, width: int, margin: float = 0.03, rounds: int = 3, device=None):
+    """Time every fitting variant and install the fastest for (form, bucket of
+    tokens, width) if it beats the heuristic's pick by more than `margin`.
+    Returns a report: the heuristic's pick and time, the best and its time,
+    and the variant installed (-1: the heuristic stays)."""
+    op, quant = FORMS[form]
+    # time at the bucket's token count, the shape every call in it shares best
+    T = bucket(tokens)
+    times = sweep(form, T, width, rounds=rounds, device=device)
+    pick = A.pick_variant(op, T, width, quant)
+    best = min(times, key=times.get)
+    chosen = best if (pick not in times or times[best] < times[pick] * (1 - margin)) else -1
+    if chosen >= 0:
+        set_variant(form, T, width, chosen)
+    name = lambda v: A.variant_name(op, v) if v >= 0 else None
+    return {"form": form, "tokens_bucket": T, "width": int(width),
+            "heuristic": name(pick), "heuristic_us": round(times.get(pick, float("nan")), 3),
+            "best": name(best), "best_us": round(times[best], 3), "installed": name(chosen)}
+
+
+def _identity() -> dict:
+    """The library build and the device kind a table belongs to."""
+    h = hashlib.sha256(open(A.lib_path(), "rb").read()).hexdigest()[:16]
+    if torch.cuda.is_available():
+        dev = torch.cuda.get_device_properties(torch.cuda.current_device())
+        name, arch = dev.name, getattr(dev, "gcnArchName", "")
+    else:
+        name, arch = "none", ""
+    return {"library_sha256": h, "device": name, "arch": arch}
+
+
+def save(path: str) -> None:
+    entries = [{"form": f, "width": w, "tokens_bucket": t, "variant": v} for (f, w, t), v in A._TUNED.items()]
+    with open(path, "w") as fh:
+        json.dump({"identity": _identity(), "entries": entries}, fh, indent=1)
+
+
+def load(path: str) -> int:
+    """Install the entries of a saved table made by this library build on this
+    kind of device; returns the number installed (0 for a stale file)."""
+    if not os.path.exists(path):
+        return 0
+    with open(path) as fh:
+        data = json.load(fh)
+    if data.get("identity") != _identity():
+        return 0
+    n = 0
+    for e in data.get("entries", []):
+        if e["form"] in FORMS:
+            A._TUNED[(e["form"], int(e["width"]), int(e["tokens_bucket"]))] = int(e["variant"])
+            n += 1
+    return n

@@ -413,7 +413,28 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
 
     # the rest of the quantisation matrix, at the same shapes
     out.update(quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream))
+
+    # start-up autotuning at the workload shapes: the heuristic's variant
+    # against the fastest one (graph-replay timings); informational, the
+    # figures above use the heuristic
+    out["autotune"] = autotune_report()
     return out
+
+
+def autotune_report():
+    from activation_add_rmsnorm_amd import tuning
+    shapes = [("fused_add_rmsnorm", 4096, 1536), ("swiglu", 4096, 8960),
+              ("fused_add_rmsnorm", 1, 1536), ("swiglu", 1, 8960),
+              ("fused_add_rmsnorm_quant_fp8", 2048, 16384), ("swiglu_quant_fp8", 8192, 28672),
+              ("rmsnorm", 4096, 1536), ("rmsnorm_quant_fp8", 2048, 16384),
+              ("fused_add_rmsnorm_quant_fp8_static", 2048, 16384), ("swiglu_quant_fp8_dynamic", 8192, 28672)]
+    rows = []
+    for form, T, W in shapes:
+        r = tuning.tune(form, T, W, rounds=3)
+        r["gain_pct"] = round(100 * (r["heuristic_us"] / r["best_us"] - 1), 1)
+        rows.append(r)
+    tuning.clear()
+    return rows
 
 
 def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
