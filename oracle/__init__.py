@@ -69,6 +69,10 @@ def _lib():
                 "aarms_oracle_swiglu": (None, [u16p, i64, i64, u16p]),
                 "aarms_oracle_swiglu_quant_fp8": (None, [u16p, i64, i64, f32, u8p]),
                 "aarms_oracle_swiglu_quant_fp8_per_row": (None, [u16p, i64, i64, u16p, u8p, f32p]),
+                "aarms_oracle_e2m1_from_f64": (C.c_uint8, [f64]),
+                "aarms_oracle_e2m1_to_f64": (f64, [C.c_uint8]),
+                "aarms_oracle_e8m0_to_f64": (f64, [C.c_uint8]),
+                "aarms_oracle_quant_mxfp4": (None, [u16p, i64, i64, u8p, u8p]),
                 "aarms_oracle_num_threads": (C.c_int, []),
                 "aarms_oracle_set_threads": (None, [C.c_int]),
             }
@@ -238,6 +242,62 @@ def rmsnorm_quant_fp8_static(x, weight, eps: float, scale: float):
     Returns (q, y, rs)."""
     out, rs = rmsnorm(x, weight, eps)
     return quant_fp8_static(out, scale), out, rs
+
+
+# ---------------------------------------------------------------- mxfp4
+
+def e2m1_from_f64(v: float) -> int:
+    return int(_lib().aarms_oracle_e2m1_from_f64(float(v)))
+
+
+def e2m1_to_f64(q: int) -> float:
+    return float(_lib().aarms_oracle_e2m1_to_f64(int(q)))
+
+
+def e2m1_table() -> np.ndarray:
+    """Values of the 16 E2M1 codes."""
+    return np.array([e2m1_to_f64(q) for q in range(16)], dtype=np.float64)
+
+
+def e8m0_to_f64(b: int) -> float:
+    return float(_lib().aarms_oracle_e8m0_to_f64(int(b)))
+
+
+def quant_mxfp4(y):
+    """MXFP4 of each row (width a multiple of 32).  Returns (q [T, H/2]
+    uint8, two codes per byte with the first in the low nibble;
+    s [T, H/32] uint8 E8M0 block scales)."""
+    y = _u16(y)
+    T, H = _rows(y)
+    if H % 32:
+        raise ValueError("width must be a multiple of 32")
+    q = np.empty((T, H // 2), np.uint8)
+    s = np.empty((T, H // 32), np.uint8)
+    _lib().aarms_oracle_quant_mxfp4(y, T, H, q, s)
+    return q, s
+
+
+def mxfp4_decode(q, s) -> np.ndarray:
+    """float64 values of MXFP4 codes q [T, H/2] with block scales s [T, H/32]."""
+    q, s = np.asarray(q, np.uint8), np.asarray(s, np.uint8)
+    tab = e2m1_table()
+    el = np.stack([tab[q & 0xF], tab[q >> 4]], axis=-1).reshape(q.shape[0], -1)
+    sc = np.array([e8m0_to_f64(b) for b in range(256)])[s]
+    return el * np.repeat(sc, 32, axis=1)
+
+
+def fused_add_rmsnorm_quant_mxfp4(x, residual, weight, eps: float):
+    """The norm, its bf16 output in MXFP4.  Returns (q, s, residual_out, y, rs)."""
+    out, res_out, rs = fused_add_rmsnorm(x, residual, weight, eps)
+    q, s = quant_mxfp4(out)
+    return q, s, res_out, out, rs
+
+
+def rmsnorm_quant_mxfp4(x, weight, eps: float):
+    """RMSNorm (no residual add), its bf16 output in MXFP4.  Returns (q, s, y, rs)."""
+    out, rs = rmsnorm(x, weight, eps)
+    q, s = quant_mxfp4(out)
+    return q, s, out, rs
 
 
 # ---------------------------------------------------------------- swiglu

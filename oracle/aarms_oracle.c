@@ -42,7 +42,16 @@
  *  - silu(+inf) = +inf, silu(-inf) = -0;
  *  - the row amax ignores NaN;
  *  - a quantisation scale of zero is treated as one (an all-zero row's
- *    dynamic scale is 0 and its codes are signed zeros).
+ *    dynamic scale is 0 and its codes are signed zeros);
+ *  - MXFP4: a block holding a NaN or an infinity gets the E8M0 NaN scale
+ *    0xFF and zero codes; an all-zero block gets the smallest scale, 2^-127.
+ *
+ * MXFP4 follows the OCP Microscaling formats the "TensorRT-LLM" walkthrough
+ * names (Part V: 32-value blocks sharing a power-of-two E8M0 scale, E2M1
+ * elements): the shared exponent is floor(log2(max |v|)) minus 2 (the
+ * exponent of E2M1's largest power of two), clamped to E8M0's range; each
+ * element is v / 2^exponent rounded to nearest even on the E2M1 grid and
+ * saturated at +-6.  Two elements per byte, the first in the low nibble.
  */
 
 #include <math.h>
@@ -131,6 +140,40 @@ double aarms_oracle_e4m3_to_f64(uint8_t q)
     if (E == 15 && M == 7) return NAN;
     if (E == 0) return sgn * ldexp((double)M, -9);
     return sgn * ldexp(1.0 + M / 8.0, E - 7);
+}
+
+/* binary64 -> E2M1 (2 significand bits, emin 0, largest finite 6), ties to
+ * even, saturating at +-6.  Code: sign in bit 3, then the magnitudes 0, 0.5,
+ * 1, 1.5, 2, 3, 4, 6 as 0..7.  NaN gives 0 (its block is marked by the
+ * scale instead). */
+uint8_t aarms_oracle_e2m1_from_f64(double v)
+{
+    if (isnan(v)) return 0;
+    uint8_t s = signbit(v) ? 0x8u : 0x0u;
+    double r = fabs(round_to_grid(v, 2, 0, 0));
+    if (r > 6.0) r = 6.0;
+    if (r == 0.0) return s;
+    if (r < 1.0) return (uint8_t)(s | 1u);          /* 0.5, the only subnormal */
+    int e;
+    (void)frexp(r, &e);
+    int lead = e - 1;                                /* 0, 1 or 2 */
+    int E = lead + 1;                                /* biased exponent 1..3 */
+    int M = (int)((ldexp(r, -lead) - 1.0) * 2.0);
+    return (uint8_t)(s | (E << 1) | M);
+}
+
+double aarms_oracle_e2m1_to_f64(uint8_t q)
+{
+    double sgn = (q & 0x8u) ? -1.0 : 1.0;
+    int E = (q >> 1) & 3, M = q & 1;
+    if (E == 0) return sgn * 0.5 * M;
+    return sgn * ldexp(1.0 + M / 2.0, E - 1);
+}
+
+/* E8M0 byte -> its value 2^(b - 127); 0xFF is NaN. */
+double aarms_oracle_e8m0_to_f64(uint8_t b)
+{
+    return b == 0xFFu ? NAN : ldexp(1.0, (int)b - 127);
 }
 
 /* ------------------------------------------------------------------ */
@@ -270,6 +313,46 @@ void aarms_oracle_fused_add_rmsnorm_quant_fp8(const uint16_t *x, const uint16_t 
 {
     aarms_oracle_fused_add_rmsnorm(x, res, w, T, H, eps, y_scratch, res_out, rs);
     aarms_oracle_quant_fp8_per_row(y_scratch, T, H, q, s);
+}
+
+/* MXFP4: each row of H values (H a multiple of 32) in blocks of 32, one E8M0
+ * scale byte per block, two E2M1 codes per byte (first in the low nibble). */
+void aarms_oracle_quant_mxfp4(const uint16_t *y, int64_t T, int64_t H, uint8_t *q, uint8_t *s)
+{
+    const int64_t nb = H / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < T; ++row) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t *yb = y + row * H + b * 32;
+            double amax = 0.0;
+            int bad = 0;
+            for (int i = 0; i < 32; ++i) {
+                double v = (double)aarms_oracle_bf16_to_f32(yb[i]);
+                if (!isfinite(v)) bad = 1;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            uint8_t *qb = q + row * (H / 2) + b * 16;
+            if (bad) {
+                s[row * nb + b] = 0xFFu;
+                for (int i = 0; i < 16; ++i) qb[i] = 0;
+                continue;
+            }
+            int x = -127;                              /* all-zero block */
+            if (amax > 0.0) {
+                int e;
+                (void)frexp(amax, &e);                 /* amax in [2^(e-1), 2^e) */
+                x = (e - 1) - 2;
+                if (x < -127) x = -127;
+                if (x > 127) x = 127;
+            }
+            s[row * nb + b] = (uint8_t)(x + 127);
+            for (int i = 0; i < 16; ++i) {
+                double v0 = ldexp((double)aarms_oracle_bf16_to_f32(yb[2 * i]), -x);
+                double v1 = ldexp((double)aarms_oracle_bf16_to_f32(yb[2 * i + 1]), -x);
+                qb[i] = (uint8_t)(aarms_oracle_e2m1_from_f64(v0) | (aarms_oracle_e2m1_from_f64(v1) << 4));
+            }
+        }
+    }
 }
 
 /* ------------------------------------------------------------------ */

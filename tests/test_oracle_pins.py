@@ -530,6 +530,97 @@ def test_dynamic_swiglu_quant_invariants_and_torch():
     assert np.array_equal(q, ref)
 
 
+# ------------------------------------------------------------------ MXFP4
+
+E2M1_GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _e2m1_brute(v: float) -> int:
+    """Nearest E2M1 magnitude by search (ties to the even code), saturating."""
+    a = min(abs(v), 6.0)
+    d = [abs(a - g) for g in E2M1_GRID]
+    best = min(d)
+    cands = [i for i, x in enumerate(d) if x == best]
+    code = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+    return code | (8 if math.copysign(1.0, v) < 0 else 0)
+
+
+def test_e2m1_values_and_rounding_exhaustive():
+    assert [oracle.e2m1_to_f64(q) for q in range(8)] == E2M1_GRID
+    assert [oracle.e2m1_to_f64(q | 8) for q in range(8)] == [-g for g in E2M1_GRID]
+    # every finite bf16, scaled into the E2M1 range by a few powers of two
+    f = f32_of(FINITE_BF16).astype(np.float64)
+    for k in (0, -3, 3):
+        v = np.ldexp(f, k)
+        v = v[np.abs(v) < 16]
+        for x in v:
+            assert oracle.e2m1_from_f64(float(x)) == _e2m1_brute(float(x)), x
+    # the ties exactly
+    for t, want in [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6), (7.0, 7)]:
+        assert oracle.e2m1_from_f64(t) == want and oracle.e2m1_from_f64(-t) == want | 8
+
+
+def test_e8m0_decode_matches_torch():
+    b = np.arange(255, dtype=np.uint8)
+    ref = torch.from_numpy(b.copy()).view(torch.float8_e8m0fnu).float().numpy().astype(np.float64)
+    mine = np.array([oracle.e8m0_to_f64(int(x)) for x in b])
+    # torch decodes byte 0 as 2^-127 like every other byte
+    assert np.array_equal(mine, ref)
+    assert math.isnan(oracle.e8m0_to_f64(255))
+
+
+def test_mxfp4_scale_rule_and_nearest_elements():
+    """Per 32-value block: 4 X <= amax < 8 X for the power of two X the scale
+    byte encodes, the block's largest element is at 4 or 6 (times X), and
+    every element decodes to the nearest point of X times the E2M1 grid
+    (ties to the even code, saturating at 6 X)."""
+    rng = np.random.default_rng(7)
+    rows = []
+    for k in (-20, -5, 0, 3, 9, 40):
+        rows.append(gen.bf16_bits_from_f32((rng.standard_normal(256) * 2.0 ** k).astype(np.float32)))
+    y = np.stack(rows)
+    q, s = oracle.quant_mxfp4(y)
+    X = np.array([[oracle.e8m0_to_f64(int(b)) for b in r] for r in s])
+    yf = f32_of(y).astype(np.float64).reshape(len(rows), -1, 32)
+    amax = np.abs(yf).max(axis=2)
+    assert np.all(4 * X <= amax) and np.all(amax < 8 * X)
+    dec = oracle.mxfp4_decode(q, s).reshape(yf.shape)
+    assert np.all(np.isin(np.abs(dec).max(axis=2) / X, [4.0, 6.0]))
+    for r in range(len(rows)):
+        for b in range(yf.shape[1]):
+            for i in range(32):
+                want = _e2m1_brute(yf[r, b, i] / X[r, b])
+                code = (q[r, b * 16 + i // 2] >> (4 * (i % 2))) & 0xF
+                assert code == want or (code & 7) == (want & 7) == 0, (r, b, i)
+
+
+def test_mxfp4_packing_zero_and_special_blocks():
+    one = oracle.bf16_from_f64
+    y = np.zeros((3, 64), np.uint16)
+    y[0, 0], y[0, 1] = one(1.0), one(6.0)          # X = 2^(2 - 2) = 1: codes 2 (1.0) and 7 (6.0)
+    y[1, 32 + 5] = 0x7FC0                          # NaN in the second block
+    y[2, 3] = 0x7F80                               # +inf
+    q, s = oracle.quant_mxfp4(y)
+    assert q[0, 0] == 0x72                         # first element in the low nibble
+    assert s[0, 0] == 127 and s[0, 1] == 0         # all-zero block: smallest scale
+    assert np.all(q[0, 16:] == 0)
+    assert s[1, 0] == 0 and s[1, 1] == 0xFF and s[2, 0] == 0xFF
+    assert np.all(q[1, 16:] == 0) and np.all(q[2, :16] == 0)
+
+
+def test_mxfp4_norm_is_composition():
+    x = gen.normal_bf16((16, 2048), 16, 1, outlier_frac=0.001)
+    r = gen.normal_bf16((16, 2048), 16, 2)
+    w = gen.normal_bf16((2048,), 16, 3, mean=1.0, std=0.1)
+    q, s, res_out, y, _ = oracle.fused_add_rmsnorm_quant_mxfp4(x, r, w, 1e-5)
+    out, res2, _ = _norm(x, r, w, 1e-5)
+    assert np.array_equal(y, out) and np.array_equal(res_out, res2)
+    q2, s2 = oracle.quant_mxfp4(out)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    q3, s3, y3, _ = oracle.rmsnorm_quant_mxfp4(x, w, 1e-5)
+    assert np.array_equal(y3, oracle.rmsnorm(x, w, 1e-5)[0])
+
+
 # ------------------------------------------------------------------ the pages' shapes
 
 def test_golden_workload_shapes_from_pages():
