@@ -22,6 +22,7 @@ __all__ = [
     "AarmsError", "load", "lib_path",
     "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_static",
     "rmsnorm", "rmsnorm_quant_fp8", "rmsnorm_quant_fp8_static",
+    "fused_add_rmsnorm_quant_mxfp4", "rmsnorm_quant_mxfp4",
     "swiglu", "swiglu_quant_fp8", "swiglu_quant_fp8_dynamic",
     "variant_count", "variant_name", "pick_variant",
     "OP_NORM", "OP_SWIGLU", "OP_SWIGLU_DYNAMIC", "OP_RMSNORM",
@@ -89,6 +90,10 @@ def load():
             "rmsnorm_quant_fp8": [vp, vp, vp, vp, i64, i64, f32, vp],
             "rmsnorm_quant_fp8_static": [vp, vp, vp, vp, i64, i64, f32, vp],
             "swiglu_quant_fp8_dynamic": [vp, vp, vp, i64, i64, vp],
+            "fused_add_rmsnorm_quant_mxfp4": [vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
+            "fused_add_rmsnorm_quant_mxfp4_ex": [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "rmsnorm_quant_mxfp4": [vp, vp, vp, vp, i64, i64, f32, vp],
+            "rmsnorm_quant_mxfp4_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],
             "rmsnorm_ex": [vp, vp, vp, i64, i64, f32, i32, vp],
             "rmsnorm_quant_fp8_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],
             "rmsnorm_quant_fp8_static_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],
@@ -296,6 +301,64 @@ def rmsnorm_quant_fp8_static(x: torch.Tensor, weight: torch.Tensor, scale: torch
                                            scale.data_ptr(), T, H, float(eps), int(variant),
                                            _stream(x.device)), "rmsnorm_quant_fp8_static")
     return out
+
+
+def _mx_outputs(T, H, device, out, scale_out):
+    if H % 32:
+        raise ValueError("hidden must be a multiple of 32 for MXFP4")
+    if out is None:
+        out = torch.empty((T, H // 2), dtype=torch.uint8, device=device)
+    if scale_out is None:
+        scale_out = torch.empty((T, H // 32), dtype=torch.uint8, device=device)
+    _require(out, "out", (torch.uint8,), (T, H // 2))
+    _require(scale_out, "scale_out", (torch.uint8,), (T, H // 32))
+    return out, scale_out
+
+
+def fused_add_rmsnorm_quant_mxfp4(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor,
+                                  eps: float, out: torch.Tensor | None = None,
+                                  scale_out: torch.Tensor | None = None,
+                                  residual_out: torch.Tensor | None = None, variant: int = -1):
+    """fused_add_rmsnorm with an MXFP4 epilogue.  Returns (q [T, H/2] uint8,
+    two E2M1 codes per byte; scale [T, H/32] uint8 E8M0; residual_out)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(residual, "residual", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    out, scale_out = _mx_outputs(T, H, x.device, out, scale_out)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _require(residual_out, "residual_out", (torch.bfloat16,), (T, H))
+    _same_device(x, residual, weight, out, scale_out, residual_out)
+    lib = load()
+    variant = _variant("fused_add_rmsnorm_quant_mxfp4", T, H, variant)
+    _check(lib.fused_add_rmsnorm_quant_mxfp4_ex(out.data_ptr(), scale_out.data_ptr(),
+                                                residual_out.data_ptr(), x.data_ptr(),
+                                                residual.data_ptr(), weight.data_ptr(), T, H,
+                                                float(eps), int(variant), _stream(x.device)),
+           "fused_add_rmsnorm_quant_mxfp4")
+    return out, scale_out, residual_out
+
+
+def rmsnorm_quant_mxfp4(x: torch.Tensor, weight: torch.Tensor, eps: float,
+                        out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
+                        variant: int = -1):
+    """rmsnorm with an MXFP4 epilogue.  Returns (q [T, H/2], scale [T, H/32])."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    out, scale_out = _mx_outputs(T, H, x.device, out, scale_out)
+    _same_device(x, weight, out, scale_out)
+    lib = load()
+    variant = _variant("rmsnorm_quant_mxfp4", T, H, variant)
+    _check(lib.rmsnorm_quant_mxfp4_ex(out.data_ptr(), scale_out.data_ptr(), x.data_ptr(),
+                                      weight.data_ptr(), T, H, float(eps), int(variant),
+                                      _stream(x.device)), "rmsnorm_quant_mxfp4")
+    return out, scale_out
 
 
 def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None, variant: int = -1):

@@ -180,12 +180,14 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
                 int64_t hidden, float eps, int epi, bool res, int variant, hipStream_t stream)
 {
     const bool dyn = epi == NORM_EPI_FP8_DYNAMIC, stat = epi == NORM_EPI_FP8_STATIC;
+    const bool mx = epi == NORM_EPI_MXFP4;
     int st = check_width(tokens, hidden, AARMS_MAX_HIDDEN);
     if (st) return st;
+    if (mx && hidden % 32 != 0) return AARMS_ERR_BAD_SHAPE;
     if ((st = check_eps(eps))) return st;
     if (variant < -1 || variant >= norm_variant_count()) return AARMS_ERR_BAD_VARIANT;
     if (tokens == 0) return AARMS_OK;
-    if (!out || !x || !weight || (res && (!residual_out || !residual)) || (dyn && !scale_out) ||
+    if (!out || !x || !weight || (res && (!residual_out || !residual)) || ((dyn || mx) && !scale_out) ||
         (stat && !scale_in))
         return AARMS_ERR_NULL_POINTER;
     if (!aligned(out, 16) || !aligned(x, 16) || !aligned(weight, 16) ||
@@ -207,14 +209,14 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     int partner[3];
     int n_out = 0;
     partner[n_out] = (epi == NORM_EPI_BF16) ? 0 : -1;
-    outs[n_out++] = {span(out, epi == NORM_EPI_BF16 ? 2 * elems : elems), out};
+    outs[n_out++] = {span(out, epi == NORM_EPI_BF16 ? 2 * elems : mx ? elems / 2 : elems), out};
     if (res) {
         partner[n_out] = res_idx;
         outs[n_out++] = {span(residual_out, 2 * elems), residual_out};
     }
-    if (dyn) {
+    if (dyn || mx) {
         partner[n_out] = -1;
-        outs[n_out++] = {span(scale_out, 4 * (uint64_t)tokens), scale_out};
+        outs[n_out++] = {span(scale_out, mx ? elems / 32 : 4 * (uint64_t)tokens), scale_out};
     }
     if ((st = check_outputs(outs, partner, n_out, ins, n_in))) return st;
     if (variant == -1) variant = pick_norm(tokens, hidden, epi != NORM_EPI_BF16, res);
@@ -226,7 +228,7 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     p.x = x;
     p.residual = res ? residual : nullptr;
     p.weight = weight;
-    p.scale_out = dyn ? scale_out : nullptr;
+    p.scale_out = (dyn || mx) ? scale_out : nullptr;
     p.scale_in = stat ? scale_in : nullptr;
     p.tokens = tokens;
     p.hidden = (int32_t)hidden;
@@ -412,6 +414,38 @@ int swiglu_quant_fp8_ex(void *out_fp8, const void *gate_up, const float *scale,
                         int64_t num_tokens, int64_t inter, int variant, hipStream_t stream)
 {
     return swiglu_common(out_fp8, gate_up, scale, num_tokens, inter, true, variant, stream);
+}
+
+int fused_add_rmsnorm_quant_mxfp4(void *out_fp4, uint8_t *scale_out, void *residual_out,
+                                  const void *x, const void *residual, const void *weight,
+                                  int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream)
+{
+    return norm_common(out_fp4, (float *)scale_out, nullptr, residual_out, x, residual, weight,
+                       num_tokens, hidden, eps, NORM_EPI_MXFP4, true, -1, stream);
+}
+
+int fused_add_rmsnorm_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, void *residual_out,
+                                     const void *x, const void *residual, const void *weight,
+                                     int64_t num_tokens, int64_t hidden, float eps, int variant,
+                                     hipStream_t stream)
+{
+    return norm_common(out_fp4, (float *)scale_out, nullptr, residual_out, x, residual, weight,
+                       num_tokens, hidden, eps, NORM_EPI_MXFP4, true, variant, stream);
+}
+
+int rmsnorm_quant_mxfp4(void *out_fp4, uint8_t *scale_out, const void *x, const void *weight,
+                        int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream)
+{
+    return norm_common(out_fp4, (float *)scale_out, nullptr, nullptr, x, nullptr, weight, num_tokens,
+                       hidden, eps, NORM_EPI_MXFP4, false, -1, stream);
+}
+
+int rmsnorm_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, const void *x, const void *weight,
+                           int64_t num_tokens, int64_t hidden, float eps, int variant,
+                           hipStream_t stream)
+{
+    return norm_common(out_fp4, (float *)scale_out, nullptr, nullptr, x, nullptr, weight, num_tokens,
+                       hidden, eps, NORM_EPI_MXFP4, false, variant, stream);
 }
 
 int swiglu_quant_fp8_dynamic(void *out_fp8, float *scale_out, const void *gate_up,

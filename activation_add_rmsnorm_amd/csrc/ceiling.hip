@@ -3,7 +3,7 @@
 // library itself does not use it).
 //
 // Two inputs of n 16-byte vectors are read and up to two outputs are written,
-// out0_bytes and out1_bytes (0, 8 or 16) per input vector, with the same
+// out0_bytes and out1_bytes (0, 4, 8 or 16) per input vector, with the same
 // streaming hints as the library kernels, one vector of each input per lane
 // and the flattest possible grid.  Its time on the same buffers is the
 // bandwidth a launch of that size and read/write mix can reach on the device,
@@ -15,6 +15,8 @@
 //   fused_add_rmsnorm_quant_fp8 [T, H]: out0 = 16, out1 = 8 (E4M3 out)
 //   swiglu [T, 2N] -> [T, N]:           in = the two halves of gate_up;
 //                                       out0 = 16 (bf16) or 8 (E4M3)
+//   fused_add_rmsnorm_quant_mxfp4:      out0 = 16, out1 = 4 (E2M1 pairs; the
+//                                       E8M0 bytes, 1/32 of the data, left out)
 // (the weight and the scales, a few KB, are left out).
 
 #include <hip/hip_runtime.h>
@@ -30,6 +32,7 @@ __device__ __forceinline__ void put(void *base, uint64_t i, u32x4 v)
 {
     if constexpr (O == 16) __builtin_nontemporal_store(v, (u32x4 *)base + i);
     if constexpr (O == 8) __builtin_nontemporal_store((u32x2){v.x ^ v.z, v.y ^ v.w}, (u32x2 *)base + i);
+    if constexpr (O == 4) __builtin_nontemporal_store(v.x ^ v.y ^ v.z ^ v.w, (uint32_t *)base + i);
 }
 
 template <int O0, int O1>
@@ -60,8 +63,9 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 // Returns 0 on success, -1 for bad arguments (nothing launched), or the HIP
 // error code of the launch.  n is at most (2^31 - 1) * 256 vectors; out0_bytes is
-// 8 or 16, out1_bytes 0, 8 or 16; inputs and 16-byte outputs 16-byte aligned,
-// 8-byte outputs 8-byte aligned.  Buffers are the caller's.
+// 8 or 16, out1_bytes 0, 4, 8 or 16; inputs and 16-byte outputs 16-byte
+// aligned, 8- and 4-byte outputs aligned to their size.  Buffers are the
+// caller's.
 extern "C" int aarms_stream_ceiling(void *out0, int out0_bytes, void *out1, int out1_bytes,
                                     const void *in0, const void *in1, int64_t n, hipStream_t stream)
 {
@@ -69,11 +73,12 @@ extern "C" int aarms_stream_ceiling(void *out0, int out0_bytes, void *out1, int 
     if (n == 0) return 0;
     if (!in0 || !in1 || !out0 || (out1_bytes && !out1)) return -1;
     if (!aligned(in0, 16) || !aligned(in1, 16) || !aligned(out0, out0_bytes == 16 ? 16 : 8)) return -1;
-    if (out1_bytes && !aligned(out1, out1_bytes == 16 ? 16 : 8)) return -1;
+    if (out1_bytes && !aligned(out1, (uintptr_t)out1_bytes)) return -1;
     const uint64_t m = (uint64_t)n;
     hipError_t e;
     if (out0_bytes == 16 && out1_bytes == 16) e = launch<16, 16>(in0, in1, out0, out1, m, stream);
     else if (out0_bytes == 16 && out1_bytes == 8) e = launch<16, 8>(in0, in1, out0, out1, m, stream);
+    else if (out0_bytes == 16 && out1_bytes == 4) e = launch<16, 4>(in0, in1, out0, out1, m, stream);
     else if (out0_bytes == 16 && out1_bytes == 0) e = launch<16, 0>(in0, in1, out0, out1, m, stream);
     else if (out0_bytes == 8 && out1_bytes == 0) e = launch<8, 0>(in0, in1, out0, out1, m, stream);
     else return -1;

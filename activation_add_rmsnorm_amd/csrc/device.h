@@ -50,6 +50,39 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return (uint32_t)v;
 }
 
+// ---------------------------------------------------------------- MXFP4
+//
+// A block of 32 values shares the E8M0 scale 2^x with x = floor(log2 amax)
+// - 2 clamped to [-127, 127]; each value v becomes E2M1(v / 2^x), rounded
+// to nearest even and saturated at +-6.  From the binary32 bits of amax
+// (exponent field e): x + 127 = max(e, 2) - 2, which also gives 2^-127 for
+// a zero or binary32-subnormal amax; amax non-finite marks the block with
+// the E8M0 NaN byte 0xFF.  v / 2^x is computed as v * 2^-x: 2^-x is a
+// normal binary32 for every x here (x <= 125) and the product is exact
+// unless it falls far below the smallest E2M1 step, where the code is a
+// signed zero either way.  v_cvt_scalef32_pk_fp4_f32 (scale operand 1.0)
+// does the rounding and saturation and packs the first value into the low
+// nibble (checked on gfx950 at every rounding tie and past 6).
+
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits)
+{
+    if (amax_bits >= 0x7F800000u) return 0xFFu;
+    const uint32_t e = amax_bits >> 23;
+    return (e > 2u ? e : 2u) - 2u;
+}
+
+// Eight values (four bf16 words) -> four bytes of E2M1 pairs, scaled by
+// 2^-x given as its binary32 value.
+__device__ __forceinline__ uint32_t pack_e2m1x8(const uint32_t (&w)[4], float inv_scale)
+{
+    uint32_t q = 0;
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, bf_lo(w[0]) * inv_scale, bf_hi(w[0]) * inv_scale, 1.0f, 0);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, bf_lo(w[1]) * inv_scale, bf_hi(w[1]) * inv_scale, 1.0f, 1);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, bf_lo(w[2]) * inv_scale, bf_hi(w[2]) * inv_scale, 1.0f, 2);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, bf_lo(w[3]) * inv_scale, bf_hi(w[3]) * inv_scale, 1.0f, 3);
+    return q;
+}
+
 // ---------------------------------------------------------------- y / scale
 //
 // q = e4m3(clamp(binary32(y / s), -448, 448)).  A scale of exactly zero is

@@ -12,6 +12,7 @@ enum NormEpilogue : int {
     NORM_EPI_BF16 = 0,        // bf16 out
     NORM_EPI_FP8_DYNAMIC = 1, // E4M3 out, per-token scale written to scale_out
     NORM_EPI_FP8_STATIC = 2,  // E4M3 out, per-tensor scale read from scale_in
+    NORM_EPI_MXFP4 = 3,       // MXFP4 out: E2M1 codes, E8M0 scale per 32 values to scale_out
 };
 
 struct NormParams {
@@ -20,7 +21,7 @@ struct NormParams {
     const void *x;           // bf16 [T,H]
     const void *residual;    // bf16 [T,H] (with the residual add), else null
     const void *weight;      // bf16 [H]
-    float *scale_out;        // fp32 [T], dynamic FP8 only
+    float *scale_out;        // fp32 [T], dynamic FP8 only; uint8 [T, H/32] for MXFP4
     const float *scale_in;   // fp32 [1], static FP8 only
     int64_t tokens;
     int32_t hidden;

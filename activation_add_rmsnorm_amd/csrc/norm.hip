@@ -179,6 +179,32 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
             for (int e = 0; e < 4; ++e) y[e] = norm_word(rv[k][e], wv[k][e], rs);
             st_stream(o + v, y);
         }
+    } else if constexpr (EPI == NORM_EPI_MXFP4) {
+        // ---- y as above; per 32-value block (the 4 slices of 4 adjacent
+        // lanes) the E8M0 scale from the block amax, then E2M1 codes
+        uint32_t *qo = (uint32_t *)((uint8_t *)p.out + (size_t)row * (size_t)(p.hidden / 2));
+        uint8_t *so = (uint8_t *)p.scale_out + (size_t)row * (size_t)(p.hidden / 32);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int v = lane + k * WPR * 64;
+            uint32_t y[4];
+            uint32_t mag = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[e] = norm_word(rv[k][e], wv[k][e], rs);
+                mag = max(mag, max((y[e] << 16) & 0x7FFFFFFFu, y[e] & 0x7FFF0000u));
+            }
+            // the block's 4 slices sit in lanes 4j..4j+3 (all inside or all
+            // past the row end, as H is a multiple of 32)
+            mag = max(mag, dpp_u32<DPP_XOR1>(mag));
+            mag = max(mag, dpp_u32<DPP_XOR2>(mag));
+            if (v >= nvec) continue;
+            const uint32_t sb = mx_scale_byte(mag);
+            const float inv = __uint_as_float((254u - (sb == 0xFFu ? 127u : sb)) << 23);
+            const uint32_t q = (sb == 0xFFu) ? 0u : pack_e2m1x8(y, inv);
+            st_stream(qo + v, q);
+            if ((lane & 3) == 0) so[v >> 2] = (uint8_t)sb;
+        }
     } else if constexpr (EPI == NORM_EPI_FP8_STATIC) {
         // ---- y as above, q = e4m3(clamp(y / s)) with the given scale
         const E4m3Scale qs = make_e4m3_scale(*p.scale_in);
@@ -402,6 +428,9 @@ hipError_t launch_norm(const NormParams &p, int epi, bool residual, int variant,
     case NORM_EPI_FP8_STATIC:
         return residual ? dispatch<NORM_EPI_FP8_STATIC, true>(p, variant, num_cus, stream)
                         : dispatch<NORM_EPI_FP8_STATIC, false>(p, variant, num_cus, stream);
+    case NORM_EPI_MXFP4:
+        return residual ? dispatch<NORM_EPI_MXFP4, true>(p, variant, num_cus, stream)
+                        : dispatch<NORM_EPI_MXFP4, false>(p, variant, num_cus, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -43,6 +43,8 @@ FORMS = {
     "rmsnorm": (A.OP_RMSNORM, False),
     "rmsnorm_quant_fp8": (A.OP_RMSNORM, True),
     "rmsnorm_quant_fp8_static": (A.OP_RMSNORM, True),
+    "fused_add_rmsnorm_quant_mxfp4": (A.OP_NORM, True),
+    "rmsnorm_quant_mxfp4": (A.OP_RMSNORM, True),
     "swiglu": (A.OP_SWIGLU, False),
     "swiglu_quant_fp8": (A.OP_SWIGLU, True),
     "swiglu_quant_fp8_dynamic": (A.OP_SWIGLU_DYNAMIC, True),
@@ -102,10 +104,16 @@ def _buffers(form: str, tokens: int, width: int, device):
     else:
         b = dict(x=torch.randn((T, W), device=device).to(torch.bfloat16),
                  r=torch.randn((T, W), device=device).to(torch.bfloat16))
-        b["o"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
+        if "mxfp4" in form:
+            b["o"] = torch.empty((T, W // 2), **f8)
+            b["s"] = torch.empty((T, W // 32), **f8)
+            out_bytes = T * W // 2 + T * W // 32
+        else:
+            b["o"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
+            b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
+            out_bytes = T * W * (1 if "fp8" in form else 2)
         b["ro"] = torch.empty((T, W), **bf)
-        b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
-        nbytes = T * W * (2 if form.startswith("rmsnorm") else 6) + T * W * (1 if "fp8" in form else 2)
+        nbytes = T * W * (2 if form.startswith("rmsnorm") else 6) + out_bytes
     return b, nbytes
 
 
@@ -124,6 +132,11 @@ def _launcher(form: str, b: dict, w, scale, variant: int):
         return lambda: A.rmsnorm_quant_fp8(b["x"], w, 1e-6, out=b["o"], scale_out=b["s"], variant=variant)
     if form == "rmsnorm_quant_fp8_static":
         return lambda: A.rmsnorm_quant_fp8_static(b["x"], w, scale, 1e-6, out=b["o"], variant=variant)
+    if form == "fused_add_rmsnorm_quant_mxfp4":
+        return lambda: A.fused_add_rmsnorm_quant_mxfp4(b["x"], b["r"], w, 1e-6, out=b["o"], scale_out=b["s"],
+                                                       residual_out=b["ro"], variant=variant)
+    if form == "rmsnorm_quant_mxfp4":
+        return lambda: A.rmsnorm_quant_mxfp4(b["x"], w, 1e-6, out=b["o"], scale_out=b["s"], variant=variant)
     if form == "swiglu":
         return lambda: A.swiglu(b["gu"], out=b["y"], variant=variant)
     if form == "swiglu_quant_fp8":

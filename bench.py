@@ -427,7 +427,8 @@ def autotune_report():
               ("fused_add_rmsnorm", 1, 1536), ("swiglu", 1, 8960),
               ("fused_add_rmsnorm_quant_fp8", 2048, 16384), ("swiglu_quant_fp8", 8192, 28672),
               ("rmsnorm", 4096, 1536), ("rmsnorm_quant_fp8", 2048, 16384),
-              ("fused_add_rmsnorm_quant_fp8_static", 2048, 16384), ("swiglu_quant_fp8_dynamic", 8192, 28672)]
+              ("fused_add_rmsnorm_quant_fp8_static", 2048, 16384), ("swiglu_quant_fp8_dynamic", 8192, 28672),
+              ("fused_add_rmsnorm_quant_mxfp4", 2048, 16384)]
     rows = []
     for form, T, W in shapes:
         r = tuning.tune(form, T, W, rounds=3)
@@ -495,6 +496,17 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
                 T, H, wl.eps, sp), "fused_add_rmsnorm_quant_fp8_static"),
             lambda i: stream(P(i, "ro"), 16, P(i, "q"), 8, P(i, "x"), P(i, "r"), T * H // 8),
             nb, {"scale": 0.02, "buffer_sets_rotated": ns})
+    mq = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+    ms_ = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    mx_sets = [(mq if i == 0 else torch.empty_like(mq), ms_ if i == 0 else torch.empty_like(ms_)) for i in range(ns)]
+    nb = T * H * 6 + T * H // 2 + T * H // 32 + H * 2
+    measure("llama405b_norm_mxfp4_2048x16384",
+            lambda i: check(lib.fused_add_rmsnorm_quant_mxfp4(
+                mx_sets[i % ns][0].data_ptr(), mx_sets[i % ns][1].data_ptr(), P(i, "ro"), P(i, "x"), P(i, "r"),
+                w0.data_ptr(), T, H, wl.eps, sp), "fused_add_rmsnorm_quant_mxfp4"),
+            lambda i: stream(P(i, "ro"), 16, mx_sets[i % ns][0].data_ptr(), 4, P(i, "x"), P(i, "r"), T * H // 8),
+            nb, {"buffer_sets_rotated": ns})
+    del mx_sets
     nb = T * H * 3 + H * 2 + T * 4
     measure("llama405b_rmsnorm_fp8_2048x16384",
             lambda i: check(lib.rmsnorm_quant_fp8(P(i, "q"), P(i, "s"), P(i, "x"), w0.data_ptr(),

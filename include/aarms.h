@@ -20,7 +20,7 @@
  *   - Arguments are validated before anything is enqueued; on any error code
  *     nothing has been launched.  No C++ exception crosses this interface.
  *   - Tensor pointers must be 16-byte aligned; fp32 scale pointers 4-byte
- *     aligned.
+ *     aligned; E8M0 scale bytes unaligned.
  *   - Outputs may not overlap any other argument, except the in-place pairs
  *     each entry point names.  Inputs may overlap each other.
  *   - Results are deterministic: the same inputs give the same bits on every
@@ -51,7 +51,8 @@ extern "C" {
 enum aarms_status {
     AARMS_OK = 0,
     AARMS_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                 */
-    AARMS_ERR_BAD_SHAPE = 2,         /* negative size, zero width, width % 8 != 0  */
+    AARMS_ERR_BAD_SHAPE = 2,         /* negative size, zero width, width % 8 != 0
+                                        (% 32 for MXFP4)                          */
     AARMS_ERR_UNSUPPORTED_SHAPE = 3, /* width or element count beyond the limits   */
     AARMS_ERR_MISALIGNED = 4,        /* pointer alignment not met                  */
     AARMS_ERR_ALIAS = 5,             /* an output overlaps another argument        */
@@ -156,6 +157,33 @@ int rmsnorm_quant_fp8_static(void *out_fp8, const void *x, const void *weight, c
                              int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream);
 
 /*
+ * fused_add_rmsnorm_quant_mxfp4 / rmsnorm_quant_mxfp4 -- the norm (with or
+ * without the residual add) whose bf16 output is written as OCP MXFP4 in the
+ * same pass: blocks of 32 values along a row share an E8M0 (power-of-two)
+ * scale and each value is an E2M1 code ("TensorRT-LLM" walkthrough, Part V,
+ * the OCP MXFP4 standard; vLLM's AllReduce + RMSNorm + Quant (FP4) fusion,
+ * "Introduction to torch.compile and How It Works with vLLM", section 4).
+ *
+ *   out_fp4      [num_tokens, hidden / 2]  uint8  written: two E2M1 codes per byte,
+ *                                                 the first value in the low nibble
+ *   scale_out    [num_tokens, hidden / 32] uint8  written: E8M0 byte b (2^(b - 127)) per
+ *                                                 block, b = clamp(floor(log2 max|y|) - 2 + 127,
+ *                                                 0, 254); 0xFF for a block holding a
+ *                                                 NaN or an infinity (its codes are 0)
+ *   residual_out, x, residual, weight, eps   as for fused_add_rmsnorm / rmsnorm
+ *   hidden       multiple of 32, <= AARMS_MAX_HIDDEN
+ * A code is E2M1(y / 2^(b - 127)) rounded to nearest even, saturated at +-6.
+ * In place: residual_out == residual is allowed.  scale_out has no
+ * alignment requirement.
+ */
+int fused_add_rmsnorm_quant_mxfp4(void *out_fp4, uint8_t *scale_out, void *residual_out,
+                                  const void *x, const void *residual, const void *weight,
+                                  int64_t num_tokens, int64_t hidden, float eps,
+                                  hipStream_t stream);
+int rmsnorm_quant_mxfp4(void *out_fp4, uint8_t *scale_out, const void *x, const void *weight,
+                        int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream);
+
+/*
  * swiglu -- silu(gate) * up over a concatenated gate_up projection output.
  *
  * TensorRT-LLM's gated MLP runs one gate_up_proj matmul followed by a fused
@@ -249,6 +277,13 @@ int rmsnorm_quant_fp8_static_ex(void *out_fp8, const void *x, const void *weight
                                 int variant, hipStream_t stream);
 int swiglu_quant_fp8_dynamic_ex(void *out_fp8, float *scale_out, const void *gate_up,
                                 int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
+int fused_add_rmsnorm_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, void *residual_out,
+                                     const void *x, const void *residual, const void *weight,
+                                     int64_t num_tokens, int64_t hidden, float eps, int variant,
+                                     hipStream_t stream);
+int rmsnorm_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, const void *x, const void *weight,
+                           int64_t num_tokens, int64_t hidden, float eps, int variant,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

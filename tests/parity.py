@@ -223,3 +223,52 @@ def check_swiglu_fp8_dynamic(gate_up, q_gpu, s_gpu):
     bad = ~_same_codes(q_gpu, q_o)
     assert not bad.any(), "codes differ at %d positions, first %s: gpu %s oracle %s" % (
         bad.sum(), np.argwhere(bad)[:5].tolist(), q_gpu[bad][:5], q_o[bad][:5])
+
+
+# ----------------------------------------------------------------- mxfp4
+
+def e2m1_ordered(q: np.ndarray) -> np.ndarray:
+    q = q.astype(np.int64)
+    mag = q & 0x7
+    return np.where(q & 0x8, -mag, mag)
+
+
+def _unpack_e2m1(q: np.ndarray) -> np.ndarray:
+    return np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1)
+
+
+def _check_mx_codes(rows_in, weight, eps, q_gpu, s_gpu, q_o, s_o) -> NormReport:
+    """MXFP4 codes and E8M0 scales of a norm of rows_in against the oracle;
+    rows that differ must match the oracle's MXFP4 of an admissible norm
+    output (scales exactly, codes within one E2M1 step)."""
+    rows = np.flatnonzero((q_gpu != q_o).any(axis=1) | (s_gpu != s_o).any(axis=1))
+    if len(rows):
+        _, lo, hi = norm_admissible(rows_in[rows], weight, eps)
+        cands = [oracle.quant_mxfp4(lo), oracle.quant_mxfp4(hi)]
+        for k, r in enumerate(rows):
+            ok_s = np.zeros(s_gpu.shape[1], bool)
+            d = np.full(q_gpu.shape[1] * 2, 99)
+            for cq, cs in cands:
+                same_s = s_gpu[r] == cs[k]
+                ok_s |= same_s
+                dd = np.abs(e2m1_ordered(_unpack_e2m1(q_gpu[r][None])[0]) -
+                            e2m1_ordered(_unpack_e2m1(cq[k][None])[0]))
+                dd[~np.repeat(same_s, 32)] = 99
+                d = np.minimum(d, dd)
+            assert ok_s.all(), "row %d: block scales outside the admissible set" % r
+            assert d.max() <= 1, "row %d: code off by %d E2M1 steps" % (r, d.max())
+    return NormReport(rows=int(q_gpu.shape[0]), rows_not_nominal=int(len(rows)),
+                      codes_not_nominal=int((q_gpu != q_o).sum()),
+                      scales_not_nominal=int((s_gpu != s_o).sum()))
+
+
+def check_norm_mxfp4(x, residual, weight, eps, q_gpu, s_gpu, res_out_gpu) -> NormReport:
+    q_o, s_o, res_o, _, _ = oracle.fused_add_rmsnorm_quant_mxfp4(x, residual, weight, eps)
+    bad_res = ~same_bf16(res_out_gpu, res_o)
+    assert not bad_res.any(), "residual_out differs at %d positions" % bad_res.sum()
+    return _check_mx_codes(res_o, weight, eps, q_gpu, s_gpu, q_o, s_o)
+
+
+def check_rmsnorm_mxfp4(x, weight, eps, q_gpu, s_gpu) -> NormReport:
+    q_o, s_o, _, _ = oracle.rmsnorm_quant_mxfp4(x, weight, eps)
+    return _check_mx_codes(x, weight, eps, q_gpu, s_gpu, q_o, s_o)

@@ -316,3 +316,22 @@ def test_binding_types_every_declared_function():
     lib = A.load()
     missing = [n for n in declared_functions() if getattr(lib, n).argtypes is None]
     assert not missing, missing
+
+
+def test_mxfp4_norm_errors():
+    lib = A.load()
+
+    def mx(out=P, s=P + BIG + 1, ro=P + 2 * BIG, x=P + 3 * BIG, r=P + 4 * BIG, w=P + 5 * BIG, T=4, H=1536,
+           variant=-1):
+        return lib.fused_add_rmsnorm_quant_mxfp4_ex(out, s, ro, x, r, w, T, H, 1e-6, variant, None)
+
+    assert mx(H=1544) == SHAPE                          # a multiple of 8 but not of 32
+    assert mx(s=0) == NULLP
+    assert mx(out=P + 4) == MISAL
+    assert mx(variant=0) == VARIANT                     # unaligned E8M0 scale bytes are fine
+    assert mx(s=P + 100) == ALIAS                       # scales inside the codes
+    assert mx(ro=P + 3 * BIG) == ALIAS                  # residual_out over x
+    assert mx(ro=P + 4 * BIG, variant=0) == VARIANT     # residual_out == residual in place
+    assert mx(T=0, out=0, s=0, ro=0, x=0, r=0, w=0) == OK
+    assert lib.rmsnorm_quant_mxfp4_ex(P, P + BIG, P + 2 * BIG, P + 3 * BIG, 4, 40, 1e-6, -1, None) == SHAPE
+    assert lib.rmsnorm_quant_mxfp4_ex(P, P + BIG, P + 2 * BIG, P + 3 * BIG, 4, 1536, 1e-6, 0, None) == VARIANT

@@ -245,3 +245,68 @@ def test_swiglu_dynamic_llama70b_full():
     P.check_swiglu_fp8_dynamic(gu, q, s)
     dec = oracle.e4m3_table()
     assert np.all(np.abs(dec[q]).max(axis=1) == 448.0)
+
+
+# ------------------------------------------------------------------ MXFP4 norms
+
+def run_fused_mx(x, r, w, eps, variant=-1):
+    announce("fused_add_rmsnorm_quant_mxfp4", x.shape, "eps", eps, "variant", variant)
+    q, s, ro = A.fused_add_rmsnorm_quant_mxfp4(bf16(x), bf16(r), bf16(w), eps, variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s), bits(ro)
+
+
+def run_rms_mx(x, w, eps, variant=-1):
+    announce("rmsnorm_quant_mxfp4", x.shape, "eps", eps, "variant", variant)
+    q, s = A.rmsnorm_quant_mxfp4(bf16(x), bf16(w), eps, variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s)
+
+
+@pytest.mark.parametrize("T,H", [(1, 32), (3, 96), (16, 1536), (257, 1536), (4, 16384), (2, 65536),
+                                 (1023, 2048)])
+def test_mxfp4_norms_default_variant(T, H):
+    x, r, w = norm_case(T, H, seed=T + 5 * H, outliers=0.002)
+    q, s, ro = run_fused_mx(x, r, w, 1e-5)
+    announce(P.check_norm_mxfp4(x, r, w, 1e-5, q, s, ro))
+    q, s = run_rms_mx(x, w, 1e-5)
+    announce(P.check_rmsnorm_mxfp4(x, w, 1e-5, q, s))
+
+
+@pytest.mark.parametrize("H", [1536, 16384])
+def test_mxfp4_norms_every_variant(H):
+    x, r, w = norm_case(37, H, seed=H + 9, outliers=0.002)
+    for v in variants_for(A.OP_NORM, H):
+        q, s, ro = run_fused_mx(x, r, w, 1e-5, v)
+        P.check_norm_mxfp4(x, r, w, 1e-5, q, s, ro)
+        q, s = run_rms_mx(x, w, 1e-5, v)
+        P.check_rmsnorm_mxfp4(x, w, 1e-5, q, s)
+
+
+def test_mxfp4_special_blocks():
+    """An all-zero block, blocks whose amax is an exact power of two, a block
+    of bf16-subnormal values (the smallest scale), one holding a NaN and one
+    an infinity (scale 0xFF, zero codes)."""
+    H = 256
+    x, _, w = norm_case(6, H, seed=77)
+    w[:] = oracle.bf16_from_f64(1.0)
+    one = oracle.bf16_from_f64
+    x[0, :32] = 0                                   # zero block, rest normal
+    x[1, :] = one(0.5)
+    x[1, 32:64] = one(1.0)                          # amax exact powers of two after the norm
+    x[2, :] = one(1.0)
+    x[2, 64:96] = 0x0001                            # bf16 subnormals beside 1.0: y tiny
+    x[3, 100] = 0x7FC0                              # NaN: the whole row's norm is NaN
+    x[4, 7] = 0x7F80                                # +inf
+    q, s = run_rms_mx(x, w, 1e-6)
+    P.check_rmsnorm_mxfp4(x, w, 1e-6, q, s)
+    assert s[0, 0] == 0 and np.all((q[0, :16] & 0x77) == 0)
+    assert np.all(s[3] == 0xFF) and np.all(q[3] == 0)
+
+
+def test_mxfp4_norm_llama405b_full():
+    wl = W.NORM_FP8_LLAMA405B
+    d = W.norm_inputs(wl)
+    q, s, ro = run_fused_mx(d["x"], d["residual"], d["weight"], wl.eps)
+    announce(P.check_norm_mxfp4(d["x"], d["residual"], d["weight"], wl.eps, q, s, ro))
+    assert np.isfinite(oracle.mxfp4_decode(q, s)).all()
