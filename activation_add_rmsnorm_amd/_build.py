@@ -9,7 +9,8 @@ Flags:
   -fhip-fp32-correctly-rounded-divide-sqrt
                        IEEE binary32 division (per-row scale and reciprocal);
   -Xclang -target-feature -Xclang -packed-fp32-ops
-                       no packed binary32 instructions.
+                       no packed binary32 instructions;
+  -fvisibility=hidden  only the functions include/aarms.h declares are exported.
 No fast-math, no denormal flushing (binary32 and binary64 denormals are kept).
 """
 
@@ -31,7 +32,7 @@ HIP_SOURCES = ["norm.hip", "swiglu.hip"]
 HOST_SOURCES = ["capi.cpp"]
 CEILING_SOURCES = ["ceiling.hip"]
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra", "-Wno-unused-parameter",
           "-ffp-contract=off", "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH, "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -66,7 +66,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 // 8 or 16, out1_bytes 0, 4, 8 or 16; inputs and 16-byte outputs 16-byte
 // aligned, 8- and 4-byte outputs aligned to their size.  Buffers are the
 // caller's.
-extern "C" int aarms_stream_ceiling(void *out0, int out0_bytes, void *out1, int out1_bytes,
+extern "C" __attribute__((visibility("default"))) int aarms_stream_ceiling(void *out0, int out0_bytes, void *out1, int out1_bytes,
                                     const void *in0, const void *in1, int64_t n, hipStream_t stream)
 {
     if (n < 0 || (uint64_t)n > (uint64_t)INT32_MAX * 256u) return -1;

@@ -47,6 +47,12 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility; everything declared
+ * here is exported. */
+#if defined(__GNUC__)
+#pragma GCC visibility push(default)
+#endif
+
 /* Return codes. */
 enum aarms_status {
     AARMS_OK = 0,
@@ -284,6 +290,10 @@ int fused_add_rmsnorm_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, void *re
 int rmsnorm_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, const void *x, const void *weight,
                            int64_t num_tokens, int64_t hidden, float eps, int variant,
                            hipStream_t stream);
+
+#if defined(__GNUC__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }

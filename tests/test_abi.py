@@ -49,6 +49,13 @@ def test_library_exports_every_declared_symbol():
     assert not missing, missing
 
 
+def test_library_exports_only_declared_symbols():
+    out = subprocess.run(["nm", "-D", "--defined-only", A.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == set(declared_functions()), exported ^ set(declared_functions())
+
+
 def test_status_strings():
     lib = A.load()
     for s in range(9):

@@ -310,3 +310,55 @@ def test_mxfp4_norm_llama405b_full():
     q, s, ro = run_fused_mx(d["x"], d["residual"], d["weight"], wl.eps)
     announce(P.check_norm_mxfp4(d["x"], d["residual"], d["weight"], wl.eps, q, s, ro))
     assert np.isfinite(oracle.mxfp4_decode(q, s)).all()
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_quant_matrix_forms_under_graph_replay():
+    """Every form launched from a captured HIP graph, replayed three times
+    with eager work in between: each replay's outputs equal the eager ones
+    bitwise (nothing in the forms allocates, synchronizes or clears memory)."""
+    T, H, N = 64, 2048, 2048
+    x, r, w = norm_case(T, H, seed=91, outliers=0.001)
+    gu = gen.normal_bf16((T, 2 * N), 92, 4, std=2.0)
+    xt, rt, wt, gut, sc = bf16(x), bf16(r), bf16(w), bf16(gu), scale_t(0.03)
+    outs = dict(
+        rms=torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+        rq=torch.empty((T, H), dtype=torch.uint8, device=DEV), rs=torch.empty((T,), device=DEV),
+        st=torch.empty((T, H), dtype=torch.uint8, device=DEV), sro=torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+        mq=torch.empty((T, H // 2), dtype=torch.uint8, device=DEV), ms=torch.empty((T, H // 32), dtype=torch.uint8, device=DEV),
+        mro=torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+        dq=torch.empty((T, N), dtype=torch.uint8, device=DEV), ds=torch.empty((T,), device=DEV))
+
+    def launch():
+        A.rmsnorm(xt, wt, 1e-5, out=outs["rms"])
+        A.rmsnorm_quant_fp8(xt, wt, 1e-5, out=outs["rq"], scale_out=outs["rs"])
+        A.fused_add_rmsnorm_quant_fp8_static(xt, rt, wt, sc, 1e-5, out=outs["st"], residual_out=outs["sro"])
+        A.fused_add_rmsnorm_quant_mxfp4(xt, rt, wt, 1e-5, out=outs["mq"], scale_out=outs["ms"],
+                                        residual_out=outs["mro"])
+        A.swiglu_quant_fp8_dynamic(gut, out=outs["dq"], scale_out=outs["ds"])
+
+    announce("quant-matrix forms, eager then graph")
+    launch()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k].view(torch.uint8), eager[k].view(torch.uint8)), (rep, k)
+        xt.add_(0)                                     # eager work between replays
+    P.check_rmsnorm(x, w, 1e-5, bits(outs["rms"]))
+    P.check_norm_mxfp4(x, r, w, 1e-5, bits(outs["mq"]), bits(outs["ms"]), bits(outs["mro"]))
