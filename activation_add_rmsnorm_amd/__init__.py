@@ -23,7 +23,7 @@ __all__ = [
     "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_static",
     "rmsnorm", "rmsnorm_quant_fp8", "rmsnorm_quant_fp8_static",
     "fused_add_rmsnorm_quant_mxfp4", "rmsnorm_quant_mxfp4",
-    "swiglu", "swiglu_quant_fp8", "swiglu_quant_fp8_dynamic",
+    "swiglu", "swiglu_quant_fp8", "swiglu_quant_fp8_dynamic", "swiglu_quant_mxfp4",
     "variant_count", "variant_name", "pick_variant",
     "OP_NORM", "OP_SWIGLU", "OP_SWIGLU_DYNAMIC", "OP_RMSNORM",
 ]
@@ -90,6 +90,8 @@ def load():
             "rmsnorm_quant_fp8": [vp, vp, vp, vp, i64, i64, f32, vp],
             "rmsnorm_quant_fp8_static": [vp, vp, vp, vp, i64, i64, f32, vp],
             "swiglu_quant_fp8_dynamic": [vp, vp, vp, i64, i64, vp],
+            "swiglu_quant_mxfp4": [vp, vp, vp, i64, i64, vp],
+            "swiglu_quant_mxfp4_ex": [vp, vp, vp, i64, i64, i32, vp],
             "fused_add_rmsnorm_quant_mxfp4": [vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
             "fused_add_rmsnorm_quant_mxfp4_ex": [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
             "rmsnorm_quant_mxfp4": [vp, vp, vp, vp, i64, i64, f32, vp],
@@ -305,7 +307,7 @@ def rmsnorm_quant_fp8_static(x: torch.Tensor, weight: torch.Tensor, scale: torch
 
 def _mx_outputs(T, H, device, out, scale_out):
     if H % 32:
-        raise ValueError("hidden must be a multiple of 32 for MXFP4")
+        raise ValueError("the row width must be a multiple of 32 for MXFP4")
     if out is None:
         out = torch.empty((T, H // 2), dtype=torch.uint8, device=device)
     if scale_out is None:
@@ -418,6 +420,23 @@ def swiglu_quant_fp8_dynamic(gate_up: torch.Tensor, out: torch.Tensor | None = N
     _check(lib.swiglu_quant_fp8_dynamic_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(),
                                            T, N, int(variant), _stream(gate_up.device)),
            "swiglu_quant_fp8_dynamic")
+    return out, scale_out
+
+
+def swiglu_quant_mxfp4(gate_up: torch.Tensor, out: torch.Tensor | None = None,
+                       scale_out: torch.Tensor | None = None, variant: int = -1):
+    """swiglu with an MXFP4 epilogue.  Returns (q [T, N/2] uint8, two E2M1
+    codes per byte; scale [T, N/32] uint8 E8M0)."""
+    if gate_up.dim() != 2 or gate_up.shape[1] % 2:
+        raise ValueError("gate_up must be [tokens, 2 * inter]")
+    T, N = gate_up.shape[0], gate_up.shape[1] // 2
+    _require(gate_up, "gate_up", (torch.bfloat16,), (T, 2 * N))
+    out, scale_out = _mx_outputs(T, N, gate_up.device, out, scale_out)
+    _same_device(gate_up, out, scale_out)
+    lib = load()
+    variant = _variant("swiglu_quant_mxfp4", T, N, variant)
+    _check(lib.swiglu_quant_mxfp4_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(), T, N,
+                                     int(variant), _stream(gate_up.device)), "swiglu_quant_mxfp4")
     return out, scale_out
 
 

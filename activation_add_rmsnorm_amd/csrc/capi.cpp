@@ -236,33 +236,39 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     return launch_status(launch_norm(p, epi, res, variant, device_cus(), stream));
 }
 
-int swiglu_common(void *out, const void *gate_up, const float *scale, int64_t tokens,
-                  int64_t inter, bool quant, int variant, hipStream_t stream)
+// swiglu, its static E4M3 form (scale) and its MXFP4 form (scale_out).
+int swiglu_common(void *out, const void *gate_up, const float *scale, uint8_t *scale_out,
+                  int64_t tokens, int64_t inter, int epi, int variant, hipStream_t stream)
 {
+    const bool fp8 = epi == SWIGLU_EPI_FP8, mx = epi == SWIGLU_EPI_MXFP4;
     int st = check_width(tokens, inter, 0);
     if (st) return st;
+    if (mx && inter % 32 != 0) return AARMS_ERR_BAD_SHAPE;
     if (inter > AARMS_MAX_INTER) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (tokens > 0 && 2 * inter > AARMS_MAX_ELEMENTS / tokens) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (variant < -1 || variant >= swiglu_variant_count()) return AARMS_ERR_BAD_VARIANT;
     if (tokens == 0) return AARMS_OK;
-    if (!out || !gate_up || (quant && !scale)) return AARMS_ERR_NULL_POINTER;
-    if (!aligned(out, 16) || !aligned(gate_up, 16) || (quant && !aligned(scale, 4)))
+    if (!out || !gate_up || (fp8 && !scale) || (mx && !scale_out)) return AARMS_ERR_NULL_POINTER;
+    if (!aligned(out, 16) || !aligned(gate_up, 16) || (fp8 && !aligned(scale, 4)))
         return AARMS_ERR_MISALIGNED;
     const uint64_t elems = (uint64_t)tokens * (uint64_t)inter;
-    const Arg outs[1] = {{span(out, quant ? elems : 2 * elems), out}};
-    const Arg ins[2] = {{span(gate_up, 4 * elems), gate_up}, {span(scale, quant ? 4 : 0), scale}};
-    const int partner[1] = {-1};
-    if ((st = check_outputs(outs, partner, 1, ins, quant ? 2 : 1))) return st;
-    if (variant == -1) variant = pick_swiglu(tokens, inter, quant);
+    Arg outs[2];
+    int n_out = 0;
+    outs[n_out++] = {span(out, fp8 ? elems : mx ? elems / 2 : 2 * elems), out};
+    if (mx) outs[n_out++] = {span(scale_out, elems / 32), scale_out};
+    const Arg ins[2] = {{span(gate_up, 4 * elems), gate_up}, {span(scale, fp8 ? 4 : 0), scale}};
+    const int partner[2] = {-1, -1};
+    if ((st = check_outputs(outs, partner, n_out, ins, fp8 ? 2 : 1))) return st;
+    if (variant == -1) variant = pick_swiglu(tokens, inter, epi != SWIGLU_EPI_BF16);
     SwigluParams p;
     p.out = out;
     p.gate_up = gate_up;
-    p.scale = scale;
-    p.scale_out = nullptr;
+    p.scale = fp8 ? scale : nullptr;
+    p.scale_out = mx ? (float *)scale_out : nullptr;
     p.tokens = tokens;
     p.inter = inter;
     p.vecs_per_row = (uint32_t)(inter / 8);
-    return launch_status(launch_swiglu(p, quant, variant, stream));
+    return launch_status(launch_swiglu(p, epi, variant, stream));
 }
 
 int swiglu_rowq_common(void *out, float *scale_out, const void *gate_up, int64_t tokens,
@@ -395,25 +401,27 @@ int rmsnorm_quant_fp8_static_ex(void *out_fp8, const void *x, const void *weight
 
 int swiglu(void *out, const void *gate_up, int64_t num_tokens, int64_t inter, hipStream_t stream)
 {
-    return swiglu_common(out, gate_up, nullptr, num_tokens, inter, false, -1, stream);
+    return swiglu_common(out, gate_up, nullptr, nullptr, num_tokens, inter, SWIGLU_EPI_BF16, -1, stream);
 }
 
 int swiglu_ex(void *out, const void *gate_up, int64_t num_tokens, int64_t inter, int variant,
               hipStream_t stream)
 {
-    return swiglu_common(out, gate_up, nullptr, num_tokens, inter, false, variant, stream);
+    return swiglu_common(out, gate_up, nullptr, nullptr, num_tokens, inter, SWIGLU_EPI_BF16, variant,
+                         stream);
 }
 
 int swiglu_quant_fp8(void *out_fp8, const void *gate_up, const float *scale, int64_t num_tokens,
                      int64_t inter, hipStream_t stream)
 {
-    return swiglu_common(out_fp8, gate_up, scale, num_tokens, inter, true, -1, stream);
+    return swiglu_common(out_fp8, gate_up, scale, nullptr, num_tokens, inter, SWIGLU_EPI_FP8, -1, stream);
 }
 
 int swiglu_quant_fp8_ex(void *out_fp8, const void *gate_up, const float *scale,
                         int64_t num_tokens, int64_t inter, int variant, hipStream_t stream)
 {
-    return swiglu_common(out_fp8, gate_up, scale, num_tokens, inter, true, variant, stream);
+    return swiglu_common(out_fp8, gate_up, scale, nullptr, num_tokens, inter, SWIGLU_EPI_FP8, variant,
+                         stream);
 }
 
 int fused_add_rmsnorm_quant_mxfp4(void *out_fp4, uint8_t *scale_out, void *residual_out,
@@ -446,6 +454,20 @@ int rmsnorm_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, const void *x, con
 {
     return norm_common(out_fp4, (float *)scale_out, nullptr, nullptr, x, nullptr, weight, num_tokens,
                        hidden, eps, NORM_EPI_MXFP4, false, variant, stream);
+}
+
+int swiglu_quant_mxfp4(void *out_fp4, uint8_t *scale_out, const void *gate_up, int64_t num_tokens,
+                       int64_t inter, hipStream_t stream)
+{
+    return swiglu_common(out_fp4, gate_up, nullptr, scale_out, num_tokens, inter, SWIGLU_EPI_MXFP4, -1,
+                         stream);
+}
+
+int swiglu_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, const void *gate_up, int64_t num_tokens,
+                          int64_t inter, int variant, hipStream_t stream)
+{
+    return swiglu_common(out_fp4, gate_up, nullptr, scale_out, num_tokens, inter, SWIGLU_EPI_MXFP4,
+                         variant, stream);
 }
 
 int swiglu_quant_fp8_dynamic(void *out_fp8, float *scale_out, const void *gate_up,

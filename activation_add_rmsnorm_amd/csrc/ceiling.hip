@@ -17,6 +17,7 @@
 //                                       out0 = 16 (bf16) or 8 (E4M3)
 //   fused_add_rmsnorm_quant_mxfp4:      out0 = 16, out1 = 4 (E2M1 pairs; the
 //                                       E8M0 bytes, 1/32 of the data, left out)
+//   swiglu_quant_mxfp4:                 out0 = 4
 // (the weight and the scales, a few KB, are left out).
 
 #include <hip/hip_runtime.h>
@@ -63,7 +64,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 // Returns 0 on success, -1 for bad arguments (nothing launched), or the HIP
 // error code of the launch.  n is at most (2^31 - 1) * 256 vectors; out0_bytes is
-// 8 or 16, out1_bytes 0, 4, 8 or 16; inputs and 16-byte outputs 16-byte
+// 4, 8 or 16, out1_bytes 0, 4, 8 or 16; inputs and 16-byte outputs 16-byte
 // aligned, 8- and 4-byte outputs aligned to their size.  Buffers are the
 // caller's.
 extern "C" __attribute__((visibility("default"))) int aarms_stream_ceiling(void *out0, int out0_bytes, void *out1, int out1_bytes,
@@ -72,7 +73,8 @@ extern "C" __attribute__((visibility("default"))) int aarms_stream_ceiling(void 
     if (n < 0 || (uint64_t)n > (uint64_t)INT32_MAX * 256u) return -1;
     if (n == 0) return 0;
     if (!in0 || !in1 || !out0 || (out1_bytes && !out1)) return -1;
-    if (!aligned(in0, 16) || !aligned(in1, 16) || !aligned(out0, out0_bytes == 16 ? 16 : 8)) return -1;
+    if (!aligned(in0, 16) || !aligned(in1, 16) || out0_bytes <= 0 || !aligned(out0, (uintptr_t)out0_bytes))
+        return -1;
     if (out1_bytes && !aligned(out1, (uintptr_t)out1_bytes)) return -1;
     const uint64_t m = (uint64_t)n;
     hipError_t e;
@@ -81,6 +83,7 @@ extern "C" __attribute__((visibility("default"))) int aarms_stream_ceiling(void 
     else if (out0_bytes == 16 && out1_bytes == 4) e = launch<16, 4>(in0, in1, out0, out1, m, stream);
     else if (out0_bytes == 16 && out1_bytes == 0) e = launch<16, 0>(in0, in1, out0, out1, m, stream);
     else if (out0_bytes == 8 && out1_bytes == 0) e = launch<8, 0>(in0, in1, out0, out1, m, stream);
+    else if (out0_bytes == 4 && out1_bytes == 0) e = launch<4, 0>(in0, in1, out0, out1, m, stream);
     else return -1;
     return (int)e;
 }

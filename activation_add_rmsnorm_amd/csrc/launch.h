@@ -28,11 +28,18 @@ struct NormParams {
     float eps;
 };
 
+// SwiGLU epilogues (the per-token FP8 form has its own row kernel).
+enum SwigluEpilogue : int {
+    SWIGLU_EPI_BF16 = 0,
+    SWIGLU_EPI_FP8 = 1,       // static per-tensor E4M3, scale read from scale
+    SWIGLU_EPI_MXFP4 = 2,     // E2M1 codes, E8M0 scale per 32 outputs to scale_out
+};
+
 struct SwigluParams {
     void *out;               // bf16 [T,N], or fp8 [T,N] when quantising
     const void *gate_up;     // bf16 [T,2N]
     const float *scale;      // fp32 [1], static FP8 only
-    float *scale_out;        // fp32 [T], per-token FP8 only
+    float *scale_out;        // fp32 [T], per-token FP8; uint8 [T, N/32] for MXFP4
     int64_t tokens;          // T
     int64_t inter;           // N
     uint32_t vecs_per_row;   // N / 8: one job = 8 adjacent outputs of a row
@@ -74,7 +81,7 @@ hipError_t launch_norm(const NormParams &p, int epi, bool residual, int variant,
                        hipStream_t stream);
 int swiglu_row_variant_count();
 const SwigluRowVariant *swiglu_row_variant(int id);
-hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, hipStream_t stream);
+hipError_t launch_swiglu(const SwigluParams &p, int epi, int variant, hipStream_t stream);
 hipError_t launch_swiglu_rowq(const SwigluParams &p, int variant, hipStream_t stream);
 
 }  // namespace aarms

@@ -85,7 +85,20 @@ __device__ __forceinline__ typename Words<W>::T swiglu_job(typename Words<W>::T 
     return y;
 }
 
-// MODE 0: bf16 output; 1: E4M3 output, fast quotient; 2: E4M3, IEEE division.
+// MXFP4 block of 32 outputs = the jobs of 32 / (2W) adjacent lanes: the
+// block amax of magnitude bits over those lanes (DPP), its E8M0 byte, then
+// the E2M1 codes of this lane's 2W outputs (see device.h).
+template <int W>
+__device__ __forceinline__ uint32_t mx_block_max(uint32_t mag)
+{
+    mag = max(mag, dpp_u32<DPP_XOR1>(mag));
+    mag = max(mag, dpp_u32<DPP_XOR2>(mag));
+    if constexpr (W == 2) mag = max(mag, dpp_u32<DPP_HALF_MIRROR>(mag));
+    return mag;
+}
+
+// MODE 0: bf16 output; 1: E4M3 output, fast quotient; 2: E4M3, IEEE
+// division; 3: MXFP4 (codes to out, E8M0 block scales to scale_out).
 template <int U, int W, int MODE>
 __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Scale &qs)
 {
@@ -104,6 +117,38 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
         const bool ok = c < njobs;
         gv[u] = ok ? ld_stream(gate + c) : (V)0u;
         uv[u] = ok ? ld_stream(up + c) : (V)0u;
+    }
+    if constexpr (MODE == 3) {
+        // every lane takes part in the block maxima (slots past the row end
+        // hold zeros; N is a multiple of 32, so a block is all in or all out)
+        constexpr uint32_t LANES = 16 / W;       // lanes per 32-output block
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = c0 + 256u * u;
+            const V y = swiglu_job<W>(gv[u], uv[u]);
+            uint32_t mag = 0;
+#pragma unroll
+            for (int e = 0; e < W; ++e)
+                mag = max(mag, max((y[e] << 16) & 0x7FFFFFFFu, y[e] & 0x7FFF0000u));
+            mag = mx_block_max<W>(mag);
+            if (c >= njobs) continue;
+            const uint32_t sb = mx_scale_byte(mag);
+            const float inv = __uint_as_float((254u - (sb == 0xFFu ? 127u : sb)) << 23);
+            if constexpr (W == 4) {
+                const uint32_t w4[4] = {y[0], y[1], y[2], y[3]};
+                const uint32_t q = (sb == 0xFFu) ? 0u : pack_e2m1x8(w4, inv);
+                st_stream((uint32_t *)p.out + job0 + c, q);
+            } else {
+                uint32_t q = 0;
+                if (sb != 0xFFu) {
+                    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, bf_lo(y[0]) * inv, bf_hi(y[0]) * inv, 1.0f, 0);
+                    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, bf_lo(y[1]) * inv, bf_hi(y[1]) * inv, 1.0f, 1);
+                }
+                st_stream((uint16_t *)p.out + job0 + c, (uint16_t)q);
+            }
+            if (c % LANES == 0) ((uint8_t *)p.scale_out)[(job0 + c) / LANES] = (uint8_t)sb;
+        }
+        return;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -131,15 +176,17 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
     }
 }
 
-template <int U, int W, bool QUANT>
+template <int U, int W, int EPI>
 __global__ void __launch_bounds__(256) swiglu_kernel(SwigluParams p)
 {
-    if constexpr (QUANT) {
+    if constexpr (EPI == SWIGLU_EPI_FP8) {
         const E4m3Scale qs = make_e4m3_scale(*p.scale);
         if (e4m3_scale_is_fast(qs))
             swiglu_block<U, W, 1>(p, qs);
         else
             swiglu_block<U, W, 2>(p, qs);
+    } else if constexpr (EPI == SWIGLU_EPI_MXFP4) {
+        swiglu_block<U, W, 3>(p, E4m3Scale{});
     } else {
         swiglu_block<U, W, 0>(p, E4m3Scale{});
     }
@@ -285,7 +332,7 @@ const SwigluVariant *swiglu_variant(int id)
     return (id >= 0 && id < kNumSwigluVariants) ? &kSwigluVariants[id] : nullptr;
 }
 
-template <int U, int W, bool Q>
+template <int U, int W, int EPI>
 static hipError_t launch_one(const SwigluParams &p, hipStream_t stream)
 {
     const uint32_t per_block = 256u * U;
@@ -296,10 +343,10 @@ static hipError_t launch_one(const SwigluParams &p, hipStream_t stream)
                     (unsigned)((T + SWIGLU_ROWS_PER_Y - 1) / SWIGLU_ROWS_PER_Y));
     SwigluParams copy = p;
     void *args[] = {&copy};
-    return hipLaunchKernel((const void *)&swiglu_kernel<U, W, Q>, grid, dim3(256), args, 0, stream);
+    return hipLaunchKernel((const void *)&swiglu_kernel<U, W, EPI>, grid, dim3(256), args, 0, stream);
 }
 
-template <bool Q>
+template <int Q>
 static hipError_t dispatch(const SwigluParams &p, int variant, hipStream_t s)
 {
     const SwigluVariant *v = swiglu_variant(variant);
@@ -316,9 +363,14 @@ static hipError_t dispatch(const SwigluParams &p, int variant, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_swiglu(const SwigluParams &p, bool quant, int variant, hipStream_t stream)
+hipError_t launch_swiglu(const SwigluParams &p, int epi, int variant, hipStream_t stream)
 {
-    return quant ? dispatch<true>(p, variant, stream) : dispatch<false>(p, variant, stream);
+    switch (epi) {
+    case SWIGLU_EPI_BF16: return dispatch<SWIGLU_EPI_BF16>(p, variant, stream);
+    case SWIGLU_EPI_FP8: return dispatch<SWIGLU_EPI_FP8>(p, variant, stream);
+    case SWIGLU_EPI_MXFP4: return dispatch<SWIGLU_EPI_MXFP4>(p, variant, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace aarms

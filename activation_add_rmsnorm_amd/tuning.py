@@ -48,6 +48,7 @@ FORMS = {
     "swiglu": (A.OP_SWIGLU, False),
     "swiglu_quant_fp8": (A.OP_SWIGLU, True),
     "swiglu_quant_fp8_dynamic": (A.OP_SWIGLU_DYNAMIC, True),
+    "swiglu_quant_mxfp4": (A.OP_SWIGLU, True),
 }
 
 
@@ -98,9 +99,14 @@ def _buffers(form: str, tokens: int, width: int, device):
     f8 = dict(dtype=torch.uint8, device=device)
     if form.startswith("swiglu"):
         b = dict(gu=(torch.randn((T, 2 * W), device=device) * 2).to(torch.bfloat16))
-        b["y"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
-        b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
-        nbytes = T * W * 4 + T * W * (1 if "fp8" in form else 2)
+        if "mxfp4" in form:
+            b["y"] = torch.empty((T, W // 2), **f8)
+            b["s"] = torch.empty((T, W // 32), **f8)
+            nbytes = T * W * 4 + T * W // 2 + T * W // 32
+        else:
+            b["y"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
+            b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
+            nbytes = T * W * 4 + T * W * (1 if "fp8" in form else 2)
     else:
         b = dict(x=torch.randn((T, W), device=device).to(torch.bfloat16),
                  r=torch.randn((T, W), device=device).to(torch.bfloat16))
@@ -141,6 +147,8 @@ def _launcher(form: str, b: dict, w, scale, variant: int):
         return lambda: A.swiglu(b["gu"], out=b["y"], variant=variant)
     if form == "swiglu_quant_fp8":
         return lambda: A.swiglu_quant_fp8(b["gu"], scale, out=b["y"], variant=variant)
+    if form == "swiglu_quant_mxfp4":
+        return lambda: A.swiglu_quant_mxfp4(b["gu"], out=b["y"], scale_out=b["s"], variant=variant)
     if form == "swiglu_quant_fp8_dynamic":
         return lambda: A.swiglu_quant_fp8_dynamic(b["gu"], out=b["y"], scale_out=b["s"], variant=variant)
     raise ValueError(form)

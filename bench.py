@@ -428,7 +428,8 @@ def autotune_report():
               ("fused_add_rmsnorm_quant_fp8", 2048, 16384), ("swiglu_quant_fp8", 8192, 28672),
               ("rmsnorm", 4096, 1536), ("rmsnorm_quant_fp8", 2048, 16384),
               ("fused_add_rmsnorm_quant_fp8_static", 2048, 16384), ("swiglu_quant_fp8_dynamic", 8192, 28672),
-              ("fused_add_rmsnorm_quant_mxfp4", 2048, 16384)]
+              ("fused_add_rmsnorm_quant_mxfp4", 2048, 16384), ("swiglu_quant_mxfp4", 8192, 28672),
+              ("swiglu_quant_mxfp4", 1, 8960)]
     rows = []
     for form, T, W in shapes:
         r = tuning.tune(form, T, W, rounds=3)
@@ -524,6 +525,16 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
     ns = rotation_sets(nb)
     sets = [(gu if i == 0 else gu.clone(), torch.empty((T, N), dtype=torch.uint8, device=dev),
              torch.empty((T,), dtype=torch.float32, device=dev)) for i in range(ns)]
+    mx_sets = [(torch.empty((T, N // 2), dtype=torch.uint8, device=dev),
+                torch.empty((T, N // 32), dtype=torch.uint8, device=dev)) for _ in range(ns)]
+    measure("llama70b_swiglu_mxfp4_8192x57344",
+            lambda i: check(lib.swiglu_quant_mxfp4(mx_sets[i % ns][0].data_ptr(), mx_sets[i % ns][1].data_ptr(),
+                                                   sets[i % ns][0].data_ptr(), T, N, sp), "swiglu_quant_mxfp4"),
+            lambda i: stream(mx_sets[i % ns][0].data_ptr(), 4, None, 0, sets[i % ns][0].data_ptr(),
+                             sets[i % ns][0].data_ptr() + T * N * 2, T * N // 8),
+            T * 2 * N * 2 + T * N // 2 + T * N // 32,
+            {"inputs": "torch.randn on device, seed 0, std 2", "buffer_sets_rotated": ns})
+    del mx_sets
     measure("llama70b_swiglu_fp8_dynamic_8192x57344",
             lambda i: check(lib.swiglu_quant_fp8_dynamic(sets[i % ns][1].data_ptr(), sets[i % ns][2].data_ptr(),
                                                          sets[i % ns][0].data_ptr(), T, N, sp),

@@ -223,6 +223,20 @@ int swiglu_quant_fp8(void *out_fp8, const void *gate_up, const float *scale,
                      int64_t num_tokens, int64_t inter, hipStream_t stream);
 
 /*
+ * swiglu_quant_mxfp4 -- swiglu whose bf16 output is written as OCP MXFP4 in
+ * the same pass, with the block rules of the MXFP4 norms above (blocks of 32
+ * along a row).
+ *
+ *   out_fp4   [num_tokens, inter / 2]  uint8  written: two E2M1 codes per byte
+ *   scale_out [num_tokens, inter / 32] uint8  written: E8M0 block scales
+ *   gate_up   [num_tokens, 2 * inter]  bf16   read, as for swiglu
+ *   inter     multiple of 32, at most AARMS_MAX_INTER
+ * No in-place form.
+ */
+int swiglu_quant_mxfp4(void *out_fp4, uint8_t *scale_out, const void *gate_up,
+                       int64_t num_tokens, int64_t inter, hipStream_t stream);
+
+/*
  * swiglu_quant_fp8_dynamic -- swiglu whose bf16 output is quantised to E4M3
  * with a dynamic per-token scale, in the same pass (vLLM's SiLU-and-mul +
  * quant fusion, sections 3 and 4 of its post, with per-token scaling as in
@@ -248,8 +262,9 @@ const char *aarms_status_string(int status);
  * aarms_variant_name() describes it (static storage) and returns NULL past
  * the end.  ops: 0 = the norms with the residual add (fused_add_rmsnorm*),
  * 3 = the norms without it (rmsnorm*), both on one variant table (quant != 0
- * for an E4M3 form); 1 = swiglu and swiglu_quant_fp8 (quant != 0 selects
- * the FP8 form); 2 = swiglu_quant_fp8_dynamic.
+ * for an E4M3 or MXFP4 form); 1 = swiglu, swiglu_quant_fp8 and
+ * swiglu_quant_mxfp4 (quant != 0 for the quantised forms); 2 =
+ * swiglu_quant_fp8_dynamic.
  * aarms_pick_variant() returns the id the plain entry point would use, or -1
  * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
  */
@@ -283,6 +298,8 @@ int rmsnorm_quant_fp8_static_ex(void *out_fp8, const void *x, const void *weight
                                 int variant, hipStream_t stream);
 int swiglu_quant_fp8_dynamic_ex(void *out_fp8, float *scale_out, const void *gate_up,
                                 int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
+int swiglu_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, const void *gate_up,
+                          int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
 int fused_add_rmsnorm_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, void *residual_out,
                                      const void *x, const void *residual, const void *weight,
                                      int64_t num_tokens, int64_t hidden, float eps, int variant,

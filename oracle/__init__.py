@@ -353,5 +353,12 @@ def set_threads(n: int) -> None:
     _lib().aarms_oracle_set_threads(int(n))
 
 
+def swiglu_quant_mxfp4(gate_up):
+    """SwiGLU, its bf16 output in MXFP4.  Returns (q, s, y)."""
+    y = swiglu(gate_up)
+    q, s = quant_mxfp4(y)
+    return q, s, y
+
+
 def num_threads() -> int:
     return int(_lib().aarms_oracle_num_threads())

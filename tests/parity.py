@@ -272,3 +272,15 @@ def check_norm_mxfp4(x, residual, weight, eps, q_gpu, s_gpu, res_out_gpu) -> Nor
 def check_rmsnorm_mxfp4(x, weight, eps, q_gpu, s_gpu) -> NormReport:
     q_o, s_o, _, _ = oracle.rmsnorm_quant_mxfp4(x, weight, eps)
     return _check_mx_codes(x, weight, eps, q_gpu, s_gpu, q_o, s_o)
+
+
+def check_swiglu_mxfp4(gate_up, q_gpu, s_gpu):
+    """MXFP4 SwiGLU: the SwiGLU output has no knife-edges, so scales and codes
+    must be bit-exact."""
+    q_o, s_o, _ = oracle.swiglu_quant_mxfp4(gate_up)
+    bad_s = s_gpu != s_o
+    assert not bad_s.any(), "block scales differ at %d blocks, first %s: gpu %s oracle %s" % (
+        bad_s.sum(), np.argwhere(bad_s)[:5].tolist(), s_gpu[bad_s][:5], s_o[bad_s][:5])
+    bad = q_gpu != q_o
+    assert not bad.any(), "codes differ at %d bytes, first %s: gpu %s oracle %s" % (
+        bad.sum(), np.argwhere(bad)[:5].tolist(), q_gpu[bad][:5], q_o[bad][:5])

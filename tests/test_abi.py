@@ -342,3 +342,18 @@ def test_mxfp4_norm_errors():
     assert mx(T=0, out=0, s=0, ro=0, x=0, r=0, w=0) == OK
     assert lib.rmsnorm_quant_mxfp4_ex(P, P + BIG, P + 2 * BIG, P + 3 * BIG, 4, 40, 1e-6, -1, None) == SHAPE
     assert lib.rmsnorm_quant_mxfp4_ex(P, P + BIG, P + 2 * BIG, P + 3 * BIG, 4, 1536, 1e-6, 0, None) == VARIANT
+
+
+def test_swiglu_mxfp4_errors():
+    lib = A.load()
+
+    def smx(out=P, s=P + BIG + 3, gu=P + 2 * BIG, T=4, N=8960, variant=-1):
+        return lib.swiglu_quant_mxfp4_ex(out, s, gu, T, N, variant, None)
+
+    assert smx(N=8968) == SHAPE                          # a multiple of 8, not of 32
+    assert smx(s=0) == NULLP
+    assert smx(out=P + 8) == MISAL
+    assert smx(s=P + 64) == ALIAS                        # scales inside the codes
+    assert smx(out=P + 2 * BIG) == ALIAS
+    assert smx(variant=A.variant_count(A.OP_SWIGLU)) == VARIANT
+    assert smx(T=0, out=0, s=0, gu=0) == OK

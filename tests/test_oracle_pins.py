@@ -619,6 +619,11 @@ def test_mxfp4_norm_is_composition():
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
     q3, s3, y3, _ = oracle.rmsnorm_quant_mxfp4(x, w, 1e-5)
     assert np.array_equal(y3, oracle.rmsnorm(x, w, 1e-5)[0])
+    gu = gen.normal_bf16((8, 2 * 1024), 16, 4, std=2.0)
+    q4, s4, y4 = oracle.swiglu_quant_mxfp4(gu)
+    assert np.array_equal(y4, oracle.swiglu(gu))
+    q5, s5 = oracle.quant_mxfp4(y4)
+    assert np.array_equal(q4, q5) and np.array_equal(s4, s5)
 
 
 # ------------------------------------------------------------------ the pages' shapes

@@ -362,3 +362,45 @@ def test_quant_matrix_forms_under_graph_replay():
         xt.add_(0)                                     # eager work between replays
     P.check_rmsnorm(x, w, 1e-5, bits(outs["rms"]))
     P.check_norm_mxfp4(x, r, w, 1e-5, bits(outs["mq"]), bits(outs["ms"]), bits(outs["mro"]))
+
+
+# ------------------------------------------------------------------ MXFP4 swiglu
+
+def run_swiglu_mx(gu, variant=-1):
+    announce("swiglu_quant_mxfp4", gu.shape, "variant", variant)
+    q, s = A.swiglu_quant_mxfp4(bf16(gu), variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s)
+
+
+@pytest.mark.parametrize("T,N", [(1, 32), (3, 96), (5, 1056), (64, 8960), (300, 8960), (7, 28672)])
+def test_swiglu_mxfp4_shapes_every_variant(T, N):
+    gu = gen.normal_bf16((T, 2 * N), T + 7 * N, 4, std=2.0)
+    for v in [-1] + list(range(A.variant_count(A.OP_SWIGLU))):
+        q, s = run_swiglu_mx(gu, v)
+        P.check_swiglu_mxfp4(gu, q, s)
+
+
+def test_swiglu_mxfp4_special_blocks_and_every_y():
+    N = 65536
+    u = np.arange(N, dtype=np.uint16)
+    finite = (u & 0x7F80) != 0x7F80
+    rows = []
+    for hi_exp in (0x3F80, 0x4700, 0x1000):            # y = 8u over several binade ranges
+        uu = np.where(finite & ((u & 0x7F80) <= hi_exp), u, u & 0x807F)
+        rows.append(np.concatenate([np.full(N, oracle.bf16_from_f64(8.0), np.uint16), uu]))
+    gu = np.stack(rows + [rows[0].copy(), rows[0].copy()])
+    gu[3, 40] = 0x7FC0                                 # NaN gate: its block gets 0xFF
+    gu[4, N + 70] = 0x7F80                             # infinite up
+    gu[4, :32] = 0                                     # a zero block
+    for v in (-1, 0, 3):
+        q, s = run_swiglu_mx(gu, v)
+        P.check_swiglu_mxfp4(gu, q, s)
+        assert s[3, 1] == 0xFF and s[4, 2] == 0xFF
+
+
+def test_swiglu_mxfp4_llama70b_full():
+    wl = W.SWIGLU_FP8_LLAMA70B
+    gu = W.swiglu_inputs(wl)["gate_up"]
+    q, s = run_swiglu_mx(gu)
+    P.check_swiglu_mxfp4(gu, q, s)
