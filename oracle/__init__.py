@@ -73,6 +73,7 @@ def _lib():
                 "aarms_oracle_e2m1_to_f64": (f64, [C.c_uint8]),
                 "aarms_oracle_e8m0_to_f64": (f64, [C.c_uint8]),
                 "aarms_oracle_quant_mxfp4": (None, [u16p, i64, i64, u8p, u8p]),
+                "aarms_oracle_quant_nvfp4": (None, [u16p, i64, i64, f32, u8p, u8p]),
                 "aarms_oracle_num_threads": (C.c_int, []),
                 "aarms_oracle_set_threads": (None, [C.c_int]),
             }
@@ -286,6 +287,44 @@ def mxfp4_decode(q, s) -> np.ndarray:
     return el * np.repeat(sc, 32, axis=1)
 
 
+def quant_nvfp4(y, tensor_scale: float):
+    """NVFP4 of each row (width a multiple of 16) under the fp32 tensor scale.
+    Returns (q [T, H/2] uint8, two codes per byte with the first in the low
+    nibble; s [T, H/16] uint8 E4M3 block scales)."""
+    y = _u16(y)
+    T, H = _rows(y)
+    if H % 16:
+        raise ValueError("width must be a multiple of 16")
+    q = np.empty((T, H // 2), np.uint8)
+    s = np.empty((T, H // 16), np.uint8)
+    _lib().aarms_oracle_quant_nvfp4(y, T, H, float(np.float32(tensor_scale)), q, s)
+    return q, s
+
+
+def nvfp4_decode(q, s, tensor_scale: float) -> np.ndarray:
+    """float64 values of NVFP4 codes q [T, H/2], block scales s [T, H/16]."""
+    q, s = np.asarray(q, np.uint8), np.asarray(s, np.uint8)
+    tab = e2m1_table()
+    el = np.stack([tab[q & 0xF], tab[q >> 4]], axis=-1).reshape(q.shape[0], -1)
+    g = float(np.float32(tensor_scale)) or 1.0
+    sc = e4m3_table()[s] * g
+    return el * np.repeat(sc, 16, axis=1)
+
+
+def fused_add_rmsnorm_quant_nvfp4(x, residual, weight, eps: float, tensor_scale: float):
+    """The norm, its bf16 output in NVFP4.  Returns (q, s, residual_out, y, rs)."""
+    out, res_out, rs = fused_add_rmsnorm(x, residual, weight, eps)
+    q, s = quant_nvfp4(out, tensor_scale)
+    return q, s, res_out, out, rs
+
+
+def rmsnorm_quant_nvfp4(x, weight, eps: float, tensor_scale: float):
+    """RMSNorm (no residual add), its bf16 output in NVFP4.  Returns (q, s, y, rs)."""
+    out, rs = rmsnorm(x, weight, eps)
+    q, s = quant_nvfp4(out, tensor_scale)
+    return q, s, out, rs
+
+
 def fused_add_rmsnorm_quant_mxfp4(x, residual, weight, eps: float):
     """The norm, its bf16 output in MXFP4.  Returns (q, s, residual_out, y, rs)."""
     out, res_out, rs = fused_add_rmsnorm(x, residual, weight, eps)
@@ -357,6 +396,13 @@ def swiglu_quant_mxfp4(gate_up):
     """SwiGLU, its bf16 output in MXFP4.  Returns (q, s, y)."""
     y = swiglu(gate_up)
     q, s = quant_mxfp4(y)
+    return q, s, y
+
+
+def swiglu_quant_nvfp4(gate_up, tensor_scale: float):
+    """SwiGLU, its bf16 output in NVFP4.  Returns (q, s, y)."""
+    y = swiglu(gate_up)
+    q, s = quant_nvfp4(y, tensor_scale)
     return q, s, y
 
 

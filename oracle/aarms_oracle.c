@@ -52,6 +52,15 @@
  * exponent of E2M1's largest power of two), clamped to E8M0's range; each
  * element is v / 2^exponent rounded to nearest even on the E2M1 grid and
  * saturated at +-6.  Two elements per byte, the first in the low nibble.
+ *
+ * NVFP4 (same walkthrough: E2M1 elements in 16-value blocks sharing an E4M3
+ * scale, one FP32 scale per tensor on top) with the tensor scale g given:
+ * the block scale is E4M3(binary32(amax / binary32(6 g))), rounded to
+ * nearest even and saturated at 448, so the block's largest value lands at
+ * E2M1's largest, 6; each element is E2M1(binary32(v / S)) with
+ * S = binary32(scale * g), and a signed zero when S is zero.  g = 0 is
+ * treated as 1; a block holding a NaN or an infinity gets the E4M3 NaN
+ * 0x7F and zero codes.
  */
 
 #include <math.h>
@@ -350,6 +359,49 @@ void aarms_oracle_quant_mxfp4(const uint16_t *y, int64_t T, int64_t H, uint8_t *
                 double v0 = ldexp((double)aarms_oracle_bf16_to_f32(yb[2 * i]), -x);
                 double v1 = ldexp((double)aarms_oracle_bf16_to_f32(yb[2 * i + 1]), -x);
                 qb[i] = (uint8_t)(aarms_oracle_e2m1_from_f64(v0) | (aarms_oracle_e2m1_from_f64(v1) << 4));
+            }
+        }
+    }
+}
+
+/* NVFP4: each row of H values (H a multiple of 16) in blocks of 16, one E4M3
+ * scale byte per block, two E2M1 codes per byte (first in the low nibble),
+ * under the tensor scale g. */
+void aarms_oracle_quant_nvfp4(const uint16_t *y, int64_t T, int64_t H, float g, uint8_t *q, uint8_t *s)
+{
+    const int64_t nb = H / 16;
+    const float gg = (g == 0.0f) ? 1.0f : g;
+    const float six_g = 6.0f * gg;                     /* binary32 product */
+    #pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < T; ++row) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t *yb = y + row * H + b * 16;
+            float amax = 0.0f;
+            int bad = 0;
+            for (int i = 0; i < 16; ++i) {
+                float v = aarms_oracle_bf16_to_f32(yb[i]);
+                if (!isfinite(v)) bad = 1;
+                else if (fabsf(v) > amax) amax = fabsf(v);
+            }
+            uint8_t *qb = q + row * (H / 2) + b * 8;
+            if (bad) {
+                s[row * nb + b] = 0x7Fu;
+                for (int i = 0; i < 8; ++i) qb[i] = 0;
+                continue;
+            }
+            float t = amax / six_g;                      /* binary32 quotient */
+            if (t > 448.0f) t = 448.0f;
+            const uint8_t sb = aarms_oracle_e4m3_from_f64((double)t);
+            s[row * nb + b] = sb;
+            const float S = (float)aarms_oracle_e4m3_to_f64(sb) * gg;   /* binary32 product */
+            for (int i = 0; i < 8; ++i) {
+                uint8_t c[2];
+                for (int h = 0; h < 2; ++h) {
+                    const float v = aarms_oracle_bf16_to_f32(yb[2 * i + h]);
+                    const float z = (S == 0.0f) ? v * 0.0f : v / S;         /* binary32 quotient */
+                    c[h] = aarms_oracle_e2m1_from_f64((double)z);
+                }
+                qb[i] = (uint8_t)(c[0] | (c[1] << 4));
             }
         }
     }

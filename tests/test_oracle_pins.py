@@ -626,6 +626,66 @@ def test_mxfp4_norm_is_composition():
     assert np.array_equal(q4, q5) and np.array_equal(s4, s5)
 
 
+# ------------------------------------------------------------------ NVFP4
+
+@pytest.mark.parametrize("g", [0.01, 1.0, 3.0e-4, 0.0])
+def test_nvfp4_scales_and_elements_vs_numpy_and_exact(g):
+    """Block scale: the E4M3 nearest (exact rationals) to numpy's binary32
+    amax / (6 g), saturated at 448; elements: brute-force E2M1 of numpy's
+    binary32 v / (scale * g).  g = 0 behaves as 1."""
+    rng = np.random.default_rng(11)
+    rows = [gen.bf16_bits_from_f32((rng.standard_normal(128) * 2.0 ** k).astype(np.float32)) for k in (-12, 0, 6)]
+    y = np.stack(rows)
+    y[1, 16:32] = 0                                 # a zero block: scale 0, signed-zero codes
+    q, s = oracle.quant_nvfp4(y, g)
+    gg = np.float32(g) if g else np.float32(1.0)
+    six_g = np.float32(6.0) * gg
+    yf = f32_of(y).reshape(len(rows), -1, 16)
+    e4m3 = oracle.e4m3_table()
+    for r in range(len(rows)):
+        for b in range(yf.shape[1]):
+            amax = np.float32(np.abs(yf[r, b]).max())
+            t = np.float32(amax / six_g)
+            t = min(t, np.float32(448.0))
+            assert s[r, b] == exact.round_to_e4m3(Fraction(float(t))), (r, b)
+            S = np.float32(np.float32(e4m3[s[r, b]]) * gg)
+            for i in range(16):
+                v = np.float32(yf[r, b, i])
+                z = np.float32(v * np.float32(0.0)) if S == 0 else np.float32(v / S)
+                code = (q[r, b * 8 + i // 2] >> (4 * (i % 2))) & 0xF
+                assert code == _e2m1_brute(float(z)), (r, b, i)
+    assert s[1, 1] == 0 and np.all((q[1, 8:16] & 0x77) == 0)
+
+
+def test_nvfp4_special_blocks_and_composition():
+    one = oracle.bf16_from_f64
+    y = np.zeros((2, 64), np.uint16)
+    y[0, 3] = 0x7FC0                                # NaN block
+    y[1, 20] = 0xFF80                               # -inf block
+    y[1, 40] = one(600.0)                           # amax / (6 g) beyond 448: saturated scale
+    q, s = oracle.quant_nvfp4(y, 0.1)
+    assert s[0, 0] == 0x7F and np.all(q[0, :8] == 0)
+    assert s[1, 1] == 0x7F and s[1, 2] == 0x7E
+    assert (q[1, 20] & 0xF) == 0x7                  # 600 / (448 * 0.1) > 6: saturates at 6
+    x = gen.normal_bf16((8, 1024), 17, 1)
+    r = gen.normal_bf16((8, 1024), 17, 2)
+    w = gen.normal_bf16((1024,), 17, 3, mean=1.0, std=0.1)
+    q1, s1, ro, yy, _ = oracle.fused_add_rmsnorm_quant_nvfp4(x, r, w, 1e-5, 0.02)
+    assert np.array_equal(yy, _norm(x, r, w, 1e-5)[0])
+    q2, s2 = oracle.quant_nvfp4(yy, 0.02)
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    gu = gen.normal_bf16((4, 2 * 512), 17, 4, std=2.0)
+    q3, s3, y3 = oracle.swiglu_quant_nvfp4(gu, 0.05)
+    assert np.array_equal(y3, oracle.swiglu(gu))
+    dec = oracle.nvfp4_decode(q3, s3, 0.05)
+    yf = f32_of(y3).astype(np.float64)
+    # a block's largest value is represented within one E2M1 step of its scale
+    blk = np.abs(yf).reshape(4, -1, 16).max(axis=2)
+    db = np.abs(dec).reshape(4, -1, 16).max(axis=2)
+    sc = oracle.e4m3_table()[s3] * 0.05
+    assert np.all(np.abs(db - blk) <= 2 * sc + 1e-12)
+
+
 # ------------------------------------------------------------------ the pages' shapes
 
 def test_golden_workload_shapes_from_pages():
