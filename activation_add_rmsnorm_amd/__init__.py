@@ -23,6 +23,7 @@ __all__ = [
     "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_static",
     "rmsnorm", "rmsnorm_quant_fp8", "rmsnorm_quant_fp8_static",
     "fused_add_rmsnorm_quant_mxfp4", "rmsnorm_quant_mxfp4",
+    "fused_add_rmsnorm_quant_nvfp4", "rmsnorm_quant_nvfp4", "swiglu_quant_nvfp4",
     "swiglu", "swiglu_quant_fp8", "swiglu_quant_fp8_dynamic", "swiglu_quant_mxfp4",
     "variant_count", "variant_name", "pick_variant",
     "OP_NORM", "OP_SWIGLU", "OP_SWIGLU_DYNAMIC", "OP_RMSNORM",
@@ -90,6 +91,12 @@ def load():
             "rmsnorm_quant_fp8": [vp, vp, vp, vp, i64, i64, f32, vp],
             "rmsnorm_quant_fp8_static": [vp, vp, vp, vp, i64, i64, f32, vp],
             "swiglu_quant_fp8_dynamic": [vp, vp, vp, i64, i64, vp],
+            "swiglu_quant_nvfp4": [vp, vp, vp, vp, i64, i64, vp],
+            "swiglu_quant_nvfp4_ex": [vp, vp, vp, vp, i64, i64, i32, vp],
+            "fused_add_rmsnorm_quant_nvfp4": [vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
+            "fused_add_rmsnorm_quant_nvfp4_ex": [vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "rmsnorm_quant_nvfp4": [vp, vp, vp, vp, vp, i64, i64, f32, vp],
+            "rmsnorm_quant_nvfp4_ex": [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
             "swiglu_quant_mxfp4": [vp, vp, vp, i64, i64, vp],
             "swiglu_quant_mxfp4_ex": [vp, vp, vp, i64, i64, i32, vp],
             "fused_add_rmsnorm_quant_mxfp4": [vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
@@ -363,6 +370,68 @@ def rmsnorm_quant_mxfp4(x: torch.Tensor, weight: torch.Tensor, eps: float,
     return out, scale_out
 
 
+def _nv_outputs(T, H, device, out, scale_out):
+    if H % 16:
+        raise ValueError("the row width must be a multiple of 16 for NVFP4")
+    if out is None:
+        out = torch.empty((T, H // 2), dtype=torch.uint8, device=device)
+    if scale_out is None:
+        scale_out = torch.empty((T, H // 16), dtype=torch.uint8, device=device)
+    _require(out, "out", (torch.uint8,), (T, H // 2))
+    _require(scale_out, "scale_out", (torch.uint8, torch.float8_e4m3fn), (T, H // 16))
+    return out, scale_out
+
+
+def fused_add_rmsnorm_quant_nvfp4(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor,
+                                  tensor_scale: torch.Tensor, eps: float, out: torch.Tensor | None = None,
+                                  scale_out: torch.Tensor | None = None,
+                                  residual_out: torch.Tensor | None = None, variant: int = -1):
+    """fused_add_rmsnorm with an NVFP4 epilogue under the 1-element fp32 GPU
+    tensor scale.  Returns (q [T, H/2] uint8, scale [T, H/16] E4M3 bytes,
+    residual_out)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(residual, "residual", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    _require(tensor_scale, "tensor_scale", (torch.float32,), (1,))
+    out, scale_out = _nv_outputs(T, H, x.device, out, scale_out)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _require(residual_out, "residual_out", (torch.bfloat16,), (T, H))
+    _same_device(x, residual, weight, tensor_scale, out, scale_out, residual_out)
+    lib = load()
+    variant = _variant("fused_add_rmsnorm_quant_nvfp4", T, H, variant)
+    _check(lib.fused_add_rmsnorm_quant_nvfp4_ex(out.data_ptr(), scale_out.data_ptr(),
+                                                residual_out.data_ptr(), x.data_ptr(),
+                                                residual.data_ptr(), weight.data_ptr(),
+                                                tensor_scale.data_ptr(), T, H, float(eps),
+                                                int(variant), _stream(x.device)),
+           "fused_add_rmsnorm_quant_nvfp4")
+    return out, scale_out, residual_out
+
+
+def rmsnorm_quant_nvfp4(x: torch.Tensor, weight: torch.Tensor, tensor_scale: torch.Tensor, eps: float,
+                        out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
+                        variant: int = -1):
+    """rmsnorm with an NVFP4 epilogue.  Returns (q [T, H/2], scale [T, H/16])."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    _require(tensor_scale, "tensor_scale", (torch.float32,), (1,))
+    out, scale_out = _nv_outputs(T, H, x.device, out, scale_out)
+    _same_device(x, weight, tensor_scale, out, scale_out)
+    lib = load()
+    variant = _variant("rmsnorm_quant_nvfp4", T, H, variant)
+    _check(lib.rmsnorm_quant_nvfp4_ex(out.data_ptr(), scale_out.data_ptr(), x.data_ptr(),
+                                      weight.data_ptr(), tensor_scale.data_ptr(), T, H, float(eps),
+                                      int(variant), _stream(x.device)), "rmsnorm_quant_nvfp4")
+    return out, scale_out
+
+
 def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None, variant: int = -1):
     """silu(gate) * up with gate_up = [gate | up] of shape [T, 2N]; returns bf16 [T, N]."""
     if gate_up.dim() != 2 or gate_up.shape[1] % 2:
@@ -437,6 +506,24 @@ def swiglu_quant_mxfp4(gate_up: torch.Tensor, out: torch.Tensor | None = None,
     variant = _variant("swiglu_quant_mxfp4", T, N, variant)
     _check(lib.swiglu_quant_mxfp4_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(), T, N,
                                      int(variant), _stream(gate_up.device)), "swiglu_quant_mxfp4")
+    return out, scale_out
+
+
+def swiglu_quant_nvfp4(gate_up: torch.Tensor, tensor_scale: torch.Tensor, out: torch.Tensor | None = None,
+                       scale_out: torch.Tensor | None = None, variant: int = -1):
+    """swiglu with an NVFP4 epilogue.  Returns (q [T, N/2] uint8, scale [T, N/16])."""
+    if gate_up.dim() != 2 or gate_up.shape[1] % 2:
+        raise ValueError("gate_up must be [tokens, 2 * inter]")
+    T, N = gate_up.shape[0], gate_up.shape[1] // 2
+    _require(gate_up, "gate_up", (torch.bfloat16,), (T, 2 * N))
+    _require(tensor_scale, "tensor_scale", (torch.float32,), (1,))
+    out, scale_out = _nv_outputs(T, N, gate_up.device, out, scale_out)
+    _same_device(gate_up, tensor_scale, out, scale_out)
+    lib = load()
+    variant = _variant("swiglu_quant_nvfp4", T, N, variant)
+    _check(lib.swiglu_quant_nvfp4_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(),
+                                     tensor_scale.data_ptr(), T, N, int(variant), _stream(gate_up.device)),
+           "swiglu_quant_nvfp4")
     return out, scale_out
 
 

@@ -180,19 +180,20 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
                 int64_t hidden, float eps, int epi, bool res, int variant, hipStream_t stream)
 {
     const bool dyn = epi == NORM_EPI_FP8_DYNAMIC, stat = epi == NORM_EPI_FP8_STATIC;
-    const bool mx = epi == NORM_EPI_MXFP4;
+    const bool mx = epi == NORM_EPI_MXFP4, nv = epi == NORM_EPI_NVFP4;
+    const bool fp4 = mx || nv;
     int st = check_width(tokens, hidden, AARMS_MAX_HIDDEN);
     if (st) return st;
-    if (mx && hidden % 32 != 0) return AARMS_ERR_BAD_SHAPE;
+    if ((mx && hidden % 32 != 0) || (nv && hidden % 16 != 0)) return AARMS_ERR_BAD_SHAPE;
     if ((st = check_eps(eps))) return st;
     if (variant < -1 || variant >= norm_variant_count()) return AARMS_ERR_BAD_VARIANT;
     if (tokens == 0) return AARMS_OK;
-    if (!out || !x || !weight || (res && (!residual_out || !residual)) || ((dyn || mx) && !scale_out) ||
-        (stat && !scale_in))
+    if (!out || !x || !weight || (res && (!residual_out || !residual)) || ((dyn || fp4) && !scale_out) ||
+        ((stat || nv) && !scale_in))
         return AARMS_ERR_NULL_POINTER;
     if (!aligned(out, 16) || !aligned(x, 16) || !aligned(weight, 16) ||
         (res && (!aligned(residual_out, 16) || !aligned(residual, 16))) ||
-        (dyn && !aligned(scale_out, 4)) || (stat && !aligned(scale_in, 4)))
+        (dyn && !aligned(scale_out, 4)) || ((stat || nv) && !aligned(scale_in, 4)))
         return AARMS_ERR_MISALIGNED;
     const uint64_t elems = (uint64_t)tokens * (uint64_t)hidden;
     // inputs: x, weight, then residual and scale_in when present
@@ -202,21 +203,21 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     ins[n_in++] = {span(weight, 2 * (uint64_t)hidden), weight};
     const int res_idx = res ? n_in : -1;
     if (res) ins[n_in++] = {span(residual, 2 * elems), residual};
-    if (stat) ins[n_in++] = {span(scale_in, 4), scale_in};
+    if (stat || nv) ins[n_in++] = {span(scale_in, 4), scale_in};
     // outputs: out (may be x itself in the bf16 form), residual_out (may be
     // the residual itself), scale_out
     Arg outs[3];
     int partner[3];
     int n_out = 0;
     partner[n_out] = (epi == NORM_EPI_BF16) ? 0 : -1;
-    outs[n_out++] = {span(out, epi == NORM_EPI_BF16 ? 2 * elems : mx ? elems / 2 : elems), out};
+    outs[n_out++] = {span(out, epi == NORM_EPI_BF16 ? 2 * elems : fp4 ? elems / 2 : elems), out};
     if (res) {
         partner[n_out] = res_idx;
         outs[n_out++] = {span(residual_out, 2 * elems), residual_out};
     }
-    if (dyn || mx) {
+    if (dyn || fp4) {
         partner[n_out] = -1;
-        outs[n_out++] = {span(scale_out, mx ? elems / 32 : 4 * (uint64_t)tokens), scale_out};
+        outs[n_out++] = {span(scale_out, mx ? elems / 32 : nv ? elems / 16 : 4 * (uint64_t)tokens), scale_out};
     }
     if ((st = check_outputs(outs, partner, n_out, ins, n_in))) return st;
     if (variant == -1) variant = pick_norm(tokens, hidden, epi != NORM_EPI_BF16, res);
@@ -228,8 +229,8 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     p.x = x;
     p.residual = res ? residual : nullptr;
     p.weight = weight;
-    p.scale_out = (dyn || mx) ? scale_out : nullptr;
-    p.scale_in = stat ? scale_in : nullptr;
+    p.scale_out = (dyn || fp4) ? scale_out : nullptr;
+    p.scale_in = (stat || nv) ? scale_in : nullptr;
     p.tokens = tokens;
     p.hidden = (int32_t)hidden;
     p.eps = eps;
@@ -240,31 +241,32 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
 int swiglu_common(void *out, const void *gate_up, const float *scale, uint8_t *scale_out,
                   int64_t tokens, int64_t inter, int epi, int variant, hipStream_t stream)
 {
-    const bool fp8 = epi == SWIGLU_EPI_FP8, mx = epi == SWIGLU_EPI_MXFP4;
+    const bool fp8 = epi == SWIGLU_EPI_FP8, mx = epi == SWIGLU_EPI_MXFP4, nv = epi == SWIGLU_EPI_NVFP4;
+    const bool with_scale = fp8 || nv, fp4 = mx || nv;
     int st = check_width(tokens, inter, 0);
     if (st) return st;
-    if (mx && inter % 32 != 0) return AARMS_ERR_BAD_SHAPE;
+    if ((mx && inter % 32 != 0) || (nv && inter % 16 != 0)) return AARMS_ERR_BAD_SHAPE;
     if (inter > AARMS_MAX_INTER) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (tokens > 0 && 2 * inter > AARMS_MAX_ELEMENTS / tokens) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (variant < -1 || variant >= swiglu_variant_count()) return AARMS_ERR_BAD_VARIANT;
     if (tokens == 0) return AARMS_OK;
-    if (!out || !gate_up || (fp8 && !scale) || (mx && !scale_out)) return AARMS_ERR_NULL_POINTER;
-    if (!aligned(out, 16) || !aligned(gate_up, 16) || (fp8 && !aligned(scale, 4)))
+    if (!out || !gate_up || (with_scale && !scale) || (fp4 && !scale_out)) return AARMS_ERR_NULL_POINTER;
+    if (!aligned(out, 16) || !aligned(gate_up, 16) || (with_scale && !aligned(scale, 4)))
         return AARMS_ERR_MISALIGNED;
     const uint64_t elems = (uint64_t)tokens * (uint64_t)inter;
     Arg outs[2];
     int n_out = 0;
-    outs[n_out++] = {span(out, fp8 ? elems : mx ? elems / 2 : 2 * elems), out};
-    if (mx) outs[n_out++] = {span(scale_out, elems / 32), scale_out};
-    const Arg ins[2] = {{span(gate_up, 4 * elems), gate_up}, {span(scale, fp8 ? 4 : 0), scale}};
+    outs[n_out++] = {span(out, fp8 ? elems : fp4 ? elems / 2 : 2 * elems), out};
+    if (fp4) outs[n_out++] = {span(scale_out, mx ? elems / 32 : elems / 16), scale_out};
+    const Arg ins[2] = {{span(gate_up, 4 * elems), gate_up}, {span(scale, with_scale ? 4 : 0), scale}};
     const int partner[2] = {-1, -1};
-    if ((st = check_outputs(outs, partner, n_out, ins, fp8 ? 2 : 1))) return st;
+    if ((st = check_outputs(outs, partner, n_out, ins, with_scale ? 2 : 1))) return st;
     if (variant == -1) variant = pick_swiglu(tokens, inter, epi != SWIGLU_EPI_BF16);
     SwigluParams p;
     p.out = out;
     p.gate_up = gate_up;
-    p.scale = fp8 ? scale : nullptr;
-    p.scale_out = mx ? (float *)scale_out : nullptr;
+    p.scale = with_scale ? scale : nullptr;
+    p.scale_out = fp4 ? (float *)scale_out : nullptr;
     p.tokens = tokens;
     p.inter = inter;
     p.vecs_per_row = (uint32_t)(inter / 8);
@@ -468,6 +470,55 @@ int swiglu_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, const void *gate_up
 {
     return swiglu_common(out_fp4, gate_up, nullptr, scale_out, num_tokens, inter, SWIGLU_EPI_MXFP4,
                          variant, stream);
+}
+
+int swiglu_quant_nvfp4(void *out_fp4, uint8_t *scale_out, const void *gate_up,
+                       const float *tensor_scale, int64_t num_tokens, int64_t inter, hipStream_t stream)
+{
+    return swiglu_common(out_fp4, gate_up, tensor_scale, scale_out, num_tokens, inter, SWIGLU_EPI_NVFP4,
+                         -1, stream);
+}
+
+int swiglu_quant_nvfp4_ex(void *out_fp4, uint8_t *scale_out, const void *gate_up,
+                          const float *tensor_scale, int64_t num_tokens, int64_t inter, int variant,
+                          hipStream_t stream)
+{
+    return swiglu_common(out_fp4, gate_up, tensor_scale, scale_out, num_tokens, inter, SWIGLU_EPI_NVFP4,
+                         variant, stream);
+}
+
+int fused_add_rmsnorm_quant_nvfp4(void *out_fp4, uint8_t *scale_out, void *residual_out,
+                                  const void *x, const void *residual, const void *weight,
+                                  const float *tensor_scale, int64_t num_tokens, int64_t hidden,
+                                  float eps, hipStream_t stream)
+{
+    return norm_common(out_fp4, (float *)scale_out, tensor_scale, residual_out, x, residual, weight,
+                       num_tokens, hidden, eps, NORM_EPI_NVFP4, true, -1, stream);
+}
+
+int fused_add_rmsnorm_quant_nvfp4_ex(void *out_fp4, uint8_t *scale_out, void *residual_out,
+                                     const void *x, const void *residual, const void *weight,
+                                     const float *tensor_scale, int64_t num_tokens, int64_t hidden,
+                                     float eps, int variant, hipStream_t stream)
+{
+    return norm_common(out_fp4, (float *)scale_out, tensor_scale, residual_out, x, residual, weight,
+                       num_tokens, hidden, eps, NORM_EPI_NVFP4, true, variant, stream);
+}
+
+int rmsnorm_quant_nvfp4(void *out_fp4, uint8_t *scale_out, const void *x, const void *weight,
+                        const float *tensor_scale, int64_t num_tokens, int64_t hidden, float eps,
+                        hipStream_t stream)
+{
+    return norm_common(out_fp4, (float *)scale_out, tensor_scale, nullptr, x, nullptr, weight,
+                       num_tokens, hidden, eps, NORM_EPI_NVFP4, false, -1, stream);
+}
+
+int rmsnorm_quant_nvfp4_ex(void *out_fp4, uint8_t *scale_out, const void *x, const void *weight,
+                           const float *tensor_scale, int64_t num_tokens, int64_t hidden, float eps,
+                           int variant, hipStream_t stream)
+{
+    return norm_common(out_fp4, (float *)scale_out, tensor_scale, nullptr, x, nullptr, weight,
+                       num_tokens, hidden, eps, NORM_EPI_NVFP4, false, variant, stream);
 }
 
 int swiglu_quant_fp8_dynamic(void *out_fp8, float *scale_out, const void *gate_up,

@@ -133,6 +133,91 @@ __device__ __forceinline__ float e4m3_quotient(float y, const E4m3Scale &q)
     }
 }
 
+// ---------------------------------------------------------------- NVFP4
+//
+// A block of 16 values shares an E4M3 scale under the fp32 tensor scale g
+// (0 means 1): scale = E4M3(binary32(amax / binary32(6 g))), nearest even,
+// saturated at 448 (v_cvt_pk_fp8_f32 after a clamp); each value becomes
+// E2M1(binary32(v / S)), S = binary32(scale * g), or a signed zero when S is
+// 0; a block holding a NaN or an infinity gets the E4M3 NaN 0x7F and zero
+// codes.  Both quotients are the correctly rounded ones of the E4M3 path
+// (e4m3_quotient).
+
+struct Nvfp4Tensor {
+    float g;
+    E4m3Scale six;           // 6 g, as the divisor of the block amax
+    bool six_fast;
+};
+
+__device__ __forceinline__ Nvfp4Tensor make_nvfp4_tensor(float g)
+{
+    Nvfp4Tensor t;
+    t.g = (g == 0.0f) ? 1.0f : g;
+    t.six = make_e4m3_scale(6.0f * t.g);
+    t.six_fast = e4m3_scale_is_fast(t.six);
+    return t;
+}
+
+// E4M3 block scale: binary32(amax / 6g) (the correctly rounded quotient of
+// the E4M3 path, its input clamped at 448 * 6g so nothing overflows),
+// saturated at 448, rounded to nearest even.
+__device__ __forceinline__ uint32_t nv_scale_byte(uint32_t amax_bits, const Nvfp4Tensor &t)
+{
+    if (amax_bits >= 0x7F800000u) return 0x7Fu;
+    const float a = __uint_as_float(amax_bits);
+    const float q = t.six_fast ? e4m3_quotient<true>(a, t.six) : e4m3_quotient<false>(a, t.six);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q, 0.0f, 448.0f), 0.0f, 0, false) &
+           0xFFu;
+}
+
+// NW bf16 words (2 NW values) of one block -> NW bytes of E2M1 pairs, the
+// first value of each pair in the low nibble.  Unless the block scale
+// saturated (448), every |v| / S stays below about 12, so the quotient needs
+// no input clamp; a saturated block takes the clamped form (its values can
+// be arbitrarily large against S).
+template <int NW, bool CLAMP>
+__device__ __forceinline__ void nv_quotients(const uint32_t (&w)[NW], const E4m3Scale &qs, bool fast, bool zero,
+                                             float (&z)[2 * NW])
+{
+#pragma unroll
+    for (int e = 0; e < NW; ++e) {
+        const float v0 = bf_lo(w[e]), v1 = bf_hi(w[e]);
+        float z0, z1;
+        if (fast) {
+            z0 = e4m3_quotient<true, CLAMP>(v0, qs);
+            z1 = e4m3_quotient<true, CLAMP>(v1, qs);
+        } else {
+            z0 = e4m3_quotient<false, CLAMP>(v0, qs);
+            z1 = e4m3_quotient<false, CLAMP>(v1, qs);
+        }
+        z[2 * e] = zero ? v0 * 0.0f : z0;
+        z[2 * e + 1] = zero ? v1 * 0.0f : z1;
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ uint32_t pack_nvfp4(const uint32_t (&w)[NW], uint32_t sb, const Nvfp4Tensor &t)
+{
+    static_assert(NW == 2 || NW == 4, "2 or 4 words");
+    const float S = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * t.g;
+    const E4m3Scale qs = make_e4m3_scale(S);
+    const bool fast = e4m3_scale_is_fast(qs), zero = S == 0.0f;
+    float z[2 * NW];
+    if (sb == 0x7Eu)
+        nv_quotients<NW, true>(w, qs, fast, zero, z);
+    else
+        nv_quotients<NW, false>(w, qs, fast, zero, z);
+    // the byte selector of the conversion is an immediate
+    uint32_t q = 0;
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, z[0], z[1], 1.0f, 0);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, z[2], z[3], 1.0f, 1);
+    if constexpr (NW == 4) {
+        q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, z[4], z[5], 1.0f, 2);
+        q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, z[6], z[7], 1.0f, 3);
+    }
+    return q;
+}
+
 // Butterfly sums and maxima over the 64 lanes of a wave, entirely in VALU
 // lane permutations (no LDS round trips, which dominate a lone row's latency).
 // Each step combines v with its value on a partner lane, and every

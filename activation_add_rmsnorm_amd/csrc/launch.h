@@ -13,6 +13,8 @@ enum NormEpilogue : int {
     NORM_EPI_FP8_DYNAMIC = 1, // E4M3 out, per-token scale written to scale_out
     NORM_EPI_FP8_STATIC = 2,  // E4M3 out, per-tensor scale read from scale_in
     NORM_EPI_MXFP4 = 3,       // MXFP4 out: E2M1 codes, E8M0 scale per 32 values to scale_out
+    NORM_EPI_NVFP4 = 4,       // NVFP4 out: E2M1 codes, E4M3 scale per 16 values to scale_out,
+                              // fp32 tensor scale from scale_in
 };
 
 struct NormParams {
@@ -33,6 +35,8 @@ enum SwigluEpilogue : int {
     SWIGLU_EPI_BF16 = 0,
     SWIGLU_EPI_FP8 = 1,       // static per-tensor E4M3, scale read from scale
     SWIGLU_EPI_MXFP4 = 2,     // E2M1 codes, E8M0 scale per 32 outputs to scale_out
+    SWIGLU_EPI_NVFP4 = 3,     // E2M1 codes, E4M3 scale per 16 outputs to scale_out, tensor
+                              // scale from scale
 };
 
 struct SwigluParams {

@@ -205,6 +205,30 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
             st_stream(qo + v, q);
             if ((lane & 3) == 0) so[v >> 2] = (uint8_t)sb;
         }
+    } else if constexpr (EPI == NORM_EPI_NVFP4) {
+        // ---- y as above; per 16-value block (the slices of 2 adjacent lanes)
+        // the E4M3 scale from the block amax under the tensor scale, then
+        // E2M1 codes
+        const Nvfp4Tensor nt = make_nvfp4_tensor(*p.scale_in);
+        uint32_t *qo = (uint32_t *)((uint8_t *)p.out + (size_t)row * (size_t)(p.hidden / 2));
+        uint8_t *so = (uint8_t *)p.scale_out + (size_t)row * (size_t)(p.hidden / 16);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int v = lane + k * WPR * 64;
+            uint32_t y[4];
+            uint32_t mag = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[e] = norm_word(rv[k][e], wv[k][e], rs);
+                mag = max(mag, max((y[e] << 16) & 0x7FFFFFFFu, y[e] & 0x7FFF0000u));
+            }
+            mag = max(mag, dpp_u32<DPP_XOR1>(mag));
+            if (v >= nvec) continue;
+            const uint32_t sb = nv_scale_byte(mag, nt);
+            const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<4>(y, sb, nt);
+            st_stream(qo + v, q);
+            if ((lane & 1) == 0) so[v >> 1] = (uint8_t)sb;
+        }
     } else if constexpr (EPI == NORM_EPI_FP8_STATIC) {
         // ---- y as above, q = e4m3(clamp(y / s)) with the given scale
         const E4m3Scale qs = make_e4m3_scale(*p.scale_in);
@@ -431,6 +455,9 @@ hipError_t launch_norm(const NormParams &p, int epi, bool residual, int variant,
     case NORM_EPI_MXFP4:
         return residual ? dispatch<NORM_EPI_MXFP4, true>(p, variant, num_cus, stream)
                         : dispatch<NORM_EPI_MXFP4, false>(p, variant, num_cus, stream);
+    case NORM_EPI_NVFP4:
+        return residual ? dispatch<NORM_EPI_NVFP4, true>(p, variant, num_cus, stream)
+                        : dispatch<NORM_EPI_NVFP4, false>(p, variant, num_cus, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -98,7 +98,9 @@ __device__ __forceinline__ uint32_t mx_block_max(uint32_t mag)
 }
 
 // MODE 0: bf16 output; 1: E4M3 output, fast quotient; 2: E4M3, IEEE
-// division; 3: MXFP4 (codes to out, E8M0 block scales to scale_out).
+// division; 3: MXFP4 (codes to out, E8M0 block scales to scale_out); 4:
+// NVFP4 (codes to out, E4M3 block scales to scale_out, tensor scale read
+// from scale).
 template <int U, int W, int MODE>
 __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Scale &qs)
 {
@@ -150,6 +152,34 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
         }
         return;
     }
+    if constexpr (MODE == 4) {
+        // a 16-output block is the jobs of 2 adjacent lanes (4 for half jobs)
+        constexpr uint32_t LANES = 8 / W;
+        const Nvfp4Tensor nt = make_nvfp4_tensor(*p.scale);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = c0 + 256u * u;
+            const V y = swiglu_job<W>(gv[u], uv[u]);
+            uint32_t mag = 0;
+            uint32_t w[W];
+#pragma unroll
+            for (int e = 0; e < W; ++e) {
+                w[e] = y[e];
+                mag = max(mag, max((y[e] << 16) & 0x7FFFFFFFu, y[e] & 0x7FFF0000u));
+            }
+            mag = max(mag, dpp_u32<DPP_XOR1>(mag));
+            if constexpr (W == 2) mag = max(mag, dpp_u32<DPP_XOR2>(mag));
+            if (c >= njobs) continue;
+            const uint32_t sb = nv_scale_byte(mag, nt);
+            const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<W>(w, sb, nt);
+            if constexpr (W == 4)
+                st_stream((uint32_t *)p.out + job0 + c, q);
+            else
+                st_stream((uint16_t *)p.out + job0 + c, (uint16_t)q);
+            if (c % LANES == 0) ((uint8_t *)p.scale_out)[(job0 + c) / LANES] = (uint8_t)sb;
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t c = c0 + 256u * u;
@@ -187,6 +217,8 @@ __global__ void __launch_bounds__(256) swiglu_kernel(SwigluParams p)
             swiglu_block<U, W, 2>(p, qs);
     } else if constexpr (EPI == SWIGLU_EPI_MXFP4) {
         swiglu_block<U, W, 3>(p, E4m3Scale{});
+    } else if constexpr (EPI == SWIGLU_EPI_NVFP4) {
+        swiglu_block<U, W, 4>(p, E4m3Scale{});
     } else {
         swiglu_block<U, W, 0>(p, E4m3Scale{});
     }
@@ -369,6 +401,7 @@ hipError_t launch_swiglu(const SwigluParams &p, int epi, int variant, hipStream_
     case SWIGLU_EPI_BF16: return dispatch<SWIGLU_EPI_BF16>(p, variant, stream);
     case SWIGLU_EPI_FP8: return dispatch<SWIGLU_EPI_FP8>(p, variant, stream);
     case SWIGLU_EPI_MXFP4: return dispatch<SWIGLU_EPI_MXFP4>(p, variant, stream);
+    case SWIGLU_EPI_NVFP4: return dispatch<SWIGLU_EPI_NVFP4>(p, variant, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -49,6 +49,9 @@ FORMS = {
     "swiglu_quant_fp8": (A.OP_SWIGLU, True),
     "swiglu_quant_fp8_dynamic": (A.OP_SWIGLU_DYNAMIC, True),
     "swiglu_quant_mxfp4": (A.OP_SWIGLU, True),
+    "fused_add_rmsnorm_quant_nvfp4": (A.OP_NORM, True),
+    "rmsnorm_quant_nvfp4": (A.OP_RMSNORM, True),
+    "swiglu_quant_nvfp4": (A.OP_SWIGLU, True),
 }
 
 
@@ -99,10 +102,11 @@ def _buffers(form: str, tokens: int, width: int, device):
     f8 = dict(dtype=torch.uint8, device=device)
     if form.startswith("swiglu"):
         b = dict(gu=(torch.randn((T, 2 * W), device=device) * 2).to(torch.bfloat16))
-        if "mxfp4" in form:
+        if "fp4" in form:
+            blk = 32 if "mxfp4" in form else 16
             b["y"] = torch.empty((T, W // 2), **f8)
-            b["s"] = torch.empty((T, W // 32), **f8)
-            nbytes = T * W * 4 + T * W // 2 + T * W // 32
+            b["s"] = torch.empty((T, W // blk), **f8)
+            nbytes = T * W * 4 + T * W // 2 + T * W // blk
         else:
             b["y"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
             b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
@@ -110,10 +114,11 @@ def _buffers(form: str, tokens: int, width: int, device):
     else:
         b = dict(x=torch.randn((T, W), device=device).to(torch.bfloat16),
                  r=torch.randn((T, W), device=device).to(torch.bfloat16))
-        if "mxfp4" in form:
+        if "fp4" in form:
+            blk = 32 if "mxfp4" in form else 16
             b["o"] = torch.empty((T, W // 2), **f8)
-            b["s"] = torch.empty((T, W // 32), **f8)
-            out_bytes = T * W // 2 + T * W // 32
+            b["s"] = torch.empty((T, W // blk), **f8)
+            out_bytes = T * W // 2 + T * W // blk
         else:
             b["o"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
             b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
@@ -147,6 +152,13 @@ def _launcher(form: str, b: dict, w, scale, variant: int):
         return lambda: A.swiglu(b["gu"], out=b["y"], variant=variant)
     if form == "swiglu_quant_fp8":
         return lambda: A.swiglu_quant_fp8(b["gu"], scale, out=b["y"], variant=variant)
+    if form == "fused_add_rmsnorm_quant_nvfp4":
+        return lambda: A.fused_add_rmsnorm_quant_nvfp4(b["x"], b["r"], w, scale, 1e-6, out=b["o"], scale_out=b["s"],
+                                                       residual_out=b["ro"], variant=variant)
+    if form == "rmsnorm_quant_nvfp4":
+        return lambda: A.rmsnorm_quant_nvfp4(b["x"], w, scale, 1e-6, out=b["o"], scale_out=b["s"], variant=variant)
+    if form == "swiglu_quant_nvfp4":
+        return lambda: A.swiglu_quant_nvfp4(b["gu"], scale, out=b["y"], scale_out=b["s"], variant=variant)
     if form == "swiglu_quant_mxfp4":
         return lambda: A.swiglu_quant_mxfp4(b["gu"], out=b["y"], scale_out=b["s"], variant=variant)
     if form == "swiglu_quant_fp8_dynamic":

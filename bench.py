@@ -429,7 +429,8 @@ def autotune_report():
               ("rmsnorm", 4096, 1536), ("rmsnorm_quant_fp8", 2048, 16384),
               ("fused_add_rmsnorm_quant_fp8_static", 2048, 16384), ("swiglu_quant_fp8_dynamic", 8192, 28672),
               ("fused_add_rmsnorm_quant_mxfp4", 2048, 16384), ("swiglu_quant_mxfp4", 8192, 28672),
-              ("swiglu_quant_mxfp4", 1, 8960)]
+              ("swiglu_quant_mxfp4", 1, 8960), ("fused_add_rmsnorm_quant_nvfp4", 2048, 16384),
+              ("swiglu_quant_nvfp4", 8192, 28672)]
     rows = []
     for form, T, W in shapes:
         r = tuning.tune(form, T, W, rounds=3)
@@ -508,6 +509,16 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
             lambda i: stream(P(i, "ro"), 16, mx_sets[i % ns][0].data_ptr(), 4, P(i, "x"), P(i, "r"), T * H // 8),
             nb, {"buffer_sets_rotated": ns})
     del mx_sets
+    nv_sets = [(torch.empty((T, H // 2), dtype=torch.uint8, device=dev),
+                torch.empty((T, H // 16), dtype=torch.uint8, device=dev)) for _ in range(ns)]
+    nb = T * H * 6 + T * H // 2 + T * H // 16 + H * 2 + 4
+    measure("llama405b_norm_nvfp4_2048x16384",
+            lambda i: check(lib.fused_add_rmsnorm_quant_nvfp4(
+                nv_sets[i % ns][0].data_ptr(), nv_sets[i % ns][1].data_ptr(), P(i, "ro"), P(i, "x"), P(i, "r"),
+                w0.data_ptr(), scale.data_ptr(), T, H, wl.eps, sp), "fused_add_rmsnorm_quant_nvfp4"),
+            lambda i: stream(P(i, "ro"), 16, nv_sets[i % ns][0].data_ptr(), 4, P(i, "x"), P(i, "r"), T * H // 8),
+            nb, {"tensor_scale": 0.02, "buffer_sets_rotated": ns})
+    del nv_sets
     nb = T * H * 3 + H * 2 + T * 4
     measure("llama405b_rmsnorm_fp8_2048x16384",
             lambda i: check(lib.rmsnorm_quant_fp8(P(i, "q"), P(i, "s"), P(i, "x"), w0.data_ptr(),
@@ -535,6 +546,18 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
             T * 2 * N * 2 + T * N // 2 + T * N // 32,
             {"inputs": "torch.randn on device, seed 0, std 2", "buffer_sets_rotated": ns})
     del mx_sets
+    nv_sets = [(torch.empty((T, N // 2), dtype=torch.uint8, device=dev),
+                torch.empty((T, N // 16), dtype=torch.uint8, device=dev)) for _ in range(ns)]
+    g_nv = torch.tensor([0.05], dtype=torch.float32, device=dev)
+    measure("llama70b_swiglu_nvfp4_8192x57344",
+            lambda i: check(lib.swiglu_quant_nvfp4(nv_sets[i % ns][0].data_ptr(), nv_sets[i % ns][1].data_ptr(),
+                                                   sets[i % ns][0].data_ptr(), g_nv.data_ptr(), T, N, sp),
+                            "swiglu_quant_nvfp4"),
+            lambda i: stream(nv_sets[i % ns][0].data_ptr(), 4, None, 0, sets[i % ns][0].data_ptr(),
+                             sets[i % ns][0].data_ptr() + T * N * 2, T * N // 8),
+            T * 2 * N * 2 + T * N // 2 + T * N // 16 + 4,
+            {"tensor_scale": 0.05, "inputs": "torch.randn on device, seed 0, std 2", "buffer_sets_rotated": ns})
+    del nv_sets
     measure("llama70b_swiglu_fp8_dynamic_8192x57344",
             lambda i: check(lib.swiglu_quant_fp8_dynamic(sets[i % ns][1].data_ptr(), sets[i % ns][2].data_ptr(),
                                                          sets[i % ns][0].data_ptr(), T, N, sp),

@@ -58,7 +58,7 @@ enum aarms_status {
     AARMS_OK = 0,
     AARMS_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                 */
     AARMS_ERR_BAD_SHAPE = 2,         /* negative size, zero width, width % 8 != 0
-                                        (% 32 for MXFP4)                          */
+                                        (% 32 for MXFP4, % 16 for NVFP4)          */
     AARMS_ERR_UNSUPPORTED_SHAPE = 3, /* width or element count beyond the limits   */
     AARMS_ERR_MISALIGNED = 4,        /* pointer alignment not met                  */
     AARMS_ERR_ALIAS = 5,             /* an output overlaps another argument        */
@@ -190,6 +190,36 @@ int rmsnorm_quant_mxfp4(void *out_fp4, uint8_t *scale_out, const void *x, const 
                         int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream);
 
 /*
+ * fused_add_rmsnorm_quant_nvfp4 / rmsnorm_quant_nvfp4 -- the norm (with or
+ * without the residual add) whose bf16 output is written as NVFP4 in the
+ * same pass: E2M1 codes in blocks of 16 along a row sharing an E4M3 scale,
+ * under a given FP32 tensor scale ("TensorRT-LLM" walkthrough, Part V; vLLM
+ * post, section 4).  The pages give the format, not the scale recipe; this
+ * library's:
+ *   block scale  E4M3(binary32(max|y| / binary32(6 g))), nearest even,
+ *                saturated at 448 (the block's largest value maps to 6)
+ *   code         E2M1(binary32(y / S)), S = binary32(block scale * g),
+ *                nearest even, saturated at +-6; a signed zero when S = 0
+ *
+ *   out_fp4      [num_tokens, hidden / 2]  uint8  written: two E2M1 codes per byte,
+ *                                                 the first value in the low nibble
+ *   scale_out    [num_tokens, hidden / 16] uint8  written: E4M3 block scales; 0x7F
+ *                                                 for a block holding a NaN or an
+ *                                                 infinity (its codes are 0)
+ *   tensor_scale [1] fp32, device memory  read: g, positive and finite; 0 means 1
+ *   residual_out, x, residual, weight, eps   as for fused_add_rmsnorm / rmsnorm
+ *   hidden       multiple of 16, <= AARMS_MAX_HIDDEN
+ * In place: residual_out == residual is allowed.
+ */
+int fused_add_rmsnorm_quant_nvfp4(void *out_fp4, uint8_t *scale_out, void *residual_out,
+                                  const void *x, const void *residual, const void *weight,
+                                  const float *tensor_scale, int64_t num_tokens, int64_t hidden,
+                                  float eps, hipStream_t stream);
+int rmsnorm_quant_nvfp4(void *out_fp4, uint8_t *scale_out, const void *x, const void *weight,
+                        const float *tensor_scale, int64_t num_tokens, int64_t hidden, float eps,
+                        hipStream_t stream);
+
+/*
  * swiglu -- silu(gate) * up over a concatenated gate_up projection output.
  *
  * TensorRT-LLM's gated MLP runs one gate_up_proj matmul followed by a fused
@@ -237,6 +267,21 @@ int swiglu_quant_mxfp4(void *out_fp4, uint8_t *scale_out, const void *gate_up,
                        int64_t num_tokens, int64_t inter, hipStream_t stream);
 
 /*
+ * swiglu_quant_nvfp4 -- swiglu whose bf16 output is written as NVFP4 in the
+ * same pass, with the block rules of the NVFP4 norms above.
+ *
+ *   out_fp4      [num_tokens, inter / 2]  uint8
+ *   scale_out    [num_tokens, inter / 16] uint8  E4M3 block scales
+ *   gate_up      [num_tokens, 2 * inter]  bf16   read, as for swiglu
+ *   tensor_scale [1] fp32, device memory
+ *   inter        multiple of 16, at most AARMS_MAX_INTER
+ * No in-place form.
+ */
+int swiglu_quant_nvfp4(void *out_fp4, uint8_t *scale_out, const void *gate_up,
+                       const float *tensor_scale, int64_t num_tokens, int64_t inter,
+                       hipStream_t stream);
+
+/*
  * swiglu_quant_fp8_dynamic -- swiglu whose bf16 output is quantised to E4M3
  * with a dynamic per-token scale, in the same pass (vLLM's SiLU-and-mul +
  * quant fusion, sections 3 and 4 of its post, with per-token scaling as in
@@ -262,8 +307,8 @@ const char *aarms_status_string(int status);
  * aarms_variant_name() describes it (static storage) and returns NULL past
  * the end.  ops: 0 = the norms with the residual add (fused_add_rmsnorm*),
  * 3 = the norms without it (rmsnorm*), both on one variant table (quant != 0
- * for an E4M3 or MXFP4 form); 1 = swiglu, swiglu_quant_fp8 and
- * swiglu_quant_mxfp4 (quant != 0 for the quantised forms); 2 =
+ * for a quantised form); 1 = swiglu, swiglu_quant_fp8, swiglu_quant_mxfp4
+ * and swiglu_quant_nvfp4 (quant != 0 for the quantised forms); 2 =
  * swiglu_quant_fp8_dynamic.
  * aarms_pick_variant() returns the id the plain entry point would use, or -1
  * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
@@ -300,6 +345,16 @@ int swiglu_quant_fp8_dynamic_ex(void *out_fp8, float *scale_out, const void *gat
                                 int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
 int swiglu_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, const void *gate_up,
                           int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
+int swiglu_quant_nvfp4_ex(void *out_fp4, uint8_t *scale_out, const void *gate_up,
+                          const float *tensor_scale, int64_t num_tokens, int64_t inter, int variant,
+                          hipStream_t stream);
+int fused_add_rmsnorm_quant_nvfp4_ex(void *out_fp4, uint8_t *scale_out, void *residual_out,
+                                     const void *x, const void *residual, const void *weight,
+                                     const float *tensor_scale, int64_t num_tokens, int64_t hidden,
+                                     float eps, int variant, hipStream_t stream);
+int rmsnorm_quant_nvfp4_ex(void *out_fp4, uint8_t *scale_out, const void *x, const void *weight,
+                           const float *tensor_scale, int64_t num_tokens, int64_t hidden, float eps,
+                           int variant, hipStream_t stream);
 int fused_add_rmsnorm_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, void *residual_out,
                                      const void *x, const void *residual, const void *weight,
                                      int64_t num_tokens, int64_t hidden, float eps, int variant,

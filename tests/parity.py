@@ -262,6 +262,44 @@ def _check_mx_codes(rows_in, weight, eps, q_gpu, s_gpu, q_o, s_o) -> NormReport:
                       scales_not_nominal=int((s_gpu != s_o).sum()))
 
 
+def _check_fp4_codes(rows_in, weight, eps, q_gpu, s_gpu, q_o, s_o, quant) -> NormReport:
+    """Block-scaled FP4 codes of a norm of rows_in against the oracle; rows
+    that differ must match the oracle's encoding (quant) of an admissible
+    norm output (scales exactly, codes within one E2M1 step)."""
+    rows = np.flatnonzero((q_gpu != q_o).any(axis=1) | (s_gpu != s_o).any(axis=1))
+    blk = (q_gpu.shape[1] * 2) // s_gpu.shape[1]
+    if len(rows):
+        _, lo, hi = norm_admissible(rows_in[rows], weight, eps)
+        cands = [quant(lo), quant(hi)]
+        for k, r in enumerate(rows):
+            ok_s = np.zeros(s_gpu.shape[1], bool)
+            d = np.full(q_gpu.shape[1] * 2, 99)
+            for cq, cs in cands:
+                same_s = s_gpu[r] == cs[k]
+                ok_s |= same_s
+                dd = np.abs(e2m1_ordered(_unpack_e2m1(q_gpu[r][None])[0]) -
+                            e2m1_ordered(_unpack_e2m1(cq[k][None])[0]))
+                dd[~np.repeat(same_s, blk)] = 99
+                d = np.minimum(d, dd)
+            assert ok_s.all(), "row %d: block scales outside the admissible set" % r
+            assert d.max() <= 1, "row %d: code off by %d E2M1 steps" % (r, d.max())
+    return NormReport(rows=int(q_gpu.shape[0]), rows_not_nominal=int(len(rows)),
+                      codes_not_nominal=int((q_gpu != q_o).sum()),
+                      scales_not_nominal=int((s_gpu != s_o).sum()))
+
+
+def check_norm_nvfp4(x, residual, weight, eps, g, q_gpu, s_gpu, res_out_gpu) -> NormReport:
+    q_o, s_o, res_o, _, _ = oracle.fused_add_rmsnorm_quant_nvfp4(x, residual, weight, eps, g)
+    bad_res = ~same_bf16(res_out_gpu, res_o)
+    assert not bad_res.any(), "residual_out differs at %d positions" % bad_res.sum()
+    return _check_fp4_codes(res_o, weight, eps, q_gpu, s_gpu, q_o, s_o, lambda y: oracle.quant_nvfp4(y, g))
+
+
+def check_rmsnorm_nvfp4(x, weight, eps, g, q_gpu, s_gpu) -> NormReport:
+    q_o, s_o, _, _ = oracle.rmsnorm_quant_nvfp4(x, weight, eps, g)
+    return _check_fp4_codes(x, weight, eps, q_gpu, s_gpu, q_o, s_o, lambda y: oracle.quant_nvfp4(y, g))
+
+
 def check_norm_mxfp4(x, residual, weight, eps, q_gpu, s_gpu, res_out_gpu) -> NormReport:
     q_o, s_o, res_o, _, _ = oracle.fused_add_rmsnorm_quant_mxfp4(x, residual, weight, eps)
     bad_res = ~same_bf16(res_out_gpu, res_o)
@@ -278,6 +316,17 @@ def check_swiglu_mxfp4(gate_up, q_gpu, s_gpu):
     """MXFP4 SwiGLU: the SwiGLU output has no knife-edges, so scales and codes
     must be bit-exact."""
     q_o, s_o, _ = oracle.swiglu_quant_mxfp4(gate_up)
+    bad_s = s_gpu != s_o
+    assert not bad_s.any(), "block scales differ at %d blocks, first %s: gpu %s oracle %s" % (
+        bad_s.sum(), np.argwhere(bad_s)[:5].tolist(), s_gpu[bad_s][:5], s_o[bad_s][:5])
+    bad = q_gpu != q_o
+    assert not bad.any(), "codes differ at %d bytes, first %s: gpu %s oracle %s" % (
+        bad.sum(), np.argwhere(bad)[:5].tolist(), q_gpu[bad][:5], q_o[bad][:5])
+
+
+def check_swiglu_nvfp4(gate_up, g, q_gpu, s_gpu):
+    """NVFP4 SwiGLU: bit-exact scales and codes (no knife-edges in y)."""
+    q_o, s_o, _ = oracle.swiglu_quant_nvfp4(gate_up, g)
     bad_s = s_gpu != s_o
     assert not bad_s.any(), "block scales differ at %d blocks, first %s: gpu %s oracle %s" % (
         bad_s.sum(), np.argwhere(bad_s)[:5].tolist(), s_gpu[bad_s][:5], s_o[bad_s][:5])

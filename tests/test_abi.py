@@ -357,3 +357,26 @@ def test_swiglu_mxfp4_errors():
     assert smx(out=P + 2 * BIG) == ALIAS
     assert smx(variant=A.variant_count(A.OP_SWIGLU)) == VARIANT
     assert smx(T=0, out=0, s=0, gu=0) == OK
+
+
+def test_nvfp4_errors():
+    lib = A.load()
+    G = P + 6 * BIG                                   # the tensor scale
+
+    def nv(out=P, s=P + BIG + 1, ro=P + 2 * BIG, x=P + 3 * BIG, r=P + 4 * BIG, w=P + 5 * BIG, g=G,
+           T=4, H=1536, variant=-1):
+        return lib.fused_add_rmsnorm_quant_nvfp4_ex(out, s, ro, x, r, w, g, T, H, 1e-6, variant, None)
+
+    assert nv(H=1544) == SHAPE                          # a multiple of 8 but not of 16
+    assert nv(g=0) == NULLP
+    assert nv(s=0) == NULLP
+    assert nv(g=G + 2) == MISAL
+    assert nv(out=P + 8) == MISAL
+    assert nv(s=P + 64) == ALIAS
+    assert nv(g=P + 8) == ALIAS                         # tensor scale inside the codes
+    assert nv(variant=0) == VARIANT
+    assert nv(T=0, out=0, s=0, ro=0, x=0, r=0, w=0, g=0) == OK
+    assert lib.rmsnorm_quant_nvfp4_ex(P, P + BIG, P + 2 * BIG, P + 3 * BIG, G, 4, 40, 1e-6, -1, None) == SHAPE
+    assert lib.swiglu_quant_nvfp4_ex(P, P + BIG, P + 2 * BIG, G, 4, 8968, -1, None) == SHAPE
+    assert lib.swiglu_quant_nvfp4_ex(P, P + BIG, P + 2 * BIG, 0, 4, 8960, -1, None) == NULLP
+    assert lib.swiglu_quant_nvfp4_ex(P, P + 64, P + 2 * BIG, G, 4, 8960, -1, None) == ALIAS

@@ -404,3 +404,97 @@ def test_swiglu_mxfp4_llama70b_full():
     gu = W.swiglu_inputs(wl)["gate_up"]
     q, s = run_swiglu_mx(gu)
     P.check_swiglu_mxfp4(gu, q, s)
+
+
+# ------------------------------------------------------------------ NVFP4
+
+NV_SCALES = [0.02, 1.0, 3.0e-4, 0.0, 2.0 ** -120, 1.0e6]
+
+
+def run_fused_nv(x, r, w, eps, g, variant=-1):
+    announce("fused_add_rmsnorm_quant_nvfp4", x.shape, "g", g, "variant", variant)
+    q, s, ro = A.fused_add_rmsnorm_quant_nvfp4(bf16(x), bf16(r), bf16(w), scale_t(g), eps, variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s), bits(ro)
+
+
+def run_rms_nv(x, w, eps, g, variant=-1):
+    announce("rmsnorm_quant_nvfp4", x.shape, "g", g, "variant", variant)
+    q, s = A.rmsnorm_quant_nvfp4(bf16(x), bf16(w), scale_t(g), eps, variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s)
+
+
+def run_swiglu_nv(gu, g, variant=-1):
+    announce("swiglu_quant_nvfp4", gu.shape, "g", g, "variant", variant)
+    q, s = A.swiglu_quant_nvfp4(bf16(gu), scale_t(g), variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s)
+
+
+@pytest.mark.parametrize("g", NV_SCALES)
+def test_nvfp4_norms_tensor_scales(g):
+    """Tensor scales from ordinary ones to g = 2^-120 (amax / 6g far past
+    448: every block scale saturates) and g = 1e6 (block scales underflow to
+    zero: signed-zero codes), and zero (treated as one)."""
+    x, r, w = norm_case(48, 2048, seed=61, outliers=0.002)
+    q, s, ro = run_fused_nv(x, r, w, 1e-5, g)
+    announce(P.check_norm_nvfp4(x, r, w, 1e-5, g, q, s, ro))
+    q, s = run_rms_nv(x, w, 1e-5, g)
+    announce(P.check_rmsnorm_nvfp4(x, w, 1e-5, g, q, s))
+
+
+@pytest.mark.parametrize("H", [1536, 16384])
+def test_nvfp4_norms_every_variant(H):
+    x, r, w = norm_case(37, H, seed=H + 13, outliers=0.002)
+    for v in variants_for(A.OP_NORM, H):
+        q, s, ro = run_fused_nv(x, r, w, 1e-5, 0.02, v)
+        P.check_norm_nvfp4(x, r, w, 1e-5, 0.02, q, s, ro)
+        q, s = run_rms_nv(x, w, 1e-5, 0.02, v)
+        P.check_rmsnorm_nvfp4(x, w, 1e-5, 0.02, q, s)
+
+
+@pytest.mark.parametrize("T,H", [(1, 16), (3, 48), (1023, 1536), (2, 65536)])
+def test_nvfp4_norm_shapes(T, H):
+    x, r, w = norm_case(T, H, seed=T + 3 * H)
+    q, s, ro = run_fused_nv(x, r, w, 1e-6, 0.01)
+    P.check_norm_nvfp4(x, r, w, 1e-6, 0.01, q, s, ro)
+
+
+def test_nvfp4_norm_llama405b_full():
+    wl = W.NORM_FP8_LLAMA405B
+    d = W.norm_inputs(wl)
+    q, s, ro = run_fused_nv(d["x"], d["residual"], d["weight"], wl.eps, 0.02)
+    announce(P.check_norm_nvfp4(d["x"], d["residual"], d["weight"], wl.eps, 0.02, q, s, ro))
+
+
+@pytest.mark.parametrize("T,N", [(1, 16), (3, 48), (5, 1040), (64, 8960), (300, 8960), (7, 28672)])
+def test_swiglu_nvfp4_shapes_every_variant(T, N):
+    gu = gen.normal_bf16((T, 2 * N), T + 11 * N, 4, std=2.0)
+    for v in [-1] + list(range(A.variant_count(A.OP_SWIGLU))):
+        q, s = run_swiglu_nv(gu, 0.05, v)
+        P.check_swiglu_nvfp4(gu, 0.05, q, s)
+
+
+def test_swiglu_nvfp4_scales_and_special_blocks():
+    N = 65536
+    u = np.arange(N, dtype=np.uint16)
+    finite = (u & 0x7F80) != 0x7F80
+    uu = np.where(finite & ((u & 0x7F80) <= 0x4700), u, u & 0x807F)
+    row = np.concatenate([np.full(N, oracle.bf16_from_f64(8.0), np.uint16), uu])
+    gu = np.stack([row, row.copy(), row.copy()])
+    gu[1, 40] = 0x7FC0                                 # NaN gate: its block gets 0x7F
+    gu[2, N + 70] = 0x7F80                             # infinite up
+    gu[2, :16] = 0                                     # a zero block
+    for g in NV_SCALES:
+        for v in (-1, 0, 3):
+            q, s = run_swiglu_nv(gu, g, v)
+            P.check_swiglu_nvfp4(gu, g, q, s)
+            assert s[1, 2] == 0x7F and s[2, 4] == 0x7F
+
+
+def test_swiglu_nvfp4_llama70b_full():
+    wl = W.SWIGLU_FP8_LLAMA70B
+    gu = W.swiglu_inputs(wl)["gate_up"]
+    q, s = run_swiglu_nv(gu, 0.05)
+    P.check_swiglu_nvfp4(gu, 0.05, q, s)
