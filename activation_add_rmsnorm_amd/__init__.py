@@ -536,5 +536,8 @@ def variant_name(op: int, variant: int) -> str | None:
     return s.decode() if s else None
 
 
-def pick_variant(op: int, tokens: int, width: int, quant: bool = False) -> int:
-    return int(load().aarms_pick_variant(int(op), int(tokens), int(width), int(bool(quant))))
+def pick_variant(op: int, tokens: int, width: int, quant: int | bool = False) -> int:
+    """The heuristic's variant.  quant: for the norms a flag (a quantised
+    form or not); for OP_SWIGLU the output format (0 bf16, 1 E4M3, 2 MXFP4,
+    3 NVFP4)."""
+    return int(load().aarms_pick_variant(int(op), int(tokens), int(width), int(quant)))

@@ -103,14 +103,17 @@ int pick_norm(int64_t tokens, int64_t hidden, bool quant, bool residual)
 {
     (void)quant;
     if (hidden <= 0 || hidden > AARMS_MAX_HIDDEN) return -1;
-    // Narrow rows: one wave per row with as few vectors per lane as fit (four
-    // waves per row for small batches).  Wide rows: the fewest waves per row
-    // that fit with at most 2 vectors per lane (the row's loads spread over
-    // many short slices, few registers per wave), else 4, else 8.  Without
-    // the residual a slice holds half the data, and 4 vectors per lane (half
-    // the waves per row, twice the rows in flight) come first.
-    if (hidden <= 4096) {
-        const int i = norm_fit(tokens < kNarrowMultiWaveTokens ? 4 : 1, hidden, 8);
+    // Narrow rows (up to 4 vectors per lane, 2,048 wide): one wave per row
+    // with as few vectors per lane as fit (four waves per row for small
+    // batches).  Wider rows: the fewest waves per row that fit with at most
+    // 2 vectors per lane (the row's loads spread over many short slices, few
+    // registers per wave), else 4, else 8; at 4,096 wide four waves of 2
+    // vectors beat one wave of 8 (146 registers) by 4-18% from 1,024 tokens
+    // up, every epilogue.  Without the residual a slice holds half the data,
+    // and 4 vectors per lane (half the waves per row, twice the rows in
+    // flight) come first.
+    if (hidden <= 2048) {
+        const int i = norm_fit(tokens < kNarrowMultiWaveTokens ? 4 : 1, hidden, 4);
         if (i >= 0) return i;
     }
     for (int max_vecs : {residual ? 2 : 4, 4, 8})
@@ -126,6 +129,7 @@ int pick_norm(int64_t tokens, int64_t hidden, bool quant, bool residual)
 // arithmetic.  Measured on MI355X over T x 8,960 and T x 28,672.
 constexpr int64_t kSwigluHalfJobOutputs = (int64_t)1 << 21;
 constexpr int64_t kSwigluFp8TwoJobOutputs = (int64_t)1 << 22;
+constexpr int64_t kSwigluNvfp4TwoJobOutputs = (int64_t)1 << 25;
 
 static int swiglu_find(int jobs_per_lane, int job_outputs)
 {
@@ -136,16 +140,22 @@ static int swiglu_find(int jobs_per_lane, int job_outputs)
     return -1;
 }
 
-int pick_swiglu(int64_t tokens, int64_t inter, bool quant)
+int pick_swiglu(int64_t tokens, int64_t inter, int epi)
 {
     if (tokens < 0 || inter <= 0) return -1;
     // tokens * inter against the thresholds, without forming the product
     if (tokens <= kSwigluHalfJobOutputs / inter) return swiglu_find(1, 4);
-    // bf16 output: one job per lane (the most blocks, each short-lived, so
-    // the blocks in flight stay on one contiguous stretch of memory).  E4M3
-    // output, from about four million outputs: two jobs per lane, which
-    // gives the longer per-job arithmetic two loads in flight to hide behind.
-    if (quant && tokens > kSwigluFp8TwoJobOutputs / inter) return swiglu_find(2, 8);
+    // bf16 and MXFP4 output: one job per lane (the most blocks, each
+    // short-lived, so the blocks in flight stay on one contiguous stretch of
+    // memory).  E4M3 output, from about four million outputs: two jobs per
+    // lane, which gives the longer per-job arithmetic two loads in flight to
+    // hide behind.  NVFP4 output (the most arithmetic per output): two jobs
+    // per lane from about 32 million outputs, when a row is a whole number
+    // of 512-job blocks (otherwise the last block of every row is mostly
+    // idle: N = 8960 rows have 1120 jobs).
+    if (epi == SWIGLU_EPI_FP8 && tokens > kSwigluFp8TwoJobOutputs / inter) return swiglu_find(2, 8);
+    if (epi == SWIGLU_EPI_NVFP4 && tokens > kSwigluNvfp4TwoJobOutputs / inter && (inter / 8) % 512 == 0)
+        return swiglu_find(2, 8);
     return swiglu_find(1, 8);
 }
 
@@ -261,7 +271,7 @@ int swiglu_common(void *out, const void *gate_up, const float *scale, uint8_t *s
     const Arg ins[2] = {{span(gate_up, 4 * elems), gate_up}, {span(scale, with_scale ? 4 : 0), scale}};
     const int partner[2] = {-1, -1};
     if ((st = check_outputs(outs, partner, n_out, ins, with_scale ? 2 : 1))) return st;
-    if (variant == -1) variant = pick_swiglu(tokens, inter, epi != SWIGLU_EPI_BF16);
+    if (variant == -1) variant = pick_swiglu(tokens, inter, epi);
     SwigluParams p;
     p.out = out;
     p.gate_up = gate_up;
@@ -576,7 +586,11 @@ const char *aarms_variant_name(int op, int variant)
 int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant)
 {
     if (op == 0 || op == 3) return pick_norm(num_tokens, width, quant != 0, op == 0);
-    if (op == 1) return (width > 0 && width % 8 == 0) ? pick_swiglu(num_tokens, width, quant != 0) : -1;
+    if (op == 1) {
+        // quant: the output format (0 bf16, 1 E4M3, 2 MXFP4, 3 NVFP4)
+        if (width <= 0 || width % 8 != 0 || quant < 0 || quant > 3) return -1;
+        return pick_swiglu(num_tokens, width, quant);
+    }
     if (op == 2) return (width > 0 && width % 8 == 0) ? pick_swiglu_rowq(num_tokens, width) : -1;
     return -1;
 }

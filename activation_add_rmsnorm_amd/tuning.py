@@ -18,8 +18,11 @@ library build and device, so a stale table is ignored rather than applied.
 
 Each variant's launches are captured once into a HIP graph and the graph is
 replayed between HIP events, so host launch overhead does not hide the
-kernels' own differences at small shapes.  This module allocates its own
-buffers and synchronizes: call it at start-up, not inside a captured graph.
+kernels' own differences at small shapes.  The graphs are replayed for a
+while before any is timed (clocks settle under load), then timed
+interleaved, and the median of the rounds is kept.  This module allocates
+its own buffers and synchronizes: call it at start-up, not inside a
+captured graph.
 """
 
 from __future__ import annotations
@@ -28,6 +31,7 @@ import hashlib
 import json
 import math
 import os
+import time
 
 import torch
 
@@ -35,7 +39,9 @@ import activation_add_rmsnorm_amd as A
 
 MALL_BYTES = 256e6          # MI355X last-level cache; rotation covers twice this
 
-# form -> (variant table op, quant flag for aarms_pick_variant)
+# form -> (variant table op, the quant argument of aarms_pick_variant: a
+# flag for the norms, the output format for swiglu: 0 bf16, 1 E4M3,
+# 2 MXFP4, 3 NVFP4)
 FORMS = {
     "fused_add_rmsnorm": (A.OP_NORM, False),
     "fused_add_rmsnorm_quant_fp8": (A.OP_NORM, True),
@@ -45,13 +51,13 @@ FORMS = {
     "rmsnorm_quant_fp8_static": (A.OP_RMSNORM, True),
     "fused_add_rmsnorm_quant_mxfp4": (A.OP_NORM, True),
     "rmsnorm_quant_mxfp4": (A.OP_RMSNORM, True),
-    "swiglu": (A.OP_SWIGLU, False),
-    "swiglu_quant_fp8": (A.OP_SWIGLU, True),
+    "swiglu": (A.OP_SWIGLU, 0),
+    "swiglu_quant_fp8": (A.OP_SWIGLU, 1),
     "swiglu_quant_fp8_dynamic": (A.OP_SWIGLU_DYNAMIC, True),
-    "swiglu_quant_mxfp4": (A.OP_SWIGLU, True),
+    "swiglu_quant_mxfp4": (A.OP_SWIGLU, 2),
     "fused_add_rmsnorm_quant_nvfp4": (A.OP_NORM, True),
     "rmsnorm_quant_nvfp4": (A.OP_RMSNORM, True),
-    "swiglu_quant_nvfp4": (A.OP_SWIGLU, True),
+    "swiglu_quant_nvfp4": (A.OP_SWIGLU, 3),
 }
 
 
@@ -166,9 +172,17 @@ def _launcher(form: str, b: dict, w, scale, variant: int):
     raise ValueError(form)
 
 
-def sweep(form: str, tokens: int, width: int, rounds: int = 3, device=None, max_sets: int = 64):
-    """Mean time per launch in microseconds of every fitting variant (the best
-    of `rounds` graph replays each), on rotated buffer sets."""
+def sweep(form: str, tokens: int, width: int, rounds: int = 5, device=None, max_sets: int = 64,
+          warm_s: float = 0.1, only=None):
+    """Mean time per launch in microseconds of every fitting variant (the
+    median of `rounds` timed regions each), on rotated buffer sets.
+
+    All variants are captured first; their graphs are then replayed in turn
+    for about `warm_s` seconds, so that the clocks have settled under load
+    (after the host has left the device idle they take some tens of
+    milliseconds, and a kernel with more arithmetic per byte is slowed more
+    until they have), and finally timed interleaved, round by round.
+    `only`: time these variant ids instead of every fitting one."""
     device = torch.device(device or "cuda")
     first, nbytes = _buffers(form, tokens, width, device)
     sets = [first]
@@ -178,11 +192,13 @@ def sweep(form: str, tokens: int, width: int, rounds: int = 3, device=None, max_
     W = int(width)
     w = (1 + 0.1 * torch.randn((W,), device=device)).to(torch.bfloat16) if not form.startswith("swiglu") else None
     scale = torch.tensor([0.05], dtype=torch.float32, device=device)
-    # about 2 ms of work per replay, at least 8 launches
+    # about 2 ms of work per replay, at least 8 launches (a whole number of
+    # passes over the buffer sets)
     est_us = max(nbytes / 5e3, 2.0)
     reps = max(8, min(512, int(2000 / est_us)))
-    times = {}
-    for v in variants_fitting(form, W):
+    reps = max(n_sets, reps - reps % n_sets)
+    graphs = {}
+    for v in (variants_fitting(form, W) if only is None else only):
         calls = [_launcher(form, s, w, scale, v) for s in sets]
         side = torch.cuda.Stream(device)
         side.wait_stream(torch.cuda.current_stream(device))
@@ -195,24 +211,33 @@ def sweep(form: str, tokens: int, width: int, rounds: int = 3, device=None, max_
         with torch.cuda.graph(g):
             for i in range(reps):
                 calls[i % len(calls)]()
-        g.replay()
+        graphs[v] = g
+    torch.cuda.synchronize(device)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for g in graphs.values():
+            g.replay()
         torch.cuda.synchronize(device)
-        best = float("inf")
-        for _ in range(rounds):
+    samples = {v: [] for v in graphs}
+    for _ in range(rounds):
+        marks = []
+        for v, g in graphs.items():
             a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             g.replay()
             e.record()
-            torch.cuda.synchronize(device)
-            best = min(best, a.elapsed_time(e) * 1e3 / reps)
-        times[v] = best
-        del g
-    return times
+            marks.append((v, a, e))
+        torch.cuda.synchronize(device)
+        for v, a, e in marks:
+            samples[v].append(a.elapsed_time(e) * 1e3 / reps)
+    del graphs
+    return {v: sorted(x)[len(x) // 2] for v, x in samples.items()}
 
 
-def tune(form: str, tokens: int, width: int, margin: float = 0.03, rounds: int = 3, device=None):
+def tune(form: str, tokens: int, width: int, margin: float = 0.03, rounds: int = 5, device=None):
     """Time every fitting variant and install the fastest for (form, bucket of
-    tokens, width) if it beats the heuristic's pick by more than `margin`.
+    tokens, width) if it beats the heuristic's pick by more than `margin`,
+    in the sweep and again in a second timing of the two alone.
     Returns a report: the heuristic's pick and time, the best and its time,
     and the variant installed (-1: the heuristic stays)."""
     op, quant = FORMS[form]
@@ -222,6 +247,11 @@ def tune(form: str, tokens: int, width: int, margin: float = 0.03, rounds: int =
     pick = A.pick_variant(op, T, width, quant)
     best = min(times, key=times.get)
     chosen = best if (pick not in times or times[best] < times[pick] * (1 - margin)) else -1
+    if chosen >= 0 and pick in times:
+        # a second, independent timing of the two must confirm the gain
+        again = sweep(form, T, width, rounds=2 * rounds + 1, device=device, only=[pick, best])
+        if not again[best] < again[pick] * (1 - margin):
+            chosen = -1
     if chosen >= 0:
         set_variant(form, T, width, chosen)
     name = lambda v: A.variant_name(op, v) if v >= 0 else None

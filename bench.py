@@ -52,6 +52,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="skip start-up tuning: the headline runs the library's heuristic variants")
+    ap.add_argument("--no-autotune-report", action="store_true",
+                    help="skip the tuner report over the supplementary shapes")
+    ap.add_argument("--variants", default=None,
+                    help="headline variants by name, 'norm=<name>;swiglu=<name>' (no tuning): to "
+                         "profile the configuration a tuned run chose")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
@@ -202,19 +209,41 @@ def main():
         sw_sets.append(s)
     eps = wn.eps
 
-    def norm_call(i):
-        st = lib.fused_add_rmsnorm(*norm_sets[i % n_norm]["p"], T, H, eps, sp)
+    # Start-up tuning (before any timed region): every variant that fits is
+    # timed on this device at the headline shapes, and one is installed only
+    # if it beats the library's heuristic choice by more than 3%; the step is
+    # then timed with the installed variants (-1: the heuristic's), and once
+    # more with the heuristic's alone for comparison.
+    from activation_add_rmsnorm_amd import tuning
+    tune_report = None
+    if args.variants:
+        given = dict(kv.split("=", 1) for kv in args.variants.split(";"))
+        by_name = lambda op, n: [v for v in range(A.variant_count(op)) if A.variant_name(op, v) == n][0]
+        variant = {"norm": by_name(A.OP_NORM, given["norm"]), "swiglu": by_name(A.OP_SWIGLU, given["swiglu"])}
+    else:
+        if not args.no_tune:
+            tune_report = [tuning.tune("fused_add_rmsnorm", T, H), tuning.tune("swiglu", T, N)]
+        variant = {"norm": tuning.variant_for("fused_add_rmsnorm", T, H),
+                   "swiglu": tuning.variant_for("swiglu", T, N)}
+
+    def norm_call(i, v=None):
+        st = lib.fused_add_rmsnorm_ex(*norm_sets[i % n_norm]["p"], T, H, eps,
+                                      variant["norm"] if v is None else v, sp)
         if st:
             raise A.AarmsError(st, "fused_add_rmsnorm")
 
-    def swiglu_call(i):
-        st = lib.swiglu(*sw_sets[i % n_sw]["p"], T, N, sp)
+    def swiglu_call(i, v=None):
+        st = lib.swiglu_ex(*sw_sets[i % n_sw]["p"], T, N, variant["swiglu"] if v is None else v, sp)
         if st:
             raise A.AarmsError(st, "swiglu")
 
     def step(i):
         norm_call(i)
         swiglu_call(i)
+
+    def step_heuristic(i):
+        norm_call(i, -1)
+        swiglu_call(i, -1)
 
     def stream(*a):
         st = clib.aarms_stream_ceiling(*a, sp)
@@ -234,6 +263,11 @@ def main():
     for i in range(Wu):
         step(i)
     ms_step = timer.region(step, K)
+    if variant["norm"] == -1 and variant["swiglu"] == -1:
+        ms_step_heuristic = ms_step
+    else:
+        timer.warm(step_heuristic, 0.02)
+        ms_step_heuristic = timer.region(step_heuristic, K)
 
     # per-kernel durations: each kernel alone, K back-to-back launches over
     # the same rotation, HIP events on the launch stream at both ends
@@ -268,6 +302,18 @@ def main():
                               **ceiling_entry(swiglu_us, swiglu_ceil_us, step_bytes_swiglu)},
         "buffer_sets_rotated": {"norm": n_norm, "swiglu": n_sw},
     }
+    name = lambda op, v, T_, W_, q: A.variant_name(op, v if v >= 0 else A.pick_variant(op, T_, W_, q))
+    headline_variants = {
+        "norm": name(A.OP_NORM, variant["norm"], T, H, False),
+        "swiglu": name(A.OP_SWIGLU, variant["swiglu"], T, N, 0),
+        "chosen_by": ("given (--variants)" if args.variants else
+                      "start-up tuning" if (variant["norm"] >= 0 or variant["swiglu"] >= 0) else "heuristic"),
+        "heuristic": {"norm": name(A.OP_NORM, -1, T, H, False), "swiglu": name(A.OP_SWIGLU, -1, T, N, 0),
+                      "ms_per_step": round(ms_step_heuristic, 5),
+                      "GB/s": round(step_bytes / (ms_step_heuristic * 1e-3) / 1e9, 1)},
+        "tuning": tune_report,
+    }
+    tuning.clear()
     del norm_sets, sw_sets, x0, r0, gu0
     torch.cuda.empty_cache()
 
@@ -306,6 +352,7 @@ def main():
                         "swiglu bf16 gate_up [4096,17920] -> [4096,8960]",
             "bytes_per_step": step_bytes,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "variants": headline_variants,
         },
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -417,7 +464,8 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
     # start-up autotuning at the workload shapes: the heuristic's variant
     # against the fastest one (graph-replay timings); informational, the
     # figures above use the heuristic
-    out["autotune"] = autotune_report()
+    if not args.no_autotune_report:
+        out["autotune"] = autotune_report()
     return out
 
 
@@ -433,7 +481,7 @@ def autotune_report():
               ("swiglu_quant_nvfp4", 8192, 28672)]
     rows = []
     for form, T, W in shapes:
-        r = tuning.tune(form, T, W, rounds=3)
+        r = tuning.tune(form, T, W)
         r["gain_pct"] = round(100 * (r["heuristic_us"] / r["best_us"] - 1), 1)
         rows.append(r)
     tuning.clear()

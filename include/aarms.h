@@ -308,7 +308,8 @@ const char *aarms_status_string(int status);
  * the end.  ops: 0 = the norms with the residual add (fused_add_rmsnorm*),
  * 3 = the norms without it (rmsnorm*), both on one variant table (quant != 0
  * for a quantised form); 1 = swiglu, swiglu_quant_fp8, swiglu_quant_mxfp4
- * and swiglu_quant_nvfp4 (quant != 0 for the quantised forms); 2 =
+ * and swiglu_quant_nvfp4 (quant = the output format: 0 bf16, 1 E4M3,
+ * 2 MXFP4, 3 NVFP4; -1 is returned for another value); 2 =
  * swiglu_quant_fp8_dynamic.
  * aarms_pick_variant() returns the id the plain entry point would use, or -1
  * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
