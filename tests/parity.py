@@ -105,6 +105,25 @@ def check_norm(x, residual, weight, eps, out_gpu, res_out_gpu) -> NormReport:
                       max_ulps_vs_nominal=int(ulps.max()) if ulps.size else 0)
 
 
+class NormExpectation:
+    """The oracle's results for one fused_add_rmsnorm input, computed once,
+    to check the outputs of many launches (every kernel variant) against."""
+
+    def __init__(self, x, residual, weight, eps):
+        self.res_out = oracle.residual_add(x, residual)
+        self.nominal, self.alt_lo, self.alt_hi = norm_admissible(self.res_out, weight, eps)
+
+    def check(self, out_gpu, res_out_gpu) -> NormReport:
+        bad_res = ~same_bf16(res_out_gpu, self.res_out)
+        assert not bad_res.any(), "residual_out differs at %d positions, first %s" % (
+            bad_res.sum(), np.argwhere(bad_res)[:5].tolist())
+        exact = same_bf16(out_gpu, self.nominal)
+        bad = ~(exact | same_bf16(out_gpu, self.alt_lo) | same_bf16(out_gpu, self.alt_hi))
+        assert not bad.any(), "out outside the admissible set at %d positions, first %s" % (
+            bad.sum(), np.argwhere(bad)[:5].tolist())
+        return NormReport(elements=int(out_gpu.size), not_nominal=int((~exact).sum()))
+
+
 def check_rmsnorm(x, weight, eps, out_gpu) -> NormReport:
     """Assert the GPU's rmsnorm (no residual add) results."""
     nominal, alt_lo, alt_hi = norm_admissible(x, weight, eps)

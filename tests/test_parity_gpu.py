@@ -152,6 +152,20 @@ def test_norm_prefill4096_full():
     announce(P.check_norm(d["x"], d["residual"], d["weight"], wl.eps, out, res_out))
 
 
+def test_norm_prefill4096_full_every_variant():
+    """Every variant that fits the row, at the full Qwen2.5-1.5B prefill
+    shape: start-up tuning may install any of them for this shape."""
+    wl = W.NORM_PREFILL4096
+    d = W.norm_inputs(wl)
+    expect = P.NormExpectation(d["x"], d["residual"], d["weight"], wl.eps)
+    xt, rt, wt = bf16(d["x"]), bf16(d["residual"]), bf16(d["weight"])
+    for v in norm_variants_for(wl.hidden):
+        announce("fused_add_rmsnorm", (wl.tokens, wl.hidden), "variant", v, A.variant_name(A.OP_NORM, v))
+        out, res_out = A.fused_add_rmsnorm(xt, rt, wt, wl.eps, variant=v)
+        torch.cuda.synchronize()
+        expect.check(bits(out), bits(res_out))
+
+
 def test_norm_closed_forms_on_gpu():
     H = 1536
     w = gen.normal_bf16((H,), 0, 3, mean=1.0, std=0.1)
@@ -255,6 +269,18 @@ def test_swiglu_prefill4096_full():
     gu = W.swiglu_inputs(wl)["gate_up"]
     y = run_swiglu(gu)
     P.check_swiglu(gu, y)
+
+
+def test_swiglu_prefill4096_full_every_variant():
+    wl = W.SWIGLU_PREFILL4096
+    gu = W.swiglu_inputs(wl)["gate_up"]
+    y_o = oracle.swiglu(gu)
+    gt = bf16(gu)
+    for v in range(A.variant_count(A.OP_SWIGLU)):
+        announce("swiglu", gu.shape, "variant", v, A.variant_name(A.OP_SWIGLU, v))
+        y = bits(A.swiglu(gt, variant=v))
+        bad = ~P.same_bf16(y, y_o)
+        assert not bad.any(), "variant %d differs at %d positions" % (v, bad.sum())
 
 
 # ------------------------------------------------------------------ swiglu + fp8
