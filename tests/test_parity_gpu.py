@@ -283,6 +283,35 @@ def test_swiglu_prefill4096_full_every_variant():
         assert not bad.any(), "variant %d differs at %d positions" % (v, bad.sum())
 
 
+def test_swiglu_forms_past_65535_rows():
+    """More rows than one grid dimension holds: rows continue in grid z."""
+    T = 2 * 65535 + 7
+    for N in (16, 32):
+        gu = gen.normal_bf16((T, 2 * N), N, 4, std=2.0)
+        gt = bf16(gu)
+        announce("swiglu forms", (T, N))
+        for v in range(A.variant_count(A.OP_SWIGLU)):
+            P.check_swiglu(gu, bits(A.swiglu(gt, variant=v)))
+        s = torch.tensor([0.05], dtype=torch.float32, device=DEV)
+        P.check_swiglu_fp8(gu, 0.05, bits(A.swiglu_quant_fp8(gt, s)))
+        q, sc = A.swiglu_quant_fp8_dynamic(gt)
+        P.check_swiglu_fp8_dynamic(gu, bits(q), bits(sc))
+        q, sc = A.swiglu_quant_nvfp4(gt, s)
+        P.check_swiglu_nvfp4(gu, 0.05, bits(q), bits(sc))
+        if N % 32 == 0:
+            q, sc = A.swiglu_quant_mxfp4(gt)
+            P.check_swiglu_mxfp4(gu, bits(q), bits(sc))
+        torch.cuda.synchronize()
+
+
+def test_norm_many_narrow_rows():
+    T, H = 3 * 65535 + 5, 8
+    x, r, w = norm_case(T, H, seed=77)
+    for v in norm_variants_for(H)[:6]:
+        out, res_out = run_norm(x, r, w, 1e-6, variant=v)
+        P.check_norm(x, r, w, 1e-6, out, res_out)
+
+
 # ------------------------------------------------------------------ swiglu + fp8
 
 def _all_y_rows():
