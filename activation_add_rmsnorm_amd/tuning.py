@@ -37,7 +37,7 @@ import torch
 
 import activation_add_rmsnorm_amd as A
 
-MALL_BYTES = 256e6          # MI355X last-level cache; rotation covers twice this
+MALL_BYTES = 256e6          # MI355X last-level cache; rotation covers three times this
 
 # form -> (variant table op, the quant argument of aarms_pick_variant: a
 # flag for the norms, the output format for swiglu: 0 bf16, 1 E4M3,
@@ -186,7 +186,7 @@ def sweep(form: str, tokens: int, width: int, rounds: int = 5, device=None, max_
     device = torch.device(device or "cuda")
     first, nbytes = _buffers(form, tokens, width, device)
     sets = [first]
-    n_sets = min(max_sets, max(2, math.ceil(2 * MALL_BYTES / max(nbytes, 1))))
+    n_sets = min(max_sets, max(2, math.ceil(3 * MALL_BYTES / max(nbytes, 1))))
     for _ in range(n_sets - 1):
         sets.append({k: (v.clone() if k in ("x", "r", "gu") else torch.empty_like(v)) for k, v in first.items()})
     W = int(width)
