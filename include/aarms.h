@@ -1,12 +1,19 @@
 /*
  * aarms.h -- C ABI of libaarms.so: fused residual-add + RMSNorm, SwiGLU, and
- * their FP8 (E4M3) epilogues, as hand-written HIP kernels for gfx950 (MI355X).
+ * their FP8 (E4M3) and block-scaled FP4 (MXFP4, NVFP4) epilogues, as
+ * hand-written HIP kernels for gfx950 (MI355X).
  *
  * Data formats
  *   bf16  : 16-bit bit pattern (the top half of an IEEE binary32), passed as
  *           uint16 storage.
  *   fp8   : one byte, OCP E4M3FN (exponent bias 7, 3 mantissa bits, no
  *           infinities, 0x7F/0xFF are NaN, largest finite 448).
+ *   fp4   : E2M1 codes (sign, 2 exponent bits, 1 mantissa bit: 0, 0.5, 1,
+ *           1.5, 2, 3, 4, 6), two per byte, the first value of each pair in
+ *           the low nibble.
+ *   e8m0  : one byte, a power of two 2^(b - 127); 0xFF is NaN (MXFP4 block
+ *           scales, one per 32 values).
+ *   NVFP4 block scales are fp8 E4M3 bytes, one per 16 values.
  *   All tensors are dense and row-major; a "row" is one token.
  *
  * Conventions common to every entry point
@@ -20,7 +27,7 @@
  *   - Arguments are validated before anything is enqueued; on any error code
  *     nothing has been launched.  No C++ exception crosses this interface.
  *   - Tensor pointers must be 16-byte aligned; fp32 scale pointers 4-byte
- *     aligned; E8M0 scale bytes unaligned.
+ *     aligned; block-scale byte arrays (E8M0, E4M3) may have any alignment.
  *   - Outputs may not overlap any other argument, except the in-place pairs
  *     each entry point names.  Inputs may overlap each other.
  *   - Results are deterministic: the same inputs give the same bits on every
