@@ -28,7 +28,7 @@ int check_width(int64_t tokens, int64_t width, int64_t max_width)
     if (tokens < 0 || width <= 0 || width % 8 != 0) return AARMS_ERR_BAD_SHAPE;
     if (max_width > 0 && width > max_width) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (tokens > 0 && width > AARMS_MAX_ELEMENTS / tokens) return AARMS_ERR_UNSUPPORTED_SHAPE;
-    if (tokens > INT32_MAX) return AARMS_ERR_UNSUPPORTED_SHAPE;
+    if (tokens > AARMS_MAX_TOKENS) return AARMS_ERR_UNSUPPORTED_SHAPE;
     return AARMS_OK;
 }
 

@@ -66,7 +66,7 @@ enum aarms_status {
     AARMS_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                 */
     AARMS_ERR_BAD_SHAPE = 2,         /* negative size, zero width, width % 8 != 0
                                         (% 32 for MXFP4, % 16 for NVFP4)          */
-    AARMS_ERR_UNSUPPORTED_SHAPE = 3, /* width or element count beyond the limits   */
+    AARMS_ERR_UNSUPPORTED_SHAPE = 3, /* width, rows or element count beyond the limits */
     AARMS_ERR_MISALIGNED = 4,        /* pointer alignment not met                  */
     AARMS_ERR_ALIAS = 5,             /* an output overlaps another argument        */
     AARMS_ERR_BAD_EPS = 6,           /* eps negative, NaN or infinite              */
@@ -77,6 +77,7 @@ enum aarms_status {
 /* Limits. */
 #define AARMS_MAX_HIDDEN 65536            /* norms: row width kept in registers    */
 #define AARMS_MAX_ELEMENTS (1LL << 40)    /* tokens x width, per tensor            */
+#define AARMS_MAX_TOKENS 2147483647LL     /* rows per call (the launch grids)     */
 #define AARMS_MAX_INTER (1LL << 33)       /* swiglu: output row width              */
 #define AARMS_MAX_INTER_PER_TOKEN 65536   /* swiglu_quant_fp8_dynamic: row kept in
                                              registers until its amax is known    */

@@ -252,6 +252,10 @@ def test_swiglu_errors():
     assert swq(lib, T=0, out=0, gu=0, scale=0) == OK
     n = A.variant_count(A.OP_SWIGLU)
     assert lib.swiglu_ex(P, P + BIG, 4, 8960, n, None) == VARIANT
+    # more rows than the launch grids can index (within the element limit)
+    assert sw(lib, T=(1 << 31), N=8) == UNSUP
+    assert sw(lib, T=(1 << 31) - 1, N=8, out=0) == NULLP       # the limit itself passes the shape checks
+    assert swq(lib, T=1 << 31, N=8) == UNSUP
 
 
 def swd(lib, out=P, scale=P + BIG, gu=P + 2 * BIG, T=4, N=8960, variant=-1):
@@ -260,6 +264,7 @@ def swd(lib, out=P, scale=P + BIG, gu=P + 2 * BIG, T=4, N=8960, variant=-1):
 
 def test_swiglu_dynamic_errors():
     lib = A.load()
+    assert swd(lib, T=1 << 31, N=8) == UNSUP
     assert swd(lib, T=-1) == SHAPE
     assert swd(lib, N=12) == SHAPE
     assert swd(lib, N=65536 + 8) == UNSUP                   # row kept in registers
