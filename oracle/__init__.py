@@ -1,4 +1,5 @@
-"""CPU oracle for fused residual-add + RMSNorm, SwiGLU and their FP8 epilogues.
+"""CPU oracle for fused residual-add + RMSNorm, SwiGLU and their FP8 and
+block-scaled FP4 (MXFP4, NVFP4) epilogues.
 
 TEST INFRASTRUCTURE ONLY: the test-suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may use it; the product path never does.  It

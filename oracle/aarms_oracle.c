@@ -1,6 +1,6 @@
 /*
  * aarms_oracle.c -- plain CPU oracle for fused residual-add + RMSNorm, SwiGLU
- * and their FP8 (E4M3) epilogues.
+ * and their FP8 (E4M3) and block-scaled FP4 (MXFP4, NVFP4) epilogues.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
  * bench's CPU-baseline leg load this file's library.  It shares no code,
