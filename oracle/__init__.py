@@ -64,6 +64,7 @@ def _lib():
                 "aarms_oracle_rmsnorm": (None, [u16p, u16p, i64, i64, f32, u16p, f32p]),
                 "aarms_oracle_quant_fp8_static": (None, [u16p, i64, f32, u8p]),
                 "aarms_oracle_quant_fp8_per_row": (None, [u16p, i64, i64, u8p, f32p]),
+                "aarms_oracle_quant_fp8_per_group": (None, [u16p, i64, i64, i64, u8p, f32p]),
                 "aarms_oracle_fused_add_rmsnorm_quant_fp8": (
                     None, [u16p, u16p, u16p, i64, i64, f32, u16p, u8p, f32p, u16p, f32p]),
                 "aarms_oracle_silu_bf16": (C.c_uint16, [C.c_uint16]),
@@ -206,6 +207,45 @@ def quant_fp8_per_row(y):
     s = np.empty(T, np.float32)
     _lib().aarms_oracle_quant_fp8_per_row(y, T, H, q, s)
     return q, s
+
+
+FP8_GROUP = 128   # values per scale group of the per-group (block) E4M3 forms
+
+
+def quant_fp8_per_group(y, group: int = FP8_GROUP):
+    """Returns (q, s): for each row, groups of `group` consecutive values,
+    s[row, g] = max|y| over the group / 448 (binary32), and the E4M3 codes of
+    y divided by its group's scale."""
+    y = _u16(y)
+    T, H = _rows(y)
+    if group <= 0 or H % group:
+        raise ValueError("the row width must be a multiple of the group size")
+    q = np.empty((T, H), np.uint8)
+    s = np.empty((T, H // group), np.float32)
+    _lib().aarms_oracle_quant_fp8_per_group(y, T, H, group, q, s)
+    return q, s
+
+
+def fused_add_rmsnorm_quant_fp8_group(x, residual, weight, eps: float, group: int = FP8_GROUP):
+    """fused_add_rmsnorm, its bf16 output quantised per group.  Returns (q,
+    s [T, H/group], residual_out, y, rs)."""
+    out, res_out, rs = fused_add_rmsnorm(x, residual, weight, eps)
+    q, s = quant_fp8_per_group(out, group)
+    return q, s, res_out, out, rs
+
+
+def rmsnorm_quant_fp8_group(x, weight, eps: float, group: int = FP8_GROUP):
+    """rmsnorm (no residual add), quantised per group.  Returns (q, s, y, rs)."""
+    out, rs = rmsnorm(x, weight, eps)
+    q, s = quant_fp8_per_group(out, group)
+    return q, s, out, rs
+
+
+def swiglu_quant_fp8_group(gate_up, group: int = FP8_GROUP):
+    """swiglu, quantised per group.  Returns (q, s [T, N/group], y)."""
+    y = swiglu(gate_up)
+    q, s = quant_fp8_per_group(y, group)
+    return q, s, y
 
 
 def fused_add_rmsnorm_quant_fp8(x, residual, weight, eps: float):

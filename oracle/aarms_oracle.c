@@ -313,6 +313,30 @@ void aarms_oracle_quant_fp8_per_row(const uint16_t *y, int64_t T, int64_t H,
     }
 }
 
+/* Per-group (dynamic, block) scales: each row in groups of G consecutive
+ * values; s[row, g] = f32(max |y| over the group / 448), and each element is
+ * divided by its group's scale -- the per-token rule above, applied to each
+ * group ("TensorRT-LLM" walkthrough, Part V: FP8 scales per tensor or per
+ * block).  H is a multiple of G; s is [T, H / G]. */
+void aarms_oracle_quant_fp8_per_group(const uint16_t *y, int64_t T, int64_t H, int64_t G,
+                                      uint8_t *q, float *s)
+{
+    const int64_t groups = H / G;
+    #pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < T; ++row) {
+        for (int64_t g = 0; g < groups; ++g) {
+            const int64_t first = row * H + g * G;
+            float a = 0.0f;
+            for (int64_t j = 0; j < G; ++j)
+                a = fmaxf(a, fabsf(aarms_oracle_bf16_to_f32(y[first + j])));
+            const float sc = a / 448.0f;
+            s[row * groups + g] = sc;
+            for (int64_t j = 0; j < G; ++j)
+                q[first + j] = quant_e4m3(aarms_oracle_bf16_to_f32(y[first + j]), sc);
+        }
+    }
+}
+
 /* fused_add_rmsnorm_quant_fp8: the norm as above, its bf16 output quantised
  * per token. */
 void aarms_oracle_fused_add_rmsnorm_quant_fp8(const uint16_t *x, const uint16_t *res,

@@ -704,3 +704,109 @@ def test_golden_workload_shapes_from_pages():
     assert round(moved / 1e6) == tune["megabytes_moved_at_4096_rows"]
     prefill = gold["prefill_intermediate"]
     assert prefill["rows"] * prefill["cols"] == 2048 * C.SWIGLU_PREFILL4096.inter
+
+
+# ------------------------------------------------------------------ per-group FP8
+
+def _torch_group_quant(yf: np.ndarray, G: int):
+    """torch: per group of G values, s = amax / 448, q = clamp(y / s) -> E4M3."""
+    T, H = yf.shape
+    yt = torch.from_numpy(yf.copy()).reshape(T, H // G, G)
+    st = yt.abs().amax(dim=2, keepdim=True) / 448.0
+    z = torch.where(st == 0, yt, yt / torch.where(st == 0, torch.ones_like(st), st))
+    q = torch.clamp(z, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8).reshape(T, H).numpy()
+    return q, st.reshape(T, H // G).numpy()
+
+
+def test_per_group_quant_against_torch_and_invariants():
+    """Per-group (block) E4M3, groups of 128: every non-zero group reaches 448
+    exactly, its scale is f32(amax / 448), all-zero groups give s = 0 and zero
+    codes; the codes equal torch's per-group clamp-and-convert."""
+    G = oracle.FP8_GROUP
+    assert G == 128
+    y = gen.normal_bf16((16, 1024), 21, 1, outlier_frac=0.001)
+    y[2, 128:256] = 0                                  # one all-zero group
+    y[3, :] = oracle.bf16_from_f64(1e-3)
+    y[3, 300] = oracle.bf16_from_f64(37.5)             # one outlier in group 2 only
+    q, s = oracle.quant_fp8_per_group(y)
+    assert q.shape == y.shape and s.shape == (16, 1024 // G)
+    yf = f32_of(y)
+    amax = np.abs(yf).reshape(16, -1, G).max(axis=2)
+    qa = np.abs(oracle.e4m3_table()[q]).reshape(16, -1, G)
+    assert s[2, 1] == 0 and np.all(qa[2, 1] == 0)
+    nz = amax > 0
+    assert np.array_equal(s[nz], (amax[nz].astype(np.float32) / np.float32(448)).astype(np.float32))
+    assert np.all(qa.max(axis=2)[nz] == 448.0)
+    assert q[3, 300] == 0x7E and s[3, 2] == np.float32(37.5) / np.float32(448)
+    assert s[3, 0] == np.float32(oracle.bf16_to_f32(oracle.bf16_from_f64(1e-3))) / np.float32(448)
+    qt, st = _torch_group_quant(yf, G)
+    assert np.array_equal(q, qt) and np.array_equal(s, st)
+
+
+def test_per_group_quant_reduces_to_per_row_and_catches_swapped_groups():
+    y = gen.normal_bf16((8, 512), 22, 1, std=3.0)
+    # one group the width of the row is the per-token form
+    qg, sg = oracle.quant_fp8_per_group(y, 512)
+    qr, sr = oracle.quant_fp8_per_row(y)
+    assert np.array_equal(qg, qr) and np.array_equal(sg[:, 0], sr)
+    # per-group codes differ from per-row codes (the scales are the groups')
+    q, s = oracle.quant_fp8_per_group(y)
+    assert not np.array_equal(q, qr)
+    # a group quantised with its neighbour's scale is wrong somewhere
+    yf = f32_of(y)
+    swapped = np.concatenate([s[:, 1:2], s[:, 0:1], s[:, 2:]], axis=1)
+    z = yf / np.repeat(swapped, 128, axis=1)
+    wrong = torch.from_numpy(np.clip(z, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert not np.array_equal(q, wrong)
+
+
+def test_per_group_quant_exact_on_a_small_case():
+    """Brute force: q = nearest-even E4M3 of the binary32 quotient y / s, with
+    s the binary32 rounding of amax / 448, all in exact rationals."""
+    y = gen.normal_bf16((3, 256), 23, 1, std=5.0)
+    y[1, 5] = oracle.bf16_from_f64(-300.0)
+    q, s = oracle.quant_fp8_per_group(y)
+    yf = f32_of(y)
+    for r in range(3):
+        for g in range(2):
+            vals = [Fraction(float(v)) for v in yf[r, g * 128:(g + 1) * 128]]
+            amax = max(abs(v) for v in vals)
+            sc = exact.round_to_f32(amax / 448)
+            assert float(s[r, g]) == sc
+            for j, v in enumerate(vals):
+                z = exact.round_to_f32(v / Fraction(sc))
+                z = max(min(Fraction(z), Fraction(448)), Fraction(-448))
+                code = exact.round_to_e4m3(z)              # sign bit included
+                got = int(q[r, g * 128 + j])
+                if z == 0:
+                    assert got & 0x7F == 0                     # a signed zero
+                else:
+                    assert got == code
+
+
+def test_per_group_quant_special_values():
+    y = np.full((2, 256), oracle.bf16_from_f64(0.5), np.uint16)
+    y[0, 3] = 0x7FC0                                   # NaN: ignored by the group amax, stays NaN
+    y[1, 130] = 0x7F80                                 # +inf: the group's scale is inf
+    q, s = oracle.quant_fp8_per_group(y)
+    assert s[0, 0] == np.float32(0.5) / np.float32(448) and (q[0, 3] & 0x7F) == 0x7F
+    assert q[0, 4] == 0x7E                              # 0.5 / s = 448
+    assert np.isinf(s[1, 1]) and s[1, 0] == np.float32(0.5) / np.float32(448)
+    assert np.all((q[1, 128:256] & 0x7F)[np.arange(128) != 2] == 0)   # finite / inf = 0
+    assert (q[1, 130] & 0x7F) == 0x7F                   # inf / inf = NaN
+
+
+def test_per_group_compositions():
+    x = gen.normal_bf16((16, 1024), 24, 1)
+    r = gen.normal_bf16((16, 1024), 24, 2)
+    w = gen.normal_bf16((1024,), 24, 3, mean=1.0, std=0.1)
+    q, s, ro, y, _ = oracle.fused_add_rmsnorm_quant_fp8_group(x, r, w, 1e-5)
+    out, ro2, _ = oracle.fused_add_rmsnorm(x, r, w, 1e-5)
+    assert np.array_equal(y, out) and np.array_equal(ro, ro2)
+    assert all(np.array_equal(a, b) for a, b in zip((q, s), oracle.quant_fp8_per_group(out)))
+    q, s, y, _ = oracle.rmsnorm_quant_fp8_group(x, w, 1e-5)
+    assert np.array_equal(y, oracle.rmsnorm(x, w, 1e-5)[0])
+    gu = gen.normal_bf16((8, 2048), 24, 4, std=2.0)
+    q, s, y = oracle.swiglu_quant_fp8_group(gu)
+    assert np.array_equal(y, oracle.swiglu(gu)) and s.shape == (8, 1024 // 128)
+    assert all(np.array_equal(a, b) for a, b in zip((q, s), oracle.quant_fp8_per_group(y)))
