@@ -107,6 +107,12 @@ def load():
             "rmsnorm_quant_fp8_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],
             "rmsnorm_quant_fp8_static_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],
             "swiglu_quant_fp8_dynamic_ex": [vp, vp, vp, i64, i64, i32, vp],
+            "fused_add_rmsnorm_quant_fp8_group": [vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
+            "fused_add_rmsnorm_quant_fp8_group_ex": [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "rmsnorm_quant_fp8_group": [vp, vp, vp, vp, i64, i64, f32, vp],
+            "rmsnorm_quant_fp8_group_ex": [vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "swiglu_quant_fp8_group": [vp, vp, vp, i64, i64, vp],
+            "swiglu_quant_fp8_group_ex": [vp, vp, vp, i64, i64, i32, vp],
             "aarms_variant_count": [i32],
             "aarms_pick_variant": [i32, i64, i64, i32],
         }
@@ -467,6 +473,86 @@ def swiglu_quant_fp8(gate_up: torch.Tensor, scale: torch.Tensor, out: torch.Tens
     _check(lib.swiglu_quant_fp8_ex(out.data_ptr(), gate_up.data_ptr(), scale.data_ptr(), T, N,
                                    int(variant), _stream(gate_up.device)), "swiglu_quant_fp8")
     return out
+
+
+FP8_GROUP = 128   # values per scale of the per-group (block) E4M3 forms
+
+
+def _group_outputs(T, W, device, out, scale_out):
+    if W % FP8_GROUP:
+        raise ValueError("the row width must be a multiple of %d for per-group E4M3" % FP8_GROUP)
+    if out is None:
+        out = torch.empty((T, W), dtype=torch.float8_e4m3fn, device=device)
+    if scale_out is None:
+        scale_out = torch.empty((T, W // FP8_GROUP), dtype=torch.float32, device=device)
+    _require(out, "out", FP8_DTYPES, (T, W))
+    _require(scale_out, "scale_out", (torch.float32,), (T, W // FP8_GROUP))
+    return out, scale_out
+
+
+def fused_add_rmsnorm_quant_fp8_group(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor,
+                                      eps: float, out: torch.Tensor | None = None,
+                                      scale_out: torch.Tensor | None = None,
+                                      residual_out: torch.Tensor | None = None, variant: int = -1):
+    """fused_add_rmsnorm with E4M3 codes under an fp32 scale per 128 values.
+    Returns (q [T, H] fp8, scale [T, H/128] fp32, residual_out [T, H] bf16)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(residual, "residual", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    out, scale_out = _group_outputs(T, H, x.device, out, scale_out)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _require(residual_out, "residual_out", (torch.bfloat16,), (T, H))
+    _same_device(x, residual, weight, out, scale_out, residual_out)
+    lib = load()
+    variant = _variant("fused_add_rmsnorm_quant_fp8_group", T, H, variant)
+    _check(lib.fused_add_rmsnorm_quant_fp8_group_ex(out.data_ptr(), scale_out.data_ptr(),
+                                                    residual_out.data_ptr(), x.data_ptr(),
+                                                    residual.data_ptr(), weight.data_ptr(), T, H,
+                                                    float(eps), int(variant), _stream(x.device)),
+           "fused_add_rmsnorm_quant_fp8_group")
+    return out, scale_out, residual_out
+
+
+def rmsnorm_quant_fp8_group(x: torch.Tensor, weight: torch.Tensor, eps: float,
+                            out: torch.Tensor | None = None, scale_out: torch.Tensor | None = None,
+                            variant: int = -1):
+    """rmsnorm with E4M3 codes under an fp32 scale per 128 values.
+    Returns (q [T, H] fp8, scale [T, H/128] fp32)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, hidden]")
+    T, H = x.shape
+    _require(x, "x", (torch.bfloat16,), (T, H))
+    _require(weight, "weight", (torch.bfloat16,), (H,))
+    out, scale_out = _group_outputs(T, H, x.device, out, scale_out)
+    _same_device(x, weight, out, scale_out)
+    lib = load()
+    variant = _variant("rmsnorm_quant_fp8_group", T, H, variant)
+    _check(lib.rmsnorm_quant_fp8_group_ex(out.data_ptr(), scale_out.data_ptr(), x.data_ptr(),
+                                          weight.data_ptr(), T, H, float(eps), int(variant),
+                                          _stream(x.device)), "rmsnorm_quant_fp8_group")
+    return out, scale_out
+
+
+def swiglu_quant_fp8_group(gate_up: torch.Tensor, out: torch.Tensor | None = None,
+                           scale_out: torch.Tensor | None = None, variant: int = -1):
+    """swiglu with E4M3 codes under an fp32 scale per 128 outputs.
+    Returns (q [T, N] fp8, scale [T, N/128] fp32)."""
+    if gate_up.dim() != 2 or gate_up.shape[1] % 2:
+        raise ValueError("gate_up must be [tokens, 2 * inter]")
+    T, N = gate_up.shape[0], gate_up.shape[1] // 2
+    _require(gate_up, "gate_up", (torch.bfloat16,), (T, 2 * N))
+    out, scale_out = _group_outputs(T, N, gate_up.device, out, scale_out)
+    _same_device(gate_up, out, scale_out)
+    lib = load()
+    variant = _variant("swiglu_quant_fp8_group", T, N, variant)
+    _check(lib.swiglu_quant_fp8_group_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(),
+                                         T, N, int(variant), _stream(gate_up.device)),
+           "swiglu_quant_fp8_group")
+    return out, scale_out
 
 
 def swiglu_quant_fp8_dynamic(gate_up: torch.Tensor, out: torch.Tensor | None = None,

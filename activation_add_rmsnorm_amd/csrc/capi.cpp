@@ -23,6 +23,8 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.h
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Row-width checks shared by all ops.
+static_assert(FP8_GROUP == AARMS_FP8_GROUP, "the kernels' group is the header's");
+
 int check_width(int64_t tokens, int64_t width, int64_t max_width)
 {
     if (tokens < 0 || width <= 0 || width % 8 != 0) return AARMS_ERR_BAD_SHAPE;
@@ -153,7 +155,8 @@ int pick_swiglu(int64_t tokens, int64_t inter, int epi)
     // per lane from about 32 million outputs, when a row is a whole number
     // of 512-job blocks (otherwise the last block of every row is mostly
     // idle: N = 8960 rows have 1120 jobs).
-    if (epi == SWIGLU_EPI_FP8 && tokens > kSwigluFp8TwoJobOutputs / inter) return swiglu_find(2, 8);
+    if ((epi == SWIGLU_EPI_FP8 || epi == SWIGLU_EPI_FP8_GROUP) && tokens > kSwigluFp8TwoJobOutputs / inter)
+        return swiglu_find(2, 8);
     if (epi == SWIGLU_EPI_NVFP4 && tokens > kSwigluNvfp4TwoJobOutputs / inter && (inter / 8) % 512 == 0)
         return swiglu_find(2, 8);
     return swiglu_find(1, 8);
@@ -189,12 +192,14 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
                 const void *x, const void *residual, const void *weight, int64_t tokens,
                 int64_t hidden, float eps, int epi, bool res, int variant, hipStream_t stream)
 {
-    const bool dyn = epi == NORM_EPI_FP8_DYNAMIC, stat = epi == NORM_EPI_FP8_STATIC;
+    const bool stat = epi == NORM_EPI_FP8_STATIC, grp = epi == NORM_EPI_FP8_GROUP;
+    const bool dyn = epi == NORM_EPI_FP8_DYNAMIC || grp;    // scales written to scale_out (fp32)
     const bool mx = epi == NORM_EPI_MXFP4, nv = epi == NORM_EPI_NVFP4;
     const bool fp4 = mx || nv;
     int st = check_width(tokens, hidden, AARMS_MAX_HIDDEN);
     if (st) return st;
-    if ((mx && hidden % 32 != 0) || (nv && hidden % 16 != 0)) return AARMS_ERR_BAD_SHAPE;
+    if ((mx && hidden % 32 != 0) || (nv && hidden % 16 != 0) || (grp && hidden % FP8_GROUP != 0))
+        return AARMS_ERR_BAD_SHAPE;
     if ((st = check_eps(eps))) return st;
     if (variant < -1 || variant >= norm_variant_count()) return AARMS_ERR_BAD_VARIANT;
     if (tokens == 0) return AARMS_OK;
@@ -227,7 +232,9 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     }
     if (dyn || fp4) {
         partner[n_out] = -1;
-        outs[n_out++] = {span(scale_out, mx ? elems / 32 : nv ? elems / 16 : 4 * (uint64_t)tokens), scale_out};
+        outs[n_out++] = {span(scale_out, mx ? elems / 32 : nv ? elems / 16
+                                         : grp ? 4 * (elems / FP8_GROUP) : 4 * (uint64_t)tokens),
+                         scale_out};
     }
     if ((st = check_outputs(outs, partner, n_out, ins, n_in))) return st;
     if (variant == -1) variant = pick_norm(tokens, hidden, epi != NORM_EPI_BF16, res);
@@ -247,27 +254,34 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     return launch_status(launch_norm(p, epi, res, variant, device_cus(), stream));
 }
 
-// swiglu, its static E4M3 form (scale) and its MXFP4 form (scale_out).
+// swiglu, its static E4M3 form (scale), its FP4 forms (codes, byte scales
+// to scale_out) and its per-group E4M3 form (codes, fp32 scales to
+// scale_out).
 int swiglu_common(void *out, const void *gate_up, const float *scale, uint8_t *scale_out,
                   int64_t tokens, int64_t inter, int epi, int variant, hipStream_t stream)
 {
     const bool fp8 = epi == SWIGLU_EPI_FP8, mx = epi == SWIGLU_EPI_MXFP4, nv = epi == SWIGLU_EPI_NVFP4;
-    const bool with_scale = fp8 || nv, fp4 = mx || nv;
+    const bool grp = epi == SWIGLU_EPI_FP8_GROUP;
+    const bool with_scale = fp8 || nv, fp4 = mx || nv, with_sout = fp4 || grp;
     int st = check_width(tokens, inter, 0);
     if (st) return st;
-    if ((mx && inter % 32 != 0) || (nv && inter % 16 != 0)) return AARMS_ERR_BAD_SHAPE;
+    if ((mx && inter % 32 != 0) || (nv && inter % 16 != 0) || (grp && inter % FP8_GROUP != 0))
+        return AARMS_ERR_BAD_SHAPE;
     if (inter > AARMS_MAX_INTER) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (tokens > 0 && 2 * inter > AARMS_MAX_ELEMENTS / tokens) return AARMS_ERR_UNSUPPORTED_SHAPE;
     if (variant < -1 || variant >= swiglu_variant_count()) return AARMS_ERR_BAD_VARIANT;
     if (tokens == 0) return AARMS_OK;
-    if (!out || !gate_up || (with_scale && !scale) || (fp4 && !scale_out)) return AARMS_ERR_NULL_POINTER;
-    if (!aligned(out, 16) || !aligned(gate_up, 16) || (with_scale && !aligned(scale, 4)))
+    if (!out || !gate_up || (with_scale && !scale) || (with_sout && !scale_out)) return AARMS_ERR_NULL_POINTER;
+    if (!aligned(out, 16) || !aligned(gate_up, 16) || (with_scale && !aligned(scale, 4)) ||
+        (grp && !aligned(scale_out, 4)))
         return AARMS_ERR_MISALIGNED;
     const uint64_t elems = (uint64_t)tokens * (uint64_t)inter;
     Arg outs[2];
     int n_out = 0;
-    outs[n_out++] = {span(out, fp8 ? elems : fp4 ? elems / 2 : 2 * elems), out};
-    if (fp4) outs[n_out++] = {span(scale_out, mx ? elems / 32 : elems / 16), scale_out};
+    outs[n_out++] = {span(out, (fp8 || grp) ? elems : fp4 ? elems / 2 : 2 * elems), out};
+    if (with_sout)
+        outs[n_out++] = {span(scale_out, mx ? elems / 32 : nv ? elems / 16 : 4 * (elems / FP8_GROUP)),
+                         scale_out};
     const Arg ins[2] = {{span(gate_up, 4 * elems), gate_up}, {span(scale, with_scale ? 4 : 0), scale}};
     const int partner[2] = {-1, -1};
     if ((st = check_outputs(outs, partner, n_out, ins, with_scale ? 2 : 1))) return st;
@@ -276,7 +290,7 @@ int swiglu_common(void *out, const void *gate_up, const float *scale, uint8_t *s
     p.out = out;
     p.gate_up = gate_up;
     p.scale = with_scale ? scale : nullptr;
-    p.scale_out = fp4 ? (float *)scale_out : nullptr;
+    p.scale_out = with_sout ? (float *)scale_out : nullptr;
     p.tokens = tokens;
     p.inter = inter;
     p.vecs_per_row = (uint32_t)(inter / 8);
@@ -583,12 +597,59 @@ const char *aarms_variant_name(int op, int variant)
     return nullptr;
 }
 
+int fused_add_rmsnorm_quant_fp8_group(void *out_fp8, float *scale_out, void *residual_out,
+                                      const void *x, const void *residual, const void *weight,
+                                      int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream)
+{
+    return norm_common(out_fp8, scale_out, nullptr, residual_out, x, residual, weight, num_tokens,
+                       hidden, eps, NORM_EPI_FP8_GROUP, true, -1, stream);
+}
+
+int fused_add_rmsnorm_quant_fp8_group_ex(void *out_fp8, float *scale_out, void *residual_out,
+                                         const void *x, const void *residual, const void *weight,
+                                         int64_t num_tokens, int64_t hidden, float eps, int variant,
+                                         hipStream_t stream)
+{
+    return norm_common(out_fp8, scale_out, nullptr, residual_out, x, residual, weight, num_tokens,
+                       hidden, eps, NORM_EPI_FP8_GROUP, true, variant, stream);
+}
+
+int rmsnorm_quant_fp8_group(void *out_fp8, float *scale_out, const void *x, const void *weight,
+                            int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream)
+{
+    return norm_common(out_fp8, scale_out, nullptr, nullptr, x, nullptr, weight, num_tokens, hidden, eps,
+                       NORM_EPI_FP8_GROUP, false, -1, stream);
+}
+
+int rmsnorm_quant_fp8_group_ex(void *out_fp8, float *scale_out, const void *x, const void *weight,
+                               int64_t num_tokens, int64_t hidden, float eps, int variant,
+                               hipStream_t stream)
+{
+    return norm_common(out_fp8, scale_out, nullptr, nullptr, x, nullptr, weight, num_tokens, hidden, eps,
+                       NORM_EPI_FP8_GROUP, false, variant, stream);
+}
+
+int swiglu_quant_fp8_group(void *out_fp8, float *scale_out, const void *gate_up, int64_t num_tokens,
+                           int64_t inter, hipStream_t stream)
+{
+    return swiglu_common(out_fp8, gate_up, nullptr, (uint8_t *)scale_out, num_tokens, inter,
+                         SWIGLU_EPI_FP8_GROUP, -1, stream);
+}
+
+int swiglu_quant_fp8_group_ex(void *out_fp8, float *scale_out, const void *gate_up, int64_t num_tokens,
+                              int64_t inter, int variant, hipStream_t stream)
+{
+    return swiglu_common(out_fp8, gate_up, nullptr, (uint8_t *)scale_out, num_tokens, inter,
+                         SWIGLU_EPI_FP8_GROUP, variant, stream);
+}
+
 int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant)
 {
     if (op == 0 || op == 3) return pick_norm(num_tokens, width, quant != 0, op == 0);
     if (op == 1) {
-        // quant: the output format (0 bf16, 1 E4M3, 2 MXFP4, 3 NVFP4)
-        if (width <= 0 || width % 8 != 0 || quant < 0 || quant > 3) return -1;
+        // quant: the output format (0 bf16, 1 E4M3, 2 MXFP4, 3 NVFP4, 4 E4M3
+        // with a scale per 128 outputs)
+        if (width <= 0 || width % 8 != 0 || quant < 0 || quant > 4) return -1;
         return pick_swiglu(num_tokens, width, quant);
     }
     if (op == 2) return (width > 0 && width % 8 == 0) ? pick_swiglu_rowq(num_tokens, width) : -1;

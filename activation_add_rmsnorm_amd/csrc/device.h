@@ -302,6 +302,21 @@ __device__ __forceinline__ float wave_max(float v)
     return swap_max_f32<32>(v);
 }
 
+// Maximum over each group of 16 adjacent lanes (one DPP row), or with
+// LANES == 32 over each aligned pair of rows; NaN is ignored (fmaxf), as in
+// the row amax.  Every lane of a group ends with the group's value.
+template <int LANES>
+__device__ __forceinline__ float group_max(float v)
+{
+    static_assert(LANES == 16 || LANES == 32, "one or two DPP rows");
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_MIRROR>(__float_as_uint(v))));
+    if constexpr (LANES == 32) v = swap_max_f32<16>(v);
+    return v;
+}
+
 // Cross-wave combine of a block's per-wave partials in LDS (N <= 16 of them):
 // lane i < N of every wave reads partial i, a 16-lane butterfly (same
 // involutions as above) combines them, and lane 0's value is broadcast.

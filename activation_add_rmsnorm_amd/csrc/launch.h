@@ -15,7 +15,12 @@ enum NormEpilogue : int {
     NORM_EPI_MXFP4 = 3,       // MXFP4 out: E2M1 codes, E8M0 scale per 32 values to scale_out
     NORM_EPI_NVFP4 = 4,       // NVFP4 out: E2M1 codes, E4M3 scale per 16 values to scale_out,
                               // fp32 tensor scale from scale_in
+    NORM_EPI_FP8_GROUP = 5,   // E4M3 out, fp32 scale per 128 values to scale_out [T, H/128]
 };
+
+// Values per scale of the per-group (block) E4M3 forms: the slices of 16
+// adjacent lanes (one DPP row).
+constexpr int FP8_GROUP = 128;
 
 struct NormParams {
     void *out;               // bf16 [T,H], or fp8 [T,H] when quantising
@@ -37,6 +42,7 @@ enum SwigluEpilogue : int {
     SWIGLU_EPI_MXFP4 = 2,     // E2M1 codes, E8M0 scale per 32 outputs to scale_out
     SWIGLU_EPI_NVFP4 = 3,     // E2M1 codes, E4M3 scale per 16 outputs to scale_out, tensor
                               // scale from scale
+    SWIGLU_EPI_FP8_GROUP = 4, // E4M3 codes, fp32 scale per 128 outputs to scale_out [T, N/128]
 };
 
 struct SwigluParams {

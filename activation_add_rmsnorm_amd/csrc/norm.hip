@@ -236,6 +236,45 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
             st_stream(qo + v, q);
             if ((lane & 1) == 0) so[v >> 1] = (uint8_t)sb;
         }
+    } else if constexpr (EPI == NORM_EPI_FP8_GROUP) {
+        // ---- y as above; per 128-value group (the slices of 16 adjacent
+        // lanes, one DPP row) the scale s = amax / 448, then the E4M3 codes of
+        // y / s.  Every lane takes part in the group maximum (slices past the
+        // row end hold w = 0, so y = 0; H is a multiple of 128, so a group is
+        // all inside or all past the row end).
+        uint8_t *qo = (uint8_t *)p.out + base;
+        float *so = p.scale_out + (size_t)row * (size_t)(p.hidden / FP8_GROUP);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int v = lane + k * WPR * 64;
+            float yf[8];
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t y = norm_word(rv[k][e], wv[k][e], rs);
+                yf[2 * e] = bf_lo(y);
+                yf[2 * e + 1] = bf_hi(y);
+                amax = fmaxf(amax, fmaxf(__builtin_fabsf(yf[2 * e]), __builtin_fabsf(yf[2 * e + 1])));
+            }
+            amax = group_max<16>(amax);
+            if (v >= nvec) continue;
+            const float s = amax / 448.0f;
+            if ((lane & 15) == 0) so[v >> 4] = s;
+            const E4m3Scale qs = make_e4m3_scale(s);
+            float z[8];
+            // |y| <= amax, so |y / s| <= 448 (1 + 2^-24): no input clamp
+            if (e4m3_scale_is_fast(qs)) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) z[j] = e4m3_quotient<true, false>(yf[j], qs);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) z[j] = e4m3_quotient<false, false>(yf[j], qs);
+            }
+            u32x2 q;
+            q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+            q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
+            st_stream((u32x2 *)(qo + (size_t)v * 8), q);
+        }
     } else if constexpr (EPI == NORM_EPI_FP8_STATIC) {
         // ---- y as above, q = e4m3(clamp(y / s)) with the given scale
         const E4m3Scale qs = make_e4m3_scale(*p.scale_in);
@@ -474,6 +513,9 @@ hipError_t launch_norm(const NormParams &p, int epi, bool residual, int variant,
     case NORM_EPI_NVFP4:
         return residual ? dispatch<NORM_EPI_NVFP4, true>(p, variant, num_cus, stream)
                         : dispatch<NORM_EPI_NVFP4, false>(p, variant, num_cus, stream);
+    case NORM_EPI_FP8_GROUP:
+        return residual ? dispatch<NORM_EPI_FP8_GROUP, true>(p, variant, num_cus, stream)
+                        : dispatch<NORM_EPI_FP8_GROUP, false>(p, variant, num_cus, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -100,7 +100,7 @@ __device__ __forceinline__ uint32_t mx_block_max(uint32_t mag)
 // MODE 0: bf16 output; 1: E4M3 output, fast quotient; 2: E4M3, IEEE
 // division; 3: MXFP4 (codes to out, E8M0 block scales to scale_out); 4:
 // NVFP4 (codes to out, E4M3 block scales to scale_out, tensor scale read
-// from scale).
+// from scale); 5: E4M3 with an fp32 scale per 128 outputs (scale_out).
 template <int U, int W, int MODE>
 __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Scale &qs)
 {
@@ -180,6 +180,50 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
         }
         return;
     }
+    if constexpr (MODE == 5) {
+        // per 128 outputs (the jobs of 16 adjacent lanes, 32 for half jobs)
+        // the scale s = amax / 448, then the E4M3 codes of y / s; every lane
+        // takes part in the group maximum (slots past the row end hold zeros;
+        // N is a multiple of 128, so a group is all in or all out)
+        constexpr uint32_t LANES = FP8_GROUP / (2 * W);
+        float *so = p.scale_out + row * (uint64_t)(p.inter / FP8_GROUP);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = c0 + 256u * u;
+            const V y = swiglu_job<W>(gv[u], uv[u]);
+            float yf[2 * W];
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < W; ++e) {
+                yf[2 * e] = bf_lo(y[e]);
+                yf[2 * e + 1] = bf_hi(y[e]);
+                amax = fmaxf(amax, fmaxf(__builtin_fabsf(yf[2 * e]), __builtin_fabsf(yf[2 * e + 1])));
+            }
+            amax = group_max<LANES>(amax);
+            if (c >= njobs) continue;
+            const float s = amax / 448.0f;
+            if (c % LANES == 0) so[c / LANES] = s;
+            const E4m3Scale gs = make_e4m3_scale(s);
+            float z[2 * W];
+            // |y| <= amax, so |y / s| <= 448 (1 + 2^-24): no input clamp
+            if (e4m3_scale_is_fast(gs)) {
+#pragma unroll
+                for (int j = 0; j < 2 * W; ++j) z[j] = e4m3_quotient<true, false>(yf[j], gs);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2 * W; ++j) z[j] = e4m3_quotient<false, false>(yf[j], gs);
+            }
+            typename Words<W>::Q q;
+            if constexpr (W == 4) {
+                q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+                q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
+            } else {
+                q = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+            }
+            st_stream((typename Words<W>::Q *)p.out + job0 + c, q);
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t c = c0 + 256u * u;
@@ -219,6 +263,8 @@ __global__ void __launch_bounds__(256) swiglu_kernel(SwigluParams p)
         swiglu_block<U, W, 3>(p, E4m3Scale{});
     } else if constexpr (EPI == SWIGLU_EPI_NVFP4) {
         swiglu_block<U, W, 4>(p, E4m3Scale{});
+    } else if constexpr (EPI == SWIGLU_EPI_FP8_GROUP) {
+        swiglu_block<U, W, 5>(p, E4m3Scale{});
     } else {
         swiglu_block<U, W, 0>(p, E4m3Scale{});
     }
@@ -402,6 +448,7 @@ hipError_t launch_swiglu(const SwigluParams &p, int epi, int variant, hipStream_
     case SWIGLU_EPI_FP8: return dispatch<SWIGLU_EPI_FP8>(p, variant, stream);
     case SWIGLU_EPI_MXFP4: return dispatch<SWIGLU_EPI_MXFP4>(p, variant, stream);
     case SWIGLU_EPI_NVFP4: return dispatch<SWIGLU_EPI_NVFP4>(p, variant, stream);
+    case SWIGLU_EPI_FP8_GROUP: return dispatch<SWIGLU_EPI_FP8_GROUP>(p, variant, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -58,6 +58,9 @@ FORMS = {
     "fused_add_rmsnorm_quant_nvfp4": (A.OP_NORM, True),
     "rmsnorm_quant_nvfp4": (A.OP_RMSNORM, True),
     "swiglu_quant_nvfp4": (A.OP_SWIGLU, 3),
+    "fused_add_rmsnorm_quant_fp8_group": (A.OP_NORM, True),
+    "rmsnorm_quant_fp8_group": (A.OP_RMSNORM, True),
+    "swiglu_quant_fp8_group": (A.OP_SWIGLU, 4),
 }
 
 
@@ -115,7 +118,8 @@ def _buffers(form: str, tokens: int, width: int, device):
             nbytes = T * W * 4 + T * W // 2 + T * W // blk
         else:
             b["y"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
-            b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
+            b["s"] = torch.empty((T, W // A.FP8_GROUP) if "group" in form else (T,), dtype=torch.float32,
+                                 device=device)
             nbytes = T * W * 4 + T * W * (1 if "fp8" in form else 2)
     else:
         b = dict(x=torch.randn((T, W), device=device).to(torch.bfloat16),
@@ -127,7 +131,8 @@ def _buffers(form: str, tokens: int, width: int, device):
             out_bytes = T * W // 2 + T * W // blk
         else:
             b["o"] = torch.empty((T, W), **(f8 if "fp8" in form else bf))
-            b["s"] = torch.empty((T,), dtype=torch.float32, device=device)
+            b["s"] = torch.empty((T, W // A.FP8_GROUP) if "group" in form else (T,), dtype=torch.float32,
+                                 device=device)
             out_bytes = T * W * (1 if "fp8" in form else 2)
         b["ro"] = torch.empty((T, W), **bf)
         nbytes = T * W * (2 if form.startswith("rmsnorm") else 6) + out_bytes
@@ -167,6 +172,13 @@ def _launcher(form: str, b: dict, w, scale, variant: int):
         return lambda: A.swiglu_quant_nvfp4(b["gu"], scale, out=b["y"], scale_out=b["s"], variant=variant)
     if form == "swiglu_quant_mxfp4":
         return lambda: A.swiglu_quant_mxfp4(b["gu"], out=b["y"], scale_out=b["s"], variant=variant)
+    if form == "fused_add_rmsnorm_quant_fp8_group":
+        return lambda: A.fused_add_rmsnorm_quant_fp8_group(b["x"], b["r"], w, 1e-6, out=b["o"], scale_out=b["s"],
+                                                           residual_out=b["ro"], variant=variant)
+    if form == "rmsnorm_quant_fp8_group":
+        return lambda: A.rmsnorm_quant_fp8_group(b["x"], w, 1e-6, out=b["o"], scale_out=b["s"], variant=variant)
+    if form == "swiglu_quant_fp8_group":
+        return lambda: A.swiglu_quant_fp8_group(b["gu"], out=b["y"], scale_out=b["s"], variant=variant)
     if form == "swiglu_quant_fp8_dynamic":
         return lambda: A.swiglu_quant_fp8_dynamic(b["gu"], out=b["y"], scale_out=b["s"], variant=variant)
     raise ValueError(form)

@@ -309,6 +309,34 @@ int swiglu_quant_fp8_dynamic(void *out_fp8, float *scale_out, const void *gate_u
 const char *aarms_status_string(int status);
 
 /*
+ * fused_add_rmsnorm_quant_fp8_group, rmsnorm_quant_fp8_group,
+ * swiglu_quant_fp8_group -- the norm (with or without the residual add) or
+ * swiglu, then E4M3 codes under one fp32 scale per group of
+ * AARMS_FP8_GROUP (128) consecutive values of a row: the per-block FP8
+ * scaling of the "TensorRT-LLM" walkthrough, Part V, with the per-token rule
+ * of fused_add_rmsnorm_quant_fp8 applied to each group.
+ *
+ *   out_fp8      [num_tokens, width]       fp8    written: e4m3(clamp(y / s_g))
+ *   scale_out    [num_tokens, width / 128] fp32   written: s_g = binary32(max |y| over
+ *                                                  the group / 448) (0 for an
+ *                                                  all-zero group, whose codes are zeros)
+ *   residual_out, x, residual, weight, hidden, eps   as for fused_add_rmsnorm
+ *   gate_up, inter                                    as for swiglu
+ * width (hidden or inter) must be a multiple of 128 (else
+ * AARMS_ERR_BAD_SHAPE).  y is the bf16 value the bf16 form would write; every
+ * non-zero group has max |q| = 448.  In place (norm with the residual):
+ * residual_out == residual is allowed.
+ */
+#define AARMS_FP8_GROUP 128
+int fused_add_rmsnorm_quant_fp8_group(void *out_fp8, float *scale_out, void *residual_out,
+                                      const void *x, const void *residual, const void *weight,
+                                      int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream);
+int rmsnorm_quant_fp8_group(void *out_fp8, float *scale_out, const void *x, const void *weight,
+                            int64_t num_tokens, int64_t hidden, float eps, hipStream_t stream);
+int swiglu_quant_fp8_group(void *out_fp8, float *scale_out, const void *gate_up, int64_t num_tokens,
+                           int64_t inter, hipStream_t stream);
+
+/*
  * Kernel variants, for tuning sweeps.  The plain entry points pick a variant
  * from (num_tokens, width, output format); the *_ex forms take it
  * explicitly.  A variant id is an index into the op's table;
@@ -316,9 +344,10 @@ const char *aarms_status_string(int status);
  * the end.  ops: 0 = the norms with the residual add (fused_add_rmsnorm*),
  * 3 = the norms without it (rmsnorm*), both on one variant table (quant != 0
  * for a quantised form); 1 = swiglu, swiglu_quant_fp8, swiglu_quant_mxfp4
- * and swiglu_quant_nvfp4 (quant = the output format: 0 bf16, 1 E4M3,
- * 2 MXFP4, 3 NVFP4; -1 is returned for another value); 2 =
- * swiglu_quant_fp8_dynamic.
+ * swiglu_quant_nvfp4 and swiglu_quant_fp8_group (quant = the output
+ * format: 0 bf16, 1 E4M3, 2 MXFP4, 3 NVFP4, 4 E4M3 per 128-value group; -1
+ * is returned for another value); 2 = swiglu_quant_fp8_dynamic.  The
+ * per-group norms share the norm tables (quant != 0).
  * aarms_pick_variant() returns the id the plain entry point would use, or -1
  * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
  */
@@ -352,6 +381,15 @@ int rmsnorm_quant_fp8_static_ex(void *out_fp8, const void *x, const void *weight
                                 int variant, hipStream_t stream);
 int swiglu_quant_fp8_dynamic_ex(void *out_fp8, float *scale_out, const void *gate_up,
                                 int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
+int fused_add_rmsnorm_quant_fp8_group_ex(void *out_fp8, float *scale_out, void *residual_out,
+                                         const void *x, const void *residual, const void *weight,
+                                         int64_t num_tokens, int64_t hidden, float eps, int variant,
+                                         hipStream_t stream);
+int rmsnorm_quant_fp8_group_ex(void *out_fp8, float *scale_out, const void *x, const void *weight,
+                               int64_t num_tokens, int64_t hidden, float eps, int variant,
+                               hipStream_t stream);
+int swiglu_quant_fp8_group_ex(void *out_fp8, float *scale_out, const void *gate_up, int64_t num_tokens,
+                              int64_t inter, int variant, hipStream_t stream);
 int swiglu_quant_mxfp4_ex(void *out_fp4, uint8_t *scale_out, const void *gate_up,
                           int64_t num_tokens, int64_t inter, int variant, hipStream_t stream);
 int swiglu_quant_nvfp4_ex(void *out_fp4, uint8_t *scale_out, const void *gate_up,

@@ -213,6 +213,62 @@ def check_rmsnorm_fp8_static(x, weight, eps, scale, q_gpu) -> NormReport:
     return _check_static_codes(x, weight, eps, scale, q_gpu, q_o)
 
 
+
+# ----------------------------------------------------------------- per-group E4M3
+
+def _same_scales(a, b):
+    return (a.view(np.uint32) == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b))
+
+
+def _check_group_codes(rows_in, weight, eps, q_gpu, s_gpu, q_o, s_o) -> NormReport:
+    """Per-group E4M3 codes and fp32 group scales of a norm of rows_in against
+    the oracle.  Rows that differ: each group scale lies between the scales of
+    the smallest and largest admissible group amax (1e-6 relative slack), and
+    each code is within 1 E4M3 ulp of the code of an admissible value under
+    the GPU's own group scale."""
+    groups = s_gpu.shape[1]
+    G = q_gpu.shape[1] // groups
+    same_s = _same_scales(s_gpu, s_o)
+    same_q = _same_codes(q_gpu, q_o)
+    rows = np.flatnonzero(~same_s.all(axis=1) | ~same_q.all(axis=1))
+    if len(rows):
+        _, lo, hi = norm_admissible(rows_in[rows], weight, eps)
+        alo, ahi = np.abs(oracle.bf16_to_f32(lo)), np.abs(oracle.bf16_to_f32(hi))
+        n = len(rows)
+        amin = np.fmax.reduce(np.fmin(alo, ahi).reshape(n, groups, G), axis=2, initial=0.0)
+        amax = np.fmax.reduce(np.fmax(alo, ahi).reshape(n, groups, G), axis=2, initial=0.0)
+        s_lo = (amin.astype(np.float32) / np.float32(448)).astype(np.float32)
+        s_hi = (amax.astype(np.float32) / np.float32(448)).astype(np.float32)
+        sg = s_gpu[rows]
+        ok_s = same_s[rows] | ((sg >= s_lo * (1 - 1e-6)) & (sg <= s_hi * (1 + 1e-6)))
+        assert ok_s.all(), "group scale outside tolerance in rows %s" % rows[~ok_s.all(axis=1)][:5].tolist()
+        for k, r in enumerate(rows):
+            for g in np.flatnonzero(~same_q[r].reshape(groups, G).all(axis=1)):
+                sl = slice(g * G, (g + 1) * G)
+                sc = float(sg[k, g])
+                d = np.minimum(e4m3_ulps(q_gpu[r, sl], oracle.quant_fp8_static(lo[k, sl], sc)),
+                               e4m3_ulps(q_gpu[r, sl], oracle.quant_fp8_static(hi[k, sl], sc)))
+                d[same_q[r, sl]] = 0
+                assert d.max() <= 1, "row %d group %d: code off by %d e4m3 ulps" % (r, g, d.max())
+    return NormReport(rows=int(q_gpu.shape[0]), rows_not_nominal=int(len(rows)),
+                      codes_not_nominal=int((~same_q).sum()),
+                      scales_not_nominal=int((~same_s).sum()))
+
+
+def check_norm_fp8_group(x, residual, weight, eps, q_gpu, s_gpu, res_out_gpu) -> NormReport:
+    """Assert fused_add_rmsnorm_quant_fp8_group results: residual_out
+    bit-exact, codes and group scales bit-exact except where the norm output
+    sits on a knife-edge (then to the tolerances above)."""
+    q_o, s_o, res_o, _, _ = oracle.fused_add_rmsnorm_quant_fp8_group(x, residual, weight, eps)
+    bad_res = ~same_bf16(res_out_gpu, res_o)
+    assert not bad_res.any(), "residual_out differs at %d positions" % bad_res.sum()
+    return _check_group_codes(res_o, weight, eps, q_gpu, s_gpu, q_o, s_o)
+
+
+def check_rmsnorm_fp8_group(x, weight, eps, q_gpu, s_gpu) -> NormReport:
+    q_o, s_o, _, _ = oracle.rmsnorm_quant_fp8_group(x, weight, eps)
+    return _check_group_codes(x, weight, eps, q_gpu, s_gpu, q_o, s_o)
+
 # ----------------------------------------------------------------- swiglu
 
 def check_swiglu(gate_up, y_gpu):
@@ -351,4 +407,16 @@ def check_swiglu_nvfp4(gate_up, g, q_gpu, s_gpu):
         bad_s.sum(), np.argwhere(bad_s)[:5].tolist(), s_gpu[bad_s][:5], s_o[bad_s][:5])
     bad = q_gpu != q_o
     assert not bad.any(), "codes differ at %d bytes, first %s: gpu %s oracle %s" % (
+        bad.sum(), np.argwhere(bad)[:5].tolist(), q_gpu[bad][:5], q_o[bad][:5])
+
+
+def check_swiglu_fp8_group(gate_up, q_gpu, s_gpu):
+    """Per-group E4M3 SwiGLU: no knife-edges in y, so group scales and codes
+    are bit-exact."""
+    q_o, s_o, _ = oracle.swiglu_quant_fp8_group(gate_up)
+    bad_s = ~_same_scales(s_gpu, s_o)
+    assert not bad_s.any(), "group scales differ at %d groups, first %s: gpu %s oracle %s" % (
+        bad_s.sum(), np.argwhere(bad_s)[:5].tolist(), s_gpu[bad_s][:5], s_o[bad_s][:5])
+    bad = ~_same_codes(q_gpu, q_o)
+    assert not bad.any(), "codes differ at %d positions, first %s: gpu %s oracle %s" % (
         bad.sum(), np.argwhere(bad)[:5].tolist(), q_gpu[bad][:5], q_o[bad][:5])

@@ -301,7 +301,7 @@ def test_pick_variant_ranges():
     assert A.pick_variant(A.OP_NORM, 16, MAX_HIDDEN + 8) == -1
     assert A.pick_variant(A.OP_SWIGLU, 16, 8960) >= 0
     assert A.pick_variant(A.OP_SWIGLU, 16, 12) == -1
-    assert A.pick_variant(A.OP_SWIGLU, 16, 8960, 4) == -1          # unknown output format
+    assert A.pick_variant(A.OP_SWIGLU, 16, 8960, 5) == -1          # unknown output format
     assert A.pick_variant(A.OP_SWIGLU, 16, 8960, -1) == -1
     name = lambda T, N, f: A.variant_name(A.OP_SWIGLU, A.pick_variant(A.OP_SWIGLU, T, N, f))
     # decode sizes: half jobs; E4M3 from ~4 M outputs: two jobs per lane;
@@ -311,6 +311,7 @@ def test_pick_variant_ranges():
     assert name(4096, 8960, 1) == "2 jobs/lane"
     assert name(4096, 8960, 3) == "1 job/lane"
     assert name(8192, 28672, 3) == "2 jobs/lane" and name(512, 28672, 3) == "1 job/lane"
+    assert name(4096, 8960, 4) == name(4096, 8960, 1)                # per-group E4M3: the E4M3 rule
 
 
 def test_ceiling_library_rejects_bad_arguments():
@@ -395,3 +396,48 @@ def test_nvfp4_errors():
     assert lib.swiglu_quant_nvfp4_ex(P, P + BIG, P + 2 * BIG, G, 4, 8968, -1, None) == SHAPE
     assert lib.swiglu_quant_nvfp4_ex(P, P + BIG, P + 2 * BIG, 0, 4, 8960, -1, None) == NULLP
     assert lib.swiglu_quant_nvfp4_ex(P, P + 64, P + 2 * BIG, G, 4, 8960, -1, None) == ALIAS
+
+
+def test_fp8_group_errors():
+    lib = A.load()
+
+    def fg(out=P, s=P + BIG, ro=P + 2 * BIG, x=P + 3 * BIG, r=P + 4 * BIG, w=P + 5 * BIG, T=4, H=1536,
+           variant=-1):
+        return lib.fused_add_rmsnorm_quant_fp8_group_ex(out, s, ro, x, r, w, T, H, 1e-6, variant, None)
+
+    def rg(out=P, s=P + BIG, x=P + 3 * BIG, w=P + 5 * BIG, T=4, H=1536, variant=-1):
+        return lib.rmsnorm_quant_fp8_group_ex(out, s, x, w, T, H, 1e-6, variant, None)
+
+    def sg(out=P, s=P + BIG, gu=P + 2 * BIG, T=4, N=8960, variant=-1):
+        return lib.swiglu_quant_fp8_group_ex(out, s, gu, T, N, variant, None)
+
+    assert A.FP8_GROUP == 128
+    for f in (fg, rg):
+        assert f(H=1544) == SHAPE                       # a multiple of 8, not of 128
+        assert f(H=MAX_HIDDEN + 128) == UNSUP
+        assert f(s=0) == NULLP
+        assert f(s=P + BIG + 2) == MISAL                # fp32 scales
+        assert f(out=P + 8) == MISAL
+        assert f(s=P + 64) == ALIAS                     # scales inside the codes
+        assert f(out=P + 3 * BIG) == ALIAS              # no in-place output
+        assert f(variant=0) == VARIANT                  # too narrow, stops before launch
+        assert f(variant=A.variant_count(A.OP_NORM)) == VARIANT
+        assert f(T=1 << 31) == UNSUP
+    assert fg(ro=P + 4 * BIG, variant=0) == VARIANT     # residual_out == residual in place
+    assert fg(ro=P + 3 * BIG) == ALIAS                  # residual_out over x
+    assert fg(ro=P + BIG + 16) == ALIAS                 # residual_out over the scales
+    assert fg(T=0, out=0, s=0, ro=0, x=0, r=0, w=0) == OK
+    assert rg(T=0, out=0, s=0, x=0, w=0) == OK
+    assert sg(N=8968) == SHAPE
+    assert sg(s=0) == NULLP
+    assert sg(s=P + BIG + 1) == MISAL
+    assert sg(out=P + 8) == MISAL
+    assert sg(s=P + 64) == ALIAS
+    assert sg(out=P + 2 * BIG) == ALIAS
+    assert sg(variant=A.variant_count(A.OP_SWIGLU)) == VARIANT
+    assert sg(T=1 << 31, N=128) == UNSUP
+    assert sg(T=0, out=0, s=0, gu=0) == OK
+    assert lib.swiglu_quant_fp8_group(P, P + BIG, P + 2 * BIG, 4, 8968, None) == SHAPE
+    assert lib.fused_add_rmsnorm_quant_fp8_group(P, P + BIG, P + 2 * BIG, P + 3 * BIG, P + 4 * BIG,
+                                                 P + 5 * BIG, 4, 1544, 1e-6, None) == SHAPE
+    assert lib.rmsnorm_quant_fp8_group(P, P + BIG, P + 3 * BIG, P + 5 * BIG, 4, 1544, 1e-6, None) == SHAPE

@@ -498,3 +498,173 @@ def test_swiglu_nvfp4_llama70b_full():
     gu = W.swiglu_inputs(wl)["gate_up"]
     q, s = run_swiglu_nv(gu, 0.05)
     P.check_swiglu_nvfp4(gu, 0.05, q, s)
+
+
+# ------------------------------------------------------------------ per-group E4M3
+
+def run_fused_grp(x, r, w, eps, variant=-1):
+    announce("fused_add_rmsnorm_quant_fp8_group", x.shape, "eps", eps, "variant", variant)
+    q, s, ro = A.fused_add_rmsnorm_quant_fp8_group(bf16(x), bf16(r), bf16(w), eps, variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s), bits(ro)
+
+
+def run_rms_grp(x, w, eps, variant=-1):
+    announce("rmsnorm_quant_fp8_group", x.shape, "eps", eps, "variant", variant)
+    q, s = A.rmsnorm_quant_fp8_group(bf16(x), bf16(w), eps, variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s)
+
+
+def run_swiglu_grp(gu, variant=-1):
+    announce("swiglu_quant_fp8_group", gu.shape, "variant", variant)
+    q, s = A.swiglu_quant_fp8_group(bf16(gu), variant=variant)
+    torch.cuda.synchronize()
+    return bits(q), bits(s)
+
+
+@pytest.mark.parametrize("T,H", [(1, 128), (3, 384), (16, 1536), (257, 1536), (4, 16384), (3, 16512),
+                                 (2, 65536), (1023, 2048)])
+def test_fp8_group_norms_default_variant(T, H):
+    x, r, w = norm_case(T, H, seed=T + 17 * H, outliers=0.002)
+    q, s, ro = run_fused_grp(x, r, w, 1e-5)
+    announce(P.check_norm_fp8_group(x, r, w, 1e-5, q, s, ro))
+    q, s = run_rms_grp(x, w, 1e-5)
+    announce(P.check_rmsnorm_fp8_group(x, w, 1e-5, q, s))
+
+
+@pytest.mark.parametrize("H", [1536, 16384])
+def test_fp8_group_norms_every_variant(H):
+    x, r, w = norm_case(37, H, seed=H + 19, outliers=0.002)
+    for v in variants_for(A.OP_NORM, H):
+        q, s, ro = run_fused_grp(x, r, w, 1e-5, v)
+        P.check_norm_fp8_group(x, r, w, 1e-5, q, s, ro)
+        q, s = run_rms_grp(x, w, 1e-5, v)
+        P.check_rmsnorm_fp8_group(x, w, 1e-5, q, s)
+
+
+def test_fp8_group_norm_special_groups():
+    """An all-zero group (scale 0, zero codes), a group of bf16 subnormals
+    beside groups near 1 (a tiny scale of its own), an outlier that only
+    its own group's scale sees, a NaN (the whole row's norm is NaN: the
+    maxima ignore it, scale 0, NaN codes) and an infinity."""
+    H = 512
+    x, _, w = norm_case(6, H, seed=78)
+    w[:] = oracle.bf16_from_f64(1.0)
+    one = oracle.bf16_from_f64
+    x[0, :128] = 0
+    x[1, :] = one(1.0)
+    x[1, 256:384] = 0x0001
+    x[2, 300] = one(200.0)
+    x[3, 100] = 0x7FC0
+    x[4, 7] = 0x7F80
+    for v in variants_for(A.OP_NORM, H):
+        q, s = run_rms_grp(x, w, 1e-6, v)
+        P.check_rmsnorm_fp8_group(x, w, 1e-6, q, s)
+        assert s[0, 0] == 0 and np.all((q[0, :128] & 0x7F) == 0)
+        assert 0 < s[1, 2] < 1e-30 and s[1, 0] == s[1, 1] == s[1, 3]
+        assert s[2, 2] > 10 * max(s[2, 0], s[2, 1], s[2, 3])
+        assert np.all(s[3] == 0) and np.all(np.isin(q[3], [0x7F, 0xFF]))
+
+
+def test_fp8_group_norm_in_place_residual():
+    x, r, w = norm_case(32, 2048, seed=25)
+    rt = bf16(r)
+    announce("fused_add_rmsnorm_quant_fp8_group residual in place", x.shape)
+    q, s, ro = A.fused_add_rmsnorm_quant_fp8_group(bf16(x), rt, bf16(w), 1e-5, residual_out=rt)
+    torch.cuda.synchronize()
+    assert ro.data_ptr() == rt.data_ptr()
+    P.check_norm_fp8_group(x, r, w, 1e-5, bits(q), bits(s), bits(rt))
+
+
+def test_fp8_group_norm_llama405b_full():
+    wl = W.NORM_FP8_LLAMA405B
+    d = W.norm_inputs(wl)
+    q, s, ro = run_fused_grp(d["x"], d["residual"], d["weight"], wl.eps)
+    announce(P.check_norm_fp8_group(d["x"], d["residual"], d["weight"], wl.eps, q, s, ro))
+    dec = oracle.e4m3_table()
+    amax = np.abs(dec[q]).reshape(q.shape[0], -1, A.FP8_GROUP).max(axis=2)
+    assert np.all(amax == 448.0)
+
+
+@pytest.mark.parametrize("T,N", [(1, 128), (3, 384), (5, 1152), (64, 8960), (300, 8960), (600, 8960),
+                                 (7, 28672), (2, 65536)])
+def test_swiglu_fp8_group_shapes_every_variant(T, N):
+    gu = gen.normal_bf16((T, 2 * N), T + 13 * N, 4, std=2.0)
+    for v in [-1] + list(range(A.variant_count(A.OP_SWIGLU))):
+        q, s = run_swiglu_grp(gu, v)
+        P.check_swiglu_fp8_group(gu, q, s)
+
+
+def test_swiglu_fp8_group_special_groups_and_every_y():
+    """y = 8u over several binade ranges (every bf16 significand passes
+    through a group scale), a NaN gate (its code NaN, the group maximum
+    ignores it), an infinite up (scale inf) and an all-zero group."""
+    N = 65536
+    u = np.arange(N, dtype=np.uint16)
+    finite = (u & 0x7F80) != 0x7F80
+    rows = []
+    for hi_exp in (0x3F80, 0x4700, 0x1000):
+        uu = np.where(finite & ((u & 0x7F80) <= hi_exp), u, u & 0x807F)
+        rows.append(np.concatenate([np.full(N, oracle.bf16_from_f64(8.0), np.uint16), uu]))
+    gu = np.stack(rows + [rows[0].copy(), rows[0].copy()])
+    gu[3, 140] = 0x7FC0
+    gu[4, N + 300] = 0x7F80
+    gu[4, :128] = 0
+    for v in [-1] + list(range(A.variant_count(A.OP_SWIGLU))):
+        q, s = run_swiglu_grp(gu, v)
+        P.check_swiglu_fp8_group(gu, q, s)
+        assert q[3, 140] in (0x7F, 0xFF) and np.isfinite(s[3, 1])
+        assert np.isinf(s[4, 2]) and s[4, 0] == 0 and np.all((q[4, :128] & 0x7F) == 0)
+
+
+def test_swiglu_fp8_group_llama70b_full():
+    wl = W.SWIGLU_FP8_LLAMA70B
+    gu = W.swiglu_inputs(wl)["gate_up"]
+    q, s = run_swiglu_grp(gu)
+    P.check_swiglu_fp8_group(gu, q, s)
+
+
+def test_fp8_group_forms_under_graph_replay():
+    """The three per-group forms from one captured graph, replayed three
+    times with eager work between: every replay equals the eager run."""
+    T, H, N = 64, 2048, 2048
+    x, r, w = norm_case(T, H, seed=93, outliers=0.001)
+    gu = gen.normal_bf16((T, 2 * N), 94, 4, std=2.0)
+    xt, rt, wt, gut = bf16(x), bf16(r), bf16(w), bf16(gu)
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    outs = dict(fq=torch.empty((T, H), **u8), fs=torch.empty((T, H // 128), device=DEV),
+                fro=torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+                rq=torch.empty((T, H), **u8), rs=torch.empty((T, H // 128), device=DEV),
+                sq=torch.empty((T, N), **u8), ss=torch.empty((T, N // 128), device=DEV))
+
+    def launch():
+        A.fused_add_rmsnorm_quant_fp8_group(xt, rt, wt, 1e-5, out=outs["fq"], scale_out=outs["fs"],
+                                            residual_out=outs["fro"])
+        A.rmsnorm_quant_fp8_group(xt, wt, 1e-5, out=outs["rq"], scale_out=outs["rs"])
+        A.swiglu_quant_fp8_group(gut, out=outs["sq"], scale_out=outs["ss"])
+
+    announce("per-group forms, eager then graph")
+    launch()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k].view(torch.uint8), eager[k].view(torch.uint8)), (rep, k)
+        xt.add_(0)
+    P.check_norm_fp8_group(x, r, w, 1e-5, bits(outs["fq"]), bits(outs["fs"]), bits(outs["fro"]))
+    P.check_swiglu_fp8_group(gu, bits(outs["sq"]), bits(outs["ss"]))
