@@ -462,6 +462,9 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
     # the rest of the quantisation matrix, at the same shapes
     out.update(quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream))
 
+    # one GPU's share of the Llama layers sharded over 8 GPUs
+    out.update(shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream))
+
     # start-up autotuning at the workload shapes: the heuristic's variant
     # against the fastest one (graph-replay timings); informational, the
     # figures above use the heuristic
@@ -479,7 +482,8 @@ def autotune_report():
               ("fused_add_rmsnorm_quant_fp8_static", 2048, 16384), ("swiglu_quant_fp8_dynamic", 8192, 28672),
               ("fused_add_rmsnorm_quant_mxfp4", 2048, 16384), ("swiglu_quant_mxfp4", 8192, 28672),
               ("swiglu_quant_mxfp4", 1, 8960), ("fused_add_rmsnorm_quant_nvfp4", 2048, 16384),
-              ("swiglu_quant_nvfp4", 8192, 28672)]
+              ("swiglu_quant_nvfp4", 8192, 28672), ("fused_add_rmsnorm_quant_fp8_group", 2048, 16384),
+              ("swiglu_quant_fp8_group", 8192, 28672)]
     rows = []
     for form, T, W in shapes:
         r = tuning.tune(form, T, W)
@@ -490,10 +494,11 @@ def autotune_report():
 
 
 def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
-    """rmsnorm (no residual add) at the Qwen prefill shape; the static-scale
-    and the no-residual per-token FP8 norms at the Llama-405B shape; the
-    per-token FP8 SwiGLU at the Llama-70B shape.  Each beside its streaming
-    ceiling, on rotated buffer sets."""
+    """rmsnorm (no residual add) at the Qwen prefill shape; the static-scale,
+    block-scaled (MXFP4, NVFP4, per-128 E4M3) and no-residual per-token norms
+    at the Llama-405B shape; the block-scaled and per-token SwiGLU forms at
+    the Llama-70B shape.  Each beside its streaming ceiling, on rotated
+    buffer sets."""
     out = {}
 
     def measure(key, call, ceil, nbytes, extra=None):
@@ -568,6 +573,16 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
             lambda i: stream(P(i, "ro"), 16, nv_sets[i % ns][0].data_ptr(), 4, P(i, "x"), P(i, "r"), T * H // 8),
             nb, {"tensor_scale": 0.02, "buffer_sets_rotated": ns})
     del nv_sets
+    G = A.FP8_GROUP
+    gs_sets = [torch.empty((T, H // G), dtype=torch.float32, device=dev) for _ in range(ns)]
+    nb = T * H * 7 + T * H // G * 4 + H * 2
+    measure("llama405b_norm_fp8_group_2048x16384",
+            lambda i: check(lib.fused_add_rmsnorm_quant_fp8_group(
+                P(i, "q"), gs_sets[i % ns].data_ptr(), P(i, "ro"), P(i, "x"), P(i, "r"), w0.data_ptr(),
+                T, H, wl.eps, sp), "fused_add_rmsnorm_quant_fp8_group"),
+            lambda i: stream(P(i, "ro"), 16, P(i, "q"), 8, P(i, "x"), P(i, "r"), T * H // 8),
+            nb, {"group": G, "buffer_sets_rotated": ns})
+    del gs_sets
     nb = T * H * 3 + H * 2 + T * 4
     measure("llama405b_rmsnorm_fp8_2048x16384",
             lambda i: check(lib.rmsnorm_quant_fp8(P(i, "q"), P(i, "s"), P(i, "x"), w0.data_ptr(),
@@ -607,6 +622,17 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
             T * 2 * N * 2 + T * N // 2 + T * N // 16 + 4,
             {"tensor_scale": 0.05, "inputs": "torch.randn on device, seed 0, std 2", "buffer_sets_rotated": ns})
     del nv_sets
+    G = A.FP8_GROUP
+    gs_sets = [torch.empty((T, N // G), dtype=torch.float32, device=dev) for _ in range(ns)]
+    measure("llama70b_swiglu_fp8_group_8192x57344",
+            lambda i: check(lib.swiglu_quant_fp8_group(sets[i % ns][1].data_ptr(), gs_sets[i % ns].data_ptr(),
+                                                       sets[i % ns][0].data_ptr(), T, N, sp),
+                            "swiglu_quant_fp8_group"),
+            lambda i: stream(sets[i % ns][1].data_ptr(), 8, None, 0, sets[i % ns][0].data_ptr(),
+                             sets[i % ns][0].data_ptr() + T * N * 2, T * N // 8),
+            T * 2 * N * 2 + T * N + T * N // G * 4,
+            {"group": G, "inputs": "torch.randn on device, seed 0, std 2", "buffer_sets_rotated": ns})
+    del gs_sets
     measure("llama70b_swiglu_fp8_dynamic_8192x57344",
             lambda i: check(lib.swiglu_quant_fp8_dynamic(sets[i % ns][1].data_ptr(), sets[i % ns][2].data_ptr(),
                                                          sets[i % ns][0].data_ptr(), T, N, sp),
@@ -614,6 +640,66 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
             lambda i: stream(sets[i % ns][1].data_ptr(), 8, None, 0, sets[i % ns][0].data_ptr(),
                              sets[i % ns][0].data_ptr() + T * N * 2, T * N // 8),
             nb, {"inputs": "torch.randn on device, seed 0, std 2", "buffer_sets_rotated": ns})
+    del sets, gu
+    torch.cuda.empty_cache()
+    return out
+
+
+def shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
+    """The kernels on one GPU's share of the sharded layers: the 405B FP8
+    norm on T/8 = 256 rows (sequence parallel), the 70B static-FP8 SwiGLU on
+    N/8 = 3,584 columns of gate and of up (tensor parallel).  Each beside its
+    streaming ceiling, on rotated buffer sets."""
+    out = {}
+
+    def entry(ms, ms_c, nbytes, extra):
+        return {"bytes": nbytes, "avg_launch_us": round(ms * 1e3, 2),
+                "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "pct_of_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                **ceiling_entry(ms * 1e3, ms_c * 1e3, nbytes), **extra}
+
+    def check(st, what):
+        if st:
+            raise A.AarmsError(st, what)
+
+    wl = W.NORM_FP8_LLAMA405B_SP8
+    T, H = wl.tokens, wl.hidden
+    d = W.norm_inputs(wl)
+    x0, r0, w0 = to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["weight"])
+    nb = norm_bytes(T, H, quant=True)
+    ns = rotation_sets(nb)
+    sets = [dict(x=x0.clone(), r=r0.clone(), q=torch.empty((T, H), dtype=torch.uint8, device=dev),
+                 s=torch.empty((T,), dtype=torch.float32, device=dev), ro=torch.empty_like(r0))
+            for _ in range(ns)]
+    P = lambda i, k: sets[i % ns][k].data_ptr()
+    call = lambda i: check(lib.fused_add_rmsnorm_quant_fp8(P(i, "q"), P(i, "s"), P(i, "ro"), P(i, "x"), P(i, "r"),
+                                                           w0.data_ptr(), T, H, wl.eps, sp),
+                           "fused_add_rmsnorm_quant_fp8")
+    ceil = lambda i: stream(P(i, "ro"), 16, P(i, "q"), 8, P(i, "x"), P(i, "r"), T * H // 8)
+    timer.warm(call)
+    ms = timer.region(call, reps)
+    timer.warm(ceil)
+    ms_c = timer.region(ceil, reps)
+    out[wl.name] = entry(ms, ms_c, nb, {"buffer_sets_rotated": ns})
+    del sets, x0, r0
+
+    wl = W.SWIGLU_FP8_LLAMA70B_TP8
+    T, N = wl.tokens, wl.inter
+    g = torch.Generator(device=dev).manual_seed(0)
+    gu = (torch.randn((T, 2 * N), generator=g, device=dev, dtype=torch.float32) * wl.gate_up_std).to(torch.bfloat16)
+    nb = swiglu_bytes(T, N, quant=True)
+    ns = rotation_sets(nb)
+    sets = [(gu if i == 0 else gu.clone(), torch.empty((T, N), dtype=torch.uint8, device=dev)) for i in range(ns)]
+    scale = torch.tensor([wl.scale], dtype=torch.float32, device=dev)
+    call = lambda i: check(lib.swiglu_quant_fp8(sets[i % ns][1].data_ptr(), sets[i % ns][0].data_ptr(),
+                                                scale.data_ptr(), T, N, sp), "swiglu_quant_fp8")
+    ceil = lambda i: stream(sets[i % ns][1].data_ptr(), 8, None, 0, sets[i % ns][0].data_ptr(),
+                            sets[i % ns][0].data_ptr() + T * N * 2, T * N // 8)
+    timer.warm(call)
+    ms = timer.region(call, reps)
+    timer.warm(ceil)
+    ms_c = timer.region(ceil, reps)
+    out[wl.name] = entry(ms, ms_c, nb, {"inputs": "torch.randn on device, seed 0, std 2", "buffer_sets_rotated": ns})
     del sets, gu
     torch.cuda.empty_cache()
     return out

@@ -371,6 +371,30 @@ def test_swiglu_fp8_llama70b_full():
     P.check_swiglu_fp8(gu, wl.scale, q)
 
 
+# ------------------------------------------------------------------ one GPU's share
+
+def test_norm_fp8_llama405b_sequence_parallel_share():
+    """[256, 16384]: the 405B norm's rows on one of 8 sequence-parallel GPUs
+    (a quarter of a wave of blocks, at the variant the library picks)."""
+    wl = W.NORM_FP8_LLAMA405B_SP8
+    d = W.norm_inputs(wl)
+    q, s, res_out = run_norm_fp8(d["x"], d["residual"], d["weight"], wl.eps)
+    announce(P.check_norm_fp8(d["x"], d["residual"], d["weight"], wl.eps, q, s, res_out))
+
+
+def test_swiglu_fp8_llama70b_tensor_parallel_share():
+    """[8192, 7168] -> [8192, 3584]: the 70B MLP activation on one of 8
+    tensor-parallel GPUs, static and per-token scales."""
+    wl = W.SWIGLU_FP8_LLAMA70B_TP8
+    gu = W.swiglu_inputs(wl)["gate_up"]
+    q = run_swiglu_fp8(gu, wl.scale)
+    P.check_swiglu_fp8(gu, wl.scale, q)
+    announce("swiglu_quant_fp8_dynamic", gu.shape)
+    qd, sd = A.swiglu_quant_fp8_dynamic(bf16(gu))
+    torch.cuda.synchronize()
+    P.check_swiglu_fp8_dynamic(gu, bits(qd), bits(sd))
+
+
 # ------------------------------------------------------------------ determinism
 
 def test_repeat_runs_are_bitwise_identical():

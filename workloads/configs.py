@@ -74,6 +74,15 @@ SWIGLU_FP8_LLAMA70B = SwigluWorkload("llama70b_swiglu_fp8_8192x57344", tokens=81
 NORM_FP8_LLAMA405B = NormWorkload("llama405b_norm_fp8_2048x16384", tokens=2048, hidden=16384,
                                   eps=1e-5, outlier_frac=0.001, outlier_mult=50.0, quant_fp8=True)
 
+# One GPU's share of the two Llama layers when the path is sharded over 8
+# GPUs: the norm under sequence parallelism runs on T/8 rows, the SwiGLU under
+# tensor parallelism on a [gate_shard | up_shard] of N/8 columns each.
+NORM_FP8_LLAMA405B_SP8 = NormWorkload("llama405b_norm_fp8_sp8_256x16384", tokens=256, hidden=16384,
+                                      eps=1e-5, outlier_frac=0.001, outlier_mult=50.0, quant_fp8=True)
+SWIGLU_FP8_LLAMA70B_TP8 = SwigluWorkload("llama70b_swiglu_fp8_tp8_8192x7168", tokens=8192, inter=3584,
+                                         gate_up_std=2.0, quant_fp8=True, scale=0.05)
+SHARDS = (NORM_FP8_LLAMA405B_SP8, SWIGLU_FP8_LLAMA70B_TP8)
+
 # name -> the ops of that workload, in the order they run
 CONFIGS = {
     "norm_decode16": (NORM_DECODE16,),
