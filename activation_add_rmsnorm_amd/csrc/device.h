@@ -149,13 +149,34 @@ struct Nvfp4Tensor {
     bool six_fast;
 };
 
-__device__ __forceinline__ Nvfp4Tensor make_nvfp4_tensor(float g)
+// The tensor scale as used (0 means 1), and the reciprocal of 6 g that the
+// block-scale quotient takes (make_e4m3_scale's divisor and reciprocal).
+__device__ __forceinline__ float nv_tensor_scale(float g)
+{
+    return (g == 0.0f) ? 1.0f : g;
+}
+
+__device__ __forceinline__ float nv_six_inverse(float g)
+{
+    return make_e4m3_scale(6.0f * nv_tensor_scale(g)).inv;
+}
+
+// six_inv = nv_six_inverse(g), passed in so that a block can compute it once.
+__device__ __forceinline__ Nvfp4Tensor make_nvfp4_tensor(float g, float six_inv)
 {
     Nvfp4Tensor t;
-    t.g = (g == 0.0f) ? 1.0f : g;
-    t.six = make_e4m3_scale(6.0f * t.g);
+    t.g = nv_tensor_scale(g);
+    const float s6 = 6.0f * t.g;
+    t.six.s = (s6 == 0.0f) ? 1.0f : s6;
+    t.six.inv = six_inv;
+    t.six.lim = __builtin_fabsf(448.0f * t.six.s);
     t.six_fast = e4m3_scale_is_fast(t.six);
     return t;
+}
+
+__device__ __forceinline__ Nvfp4Tensor make_nvfp4_tensor(float g)
+{
+    return make_nvfp4_tensor(g, nv_six_inverse(g));
 }
 
 // E4M3 block scale: binary32(amax / 6g) (the correctly rounded quotient of
@@ -176,37 +197,56 @@ __device__ __forceinline__ uint32_t nv_scale_byte(uint32_t amax_bits, const Nvfp
 // no input clamp; a saturated block takes the clamped form (its values can
 // be arbitrarily large against S).
 template <int NW, bool CLAMP>
-__device__ __forceinline__ void nv_quotients(const uint32_t (&w)[NW], const E4m3Scale &qs, bool fast, bool zero,
+__device__ __forceinline__ void nv_quotients(const uint32_t (&w)[NW], const E4m3Scale &qs, bool fast,
                                              float (&z)[2 * NW])
 {
 #pragma unroll
     for (int e = 0; e < NW; ++e) {
         const float v0 = bf_lo(w[e]), v1 = bf_hi(w[e]);
-        float z0, z1;
         if (fast) {
-            z0 = e4m3_quotient<true, CLAMP>(v0, qs);
-            z1 = e4m3_quotient<true, CLAMP>(v1, qs);
+            z[2 * e] = e4m3_quotient<true, CLAMP>(v0, qs);
+            z[2 * e + 1] = e4m3_quotient<true, CLAMP>(v1, qs);
         } else {
-            z0 = e4m3_quotient<false, CLAMP>(v0, qs);
-            z1 = e4m3_quotient<false, CLAMP>(v1, qs);
+            z[2 * e] = e4m3_quotient<false, CLAMP>(v0, qs);
+            z[2 * e + 1] = e4m3_quotient<false, CLAMP>(v1, qs);
         }
-        z[2 * e] = zero ? v0 * 0.0f : z0;
-        z[2 * e + 1] = zero ? v1 * 0.0f : z1;
     }
 }
 
+// The block divisor S = binary32(E4M3(sb) * g) and its reciprocal as the
+// fast quotient takes it: binary32(1 / S), or 0 when S is 0.  With divisor 1
+// and reciprocal 0 the fast quotient returns the zero of v's sign for every
+// finite v (q0 = v * 0, rem = -v, z = -v * -0 + q0), which is what a block
+// whose scale is zero encodes, so no per-value select is needed.
+__device__ __forceinline__ float nv_block_divisor(uint32_t sb, float g)
+{
+    return __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
+}
+
+// g as used (nv_tensor_scale)
+__device__ __forceinline__ float nv_block_inverse(uint32_t sb, float g)
+{
+    const float S = nv_block_divisor(sb, g);
+    return S == 0.0f ? 0.0f : 1.0f / S;
+}
+
+// inv = nv_block_inverse(sb, t), passed in so that a caller can take it from
+// a table of the 127 finite block scales.
 template <int NW>
-__device__ __forceinline__ uint32_t pack_nvfp4(const uint32_t (&w)[NW], uint32_t sb, const Nvfp4Tensor &t)
+__device__ __forceinline__ uint32_t pack_nvfp4(const uint32_t (&w)[NW], uint32_t sb, const Nvfp4Tensor &t, float inv)
 {
     static_assert(NW == 2 || NW == 4, "2 or 4 words");
-    const float S = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * t.g;
-    const E4m3Scale qs = make_e4m3_scale(S);
-    const bool fast = e4m3_scale_is_fast(qs), zero = S == 0.0f;
+    const float S = nv_block_divisor(sb, t.g);
+    E4m3Scale qs;
+    qs.s = (S == 0.0f) ? 1.0f : S;
+    qs.inv = inv;
+    qs.lim = __builtin_fabsf(448.0f * qs.s);
+    const bool fast = e4m3_scale_is_fast(qs);
     float z[2 * NW];
     if (sb == 0x7Eu)
-        nv_quotients<NW, true>(w, qs, fast, zero, z);
+        nv_quotients<NW, true>(w, qs, fast, z);
     else
-        nv_quotients<NW, false>(w, qs, fast, zero, z);
+        nv_quotients<NW, false>(w, qs, fast, z);
     // the byte selector of the conversion is an immediate
     uint32_t q = 0;
     q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, z[0], z[1], 1.0f, 0);

@@ -232,7 +232,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
             mag = max(mag, dpp_u32<DPP_XOR1>(mag));
             if (v >= nvec) continue;
             const uint32_t sb = nv_scale_byte(mag, nt);
-            const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<4>(y, sb, nt);
+            const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<4>(y, sb, nt, nv_block_inverse(sb, nt.g));
             st_stream(qo + v, q);
             if ((lane & 1) == 0) so[v >> 1] = (uint8_t)sb;
         }

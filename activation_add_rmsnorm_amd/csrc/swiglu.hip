@@ -155,7 +155,19 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
     if constexpr (MODE == 4) {
         // a 16-output block is the jobs of 2 adjacent lanes (4 for half jobs)
         constexpr uint32_t LANES = 8 / W;
-        const Nvfp4Tensor nt = make_nvfp4_tensor(*p.scale);
+        // 1/S for each of the 127 finite block scales, and 1/(6 g) in the
+        // slot of the NaN scale byte (which never divides): one correctly
+        // rounded division per thread while the loads are in flight, instead
+        // of per job (the row test above is uniform per block, so every
+        // thread reaches the barrier)
+        const float g = *p.scale;
+        __shared__ float nv_inv[128];
+        if (threadIdx.x < 127u)
+            nv_inv[threadIdx.x] = nv_block_inverse(threadIdx.x, nv_tensor_scale(g));
+        else if (threadIdx.x == 127u)
+            nv_inv[127] = nv_six_inverse(g);
+        __syncthreads();
+        const Nvfp4Tensor nt = make_nvfp4_tensor(g, nv_inv[127]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t c = c0 + 256u * u;
@@ -171,7 +183,7 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
             if constexpr (W == 2) mag = max(mag, dpp_u32<DPP_XOR2>(mag));
             if (c >= njobs) continue;
             const uint32_t sb = nv_scale_byte(mag, nt);
-            const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<W>(w, sb, nt);
+            const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<W>(w, sb, nt, nv_inv[sb]);
             if constexpr (W == 4)
                 st_stream((uint32_t *)p.out + job0 + c, q);
             else
