@@ -35,6 +35,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -60,6 +61,9 @@ def parse():
                     help="headline variants by name, 'norm=<name>;swiglu=<name>' (no tuning): to "
                          "profile the configuration a tuned run chose")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--configs", default=None,
+                    help="regular expression: time only the supplementary measurements whose key "
+                         "matches (the headline always runs); for counter passes over a few kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -368,13 +372,39 @@ def main():
 def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
     out = {}
     reps = max(20, args.steps // 2)
+    want = (lambda key: re.search(args.configs, key) is not None) if args.configs else (lambda key: True)
 
     def stream(*a):
         st = clib.aarms_stream_ceiling(*a, sp)
         if st:
             raise RuntimeError("aarms_stream_ceiling: %d" % st)
 
-    # static-FP8 SwiGLU, Llama-70B MLP: [8192, 57344] -> e4m3 [8192, 28672]
+    if want("llama70b_swiglu_fp8_8192x57344"):
+        out.update(config4(torch, A, lib, W, dev, sp, timer, reps, stream))
+    if want("llama405b_norm_fp8_2048x16384"):
+        out.update(config5(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream))
+    if want("qwen1.5b_norm_16x1536"):
+        out.update(config1(A, lib, W, sp, timer, to_dev, reps))
+    if want("qwen1.5b_decode_28layers_graph"):
+        out["qwen1.5b_decode_28layers_graph"] = decode_graph(torch, np, A, W, dev, to_dev, timer)
+
+    # the rest of the quantisation matrix, at the same shapes
+    out.update(quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream, want))
+
+    # one GPU's share of the Llama layers sharded over 8 GPUs
+    out.update(shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream, want))
+
+    # start-up autotuning at the workload shapes: the heuristic's variant
+    # against the fastest one (graph-replay timings); informational, the
+    # figures above use the heuristic
+    if not args.no_autotune_report and want("autotune"):
+        out["autotune"] = autotune_report()
+    return out
+
+
+def config4(torch, A, lib, W, dev, sp, timer, reps, stream):
+    """Static-FP8 SwiGLU, Llama-70B MLP: [8192, 57344] -> e4m3 [8192, 28672]."""
+    out = {}
     wl = W.SWIGLU_FP8_LLAMA70B
     T, N = wl.tokens, wl.inter
     g = torch.Generator(device=dev).manual_seed(0)
@@ -405,8 +435,12 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
                                               "inputs": "torch.randn on device, seed 0, std 2"}
     del sets, gu, ptr
     torch.cuda.empty_cache()
+    return out
 
-    # dynamic-FP8 norm, Llama-405B: [2048, 16384]
+
+def config5(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
+    """Dynamic-FP8 norm, Llama-405B: [2048, 16384]."""
+    out = {}
     wl = W.NORM_FP8_LLAMA405B
     T, H = wl.tokens, wl.hidden
     d = W.norm_inputs(wl)
@@ -441,8 +475,12 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
                                              "buffer_sets_rotated": n_sets}
     del sets
     torch.cuda.empty_cache()
+    return out
 
-    # 16-token norm (launch-bound)
+
+def config1(A, lib, W, sp, timer, to_dev, reps):
+    """The 16-token norm (launch-bound, microseconds)."""
+    out = {}
     wl = W.NORM_DECODE16
     d = W.norm_inputs(wl)
     x, r, w = to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["weight"])
@@ -455,21 +493,6 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
     timer.warm(call1, 0.02)
     ms = timer.region(call1, reps)
     out["qwen1.5b_norm_16x1536"] = {"bytes": norm_bytes(16, 1536), "avg_launch_us": round(ms * 1e3, 2)}
-
-    # decode chain under a HIP graph, per token count
-    out["qwen1.5b_decode_28layers_graph"] = decode_graph(torch, np, A, W, dev, to_dev, timer)
-
-    # the rest of the quantisation matrix, at the same shapes
-    out.update(quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream))
-
-    # one GPU's share of the Llama layers sharded over 8 GPUs
-    out.update(shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream))
-
-    # start-up autotuning at the workload shapes: the heuristic's variant
-    # against the fastest one (graph-replay timings); informational, the
-    # figures above use the heuristic
-    if not args.no_autotune_report:
-        out["autotune"] = autotune_report()
     return out
 
 
@@ -493,7 +516,7 @@ def autotune_report():
     return rows
 
 
-def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
+def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream, want=lambda key: True):
     """rmsnorm (no residual add) at the Qwen prefill shape; the static-scale,
     block-scaled (MXFP4, NVFP4, per-128 E4M3) and no-residual per-token norms
     at the Llama-405B shape; the block-scaled and per-token SwiGLU forms at
@@ -502,6 +525,8 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
     out = {}
 
     def measure(key, call, ceil, nbytes, extra=None):
+        if not want(key):
+            return
         timer.warm(call)
         ms = timer.region(call, reps)
         timer.warm(ceil)
@@ -645,7 +670,7 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
     return out
 
 
-def shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
+def shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream, want=lambda key: True):
     """The kernels on one GPU's share of the sharded layers: the 405B FP8
     norm on T/8 = 256 rows (sequence parallel), the 70B static-FP8 SwiGLU on
     N/8 = 3,584 columns of gate and of up (tensor parallel).  Each beside its

@@ -31,3 +31,11 @@ def test_rotation_covers_three_times_the_last_level_cache():
     for b in (25_168_896, 50_334_720, 220_200_960, 234_921_984, 1_174_405_124):
         n = bench.rotation_sets(b)
         assert n >= 2 and n * b >= 3 * bench.MALL_BYTES
+
+
+def test_configs_filter_parses(monkeypatch):
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--configs", "llama70b_swiglu"])
+    args = bench.parse()
+    assert args.configs == "llama70b_swiglu" and args.gpus == 1
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    assert bench.parse().configs is None
