@@ -110,7 +110,8 @@ __device__ __forceinline__ void load_weight(const NormParams &p, int lane, int n
 template <int WPR, int VPT, int EPI, bool RES, bool W_LATE>
 __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int lane, int nvec,
                                            const u32x4 (&xv)[VPT], u32x4 (&rv)[VPT],
-                                           u32x4 (&wv)[VPT], double *psum, float *pmax)
+                                           u32x4 (&wv)[VPT], double *psum, float *pmax,
+                                           const float *nv_inv)
 {
     constexpr bool QUANT = EPI == NORM_EPI_FP8_DYNAMIC;
     const size_t base = (size_t)row * (size_t)p.hidden;
@@ -216,7 +217,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         // ---- y as above; per 16-value block (the slices of 2 adjacent lanes)
         // the E4M3 scale from the block amax under the tensor scale, then
         // E2M1 codes
-        const Nvfp4Tensor nt = make_nvfp4_tensor(*p.scale_in);
+        const Nvfp4Tensor nt = make_nvfp4_tensor(*p.scale_in, nv_inv[127]);
         uint32_t *qo = (uint32_t *)((uint8_t *)p.out + (size_t)row * (size_t)(p.hidden / 2));
         uint8_t *so = (uint8_t *)p.scale_out + (size_t)row * (size_t)(p.hidden / 16);
 #pragma unroll
@@ -232,7 +233,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
             mag = max(mag, dpp_u32<DPP_XOR1>(mag));
             if (v >= nvec) continue;
             const uint32_t sb = nv_scale_byte(mag, nt);
-            const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<4>(y, sb, nt, nv_block_inverse(sb, nt.g));
+            const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<4>(y, sb, nt, nv_inv[sb]);
             st_stream(qo + v, q);
             if ((lane & 1) == 0) so[v >> 1] = (uint8_t)sb;
         }
@@ -327,6 +328,23 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
     }
 }
 
+// NVFP4: 1/S for each of the 127 finite block scales and 1/(6 g) in the
+// slot of the NaN scale byte, one correctly rounded division per thread at
+// the start of the block (before any early exit: every thread reaches the
+// barrier), instead of one per block of 16 values on the row's critical path.
+template <int EPI>
+__device__ __forceinline__ void fill_nv_table(const NormParams &p, float *nv_inv)
+{
+    if constexpr (EPI == NORM_EPI_NVFP4) {
+        const float g = *p.scale_in;
+        if (threadIdx.x < 127u)
+            nv_inv[threadIdx.x] = nv_block_inverse(threadIdx.x, nv_tensor_scale(g));
+        else if (threadIdx.x == 127u)
+            nv_inv[127] = nv_six_inverse(g);
+        __syncthreads();
+    }
+}
+
 // One row per block (WPR > 1) or per wave (WPR == 1, four rows per block);
 // one block per row or row quartet.
 template <int WPR, int VPT, int EPI, bool RES>
@@ -337,6 +355,8 @@ norm_kernel(NormParams p)
     constexpr int ROWS_PER_BLOCK = (WPR == 1) ? 4 : 1;
     __shared__ double psum[WPR];
     __shared__ float pmax[WPR];
+    __shared__ float nv_inv[EPI == NORM_EPI_NVFP4 ? 128 : 1];
+    fill_nv_table<EPI>(p, nv_inv);
 
     const int tid = threadIdx.x;
     const int lane = tid % ROW_THREADS;
@@ -357,7 +377,7 @@ norm_kernel(NormParams p)
     // there are registers to spare and the weight is loaded with the row
     constexpr bool W_LATE = WPR > 1 && RES;
     if constexpr (!W_LATE) load_weight<WPR, VPT>(p, lane, nvec, wv);
-    finish_row<WPR, VPT, EPI, RES, W_LATE>(p, row, lane, nvec, xv, rv, wv, psum, pmax);
+    finish_row<WPR, VPT, EPI, RES, W_LATE>(p, row, lane, nvec, xv, rv, wv, psum, pmax, nv_inv);
 }
 
 // Persistent and software-pipelined: a fixed grid of blocks walks the rows
@@ -375,6 +395,8 @@ norm_kernel_pipelined(NormParams p)
     // next row's partial sums while a slow one still reads these: two sets
     __shared__ double psum[2][WPR];
     __shared__ float pmax[WPR];
+    __shared__ float nv_inv[EPI == NORM_EPI_NVFP4 ? 128 : 1];
+    fill_nv_table<EPI>(p, nv_inv);
 
     const int tid = threadIdx.x;
     const int lane = tid % ROW_THREADS;
@@ -400,7 +422,7 @@ norm_kernel_pipelined(NormParams p)
 #pragma unroll
             for (int k = 0; k < VPT; ++k) xb[k] = rb[k] = (u32x4)0u;
         }
-        finish_row<WPR, VPT, EPI, RES, false>(p, row, lane, nvec, xa, ra, wv, psum[par], pmax);
+        finish_row<WPR, VPT, EPI, RES, false>(p, row, lane, nvec, xa, ra, wv, psum[par], pmax, nv_inv);
         if (!more) break;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
