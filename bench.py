@@ -167,7 +167,7 @@ def kernel_sources_hash():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the kernels are row-independent and this build "
+        print("bench.py measures one GPU only: the kernels are row-independent and the library "
               "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
