@@ -85,8 +85,8 @@ enum aarms_status {
 /*
  * fused_add_rmsnorm -- residual add followed by RMSNorm in one pass.
  *
- * TensorRT-LLM's RMSNorm "adds the residual and normalizes in one kernel";
- * the norm itself is the eight operations of Hugging Face's RMSNorm (cast to
+ * TensorRT-LLM folds the residual add into its normalization kernel; the
+ * norm itself is the eight operations of Hugging Face's RMSNorm (cast to
  * float, square, mean, add epsilon, reciprocal square root, multiply, cast
  * back, multiply by the weight): "TensorRT-LLM: Compiling Inference Engines
  * Ahead of Time", section "Fusing operations, measured".

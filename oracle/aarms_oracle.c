@@ -223,8 +223,9 @@ void aarms_oracle_rms_scale(const uint16_t *r, int64_t T, int64_t H, float eps,
 }
 
 /* Normalize and weight with a given per-row multiplier rho:
- * t = bf16(f32(h * rho)) ("multiply, cast back"), y = bf16(f32(w) * f32(t))
- * ("multiply by the weight"; the product of two bf16 is exact in binary32). */
+ * t = bf16(f32(h * rho)) (the multiply and the cast back to the tensor type),
+ * y = bf16(f32(w) * f32(t)) (the weight multiply; the product of two bf16 is
+ * exact in binary32). */
 void aarms_oracle_rmsnorm_apply(const uint16_t *r, const uint16_t *w, const float *rho,
                                 int64_t T, int64_t H, uint16_t *y)
 {

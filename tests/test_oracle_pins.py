@@ -698,8 +698,8 @@ def test_golden_workload_shapes_from_pages():
     assert C.SWIGLU_PREFILL4096.inter == q["intermediate"]
     assert C.DECODE_GRAPH.layers == q["layers"]
     tune = gold["rmsnorm_tuning"]
-    # "every version moves the same 25 MB" at 4,096 rows of 1,536 fp16:
-    # one read and one write of the rows
+    # the tuning study gives 25 MB moved by every variant at 4,096 rows of
+    # 1,536 fp16: one read and one write of the rows
     moved = tune["rows"][-1] * tune["hidden"] * 2 * 2
     assert round(moved / 1e6) == tune["megabytes_moved_at_4096_rows"]
     prefill = gold["prefill_intermediate"]
