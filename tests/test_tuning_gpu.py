@@ -54,3 +54,31 @@ def test_installed_variant_runs_and_matches_oracle():
     q, s = A.swiglu_quant_fp8_dynamic(P.to_gpu_bf16(gu))
     torch.cuda.synchronize()
     P.check_swiglu_fp8_dynamic(gu, P.from_gpu_bits(q), P.from_gpu_bits(s))
+
+
+@pytest.mark.parametrize("form", sorted(tuning.FORMS))
+def test_every_form_sweeps_every_fitting_variant(form):
+    # 2,048 wide: a multiple of every block size (16, 32, 128)
+    print("[gpu] tuning sweep", form, "[16,2048]", flush=True)
+    times = tuning.sweep(form, 16, 2048, rounds=1)
+    assert set(times) == set(tuning.variants_fitting(form, 2048))
+    assert all(0 < t < 1e4 for t in times.values())
+
+
+def test_installed_group_variant_matches_oracle():
+    rep = tuning.tune("swiglu_quant_fp8_group", 32, 8960, margin=-1.0, rounds=1)
+    print("[gpu]", rep, flush=True)
+    assert rep["installed"] == rep["best"]
+    gu = gen.normal_bf16((32, 2 * 8960), 43, 4, std=2.0)
+    q, s = A.swiglu_quant_fp8_group(P.to_gpu_bf16(gu))
+    torch.cuda.synchronize()
+    P.check_swiglu_fp8_group(gu, P.from_gpu_bits(q), P.from_gpu_bits(s))
+
+    rep = tuning.tune("fused_add_rmsnorm_quant_fp8_group", 32, 4096, margin=-1.0, rounds=1)
+    print("[gpu]", rep, flush=True)
+    x = gen.normal_bf16((32, 4096), 44, 1)
+    r = gen.normal_bf16((32, 4096), 44, 2)
+    w = gen.normal_bf16((4096,), 44, 3, mean=1.0, std=0.1)
+    q, s, ro = A.fused_add_rmsnorm_quant_fp8_group(P.to_gpu_bf16(x), P.to_gpu_bf16(r), P.to_gpu_bf16(w), 1e-5)
+    torch.cuda.synchronize()
+    P.check_norm_fp8_group(x, r, w, 1e-5, P.from_gpu_bits(q), P.from_gpu_bits(s), P.from_gpu_bits(ro))
