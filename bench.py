@@ -384,7 +384,7 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
     if want("llama405b_norm_fp8_2048x16384"):
         out.update(config5(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream))
     if want("qwen1.5b_norm_16x1536"):
-        out.update(config1(A, lib, W, sp, timer, to_dev, reps))
+        out.update(config1(torch, A, lib, W, sp, timer, to_dev, reps))
     if want("qwen1.5b_decode_28layers_graph"):
         out["qwen1.5b_decode_28layers_graph"] = decode_graph(torch, np, A, W, dev, to_dev, timer)
 
@@ -478,7 +478,7 @@ def config5(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream):
     return out
 
 
-def config1(A, lib, W, sp, timer, to_dev, reps):
+def config1(torch, A, lib, W, sp, timer, to_dev, reps):
     """The 16-token norm (launch-bound, microseconds)."""
     out = {}
     wl = W.NORM_DECODE16
