@@ -286,7 +286,7 @@ def test_swiglu_prefill4096_full_every_variant():
 def test_swiglu_forms_past_65535_rows():
     """More rows than one grid dimension holds: rows continue in grid z."""
     T = 2 * 65535 + 7
-    for N in (16, 32):
+    for N in (16, 32, 128):
         gu = gen.normal_bf16((T, 2 * N), N, 4, std=2.0)
         gt = bf16(gu)
         announce("swiglu forms", (T, N))
@@ -301,6 +301,9 @@ def test_swiglu_forms_past_65535_rows():
         if N % 32 == 0:
             q, sc = A.swiglu_quant_mxfp4(gt)
             P.check_swiglu_mxfp4(gu, bits(q), bits(sc))
+        if N % A.FP8_GROUP == 0:
+            q, sc = A.swiglu_quant_fp8_group(gt)
+            P.check_swiglu_fp8_group(gu, bits(q), bits(sc))
         torch.cuda.synchronize()
 
 
