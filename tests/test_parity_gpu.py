@@ -315,6 +315,31 @@ def test_norm_many_narrow_rows():
         P.check_norm(x, r, w, 1e-6, out, res_out)
 
 
+def test_quantised_norms_many_narrow_rows():
+    """300,000 rows of 128 (75,000 four-row blocks): every quantised norm
+    form, with and without the residual add, at the library's variant."""
+    T, H = 300000, 128
+    x, r, w = norm_case(T, H, seed=78, outliers=0.001)
+    xt, rt, wt = bf16(x), bf16(r), bf16(w)
+    g = torch.tensor([0.02], dtype=torch.float32, device=DEV)
+    announce("quantised norms", (T, H))
+    q, s, ro = A.fused_add_rmsnorm_quant_fp8(xt, rt, wt, 1e-5)
+    P.check_norm_fp8(x, r, w, 1e-5, bits(q), bits(s), bits(ro))
+    q, ro = A.fused_add_rmsnorm_quant_fp8_static(xt, rt, wt, g, 1e-5)
+    P.check_norm_fp8_static(x, r, w, 1e-5, 0.02, bits(q), bits(ro))
+    q, s, ro = A.fused_add_rmsnorm_quant_fp8_group(xt, rt, wt, 1e-5)
+    P.check_norm_fp8_group(x, r, w, 1e-5, bits(q), bits(s), bits(ro))
+    q, s, ro = A.fused_add_rmsnorm_quant_mxfp4(xt, rt, wt, 1e-5)
+    P.check_norm_mxfp4(x, r, w, 1e-5, bits(q), bits(s), bits(ro))
+    q, s, ro = A.fused_add_rmsnorm_quant_nvfp4(xt, rt, wt, g, 1e-5)
+    P.check_norm_nvfp4(x, r, w, 1e-5, 0.02, bits(q), bits(s), bits(ro))
+    q, s = A.rmsnorm_quant_fp8(xt, wt, 1e-5)
+    P.check_rmsnorm_fp8(x, w, 1e-5, bits(q), bits(s))
+    q, s = A.rmsnorm_quant_fp8_group(xt, wt, 1e-5)
+    P.check_rmsnorm_fp8_group(x, w, 1e-5, bits(q), bits(s))
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ swiglu + fp8
 
 def _all_y_rows():
