@@ -773,6 +773,17 @@ def decode_graph(torch, np, A, W, dev, to_dev, timer):
     return res
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo where there is one."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(np, W, nd, gd, step_bytes, seconds):
     """The oracle as it stands, on the headline workload, repeated for a
     bounded time on all of the host's cores, then on one core over a row
@@ -797,7 +808,8 @@ def cpu_baseline(np, W, nd, gd, step_bytes, seconds):
     reps, el = timed(T, seconds)
     out = {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": cores,
            "kind": "oracle", "sample": "%d full passes of the headline workload (norm [4096,1536] + "
-                                       "swiglu [4096,17920]) in %.1f s" % (reps, el)}
+                                       "swiglu [4096,17920]) in %.1f s" % (reps, el),
+           "ms_per_step": round(el / reps * 1e3, 1), "cpu_model": cpu_model()}
     # one core, on the first 256 rows of the same tensors (the bytes scale with rows)
     rows = 256
     oracle.set_threads(1)
@@ -807,7 +819,8 @@ def cpu_baseline(np, W, nd, gd, step_bytes, seconds):
         oracle.set_threads(cores)
     out["single_core"] = {"value": round(step_bytes * rows / T * reps1 / el1 / 1e9, 3), "unit": "GB/s",
                           "cores": 1, "sample": "%d passes over the first %d rows of the headline workload "
-                                                "in %.1f s" % (reps1, rows, el1)}
+                                                "in %.1f s" % (reps1, rows, el1),
+                          "ms_per_step": round(el1 / reps1 * T / rows * 1e3, 1)}
     return out
 
 

@@ -39,3 +39,8 @@ def test_configs_filter_parses(monkeypatch):
     assert args.configs == "llama70b_swiglu" and args.gpus == 1
     monkeypatch.setattr(sys, "argv", ["bench.py"])
     assert bench.parse().configs is None
+
+
+def test_cpu_model_is_named_or_none():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
