@@ -318,8 +318,9 @@ const char *aarms_status_string(int status);
  *
  *   out_fp8      [num_tokens, width]       fp8    written: e4m3(clamp(y / s_g))
  *   scale_out    [num_tokens, width / 128] fp32   written: s_g = binary32(max |y| over
- *                                                  the group / 448) (0 for an
- *                                                  all-zero group, whose codes are zeros)
+ *                                                  the group / 448), NaN values
+ *                                                  ignored (0 for an all-zero group,
+ *                                                  whose codes are zeros); 4-byte aligned
  *   residual_out, x, residual, weight, hidden, eps   as for fused_add_rmsnorm
  *   gate_up, inter                                    as for swiglu
  * width (hidden or inter) must be a multiple of 128 (else
