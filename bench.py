@@ -350,7 +350,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",
+        "io_dtype": "bf16",
         "data": "synthetic (seeded normals, Qwen2.5-1.5B prefill-layer shapes; no weights)",
         "config": {
             "workload": "qwen1.5b_prefill4096: fused_add_rmsnorm bf16 [4096,1536] eps 1e-6 + "
