@@ -668,3 +668,66 @@ def test_fp8_group_forms_under_graph_replay():
         xt.add_(0)
     P.check_norm_fp8_group(x, r, w, 1e-5, bits(outs["fq"]), bits(outs["fs"]), bits(outs["fro"]))
     P.check_swiglu_fp8_group(gu, bits(outs["sq"]), bits(outs["ss"]))
+
+
+# ------------------------------------------------------------------ seeded random shapes
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng([2024, seed])
+    out = []
+    for _ in range(n):
+        T = int(rng.integers(1, 300))
+        W = 8 * int(rng.integers(1, 1025))          # 8 .. 8,192, any multiple of 8
+        if rng.random() < 0.3:
+            W = 128 * int(rng.integers(1, 65))      # whole 128-value groups
+        out.append((T, W))
+    return out
+
+
+@pytest.mark.parametrize("T,H", _random_shapes(24, 1))
+def test_random_shapes_every_norm_form(T, H):
+    x, r, w = norm_case(T, H, seed=T * 131 + H, outliers=0.002)
+    xt, rt, wt = bf16(x), bf16(r), bf16(w)
+    g = scale_t(0.02)
+    announce("norm forms", (T, H))
+    out, ro = A.fused_add_rmsnorm(xt, rt, wt, 1e-5)
+    P.check_norm(x, r, w, 1e-5, bits(out), bits(ro))
+    q, s, ro = A.fused_add_rmsnorm_quant_fp8(xt, rt, wt, 1e-5)
+    P.check_norm_fp8(x, r, w, 1e-5, bits(q), bits(s), bits(ro))
+    q, ro = A.fused_add_rmsnorm_quant_fp8_static(xt, rt, wt, g, 1e-5)
+    P.check_norm_fp8_static(x, r, w, 1e-5, 0.02, bits(q), bits(ro))
+    P.check_rmsnorm(x, w, 1e-5, bits(A.rmsnorm(xt, wt, 1e-5)))
+    q, s = A.rmsnorm_quant_fp8(xt, wt, 1e-5)
+    P.check_rmsnorm_fp8(x, w, 1e-5, bits(q), bits(s))
+    if H % 16 == 0:
+        q, s, ro = A.fused_add_rmsnorm_quant_nvfp4(xt, rt, wt, g, 1e-5)
+        P.check_norm_nvfp4(x, r, w, 1e-5, 0.02, bits(q), bits(s), bits(ro))
+    if H % 32 == 0:
+        q, s, ro = A.fused_add_rmsnorm_quant_mxfp4(xt, rt, wt, 1e-5)
+        P.check_norm_mxfp4(x, r, w, 1e-5, bits(q), bits(s), bits(ro))
+    if H % A.FP8_GROUP == 0:
+        q, s, ro = A.fused_add_rmsnorm_quant_fp8_group(xt, rt, wt, 1e-5)
+        P.check_norm_fp8_group(x, r, w, 1e-5, bits(q), bits(s), bits(ro))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,N", _random_shapes(24, 2))
+def test_random_shapes_every_swiglu_form(T, N):
+    gu = gen.normal_bf16((T, 2 * N), T * 137 + N, 4, std=2.0)
+    gt = bf16(gu)
+    s = scale_t(0.05)
+    announce("swiglu forms", (T, N))
+    P.check_swiglu(gu, bits(A.swiglu(gt)))
+    P.check_swiglu_fp8(gu, 0.05, bits(A.swiglu_quant_fp8(gt, s)))
+    q, sc = A.swiglu_quant_fp8_dynamic(gt)
+    P.check_swiglu_fp8_dynamic(gu, bits(q), bits(sc))
+    if N % 16 == 0:
+        q, sc = A.swiglu_quant_nvfp4(gt, s)
+        P.check_swiglu_nvfp4(gu, 0.05, bits(q), bits(sc))
+    if N % 32 == 0:
+        q, sc = A.swiglu_quant_mxfp4(gt)
+        P.check_swiglu_mxfp4(gu, bits(q), bits(sc))
+    if N % A.FP8_GROUP == 0:
+        q, sc = A.swiglu_quant_fp8_group(gt)
+        P.check_swiglu_fp8_group(gu, bits(q), bits(sc))
+    torch.cuda.synchronize()
