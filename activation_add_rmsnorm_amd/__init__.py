@@ -623,7 +623,8 @@ def variant_name(op: int, variant: int) -> str | None:
 
 
 def pick_variant(op: int, tokens: int, width: int, quant: int | bool = False) -> int:
-    """The heuristic's variant.  quant: for the norms a flag (a quantised
-    form or not); for OP_SWIGLU the output format (0 bf16, 1 E4M3, 2 MXFP4,
-    3 NVFP4)."""
+    """The heuristic's variant.  quant, the output format: for the norms
+    (OP_NORM, OP_RMSNORM) 0 bf16, 1 E4M3 per token, 2 E4M3 per tensor,
+    3 MXFP4, 4 NVFP4, 5 E4M3 per 128-value group; for OP_SWIGLU 0 bf16,
+    1 E4M3, 2 MXFP4, 3 NVFP4, 4 E4M3 per 128-value group."""
     return int(load().aarms_pick_variant(int(op), int(tokens), int(width), int(quant)))

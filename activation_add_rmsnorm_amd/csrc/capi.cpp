@@ -101,10 +101,22 @@ static int norm_fit(int waves, int64_t hidden, int max_vecs)
 // wins (measured on MI355X, 256 CUs, rows of 1,536).
 constexpr int64_t kNarrowMultiWaveTokens = 1024;
 
-int pick_norm(int64_t tokens, int64_t hidden, bool quant, bool residual)
+// Per-token E4M3 with the residual add reduces each row twice (sum of
+// squares, then amax), so the cost of a cross-wave barrier weighs more: for
+// rows wider than 8,192 in batches up to 1,024 tokens, 8 waves of 4 vectors
+// per lane beat 16 waves of 2 (1.5-7% at 1 to 1,024 tokens of 12,288 and
+// 16,384; from 2,048 tokens 16 x 2 is as fast or faster).  The block-scaled
+// forms, with one reduction, keep 16 x 2.
+constexpr int64_t kDynamicFp8FewWavesTokens = 1024;
+
+// epi: the output format (NORM_EPI_*); residual: with the add in front.
+int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
 {
-    (void)quant;
     if (hidden <= 0 || hidden > AARMS_MAX_HIDDEN) return -1;
+    if (epi == NORM_EPI_FP8_DYNAMIC && residual && hidden > 8192 && tokens <= kDynamicFp8FewWavesTokens) {
+        const int i = norm_fit(8, hidden, 4);
+        if (i >= 0) return i;
+    }
     // Narrow rows (up to 4 vectors per lane, 2,048 wide): one wave per row
     // with as few vectors per lane as fit (four waves per row for small
     // batches).  Wider rows: the fewest waves per row that fit with at most
@@ -237,7 +249,7 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
                          scale_out};
     }
     if ((st = check_outputs(outs, partner, n_out, ins, n_in))) return st;
-    if (variant == -1) variant = pick_norm(tokens, hidden, epi != NORM_EPI_BF16, res);
+    if (variant == -1) variant = pick_norm(tokens, hidden, epi, res);
     const NormVariant *v = norm_variant(variant);
     if (!v || norm_capacity(v) < hidden) return AARMS_ERR_BAD_VARIANT;
     NormParams p;
@@ -645,7 +657,12 @@ int swiglu_quant_fp8_group_ex(void *out_fp8, float *scale_out, const void *gate_
 
 int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant)
 {
-    if (op == 0 || op == 3) return pick_norm(num_tokens, width, quant != 0, op == 0);
+    if (op == 0 || op == 3) {
+        // quant: the output format (0 bf16, 1 E4M3 per token, 2 E4M3 per
+        // tensor, 3 MXFP4, 4 NVFP4, 5 E4M3 per 128-value group)
+        if (quant < NORM_EPI_BF16 || quant > NORM_EPI_FP8_GROUP) return -1;
+        return pick_norm(num_tokens, width, quant, op == 0);
+    }
     if (op == 1) {
         // quant: the output format (0 bf16, 1 E4M3, 2 MXFP4, 3 NVFP4, 4 E4M3
         // with a scale per 128 outputs)

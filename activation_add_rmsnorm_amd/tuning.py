@@ -39,27 +39,28 @@ import activation_add_rmsnorm_amd as A
 
 MALL_BYTES = 256e6          # MI355X last-level cache; rotation covers three times this
 
-# form -> (variant table op, the quant argument of aarms_pick_variant: a
-# flag for the norms, the output format for swiglu: 0 bf16, 1 E4M3,
-# 2 MXFP4, 3 NVFP4)
+# form -> (variant table op, the quant argument of aarms_pick_variant: the
+# output format; norms: 0 bf16, 1 E4M3 per token, 2 E4M3 per tensor,
+# 3 MXFP4, 4 NVFP4, 5 E4M3 per group; swiglu: 0 bf16, 1 E4M3, 2 MXFP4,
+# 3 NVFP4, 4 E4M3 per group)
 FORMS = {
-    "fused_add_rmsnorm": (A.OP_NORM, False),
-    "fused_add_rmsnorm_quant_fp8": (A.OP_NORM, True),
-    "fused_add_rmsnorm_quant_fp8_static": (A.OP_NORM, True),
-    "rmsnorm": (A.OP_RMSNORM, False),
-    "rmsnorm_quant_fp8": (A.OP_RMSNORM, True),
-    "rmsnorm_quant_fp8_static": (A.OP_RMSNORM, True),
-    "fused_add_rmsnorm_quant_mxfp4": (A.OP_NORM, True),
-    "rmsnorm_quant_mxfp4": (A.OP_RMSNORM, True),
+    "fused_add_rmsnorm": (A.OP_NORM, 0),
+    "fused_add_rmsnorm_quant_fp8": (A.OP_NORM, 1),
+    "fused_add_rmsnorm_quant_fp8_static": (A.OP_NORM, 2),
+    "rmsnorm": (A.OP_RMSNORM, 0),
+    "rmsnorm_quant_fp8": (A.OP_RMSNORM, 1),
+    "rmsnorm_quant_fp8_static": (A.OP_RMSNORM, 2),
+    "fused_add_rmsnorm_quant_mxfp4": (A.OP_NORM, 3),
+    "rmsnorm_quant_mxfp4": (A.OP_RMSNORM, 3),
     "swiglu": (A.OP_SWIGLU, 0),
     "swiglu_quant_fp8": (A.OP_SWIGLU, 1),
     "swiglu_quant_fp8_dynamic": (A.OP_SWIGLU_DYNAMIC, True),
     "swiglu_quant_mxfp4": (A.OP_SWIGLU, 2),
-    "fused_add_rmsnorm_quant_nvfp4": (A.OP_NORM, True),
-    "rmsnorm_quant_nvfp4": (A.OP_RMSNORM, True),
+    "fused_add_rmsnorm_quant_nvfp4": (A.OP_NORM, 4),
+    "rmsnorm_quant_nvfp4": (A.OP_RMSNORM, 4),
     "swiglu_quant_nvfp4": (A.OP_SWIGLU, 3),
-    "fused_add_rmsnorm_quant_fp8_group": (A.OP_NORM, True),
-    "rmsnorm_quant_fp8_group": (A.OP_RMSNORM, True),
+    "fused_add_rmsnorm_quant_fp8_group": (A.OP_NORM, 5),
+    "rmsnorm_quant_fp8_group": (A.OP_RMSNORM, 5),
     "swiglu_quant_fp8_group": (A.OP_SWIGLU, 4),
 }
 

@@ -689,6 +689,16 @@ def shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream, want=lambda k
             raise A.AarmsError(st, what)
 
     wl = W.NORM_FP8_LLAMA405B_SP8
+    if want(wl.name):
+        _share_norm(out, wl, torch, A, lib, dev, sp, timer, to_dev, reps, stream, entry, check, W)
+    wl = W.SWIGLU_FP8_LLAMA70B_TP8
+    if want(wl.name):
+        _share_swiglu(out, wl, torch, A, lib, dev, sp, timer, reps, stream, entry, check)
+    torch.cuda.empty_cache()
+    return out
+
+
+def _share_norm(out, wl, torch, A, lib, dev, sp, timer, to_dev, reps, stream, entry, check, W):
     T, H = wl.tokens, wl.hidden
     d = W.norm_inputs(wl)
     x0, r0, w0 = to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["weight"])
@@ -709,7 +719,8 @@ def shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream, want=lambda k
     out[wl.name] = entry(ms, ms_c, nb, {"buffer_sets_rotated": ns})
     del sets, x0, r0
 
-    wl = W.SWIGLU_FP8_LLAMA70B_TP8
+
+def _share_swiglu(out, wl, torch, A, lib, dev, sp, timer, reps, stream, entry, check):
     T, N = wl.tokens, wl.inter
     g = torch.Generator(device=dev).manual_seed(0)
     gu = (torch.randn((T, 2 * N), generator=g, device=dev, dtype=torch.float32) * wl.gate_up_std).to(torch.bfloat16)
@@ -727,8 +738,6 @@ def shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream, want=lambda k
     ms_c = timer.region(ceil, reps)
     out[wl.name] = entry(ms, ms_c, nb, {"inputs": "torch.randn on device, seed 0, std 2", "buffer_sets_rotated": ns})
     del sets, gu
-    torch.cuda.empty_cache()
-    return out
 
 
 def decode_graph(torch, np, A, W, dev, to_dev, timer):

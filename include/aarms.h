@@ -343,12 +343,13 @@ int swiglu_quant_fp8_group(void *out_fp8, float *scale_out, const void *gate_up,
  * explicitly.  A variant id is an index into the op's table;
  * aarms_variant_name() describes it (static storage) and returns NULL past
  * the end.  ops: 0 = the norms with the residual add (fused_add_rmsnorm*),
- * 3 = the norms without it (rmsnorm*), both on one variant table (quant != 0
- * for a quantised form); 1 = swiglu, swiglu_quant_fp8, swiglu_quant_mxfp4
- * swiglu_quant_nvfp4 and swiglu_quant_fp8_group (quant = the output
- * format: 0 bf16, 1 E4M3, 2 MXFP4, 3 NVFP4, 4 E4M3 per 128-value group; -1
- * is returned for another value); 2 = swiglu_quant_fp8_dynamic.  The
- * per-group norms share the norm tables (quant != 0).
+ * 3 = the norms without it (rmsnorm*), both on one variant table (quant = the
+ * output format: 0 bf16, 1 E4M3 per token, 2 E4M3 per tensor (the _static
+ * forms), 3 MXFP4, 4 NVFP4, 5 E4M3 per 128-value group); 1 = swiglu,
+ * swiglu_quant_fp8, swiglu_quant_mxfp4, swiglu_quant_nvfp4 and
+ * swiglu_quant_fp8_group (quant = the output format: 0 bf16, 1 E4M3, 2 MXFP4,
+ * 3 NVFP4, 4 E4M3 per 128-value group); 2 = swiglu_quant_fp8_dynamic.  -1
+ * is returned for a format code outside these.
  * aarms_pick_variant() returns the id the plain entry point would use, or -1
  * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
  */

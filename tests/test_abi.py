@@ -312,6 +312,19 @@ def test_pick_variant_ranges():
     assert name(4096, 8960, 3) == "1 job/lane"
     assert name(8192, 28672, 3) == "2 jobs/lane" and name(512, 28672, 3) == "1 job/lane"
     assert name(4096, 8960, 4) == name(4096, 8960, 1)                # per-group E4M3: the E4M3 rule
+    # norms: the output format decides only for per-token E4M3 with the residual
+    # on rows wider than 8,192 up to 1,024 tokens (two row reductions: fewer waves)
+    nname = lambda op, T, H, f: A.variant_name(op, A.pick_variant(op, T, H, f))
+    for f in (0, 2, 3, 4, 5):
+        assert nname(A.OP_NORM, 256, 16384, f) == "16 waves/row x2 vec"
+    assert nname(A.OP_NORM, 256, 16384, 1) == "8 waves/row x4 vec"
+    assert nname(A.OP_NORM, 1, 12288, 1) == "8 waves/row x4 vec"
+    assert nname(A.OP_NORM, 1024, 16384, 1) == "8 waves/row x4 vec"
+    assert nname(A.OP_NORM, 2048, 16384, 1) == "16 waves/row x2 vec"   # the 405B workload
+    assert nname(A.OP_NORM, 256, 8192, 1) == nname(A.OP_NORM, 256, 8192, 0) == "8 waves/row x2 vec"
+    assert nname(A.OP_RMSNORM, 256, 16384, 1) == nname(A.OP_RMSNORM, 256, 16384, 0)
+    for f in (-1, 6):
+        assert A.pick_variant(A.OP_NORM, 16, 1536, f) == -1            # unknown output format
 
 
 def test_ceiling_library_rejects_bad_arguments():

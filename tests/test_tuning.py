@@ -43,8 +43,8 @@ def test_variants_fitting_respect_capacity():
         for width in (8, 1536, 16384, 65536):
             vs = tuning.variants_fitting(form, width)
             if form == "swiglu_quant_fp8_dynamic" or not form.startswith("swiglu"):
-                op, _ = tuning.FORMS[form]
-                assert A.pick_variant(op, 16, width, True) in vs
+                op, fmt = tuning.FORMS[form]
+                assert A.pick_variant(op, 16, width, fmt) in vs
             assert vs
 
 
