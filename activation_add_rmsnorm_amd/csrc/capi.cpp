@@ -95,6 +95,16 @@ static int norm_fit(int waves, int64_t hidden, int max_vecs)
     return best;
 }
 
+// The variant with exactly these parameters, or -1.
+static int norm_find(int waves, int vecs, int blocks_per_cu)
+{
+    for (int i = 0; i < norm_variant_count(); ++i) {
+        const NormVariant *v = norm_variant(i);
+        if (v->waves_per_row == waves && v->vecs_per_lane == vecs && v->blocks_per_cu == blocks_per_cu) return i;
+    }
+    return -1;
+}
+
 // Below this many rows a narrow-row launch is latency-bound (a few waves per
 // CU at most) and splitting each row over four waves shortens every row's
 // dependent chain of loads and reductions; from here on one wave per row
@@ -109,10 +119,23 @@ constexpr int64_t kNarrowMultiWaveTokens = 1024;
 // forms, with one reduction, keep 16 x 2.
 constexpr int64_t kDynamicFp8FewWavesTokens = 1024;
 
+// bf16 with the residual add on rows of 4,097-8,192: from 768 to 1,536
+// tokens a one-shot grid of 8-wave blocks runs about 0.75-1.5 generations
+// and leaves a partial one; the persistent, software-pipelined 8 x 2 variant
+// (two blocks per CU, each walking rows and loading the next during the
+// current one's reductions) measured 0-19% faster there at 5,120-8,192 wide,
+// and no faster below 768 or from 2,048 tokens.
+constexpr int64_t kPipelinedMinTokens = 768, kPipelinedMaxTokens = 1536;
+
 // epi: the output format (NORM_EPI_*); residual: with the add in front.
 int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
 {
     if (hidden <= 0 || hidden > AARMS_MAX_HIDDEN) return -1;
+    if (epi == NORM_EPI_BF16 && residual && hidden > 4096 && hidden <= 8192 &&
+        tokens >= kPipelinedMinTokens && tokens <= kPipelinedMaxTokens) {
+        const int i = norm_find(8, 2, 2);
+        if (i >= 0) return i;
+    }
     if (epi == NORM_EPI_FP8_DYNAMIC && residual && hidden > 8192 && tokens <= kDynamicFp8FewWavesTokens) {
         const int i = norm_fit(8, hidden, 4);
         if (i >= 0) return i;

@@ -325,6 +325,13 @@ def test_pick_variant_ranges():
     assert nname(A.OP_RMSNORM, 256, 16384, 1) == nname(A.OP_RMSNORM, 256, 16384, 0)
     for f in (-1, 6):
         assert A.pick_variant(A.OP_NORM, 16, 1536, f) == -1            # unknown output format
+    # bf16 with the residual, 4,097-8,192 wide, 768-1,536 tokens: the pipelined 8 x 2
+    for T, H in ((768, 5120), (1024, 8192), (1536, 6144)):
+        assert nname(A.OP_NORM, T, H, 0) == "8 waves/row x2 vec, pipelined 2 blocks/CU"
+    for T, H in ((512, 8192), (2048, 8192), (1024, 4096), (1024, 12288)):
+        assert "pipelined" not in nname(A.OP_NORM, T, H, 0)
+    assert "pipelined" not in nname(A.OP_NORM, 1024, 8192, 1)           # not the quantised forms
+    assert "pipelined" not in nname(A.OP_RMSNORM, 1024, 8192, 0)        # nor without the add
 
 
 def test_ceiling_library_rejects_bad_arguments():

@@ -138,6 +138,15 @@ def test_norm_pipelined_variants_walk_several_rows():
         P.check_norm_fp8(x, r, wt, 1e-5, q, s, res_q)
 
 
+@pytest.mark.parametrize("T,H", [(768, 5120), (1024, 8192), (1536, 6144), (1000, 7168)])
+def test_norm_default_variant_mid_batches(T, H):
+    """Batches where the library picks the persistent, pipelined variant for
+    the bf16 form (each block walks several rows)."""
+    x, r, w = norm_case(T, H, seed=T + H, outliers=0.001)
+    out, res_out = run_norm(x, r, w, 1e-6)
+    P.check_norm(x, r, w, 1e-6, out, res_out)
+
+
 def test_norm_decode16_full():
     wl = W.NORM_DECODE16
     d = W.norm_inputs(wl)
