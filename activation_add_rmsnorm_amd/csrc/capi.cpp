@@ -136,6 +136,23 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
         const int i = norm_find(8, 2, 2);
         if (i >= 0) return i;
     }
+    // The same band without the residual add, on rows of 8,193-16,384 (8
+    // waves of 4 vectors): the pipelined 8 x 4 grid measured 5-25% faster
+    // from 512 to 2,048 tokens at 16,384 wide (bf16 only: the per-token E4M3
+    // form is slower pipelined).
+    if (epi == NORM_EPI_BF16 && !residual && hidden > 8192 && hidden <= 16384 && tokens >= 512 &&
+        tokens <= 2048) {
+        const int i = norm_find(8, 4, 2);
+        if (i >= 0) return i;
+    }
+    // Without the residual, rows of 2,049-4,096 in batches under 1,024
+    // tokens: 4 waves of 2 vectors per lane beat 2 waves of 4 by 9-18% (the
+    // shorter per-lane chain matters while the launch is latency-bound);
+    // from 1,024 tokens 2 x 4 is as fast or faster.
+    if (!residual && hidden > 2048 && hidden <= 4096 && tokens < kNarrowMultiWaveTokens) {
+        const int i = norm_fit(4, hidden, 2);
+        if (i >= 0) return i;
+    }
     if (epi == NORM_EPI_FP8_DYNAMIC && residual && hidden > 8192 && tokens <= kDynamicFp8FewWavesTokens) {
         const int i = norm_fit(8, hidden, 4);
         if (i >= 0) return i;
@@ -202,11 +219,19 @@ int rowq_capacity(const SwigluRowVariant *v) { return v->waves_per_row * 64 * v-
 // Per-token FP8 SwiGLU: the fewest waves per row (one, else 4, 8, 16) that
 // hold the row with at most 4 jobs per lane, the fewest jobs for that count;
 // else the widest variant.
+// A row on one wave takes up to 4 jobs per lane; a row over several waves
+// takes at most 3 jobs per lane before it takes 4 (twice the waves with half
+// the jobs measured 2-25% faster at 5,632 and 14,336 wide up to 2,048 tokens,
+// and never slower by more than 0.3%), then 8.
 int pick_swiglu_rowq(int64_t tokens, int64_t inter)
 {
     if (tokens < 0 || inter <= 0 || inter > AARMS_MAX_INTER_PER_TOKEN) return -1;
-    for (int max_jobs : {4, 8})
-        for (int w : {1, 4, 8, 16}) {
+    for (int i = 0; i < swiglu_row_variant_count(); ++i) {
+        const SwigluRowVariant *v = swiglu_row_variant(i);
+        if (v->waves_per_row == 1 && v->jobs_per_lane <= 4 && rowq_capacity(v) >= inter) return i;
+    }
+    for (int max_jobs : {3, 4, 8})
+        for (int w : {4, 8, 16}) {
             int best = -1;
             for (int i = 0; i < swiglu_row_variant_count(); ++i) {
                 const SwigluRowVariant *v = swiglu_row_variant(i);

@@ -331,7 +331,18 @@ def test_pick_variant_ranges():
     for T, H in ((512, 8192), (2048, 8192), (1024, 4096), (1024, 12288)):
         assert "pipelined" not in nname(A.OP_NORM, T, H, 0)
     assert "pipelined" not in nname(A.OP_NORM, 1024, 8192, 1)           # not the quantised forms
-    assert "pipelined" not in nname(A.OP_RMSNORM, 1024, 8192, 0)        # nor without the add
+    assert "pipelined" not in nname(A.OP_RMSNORM, 1024, 8192, 0)        # nor without the add at 8,192
+    # without the add: 4 waves x 2 below 1,024 tokens up to 4,096 wide; the
+    # pipelined 8 x 4 for bf16 at 8,193-16,384 wide from 512 to 2,048 tokens
+    assert nname(A.OP_RMSNORM, 512, 4096, 0) == nname(A.OP_RMSNORM, 1, 4096, 1) == "4 waves/row x2 vec"
+    assert nname(A.OP_RMSNORM, 1024, 4096, 0) == "2 waves/row x4 vec"
+    assert nname(A.OP_RMSNORM, 1024, 16384, 0) == "8 waves/row x4 vec, pipelined 2 blocks/CU"
+    assert nname(A.OP_RMSNORM, 1024, 16384, 1) == nname(A.OP_RMSNORM, 4096, 16384, 0) == "8 waves/row x4 vec"
+    # per-token SwiGLU: several waves per row take at most 3 jobs before 4
+    rq = lambda N: A.variant_name(A.OP_SWIGLU_DYNAMIC, A.pick_variant(A.OP_SWIGLU_DYNAMIC, 64, N))
+    assert rq(2048) == "wave/row x4 jobs" and rq(5632) == "8 waves/row x2 jobs"
+    assert rq(8960) == "8 waves/row x3 jobs" and rq(14336) == "16 waves/row x2 jobs"
+    assert rq(28672) == "16 waves/row x4 jobs"
 
 
 def test_ceiling_library_rejects_bad_arguments():
