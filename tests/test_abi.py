@@ -472,3 +472,23 @@ def test_fp8_group_errors():
     assert lib.fused_add_rmsnorm_quant_fp8_group(P, P + BIG, P + 2 * BIG, P + 3 * BIG, P + 4 * BIG,
                                                  P + 5 * BIG, 4, 1544, 1e-6, None) == SHAPE
     assert lib.rmsnorm_quant_fp8_group(P, P + BIG, P + 3 * BIG, P + 5 * BIG, 4, 1544, 1e-6, None) == SHAPE
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """A copy of the package without libaarms.so and without the sources to
+    build it: load() must raise (there is no CPU fallback)."""
+    import shutil
+    import sys
+    pkg = tmp_path / "activation_add_rmsnorm_amd"
+    pkg.mkdir()
+    src = os.path.join(ROOT, "activation_add_rmsnorm_amd")
+    for f in ("__init__.py", "_build.py", "tuning.py"):
+        shutil.copy(os.path.join(src, f), pkg / f)
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import activation_add_rmsnorm_amd as A\n"
+            "assert A.lib_path().startswith(%r)\n"
+            "try:\n    A.load()\nexcept Exception as e:\n    print('raised', type(e).__name__)\n"
+            "else:\n    print('loaded')\n") % (str(tmp_path), str(tmp_path))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=str(tmp_path))
+    assert "raised" in r.stdout, r.stdout + r.stderr
+    assert not os.path.exists(pkg / "libaarms.so")
