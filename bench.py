@@ -130,7 +130,8 @@ def traffic_from_profiles(kernel_key: str, src_hash: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel sources; else None."""
     for path in glob.glob(os.path.join(ROOT, "profiles", "*counters*.md")):
-        txt = open(path).read()
+        with open(path) as f:
+            txt = f.read()
         if ("kernel_sources_sha256: " + src_hash) not in txt:
             continue
         for line in txt.splitlines():
@@ -160,7 +161,8 @@ def ceiling_entry(kernel_us, ceiling_us, nbytes):
 def kernel_sources_hash():
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "activation_add_rmsnorm_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+        with open(p, "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -786,9 +788,10 @@ def decode_graph(torch, np, A, W, dev, to_dev, timer):
 def cpu_model():
     """The host CPU's model name, from /proc/cpuinfo where there is one."""
     try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
     return None
