@@ -6,9 +6,9 @@ ops over 4,096 tokens: fused_add_rmsnorm on bf16 [4096, 1536] followed by
 swiglu on bf16 gate_up [4096, 17920] -> [4096, 8960].  ``value`` is the
 effective HBM bandwidth of the step: the algorithmic bytes (every input read
 once, every output written once, the weight once) divided by the wall time of
-K back-to-back steps with the inputs already resident in HBM.  Three buffer
-sets are rotated so that every step reads HBM rather than the 256 MB
-last-level cache.
+K back-to-back steps with the inputs already resident in HBM.  Each op
+rotates through buffer sets covering three times the 256 MB last-level
+cache, so that every step reads HBM rather than that cache.
 
 Beside every kernel the same rotation of buffers is also streamed by a plain
 copy-like kernel (libaarms_ceiling.so) that reads and writes exactly the same
@@ -19,11 +19,12 @@ kernel's time measured against it.
 The same run also measures, as supplementary figures, the static-FP8 SwiGLU
 on Llama-70B's [8192, 57344] gate_up, the dynamic-FP8 norm on Llama-405B's
 [2048, 16384] rows, the 16-token norm, the 28-layer decode chain under a
-HIP graph, and the rest of the quantisation matrix (rmsnorm without the
-residual add, the static-scale FP8 norm, the per-token FP8 norm without the
-residual, the per-token FP8 SwiGLU) at the same shapes; and it times the CPU
+HIP graph, the rest of the quantisation matrix at the same shapes (rmsnorm
+without the residual add, the static-scale and per-token E4M3 forms, MXFP4,
+NVFP4 and per-128-value E4M3), one GPU's share of both Llama layers under
+8-way sharding, and the start-up tuner's report; and it times the CPU
 oracle on the host's cores on the headline workload (a baseline, not a
-target).
+target).  --configs restricts the supplementary figures to matching keys.
 
 Prints exactly one JSON line.
 """
