@@ -709,6 +709,7 @@ int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant)
         // quant: the output format (0 bf16, 1 E4M3 per token, 2 E4M3 per
         // tensor, 3 MXFP4, 4 NVFP4, 5 E4M3 per 128-value group)
         if (quant < NORM_EPI_BF16 || quant > NORM_EPI_FP8_GROUP) return -1;
+        if (num_tokens < 0 || width % 8 != 0) return -1;
         return pick_norm(num_tokens, width, quant, op == 0);
     }
     if (op == 1) {

@@ -325,6 +325,10 @@ def test_pick_variant_ranges():
     assert nname(A.OP_RMSNORM, 256, 16384, 1) == nname(A.OP_RMSNORM, 256, 16384, 0)
     for f in (-1, 6):
         assert A.pick_variant(A.OP_NORM, 16, 1536, f) == -1            # unknown output format
+    for op in (A.OP_NORM, A.OP_RMSNORM, A.OP_SWIGLU, A.OP_SWIGLU_DYNAMIC):
+        assert A.pick_variant(op, -1, 1536) == -1                      # what the entry points reject
+        assert A.pick_variant(op, 16, 1540) == -1
+        assert A.pick_variant(op, 0, 1536) >= 0                        # zero tokens is a valid call
     # bf16 with the residual, 4,097-8,192 wide, 768-1,536 tokens: the pipelined 8 x 2
     for T, H in ((768, 5120), (1024, 8192), (1536, 6144)):
         assert nname(A.OP_NORM, T, H, 0) == "8 waves/row x2 vec, pipelined 2 blocks/CU"
