@@ -311,7 +311,8 @@ def test_pick_variant_ranges():
     assert name(4096, 8960, 1) == "2 jobs/lane"
     assert name(4096, 8960, 3) == "1 job/lane"
     assert name(8192, 28672, 3) == "2 jobs/lane" and name(512, 28672, 3) == "1 job/lane"
-    assert name(4096, 8960, 4) == name(4096, 8960, 1)                # per-group E4M3: the E4M3 rule
+    assert name(4096, 8960, 4) == "1 job/lane"                       # per-group E4M3: one job per lane
+    assert name(16, 8960, 4) == "1 half job/lane"
     # norms: the output format decides only for per-token E4M3 with the residual
     # on rows wider than 8,192 up to 1,024 tokens (two row reductions: fewer waves)
     nname = lambda op, T, H, f: A.variant_name(op, A.pick_variant(op, T, H, f))
