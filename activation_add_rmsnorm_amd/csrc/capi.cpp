@@ -199,19 +199,21 @@ int pick_swiglu(int64_t tokens, int64_t inter, int epi)
     if (tokens < 0 || inter <= 0) return -1;
     // tokens * inter against the thresholds, without forming the product
     if (tokens <= kSwigluHalfJobOutputs / inter) return swiglu_find(1, 4);
-    // bf16, MXFP4 and per-group E4M3 output: one job per lane (the most
-    // blocks, each short-lived, so the blocks in flight stay on one
-    // contiguous stretch of memory; for the per-group form one job measured
-    // 7-26% faster than two from 1,024 tokens at 5,632-14,336 wide, as fast
-    // at 28,672).  Per-tensor E4M3 output, from about four million outputs:
-    // two jobs per lane, which gives the longer per-job arithmetic two loads
-    // in flight to hide behind.  NVFP4 output (the most arithmetic per
-    // output): two jobs per lane from about 32 million outputs, when a row is
-    // a whole number of 512-job blocks (otherwise the last block of every
-    // row is mostly idle: N = 8960 rows have 1120 jobs).
+    // bf16 and MXFP4 output: one job per lane (the most blocks, each
+    // short-lived, so the blocks in flight stay on one contiguous stretch of
+    // memory).  Per-tensor E4M3 output, from about four million outputs: two
+    // jobs per lane, which gives the longer per-job arithmetic two loads in
+    // flight to hide behind.  NVFP4 and per-group E4M3 output (the most
+    // arithmetic per output): two jobs per lane from about 32 million
+    // outputs, when a row is a whole number of 512-job blocks; otherwise the
+    // last block of every row is mostly idle (N = 8,960 rows have 1,120
+    // jobs) and one job per lane measured about 10% faster for the per-group
+    // form at 8,960 and 14,336 wide, while two jobs measured 1-4% faster at
+    // 28,672 wide from 2,048 tokens.
     if (epi == SWIGLU_EPI_FP8 && tokens > kSwigluFp8TwoJobOutputs / inter)
         return swiglu_find(2, 8);
-    if (epi == SWIGLU_EPI_NVFP4 && tokens > kSwigluNvfp4TwoJobOutputs / inter && (inter / 8) % 512 == 0)
+    if ((epi == SWIGLU_EPI_NVFP4 || epi == SWIGLU_EPI_FP8_GROUP) && tokens > kSwigluNvfp4TwoJobOutputs / inter &&
+        (inter / 8) % 512 == 0)
         return swiglu_find(2, 8);
     return swiglu_find(1, 8);
 }

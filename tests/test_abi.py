@@ -305,13 +305,15 @@ def test_pick_variant_ranges():
     assert A.pick_variant(A.OP_SWIGLU, 16, 8960, -1) == -1
     name = lambda T, N, f: A.variant_name(A.OP_SWIGLU, A.pick_variant(A.OP_SWIGLU, T, N, f))
     # decode sizes: half jobs; E4M3 from ~4 M outputs: two jobs per lane;
-    # NVFP4 two jobs only from ~32 M outputs on rows of whole 512-job blocks
+    # NVFP4 and per-group E4M3: two jobs only from ~32 M outputs on rows of
+    # whole 512-job blocks
     assert name(16, 8960, 0) == name(16, 8960, 3) == "1 half job/lane"
     assert name(4096, 8960, 0) == name(4096, 8960, 2) == "1 job/lane"
     assert name(4096, 8960, 1) == "2 jobs/lane"
     assert name(4096, 8960, 3) == "1 job/lane"
     assert name(8192, 28672, 3) == "2 jobs/lane" and name(512, 28672, 3) == "1 job/lane"
-    assert name(4096, 8960, 4) == "1 job/lane"                       # per-group E4M3: one job per lane
+    assert name(4096, 8960, 4) == name(8192, 14336, 4) == "1 job/lane"
+    assert name(8192, 28672, 4) == "2 jobs/lane" and name(512, 28672, 4) == "1 job/lane"
     assert name(16, 8960, 4) == "1 half job/lane"
     # norms: the output format decides only for per-token E4M3 with the residual
     # on rows wider than 8,192 up to 1,024 tokens (two row reductions: fewer waves)
