@@ -13,8 +13,6 @@ import os
 import re
 import subprocess
 
-import pytest
-
 import activation_add_rmsnorm_amd as A
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

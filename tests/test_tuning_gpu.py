@@ -4,7 +4,6 @@ run, and results stay equal to the oracle's."""
 
 from __future__ import annotations
 
-import numpy as np
 import pytest
 import torch
 

@@ -10,7 +10,7 @@ are used: every tensor is a seeded draw from ``gen``.
 
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 
 from .gen import normal_bf16
 
