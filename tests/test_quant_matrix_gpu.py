@@ -731,3 +731,73 @@ def test_random_shapes_every_swiglu_form(T, N):
         q, sc = A.swiglu_quant_fp8_group(gt)
         P.check_swiglu_fp8_group(gu, bits(q), bits(sc))
     torch.cuda.synchronize()
+
+
+def _large_shapes(n, seed, max_width, max_outputs, whole_blocks):
+    """Seeded shapes from a few hundred tokens up, where the default picks
+    change with the token count and width (two jobs per lane, pipelined and
+    few-wave norms, more waves per row): tokens x width between about two
+    million and `max_outputs`; with probability 0.4 a width that is a
+    multiple of `whole_blocks`."""
+    rng = np.random.default_rng([2025, seed])
+    out = []
+    for _ in range(n):
+        if rng.random() < 0.4:
+            W = whole_blocks * int(rng.integers(1, max_width // whole_blocks + 1))
+        else:
+            W = 8 * int(rng.integers(64, max_width // 8 + 1))
+        lo = max(1, (2 << 20) // W)
+        hi = max(lo + 1, max_outputs // W)
+        out.append((int(rng.integers(lo, hi)), W))
+    return out
+
+
+@pytest.mark.parametrize("T,H", _large_shapes(8, 1, 16384, 24 << 20, 2048))
+def test_large_random_shapes_every_norm_form(T, H):
+    x, r, w = norm_case(T, H, seed=T * 7 + H, outliers=0.001)
+    xt, rt, wt = bf16(x), bf16(r), bf16(w)
+    g = scale_t(0.02)
+    announce("norm forms", (T, H), A.variant_name(A.OP_NORM, A.pick_variant(A.OP_NORM, T, H, 0)),
+             A.variant_name(A.OP_NORM, A.pick_variant(A.OP_NORM, T, H, 1)))
+    out, ro = A.fused_add_rmsnorm(xt, rt, wt, 1e-6)
+    P.check_norm(x, r, w, 1e-6, bits(out), bits(ro))
+    q, s, ro = A.fused_add_rmsnorm_quant_fp8(xt, rt, wt, 1e-6)
+    P.check_norm_fp8(x, r, w, 1e-6, bits(q), bits(s), bits(ro))
+    q, ro = A.fused_add_rmsnorm_quant_fp8_static(xt, rt, wt, g, 1e-6)
+    P.check_norm_fp8_static(x, r, w, 1e-6, 0.02, bits(q), bits(ro))
+    P.check_rmsnorm(x, w, 1e-6, bits(A.rmsnorm(xt, wt, 1e-6)))
+    q, s = A.rmsnorm_quant_fp8(xt, wt, 1e-6)
+    P.check_rmsnorm_fp8(x, w, 1e-6, bits(q), bits(s))
+    if H % 16 == 0:
+        q, s, ro = A.fused_add_rmsnorm_quant_nvfp4(xt, rt, wt, g, 1e-6)
+        P.check_norm_nvfp4(x, r, w, 1e-6, 0.02, bits(q), bits(s), bits(ro))
+    if H % 32 == 0:
+        q, s, ro = A.fused_add_rmsnorm_quant_mxfp4(xt, rt, wt, 1e-6)
+        P.check_norm_mxfp4(x, r, w, 1e-6, bits(q), bits(s), bits(ro))
+    if H % A.FP8_GROUP == 0:
+        q, s, ro = A.fused_add_rmsnorm_quant_fp8_group(xt, rt, wt, 1e-6)
+        P.check_norm_fp8_group(x, r, w, 1e-6, bits(q), bits(s), bits(ro))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,N", _large_shapes(8, 2, 28672, 48 << 20, 4096))
+def test_large_random_shapes_every_swiglu_form(T, N):
+    gu = gen.normal_bf16((T, 2 * N), T * 11 + N, 4, std=2.0)
+    gt = bf16(gu)
+    s = scale_t(0.05)
+    announce("swiglu forms", (T, N), *(A.variant_name(A.OP_SWIGLU, A.pick_variant(A.OP_SWIGLU, T, N, f))
+                                      for f in range(5)))
+    P.check_swiglu(gu, bits(A.swiglu(gt)))
+    P.check_swiglu_fp8(gu, 0.05, bits(A.swiglu_quant_fp8(gt, s)))
+    q, sc = A.swiglu_quant_fp8_dynamic(gt)
+    P.check_swiglu_fp8_dynamic(gu, bits(q), bits(sc))
+    if N % 16 == 0:
+        q, sc = A.swiglu_quant_nvfp4(gt, s)
+        P.check_swiglu_nvfp4(gu, 0.05, bits(q), bits(sc))
+    if N % 32 == 0:
+        q, sc = A.swiglu_quant_mxfp4(gt)
+        P.check_swiglu_mxfp4(gu, bits(q), bits(sc))
+    if N % A.FP8_GROUP == 0:
+        q, sc = A.swiglu_quant_fp8_group(gt)
+        P.check_swiglu_fp8_group(gu, bits(q), bits(sc))
+    torch.cuda.synchronize()
