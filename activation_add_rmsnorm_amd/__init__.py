@@ -42,7 +42,9 @@ def _variant(form: str, tokens: int, width: int, variant: int) -> int:
 
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libaarms.so")
+# AARMS_LIB names another build of the same library (the host-sanitizer test
+# loads one whose C entry points are built with AddressSanitizer and UBSan).
+_LIB_PATH = os.environ.get("AARMS_LIB") or os.path.join(_HERE, "libaarms.so")
 _LOCK = threading.Lock()
 _LIB = None
 

@@ -22,7 +22,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "aarms_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# AARMS_ORACLE_LIB names another build of aarms_oracle.c (the host-sanitizer
+# test loads one built with AddressSanitizer and UBSan).
+_LIB_PATH = os.environ.get("AARMS_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _LOCK = threading.Lock()
 _LIB = None
 

@@ -494,6 +494,8 @@ def test_missing_library_fails_loudly(tmp_path):
             "assert A.lib_path().startswith(%r)\n"
             "try:\n    A.load()\nexcept Exception as e:\n    print('raised', type(e).__name__)\n"
             "else:\n    print('loaded')\n") % (str(tmp_path), str(tmp_path))
-    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=str(tmp_path))
+    env = {k: v for k, v in os.environ.items() if k != "AARMS_LIB"}   # the copy's own path
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=str(tmp_path),
+                       env=env)
     assert "raised" in r.stdout, r.stdout + r.stderr
     assert not os.path.exists(pkg / "libaarms.so")
