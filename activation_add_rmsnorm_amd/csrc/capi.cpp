@@ -127,6 +127,32 @@ constexpr int64_t kDynamicFp8FewWavesTokens = 1024;
 // and no faster below 768 or from 2,048 tokens.
 constexpr int64_t kPipelinedMinTokens = 768, kPipelinedMaxTokens = 1536;
 
+// Store hold of the one-shot kernel (norm.hip, hold_stores): each row's
+// stores wait until about the time the launch's reads take after its wave
+// started, so that HBM serves the reads of a launch whose blocks are all
+// resident before its writes.  Measured on MI355X for the bf16 output with
+// one wave per row (with and without the residual add): 12-21% faster at
+// 4,096-8,192 rows of 896-2,048 (22-50 MB of reads), with the best hold
+// near reads / 7-8 TB/s and falling off on both sides (a hold too short
+// gains little, one too long adds its excess); reads / 7.4 TB/s is within
+// 1-4% of the best hold at every measured shape.  No gain below 4,096 rows,
+// below about 20 MB of reads (16.8 MB at [4096, 1024]) or with several
+// waves per row.  The launcher drops the hold when the grid does not fit
+// on the device at once.
+constexpr int64_t kHoldMinTokens = 4096;
+constexpr double kHoldMinReadBytes = 20e6;
+constexpr double kHoldReadBytesPerTick = 74000.0;   // 7.4 TB/s in 10 ns ticks
+
+uint32_t norm_hold_ticks(int64_t tokens, int64_t hidden, int epi, bool res, const NormVariant *v)
+{
+    if (epi != NORM_EPI_BF16 || v->waves_per_row != 1 || v->blocks_per_cu != 0 || tokens < kHoldMinTokens)
+        return 0;
+    const double reads = (double)tokens * (double)hidden * (res ? 4.0 : 2.0);
+    if (reads < kHoldMinReadBytes) return 0;
+    const double ticks = reads / kHoldReadBytesPerTick;
+    return ticks > (double)NORM_HOLD_MAX_TICKS ? 0u : (uint32_t)(ticks + 0.5);
+}
+
 // epi: the output format (NORM_EPI_*); residual: with the add in front.
 int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
 {
@@ -315,6 +341,7 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     p.tokens = tokens;
     p.hidden = (int32_t)hidden;
     p.eps = eps;
+    p.hold_ticks = norm_hold_ticks(tokens, hidden, epi, res, v);
     return launch_status(launch_norm(p, epi, res, variant, device_cus(), stream));
 }
 

@@ -33,7 +33,13 @@ struct NormParams {
     int64_t tokens;
     int32_t hidden;
     float eps;
+    // Store hold of the one-shot kernel, in ticks of the 100 MHz real-time
+    // clock: a row's stores wait until this long after its wave started (0:
+    // none).  At most NORM_HOLD_MAX_TICKS.
+    uint32_t hold_ticks;
 };
+
+constexpr uint32_t NORM_HOLD_MAX_TICKS = 2000;   // 20 us
 
 // SwiGLU epilogues (the per-token FP8 form has its own row kernel).
 enum SwigluEpilogue : int {

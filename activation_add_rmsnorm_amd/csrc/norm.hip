@@ -21,6 +21,8 @@
 #include "device.h"
 #include "launch.h"
 
+#include <atomic>
+
 namespace aarms {
 
 // q = e4m3(clamp(y / s)) for this lane's slices of the row (y as binary32
@@ -102,16 +104,40 @@ __device__ __forceinline__ void load_weight(const NormParams &p, int lane, int n
     }
 }
 
+// Store hold.  In a launch whose blocks are all resident at once, every
+// wave issues its loads at the start and would store its row as soon as the
+// row is done, so the writes of the first rows finished compete in HBM with
+// the reads still outstanding for the rest.  Holding each row's stores until
+// a fixed time after its wave started (about the time the launch's reads
+// take) serves the reads first and the writes after them, with fewer
+// read/write turnarounds (measured 16-19% faster on one-wave-per-row bf16
+// launches of 25-38 MB of reads).  The wait is bounded: it ends once the
+// real-time clock (100 MHz, s_memrealtime) has advanced hold_ticks past
+// t_start, or if the clock reads below t_start.  dep ties the wait to a
+// value computed from the row, so it starts after the row's loads landed.
+__device__ __forceinline__ void hold_stores(uint64_t t_start, uint32_t hold_ticks, double dep)
+{
+    if (hold_ticks == 0) return;
+    asm volatile("" : : "v"(dep));
+    while (true) {
+        const uint64_t now = __builtin_amdgcn_s_memrealtime();
+        if (now < t_start || now - t_start >= hold_ticks) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 // Everything after the row's loads: residual add and store (RES), sum of
 // squares, the row reduction (through psum when the row spans several
 // waves), the normalization and the epilogue.  With W_LATE the weight is
 // loaded here, after the first pass, so that its registers are not live
 // while the row loads are in flight.
+// t_start: the wave's start on the real-time clock, for the store hold (the
+// stores issued after the sum of squares: all of them in the bf16 form).
 template <int WPR, int VPT, int EPI, bool RES, bool W_LATE>
 __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int lane, int nvec,
                                            const u32x4 (&xv)[VPT], u32x4 (&rv)[VPT],
                                            u32x4 (&wv)[VPT], double *psum, float *pmax,
-                                           const float *nv_inv)
+                                           const float *nv_inv, uint64_t t_start = 0)
 {
     constexpr bool QUANT = EPI == NORM_EPI_FP8_DYNAMIC;
     const size_t base = (size_t)row * (size_t)p.hidden;
@@ -158,6 +184,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         }
     }
     double acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    hold_stores(t_start, p.hold_ticks, acc);
     if constexpr (W_LATE) {
         // keep the scheduler from hoisting these loads back to the top
         __builtin_amdgcn_sched_barrier(0);
@@ -368,6 +395,7 @@ norm_kernel(NormParams p)
     // one row per block, so the whole block leaves together.
     if (row >= p.tokens) return;
     const int nvec = p.hidden >> 3;
+    const uint64_t t_start = p.hold_ticks ? __builtin_amdgcn_s_memrealtime() : 0;
 
     // all loads of the row slice in flight before any use
     u32x4 xv[VPT], rv[VPT], wv[VPT];
@@ -377,7 +405,7 @@ norm_kernel(NormParams p)
     // there are registers to spare and the weight is loaded with the row
     constexpr bool W_LATE = WPR > 1 && RES;
     if constexpr (!W_LATE) load_weight<WPR, VPT>(p, lane, nvec, wv);
-    finish_row<WPR, VPT, EPI, RES, W_LATE>(p, row, lane, nvec, xv, rv, wv, psum, pmax, nv_inv);
+    finish_row<WPR, VPT, EPI, RES, W_LATE>(p, row, lane, nvec, xv, rv, wv, psum, pmax, nv_inv, t_start);
 }
 
 // Persistent and software-pipelined: a fixed grid of blocks walks the rows
@@ -456,6 +484,7 @@ static const NormVariant kNormVariants[] = {
     {16, 8, 1, "16 waves/row x8 vec, pipelined 1 block/CU"},
 };
 constexpr int kNumNormVariants = sizeof(kNormVariants) / sizeof(kNormVariants[0]);
+static_assert(kNumNormVariants <= 64, "the occupancy cache holds 64 variants per form");
 
 int norm_variant_count() { return kNumNormVariants; }
 const NormVariant *norm_variant(int id)
@@ -463,8 +492,24 @@ const NormVariant *norm_variant(int id)
     return (id >= 0 && id < kNumNormVariants) ? &kNormVariants[id] : nullptr;
 }
 
+// Blocks of a kernel resident per CU at once (the HIP occupancy calculator),
+// cached per (epilogue, residual, variant); 0 if the query fails.
+constexpr int kOccupancySlots = 6 * 2 * 64;
+
+static int resident_blocks_per_cu(const void *fn, int threads, int slot)
+{
+    static std::atomic<int> cache[kOccupancySlots];
+    if (slot < 0 || slot >= kOccupancySlots) return 0;
+    int n = cache[slot].load(std::memory_order_relaxed);
+    if (n != 0) return n > 0 ? n : 0;
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, threads, 0) != hipSuccess || b <= 0) b = -1;
+    cache[slot].store(b, std::memory_order_relaxed);
+    return b > 0 ? b : 0;
+}
+
 template <int WPR, int VPT, int EPI, bool RES, bool PIPE>
-static hipError_t launch_one(const NormParams &p, int blocks_per_cu, int num_cus,
+static hipError_t launch_one(const NormParams &p, int blocks_per_cu, int num_cus, int slot,
                              hipStream_t stream)
 {
     constexpr int threads = (WPR == 1) ? 256 : WPR * 64;
@@ -478,6 +523,13 @@ static hipError_t launch_one(const NormParams &p, int blocks_per_cu, int num_cus
     void *args[] = {&copy};
     const void *fn = PIPE ? (const void *)&norm_kernel_pipelined<WPR, VPT, EPI, RES>
                           : (const void *)&norm_kernel<WPR, VPT, EPI, RES>;
+    // the store hold only orders the reads and writes of one generation of
+    // blocks: a grid that does not fit on the device at once runs without it
+    if (copy.hold_ticks != 0) {
+        const int rb = PIPE ? 0 : resident_blocks_per_cu(fn, threads, slot);
+        if (rb <= 0 || blocks > (int64_t)rb * num_cus) copy.hold_ticks = 0;
+        if (copy.hold_ticks > NORM_HOLD_MAX_TICKS) copy.hold_ticks = NORM_HOLD_MAX_TICKS;
+    }
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
 }
 
@@ -487,10 +539,11 @@ static hipError_t dispatch(const NormParams &p, int variant, int num_cus, hipStr
     const NormVariant *v = norm_variant(variant);
     if (!v) return hipErrorInvalidValue;
     const int b = v->blocks_per_cu;
+    const int slot = (EPI * 2 + (RES ? 1 : 0)) * 64 + variant;
 #define AARMS_NORM_CASE(W, V)                                                              \
     if (v->waves_per_row == W && v->vecs_per_lane == V)                                    \
-        return b ? launch_one<W, V, EPI, RES, true>(p, b, num_cus, s)                       \
-                 : launch_one<W, V, EPI, RES, false>(p, 0, num_cus, s);
+        return b ? launch_one<W, V, EPI, RES, true>(p, b, num_cus, slot, s)                 \
+                 : launch_one<W, V, EPI, RES, false>(p, 0, num_cus, slot, s);
     AARMS_NORM_CASE(1, 1)
     AARMS_NORM_CASE(1, 2)
     AARMS_NORM_CASE(1, 3)
