@@ -1,5 +1,5 @@
-"""Build libaarms.so (the library) and libaarms_ceiling.so (a plain streaming
-kernel that bench.py times beside the library kernels) in-tree with hipcc for
+"""Build libaarms.so (the library) and libaarms_refcopy.so (plain streaming
+copies that bench.py times beside the library kernels) in-tree with hipcc for
 gfx950.
 
 Flags:
@@ -25,12 +25,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libaarms.so")
-CEILING_PATH = os.path.join(PKG, "libaarms_ceiling.so")
+REFCOPY_PATH = os.path.join(PKG, "libaarms_refcopy.so")
 ARCH = os.environ.get("AARMS_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["norm.hip", "swiglu.hip"]
 HOST_SOURCES = ["capi.cpp"]
-CEILING_SOURCES = ["ceiling.hip"]
+REFCOPY_SOURCES = ["refcopy.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra", "-Wno-unused-parameter",
           "-ffp-contract=off", "-I", INCLUDE, "-I", CSRC]
@@ -74,7 +74,7 @@ def _link(hipcc, objs, path):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source, link libaarms.so and libaarms_ceiling.so;
+    """Compile every source, link libaarms.so and libaarms_refcopy.so;
     returns the path of libaarms.so."""
     hipcc = _hipcc()
     objdir = os.path.join(ROOT, "_build")
@@ -84,11 +84,11 @@ def build(verbose: bool = False) -> str:
         return os.path.join(objdir, src + ".o")
 
     jobs = [[hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, s), "-o", obj(s)]
-            for s in HIP_SOURCES + CEILING_SOURCES]
+            for s in HIP_SOURCES + REFCOPY_SOURCES]
     jobs += [[hipcc, *COMMON, "-c", os.path.join(CSRC, s), "-o", obj(s)] for s in HOST_SOURCES]
     _run(jobs, verbose)
     _link(hipcc, [obj(s) for s in HIP_SOURCES + HOST_SOURCES], LIB_PATH)
-    _link(hipcc, [obj(s) for s in CEILING_SOURCES], CEILING_PATH)
+    _link(hipcc, [obj(s) for s in REFCOPY_SOURCES], REFCOPY_PATH)
     return LIB_PATH
 
 

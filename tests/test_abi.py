@@ -350,15 +350,15 @@ def test_pick_variant_ranges():
     assert rq(28672) == "16 waves/row x4 jobs"
 
 
-def test_ceiling_library_rejects_bad_arguments():
-    # the streaming reference kernel bench.py times beside each op: only its
+def test_reference_copy_library_rejects_bad_arguments():
+    # the plain streaming copies bench.py times beside each op: only their
     # argument checks run here (they return before any HIP call)
     from activation_add_rmsnorm_amd import _build
-    if not os.path.exists(_build.CEILING_PATH):
+    if not os.path.exists(_build.REFCOPY_PATH):
         _build.build()
-    lib = C.CDLL(_build.CEILING_PATH)
+    lib = C.CDLL(_build.REFCOPY_PATH)
     vp, i32, i64 = C.c_void_p, C.c_int, C.c_int64
-    f = lib.aarms_stream_ceiling
+    f = lib.aarms_reference_copy
     f.argtypes = [vp, i32, vp, i32, vp, vp, i64, vp]
     P = 1 << 40
     assert f(P, 16, P + (1 << 30), 16, P + (2 << 30), P + (3 << 30), 0, None) == 0   # empty: no launch
@@ -367,6 +367,14 @@ def test_ceiling_library_rejects_bad_arguments():
     assert f(P, 16, None, 8, P, P, 8, None) == -1                                     # out1 missing
     assert f(P, 16, None, 0, P + 8, P, 8, None) == -1                                 # misaligned
     assert f(P, 16, None, 0, P, P, (2**31) * 256, None) == -1                         # grid too large
+    d = lib.aarms_copy_design
+    d.argtypes = [i32, i32, i32, i64, vp, vp, vp, vp, i64, vp]
+    assert d(0, 1, 1, 0, P, None, P + (1 << 30), P + (2 << 30), 0, None) == 0        # empty: no launch
+    assert d(3, 1, 1, 0, P, P, P, P, 8, None) == -1                                   # bad kind
+    assert d(0, 3, 1, 0, P, None, P, P, 8, None) == -1                                # bad vectors per lane
+    assert d(1, 1, 1, 0, P, None, P, P, 8, None) == -1                                # out1 missing
+    assert d(2, 1, 1, 0, P, P + 4, P, P, 8, None) == -1                               # out1 misaligned
+    assert d(0, 1, 1, -1, P, None, P, P, 8, None) == -1                               # negative grid
 
 
 def test_binding_types_every_declared_function():
