@@ -26,6 +26,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libaarms.so")
 REFCOPY_PATH = os.path.join(PKG, "libaarms_refcopy.so")
+# Measurement build: the library with phase stamps in the norm kernels
+# (-DAARMS_PHASE_STAMPS, bench.py --phase-timeline); never loaded by the
+# package itself.
+STAMPS_PATH = os.path.join(PKG, "libaarms_stamps.so")
 ARCH = os.environ.get("AARMS_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["norm.hip", "swiglu.hip"]
@@ -74,8 +78,8 @@ def _link(hipcc, objs, path):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source, link libaarms.so and libaarms_refcopy.so;
-    returns the path of libaarms.so."""
+    """Compile every source, link libaarms.so, libaarms_refcopy.so and
+    libaarms_stamps.so; returns the path of libaarms.so."""
     hipcc = _hipcc()
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -83,12 +87,19 @@ def build(verbose: bool = False) -> str:
     def obj(src):
         return os.path.join(objdir, src + ".o")
 
+    def sobj(src):
+        return os.path.join(objdir, src + ".stamps.o")
+
+    stamps = ["-DAARMS_PHASE_STAMPS"]
     jobs = [[hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, s), "-o", obj(s)]
             for s in HIP_SOURCES + REFCOPY_SOURCES]
     jobs += [[hipcc, *COMMON, "-c", os.path.join(CSRC, s), "-o", obj(s)] for s in HOST_SOURCES]
+    jobs += [[hipcc, *COMMON, *DEVICE, *stamps, "-c", os.path.join(CSRC, "norm.hip"), "-o", sobj("norm.hip")],
+             [hipcc, *COMMON, *stamps, "-c", os.path.join(CSRC, "capi.cpp"), "-o", sobj("capi.cpp")]]
     _run(jobs, verbose)
     _link(hipcc, [obj(s) for s in HIP_SOURCES + HOST_SOURCES], LIB_PATH)
     _link(hipcc, [obj(s) for s in REFCOPY_SOURCES], REFCOPY_PATH)
+    _link(hipcc, [sobj("norm.hip"), obj("swiglu.hip"), sobj("capi.cpp")], STAMPS_PATH)
     return LIB_PATH
 
 

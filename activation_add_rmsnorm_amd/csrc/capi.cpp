@@ -12,6 +12,16 @@
 
 using namespace aarms;
 
+#ifdef AARMS_PHASE_STAMPS
+// Measurement build only (libaarms_stamps.so): where the one-shot norm kernel
+// writes its phase stamps (16 uint64 per wave of each row; null: none).
+static uint64_t *g_phase_stamps = nullptr;
+extern "C" __attribute__((visibility("default"))) void aarms_set_phase_stamps(void *stamps)
+{
+    g_phase_stamps = (uint64_t *)stamps;
+}
+#endif
+
 namespace {
 
 struct Range {
@@ -131,16 +141,18 @@ constexpr int64_t kPipelinedMinTokens = 768, kPipelinedMaxTokens = 1536;
 // stores wait until about the time the launch's reads take after its wave
 // started, so that HBM serves the reads of a launch whose blocks are all
 // resident before its writes.  Measured on MI355X for the bf16 output with
-// one wave per row (with and without the residual add): 12-21% faster at
-// 4,096-8,192 rows of 896-2,048 (22-50 MB of reads), with the best hold
+// one wave per row: with the residual add 12-21% faster at 4,096-8,192
+// rows of 896-2,048 (22-50 MB of reads), with the best hold
 // near reads / 7-8 TB/s and falling off on both sides (a hold too short
 // gains little, one too long adds its excess); reads / 7.4 TB/s is within
-// 1-4% of the best hold at every measured shape.  No gain below 4,096 rows,
-// below about 20 MB of reads (16.8 MB at [4096, 1024]) or with several
-// waves per row.  The launcher drops the hold when the grid does not fit
-// on the device at once.
+// 1-4% of the best hold at every measured shape.  Without the residual add
+// (rmsnorm) the gain starts at about 12 MB of reads (4-18% at 12.6-18.9 MB,
+// 4,096-8,192 rows of 896-2,048).  No gain below 4,096 rows, below those
+// read sizes (16.8 MB with the add at [4096, 1024]; 7-8 MB without) or
+// with several waves per row.  The launcher drops the hold when the grid
+// does not fit on the device at once.
 constexpr int64_t kHoldMinTokens = 4096;
-constexpr double kHoldMinReadBytes = 20e6;
+constexpr double kHoldMinReadBytesAdd = 20e6, kHoldMinReadBytesNoAdd = 12e6;
 constexpr double kHoldReadBytesPerTick = 74000.0;   // 7.4 TB/s in 10 ns ticks
 
 uint32_t norm_hold_ticks(int64_t tokens, int64_t hidden, int epi, bool res, const NormVariant *v)
@@ -148,7 +160,7 @@ uint32_t norm_hold_ticks(int64_t tokens, int64_t hidden, int epi, bool res, cons
     if (epi != NORM_EPI_BF16 || v->waves_per_row != 1 || v->blocks_per_cu != 0 || tokens < kHoldMinTokens)
         return 0;
     const double reads = (double)tokens * (double)hidden * (res ? 4.0 : 2.0);
-    if (reads < kHoldMinReadBytes) return 0;
+    if (reads < (res ? kHoldMinReadBytesAdd : kHoldMinReadBytesNoAdd)) return 0;
     const double ticks = reads / kHoldReadBytesPerTick;
     return ticks > (double)NORM_HOLD_MAX_TICKS ? 0u : (uint32_t)(ticks + 0.5);
 }
@@ -342,6 +354,9 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     p.hidden = (int32_t)hidden;
     p.eps = eps;
     p.hold_ticks = norm_hold_ticks(tokens, hidden, epi, res, v);
+#ifdef AARMS_PHASE_STAMPS
+    p.stamps = g_phase_stamps;
+#endif
     return launch_status(launch_norm(p, epi, res, variant, device_cus(), stream));
 }
 

@@ -37,6 +37,11 @@ struct NormParams {
     // clock: a row's stores wait until this long after its wave started (0:
     // none).  At most NORM_HOLD_MAX_TICKS.
     uint32_t hold_ticks;
+#ifdef AARMS_PHASE_STAMPS
+    // Measurement build only (libaarms_stamps.so): per wave of each row,
+    // 16 slots of real-time-clock stamps at the phases of norm_kernel.
+    uint64_t *stamps;
+#endif
 };
 
 constexpr uint32_t NORM_HOLD_MAX_TICKS = 2000;   // 20 us

@@ -104,6 +104,30 @@ __device__ __forceinline__ void load_weight(const NormParams &p, int lane, int n
     }
 }
 
+// Phase stamps (measurement build only, -DAARMS_PHASE_STAMPS): lane 0 of
+// each wave records the real-time clock (100 MHz) when the wave reaches slot
+// k, after dep has been computed, into stamps[(row * WPR + wave) * 16 + k]:
+// 0 start, 1 row loads consumed, 2 wave sum, 3 first barrier passed, 4 row
+// amax (per-token E4M3) or outputs computed, 5 wave maximum, 6 second
+// barrier passed, 7 last store issued; 8 and 9 hold the HW_ID and XCC_ID
+// registers (which CU ran the wave).
+#ifdef AARMS_PHASE_STAMPS
+__device__ __forceinline__ uint64_t stamp_after(float dep)
+{
+    asm volatile("" : : "v"(dep));
+    return __builtin_amdgcn_s_memrealtime();
+}
+#define AARMS_STAMP(k, dep)                                                                        \
+    do {                                                                                           \
+        if (p.stamps) {                                                                            \
+            const uint64_t t_ = stamp_after(dep);                                                  \
+            if ((lane & 63) == 0) p.stamps[((size_t)row * WPR + (size_t)(lane >> 6)) * 16 + (k)] = t_; \
+        }                                                                                          \
+    } while (0)
+#else
+#define AARMS_STAMP(k, dep) do {} while (0)
+#endif
+
 // Store hold.  In a launch whose blocks are all resident at once, every
 // wave issues its loads at the start and would store its row as soon as the
 // row is done, so the writes of the first rows finished compete in HBM with
@@ -184,6 +208,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         }
     }
     double acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    AARMS_STAMP(1, (float)acc);
     hold_stores(t_start, p.hold_ticks, acc);
     if constexpr (W_LATE) {
         // keep the scheduler from hoisting these loads back to the top
@@ -191,9 +216,11 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         load_weight<WPR, VPT>(p, lane, nvec, wv);
     }
     acc = wave_sum(acc);
+    AARMS_STAMP(2, (float)acc);
     if constexpr (WPR > 1) {
         if ((lane & 63) == 0) psum[lane >> 6] = acc;
         __syncthreads();
+        AARMS_STAMP(3, (float)acc);
         acc = block_sum<WPR>(psum, lane & 63);
     }
 
@@ -328,10 +355,13 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
                 amax = fmaxf(amax, fmaxf(__builtin_fabsf(hf[k][2 * e]), __builtin_fabsf(hf[k][2 * e + 1])));
             }
         }
+        AARMS_STAMP(4, amax);
         amax = wave_max(amax);
+        AARMS_STAMP(5, amax);
         if constexpr (WPR > 1) {
             if ((lane & 63) == 0) pmax[lane >> 6] = amax;
             __syncthreads();
+            AARMS_STAMP(6, amax);
             amax = block_max<WPR>(pmax, lane & 63);
         }
         // ---- per-token scale, then q = e4m3(clamp(y / s))
@@ -353,6 +383,14 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
             if (v < nvec) st_stream(ro + v, rv[k]);
         }
     }
+    AARMS_STAMP(7, 0.0f);
+#ifdef AARMS_PHASE_STAMPS
+    if (p.stamps && (lane & 63) == 0) {
+        uint64_t *s = p.stamps + ((size_t)row * WPR + (size_t)(lane >> 6)) * 16;
+        s[8] = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID
+        s[9] = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID
+    }
+#endif
 }
 
 // NVFP4: 1/S for each of the 127 finite block scales and 1/(6 g) in the
@@ -396,6 +434,7 @@ norm_kernel(NormParams p)
     if (row >= p.tokens) return;
     const int nvec = p.hidden >> 3;
     const uint64_t t_start = p.hold_ticks ? __builtin_amdgcn_s_memrealtime() : 0;
+    AARMS_STAMP(0, 0.0f);
 
     // all loads of the row slice in flight before any use
     u32x4 xv[VPT], rv[VPT], wv[VPT];

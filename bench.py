@@ -74,6 +74,9 @@ def parse():
                     help="instead of the workloads, time plain copy designs (vectors per lane, one-shot or "
                          "grid-stride grid, streaming hints) at the read/write mixes and sizes of the "
                          "headline kernels and the Llama-405B norm; prints them as the JSON line")
+    ap.add_argument("--phase-timeline", action="store_true",
+                    help="instead of the workloads, record the per-wave phase timeline of the Llama-405B "
+                         "per-token E4M3 norm (libaarms_stamps.so) and print its summary as the JSON line")
     return ap.parse_args()
 
 
@@ -91,6 +94,11 @@ def swiglu_bytes(T, N, quant=False):
 
 
 # ----------------------------------------------------------------- timing
+
+def progress(*what):
+    """A progress line on stderr (the JSON line goes to stdout)."""
+    print("[bench]", *what, file=sys.stderr, flush=True)
+
 
 class Timer:
     def __init__(self, torch):
@@ -198,6 +206,9 @@ def main():
     if args.copy_sweep:
         print(json.dumps(copy_sweep(args, torch, clib, dev, sp, timer)), flush=True)
         return
+    if args.phase_timeline:
+        print(json.dumps(phase_timeline(args, torch, np, W, dev, sp, timer)), flush=True)
+        return
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -279,6 +290,7 @@ def main():
         stream(s["y"].data_ptr(), 16, None, 0, gu, gu + T * N * 2, T * N // 8)
 
     K, Wu = args.steps, args.warmup
+    progress("headline step")
     for i in range(Wu):
         step(i)
     ms_step = timer.region(step, K)
@@ -321,6 +333,12 @@ def main():
                               **refcopy_entry(swiglu_us, swiglu_copy_us, step_bytes_swiglu)},
         "buffer_sets_rotated": {"norm": n_norm, "swiglu": n_sw},
     }
+    for k, tkey, nb in (("norm_4096x1536", "norm_qwen_prefill4096", step_bytes_norm),
+                        ("swiglu_4096x17920", "swiglu_qwen_prefill4096", step_bytes_swiglu)):
+        t = traffic_from_profiles(tkey, src_hash)
+        if t is not None:
+            extra[k]["traffic_bytes_per_launch"] = t
+            extra[k]["traffic_over_algorithmic"] = round(t / nb, 4)
     name = lambda op, v, T_, W_, q: A.variant_name(op, v if v >= 0 else A.pick_variant(op, T_, W_, q))
     headline_variants = {
         "norm": name(A.OP_NORM, variant["norm"], T, H, False),
@@ -441,6 +459,114 @@ def copy_sweep(args, torch, clib, dev, sp, timer):
     return out
 
 
+def phase_timeline(args, torch, np, W, dev, sp, timer):
+    """Per-wave phase stamps of the Llama-405B per-token E4M3 norm
+    ([2048, 16384], the library's default variant) from the measurement build
+    libaarms_stamps.so (real-time clock, 100 MHz): one launch in the middle of
+    a back-to-back run over rotated buffer sets.  Reports the launch time with
+    and without the stamps, the per-block phase times, the same by start-time
+    octile, and the blocks in flight and waves still waiting for their row's
+    loads at 40 points across the launch."""
+    import ctypes as C
+    from activation_add_rmsnorm_amd import _build
+    if not os.path.exists(_build.STAMPS_PATH):
+        _build.build()
+    L = C.CDLL(_build.STAMPS_PATH)
+    vp, i64, f32, i32 = C.c_void_p, C.c_int64, C.c_float, C.c_int
+    L.fused_add_rmsnorm_quant_fp8_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp]
+    L.aarms_set_phase_stamps.argtypes = [vp]
+    L.aarms_set_phase_stamps.restype = None
+    L.aarms_pick_variant.argtypes = [i32, i64, i64, i32]
+    L.aarms_variant_name.argtypes = [i32, i32]
+    L.aarms_variant_name.restype = C.c_char_p
+    wl = W.NORM_FP8_LLAMA405B
+    T, H = wl.tokens, wl.hidden
+    v = L.aarms_pick_variant(0, T, H, 1)
+    vname = L.aarms_variant_name(0, v).decode()
+    wpr = 1 if vname.startswith("wave/row") else int(vname.split()[0])
+    d = W.norm_inputs(wl)
+    to = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    x0, r0, w0 = to(d["x"]), to(d["residual"]), to(d["weight"])
+    ns = rotation_sets(norm_bytes(T, H, quant=True))
+    sets = [dict(x=x0.clone(), r=r0.clone(), q=torch.empty((T, H), dtype=torch.uint8, device=dev),
+                 s=torch.empty((T,), dtype=torch.float32, device=dev), ro=torch.empty_like(r0)) for _ in range(ns)]
+
+    def call(i):
+        z = sets[i % ns]
+        st = L.fused_add_rmsnorm_quant_fp8_ex(z["q"].data_ptr(), z["s"].data_ptr(), z["ro"].data_ptr(),
+                                               z["x"].data_ptr(), z["r"].data_ptr(), w0.data_ptr(), T, H, wl.eps, v, sp)
+        if st:
+            raise RuntimeError("fused_add_rmsnorm_quant_fp8_ex: %d" % st)
+
+    reps = max(20, args.steps // 2)
+    stamps = torch.zeros(T * wpr * 16, dtype=torch.int64, device=dev)
+    L.aarms_set_phase_stamps(None)
+    timer.warm(call)
+    us_plain = timer.region(call, reps) * 1e3
+    L.aarms_set_phase_stamps(stamps.data_ptr())
+    timer.warm(call)
+    us_stamped = timer.region(call, reps) * 1e3
+    # the stamps of the last launch of a back-to-back run
+    stamps.zero_()
+    torch.cuda.synchronize()
+    for i in range(2 * ns):
+        call(i)
+    torch.cuda.synchronize()
+    L.aarms_set_phase_stamps(None)
+    a = stamps.cpu().numpy().reshape(T, wpr, 16).astype(np.float64)
+    t = (a[:, :, :8] - a[:, :, 0].min()) * 0.01          # us from the first wave's start
+    bstart = t[:, :, 0].min(1)
+    span = float(t[:, :, 7].max())
+    pct = lambda v: {"p10": round(float(np.percentile(v, 10)), 2), "median": round(float(np.median(v)), 2),
+                     "p90": round(float(np.percentile(v, 90)), 2), "max": round(float(v.max()), 2)}
+    phases = {
+        "last wave's row loads consumed": pct(t[:, :, 1].max(1) - bstart),
+        "first wave's row loads consumed": pct(t[:, :, 1].min(1) - bstart),
+        "first barrier passed": pct(t[:, :, 3].min(1) - bstart),
+        "row amax computed (last wave)": pct(t[:, :, 4].max(1) - bstart),
+        "second barrier passed": pct(t[:, :, 6].min(1) - bstart),
+        "last store issued (last wave)": pct(t[:, :, 7].max(1) - bstart),
+    }
+    per_wave = {
+        "loads consumed -> wave sum": pct((t[:, :, 2] - t[:, :, 1]).ravel()),
+        "first barrier -> row amax computed": pct((t[:, :, 4] - t[:, :, 3]).ravel()),
+        "row amax -> wave maximum": pct((t[:, :, 5] - t[:, :, 4]).ravel()),
+        "second barrier -> last store issued": pct((t[:, :, 7] - t[:, :, 6]).ravel()),
+    }
+    order = np.argsort(bstart)
+    octiles = []
+    for g in range(8):
+        sl = order[g * T // 8:(g + 1) * T // 8]
+        octiles.append({"start_us": round(float(np.median(bstart[sl])), 2),
+                        "loads_us": round(float(np.median(t[sl, :, 1].max(1) - bstart[sl])), 2),
+                        "barrier1_us": round(float(np.median(t[sl, :, 3].min(1) - bstart[sl])), 2),
+                        "barrier2_us": round(float(np.median(t[sl, :, 6].min(1) - bstart[sl])), 2),
+                        "end_us": round(float(np.median(t[sl, :, 7].max(1) - bstart[sl])), 2)})
+    grid = np.linspace(0.0, span, 41)
+    bend = t[:, :, 7].max(1)
+    in_flight = [int(((bstart <= g) & (bend > g)).sum()) for g in grid]
+    awaiting = [int(((t[:, :, 0] <= g) & (t[:, :, 1] > g)).sum()) for g in grid]
+    hw, xcc = a[:, 0, 8].astype(np.int64), a[:, 0, 9].astype(np.int64) & 0xF
+    cu = ((xcc * 8 + ((hw >> 13) & 7)) * 2 + ((hw >> 12) & 1)) * 16 + ((hw >> 8) & 0xF)
+    _, per_cu = np.unique(cu, return_counts=True)
+    return {"metric": "per-wave phase timeline, fused_add_rmsnorm_quant_fp8 [2048,16384] (Llama-405B)",
+            "variant": vname, "waves_per_row": wpr, "launch_us": round(us_plain, 2),
+            "launch_us_with_stamps": round(us_stamped, 2), "span_us": round(span, 2),
+            "per_block_from_block_start_us": phases, "per_wave_us": per_wave, "octiles_by_start": octiles,
+            "grid_us": [round(float(g), 2) for g in grid], "blocks_in_flight": in_flight,
+            "waves_awaiting_row_loads": awaiting, "distinct_cus": int(len(per_cu)),
+            "blocks_per_cu": {"min": int(per_cu.min()), "max": int(per_cu.max())},
+            "buffer_sets_rotated": ns}
+
+
+# Supplementary entries and the keys of their traffic lines in profiles/.
+TRAFFIC_KEYS = {
+    "llama70b_swiglu_fp8_8192x57344": "swiglu_fp8_llama70b",
+    "llama405b_norm_fp8_2048x16384": "norm_fp8_llama405b",
+    "llama70b_swiglu_nvfp4_8192x57344": "swiglu_nvfp4_llama70b",
+}
+
+
 def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
     out = {}
     reps = max(20, args.steps // 2)
@@ -452,12 +578,16 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
             raise RuntimeError("aarms_reference_copy: %d" % st)
 
     if want("llama70b_swiglu_fp8_8192x57344"):
+        progress("llama70b_swiglu_fp8_8192x57344")
         out.update(config4(torch, A, lib, W, dev, sp, timer, reps, stream))
     if want("llama405b_norm_fp8_2048x16384"):
+        progress("llama405b_norm_fp8_2048x16384")
         out.update(config5(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream))
     if want("qwen1.5b_norm_16x1536"):
+        progress("qwen1.5b_norm_16x1536")
         out.update(config1(torch, A, lib, W, sp, timer, to_dev, reps))
     if want("qwen1.5b_decode_28layers_graph"):
+        progress("qwen1.5b_decode_28layers_graph")
         out["qwen1.5b_decode_28layers_graph"] = decode_graph(torch, np, A, W, dev, to_dev, timer)
 
     # the rest of the quantisation matrix, at the same shapes
@@ -466,10 +596,20 @@ def supplementary(args, torch, np, A, lib, clib, W, dev, sp, timer, to_dev):
     # one GPU's share of the Llama layers sharded over 8 GPUs
     out.update(shares(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream, want))
 
+    # calibrated HBM traffic per launch, from the committed counter summaries
+    # taken on the current kernel sources (else absent)
+    src_hash = kernel_sources_hash()
+    for key, tkey in TRAFFIC_KEYS.items():
+        t = traffic_from_profiles(tkey, src_hash)
+        if key in out and t is not None:
+            out[key]["traffic_bytes_per_launch"] = t
+            out[key]["traffic_over_algorithmic"] = round(t / out[key]["bytes"], 4)
+
     # start-up autotuning at the workload shapes: the heuristic's variant
     # against the fastest one (graph-replay timings); informational, the
     # figures above use the heuristic
     if not args.no_autotune_report and want("autotune"):
+        progress("autotune report")
         out["autotune"] = autotune_report()
     return out
 
@@ -599,6 +739,7 @@ def quant_matrix(torch, A, lib, W, dev, sp, timer, to_dev, reps, stream, want=la
     def measure(key, call, refcopy, nbytes, extra=None):
         if not want(key):
             return
+        progress(key)
         timer.warm(call)
         ms = timer.region(call, reps)
         timer.warm(refcopy)
