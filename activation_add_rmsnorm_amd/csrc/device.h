@@ -267,10 +267,15 @@ __device__ __forceinline__ uint32_t pack_nvfp4(const uint32_t (&w)[NW], uint32_t
 // row), then the two 16-lane rows of each 32-lane half and the two halves
 // (v_permlane16_swap / v_permlane32_swap, which hand every lane both
 // operands in the same order).  So every lane ends with the same bits.
+// Every lane's source lane exists under these permutations, so the move
+// needs no fill value and bound_ctrl (zero for a missing source) never
+// applies; without a fill value the compiler folds the move into the
+// integer maxima below (v_max_u32 with DPP) and drops a register
+// initialisation per step of the sums.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
 template <int CTRL>
@@ -324,37 +329,47 @@ __device__ __forceinline__ double wave_sum(double v)
     return swap_sum_f64<32>(v);
 }
 
+// Maxima of non-negative, non-NaN binary32 values (magnitudes folded with
+// fmaxf from 0, which drops NaN).  For those, the order of the bit patterns
+// as unsigned integers is the order of the values, so the butterflies take
+// integer maxima: the same result as fmaxf, without the NaN quieting that a
+// floating-point maximum of a permuted lane needs first.
+__device__ __forceinline__ uint32_t max_dpp_step(uint32_t v, uint32_t w) { return v > w ? v : w; }
+
 template <int SPAN>
-__device__ __forceinline__ float swap_max_f32(float v)
+__device__ __forceinline__ uint32_t swap_max_u32(uint32_t v)
 {
     uint32_t a, b;
-    swap_pair_u32<SPAN>(__float_as_uint(v), a, b);
-    return fmaxf(__uint_as_float(a), __uint_as_float(b));
+    swap_pair_u32<SPAN>(v, a, b);
+    return max_dpp_step(a, b);
 }
 
-__device__ __forceinline__ float wave_max(float v)
+__device__ __forceinline__ float wave_max(float x)
 {
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR1>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR2>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_MIRROR>(__float_as_uint(v))));
-    v = swap_max_f32<16>(v);
-    return swap_max_f32<32>(v);
+    uint32_t v = __float_as_uint(x);
+    v = max_dpp_step(v, dpp_u32<DPP_XOR1>(v));
+    v = max_dpp_step(v, dpp_u32<DPP_XOR2>(v));
+    v = max_dpp_step(v, dpp_u32<DPP_HALF_MIRROR>(v));
+    v = max_dpp_step(v, dpp_u32<DPP_MIRROR>(v));
+    v = swap_max_u32<16>(v);
+    return __uint_as_float(swap_max_u32<32>(v));
 }
 
 // Maximum over each group of 16 adjacent lanes (one DPP row), or with
-// LANES == 32 over each aligned pair of rows; NaN is ignored (fmaxf), as in
-// the row amax.  Every lane of a group ends with the group's value.
+// LANES == 32 over each aligned pair of rows, of non-negative non-NaN
+// values (the group amax, NaN already dropped).  Every lane of a group ends
+// with the group's value.
 template <int LANES>
-__device__ __forceinline__ float group_max(float v)
+__device__ __forceinline__ float group_max(float x)
 {
     static_assert(LANES == 16 || LANES == 32, "one or two DPP rows");
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR1>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR2>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_MIRROR>(__float_as_uint(v))));
-    if constexpr (LANES == 32) v = swap_max_f32<16>(v);
-    return v;
+    uint32_t v = __float_as_uint(x);
+    v = max_dpp_step(v, dpp_u32<DPP_XOR1>(v));
+    v = max_dpp_step(v, dpp_u32<DPP_XOR2>(v));
+    v = max_dpp_step(v, dpp_u32<DPP_HALF_MIRROR>(v));
+    v = max_dpp_step(v, dpp_u32<DPP_MIRROR>(v));
+    if constexpr (LANES == 32) v = swap_max_u32<16>(v);
+    return __uint_as_float(v);
 }
 
 // Cross-wave combine of a block's per-wave partials in LDS (N <= 16 of them):
@@ -377,17 +392,18 @@ __device__ __forceinline__ double block_sum(const double *part, int wave_lane)
     return __builtin_bit_cast(double, (hi << 32) | lo);
 }
 
-// The same for maxima of non-negative values (absent partials read as 0).
+// The same for maxima of non-negative non-NaN values, integer maxima of the
+// bit patterns as in wave_max (absent partials read as 0).
 template <int N>
 __device__ __forceinline__ float block_max(const float *part, int wave_lane)
 {
     static_assert(N >= 1 && N <= 16, "up to 16 waves");
-    float v = (wave_lane < N) ? part[wave_lane] : 0.0f;
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR1>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_XOR2>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_MIRROR>(__float_as_uint(v))));
-    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+    uint32_t v = (wave_lane < N) ? __float_as_uint(part[wave_lane]) : 0u;
+    v = max_dpp_step(v, dpp_u32<DPP_XOR1>(v));
+    v = max_dpp_step(v, dpp_u32<DPP_XOR2>(v));
+    v = max_dpp_step(v, dpp_u32<DPP_HALF_MIRROR>(v));
+    v = max_dpp_step(v, dpp_u32<DPP_MIRROR>(v));
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)v, 0));
 }
 
 // ---------------------------------------------------------------- SiLU
