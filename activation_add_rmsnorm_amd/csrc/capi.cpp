@@ -353,6 +353,7 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     p.tokens = tokens;
     p.hidden = (int32_t)hidden;
     p.eps = eps;
+    p.inv_hidden = 1.0 / (double)hidden;
     p.hold_ticks = norm_hold_ticks(tokens, hidden, epi, res, v);
 #ifdef AARMS_PHASE_STAMPS
     p.stamps = g_phase_stamps;

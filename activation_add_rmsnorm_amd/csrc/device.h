@@ -50,6 +50,46 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return (uint32_t)v;
 }
 
+// ---------------------------------------------------------------- row scale
+//
+// The row statistics as the unfused definition computes them in binary64,
+// mean = binary32(acc / n) and rs = binary32(1 / sqrt(v)), without the
+// binary64 division and square-root sequences (about 40 instructions per
+// wave, run by every wave of a row).
+//  - row_mean: q0 = acc * inv_n with inv_n = binary64(1 / n), then one
+//    correction from the exact remainder acc - q0 n (an fma).  With inv_n
+//    correctly rounded and q0 within an ulp, the corrected quotient is the
+//    correctly rounded one (Markstein's theorem), so the result is
+//    binary32(binary64(acc / n)) exactly.  Finite acc (the caller branches).
+//  - row_rsqrt: r0 = v_rsq_f32(v), then two Newton steps
+//    r <- r + r (1 - v r^2) / 2 in binary64 (r0 is within about 2^-22; the
+//    steps leave an error of a few units of 2^-53, as the division of the
+//    unfused form has), rounded once to binary32.  Normal v in
+//    [2^-126, 2^126) (the caller branches).
+__device__ __forceinline__ float row_mean(double acc, double n, double inv_n)
+{
+    const double q0 = acc * inv_n;
+    const double rem = __builtin_fma(-q0, n, acc);
+    return (float)__builtin_fma(rem, inv_n, q0);
+}
+
+__device__ __forceinline__ bool row_rsqrt_in_range(float v)
+{
+    return v >= 0x1p-126f && v < 0x1p126f;
+}
+
+__device__ __forceinline__ float row_rsqrt(float v)
+{
+    const double vd = v;
+    double r = (double)__builtin_amdgcn_rsqf(v);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const double e = __builtin_fma(-(vd * r), r, 1.0);
+        r = __builtin_fma(0.5 * r, e, r);
+    }
+    return (float)r;
+}
+
 // ---------------------------------------------------------------- MXFP4
 //
 // A block of 32 values shares the E8M0 scale 2^x with x = floor(log2 amax)

@@ -33,6 +33,7 @@ struct NormParams {
     int64_t tokens;
     int32_t hidden;
     float eps;
+    double inv_hidden;       // binary64(1 / hidden), correctly rounded
     // Store hold of the one-shot kernel, in ticks of the 100 MHz real-time
     // clock: a row's stores wait until this long after its wave started (0:
     // none).  At most NORM_HOLD_MAX_TICKS.

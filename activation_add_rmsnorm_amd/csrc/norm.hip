@@ -69,6 +69,24 @@ __device__ __forceinline__ uint32_t norm_word(uint32_t r, uint32_t w, float rs)
     return pack_bf16(bf_lo(w) * bf_lo(t), bf_hi(w) * bf_hi(t));
 }
 
+// The same, also handing back the binary32 products p0 = w t before their
+// rounding.  Rounding to nearest is monotone and symmetric, so the largest
+// |p| rounds to the largest |y|: amax reductions run on the products (one
+// three-operand maximum per word) and round once at the end.
+__device__ __forceinline__ uint32_t norm_word(uint32_t r, uint32_t w, float rs, float &p0, float &p1)
+{
+    const uint32_t t = pack_bf16(bf_lo(r) * rs, bf_hi(r) * rs);
+    p0 = bf_lo(w) * bf_lo(t);
+    p1 = bf_hi(w) * bf_hi(t);
+    return pack_bf16(p0, p1);
+}
+
+// binary32 value of bf16(a), a >= 0 or NaN
+__device__ __forceinline__ float round_bf16(float a)
+{
+    return bf_lo(pack_bf16(a, a));
+}
+
 // Static per-tensor E4M3 epilogue: q = e4m3(clamp(y / s)) straight from the
 // row, 8 bytes per 16-byte slice.
 template <int WPR, int VPT, bool FAST>
@@ -224,10 +242,19 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         acc = block_sum<WPR>(psum, lane & 63);
     }
 
-    // ---- mean (rounded once to binary32), + eps, reciprocal square root
-    const float mean = (float)(acc / (double)p.hidden);
+    // ---- mean (rounded once to binary32), + eps, reciprocal square root;
+    // the branches are uniform over the row (acc and var are the row's)
+    float mean;
+    if (acc <= __DBL_MAX__)
+        mean = row_mean(acc, (double)p.hidden, p.inv_hidden);
+    else
+        mean = (float)(acc / (double)p.hidden);
     const float var = mean + p.eps;
-    const float rs = (float)(1.0 / sqrt((double)var));
+    float rs;
+    if (row_rsqrt_in_range(var))
+        rs = row_rsqrt(var);
+    else
+        rs = (float)(1.0 / sqrt((double)var));
 
     if constexpr (EPI == NORM_EPI_BF16) {
         // ---- t = bf16(h * rs), y = bf16(w * t)
@@ -250,12 +277,16 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         for (int k = 0; k < VPT; ++k) {
             const int v = lane + k * WPR * 64;
             uint32_t y[4];
-            uint32_t mag = 0;
+            // NaN-propagating maxima: a block holding a NaN gets the NaN scale
+            float amax = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                y[e] = norm_word(rv[k][e], wv[k][e], rs);
-                mag = max(mag, max((y[e] << 16) & 0x7FFFFFFFu, y[e] & 0x7FFF0000u));
+                float p0, p1;
+                y[e] = norm_word(rv[k][e], wv[k][e], rs, p0, p1);
+                amax = __builtin_elementwise_maximum(
+                    amax, __builtin_elementwise_maximum(__builtin_fabsf(p0), __builtin_fabsf(p1)));
             }
+            uint32_t mag = __float_as_uint(round_bf16(amax));
             // the block's 4 slices sit in lanes 4j..4j+3 (all inside or all
             // past the row end, as H is a multiple of 32)
             mag = max(mag, dpp_u32<DPP_XOR1>(mag));
@@ -278,12 +309,15 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         for (int k = 0; k < VPT; ++k) {
             const int v = lane + k * WPR * 64;
             uint32_t y[4];
-            uint32_t mag = 0;
+            float amax = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                y[e] = norm_word(rv[k][e], wv[k][e], rs);
-                mag = max(mag, max((y[e] << 16) & 0x7FFFFFFFu, y[e] & 0x7FFF0000u));
+                float p0, p1;
+                y[e] = norm_word(rv[k][e], wv[k][e], rs, p0, p1);
+                amax = __builtin_elementwise_maximum(
+                    amax, __builtin_elementwise_maximum(__builtin_fabsf(p0), __builtin_fabsf(p1)));
             }
+            uint32_t mag = __float_as_uint(round_bf16(amax));
             mag = max(mag, dpp_u32<DPP_XOR1>(mag));
             if (v >= nvec) continue;
             const uint32_t sb = nv_scale_byte(mag, nt);
@@ -306,12 +340,13 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
             float amax = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t y = norm_word(rv[k][e], wv[k][e], rs);
+                float p0, p1;
+                const uint32_t y = norm_word(rv[k][e], wv[k][e], rs, p0, p1);
                 yf[2 * e] = bf_lo(y);
                 yf[2 * e + 1] = bf_hi(y);
-                amax = fmaxf(amax, fmaxf(__builtin_fabsf(yf[2 * e]), __builtin_fabsf(yf[2 * e + 1])));
+                amax = fmaxf(amax, fmaxf(__builtin_fabsf(p0), __builtin_fabsf(p1)));
             }
-            amax = group_max<16>(amax);
+            amax = group_max<16>(round_bf16(amax));
             if (v >= nvec) continue;
             const float s = amax / 448.0f;
             if ((lane & 15) == 0) so[v >> 4] = s;
@@ -339,8 +374,9 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         else
             store_static_fp8<WPR, VPT, false>(rv, wv, rs, qs, qo, lane, nvec);
     } else {
-        // ---- y as above, kept as binary32 values of bf16; row amax.  Slices
-        // past the row end hold w = 0, so y = 0 there.
+        // ---- y as above, kept as binary32 values of bf16; row amax (from
+        // the products, rounded once).  Slices past the row end hold w = 0,
+        // so y = 0 there.
         float amax = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
@@ -349,12 +385,14 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
                 const float h0 = KEEP ? hf[k][2 * e] : bf_lo(rv[k][e]);
                 const float h1 = KEEP ? hf[k][2 * e + 1] : bf_hi(rv[k][e]);
                 const uint32_t t = pack_bf16(h0 * rs, h1 * rs);
-                const uint32_t y = pack_bf16(bf_lo(wv[k][e]) * bf_lo(t), bf_hi(wv[k][e]) * bf_hi(t));
+                const float p0 = bf_lo(wv[k][e]) * bf_lo(t), p1 = bf_hi(wv[k][e]) * bf_hi(t);
+                const uint32_t y = pack_bf16(p0, p1);
                 hf[k][2 * e] = bf_lo(y);
                 hf[k][2 * e + 1] = bf_hi(y);
-                amax = fmaxf(amax, fmaxf(__builtin_fabsf(hf[k][2 * e]), __builtin_fabsf(hf[k][2 * e + 1])));
+                amax = fmaxf(amax, fmaxf(__builtin_fabsf(p0), __builtin_fabsf(p1)));
             }
         }
+        amax = round_bf16(amax);
         AARMS_STAMP(4, amax);
         amax = wave_max(amax);
         AARMS_STAMP(5, amax);
