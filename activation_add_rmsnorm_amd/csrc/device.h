@@ -33,6 +33,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// The binary32 value of bf16(a).  Rounding to nearest is monotone and
+// symmetric, so the bf16 rounding of the largest |p| of a set of binary32
+// values is the largest |bf16(p)|: maxima of rounded outputs are taken on the
+// products before their rounding and rounded once.
+__device__ __forceinline__ float round_bf16(float a)
+{
+    return bf_lo(pack_bf16(a, a));
+}
+
 // Saturate to the E4M3 range, keeping NaN: the conversion below turns
 // anything beyond 464 into NaN, and v_med3_f32 drops a NaN operand.
 __device__ __forceinline__ float clamp_e4m3(float z)

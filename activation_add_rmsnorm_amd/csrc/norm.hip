@@ -81,12 +81,6 @@ __device__ __forceinline__ uint32_t norm_word(uint32_t r, uint32_t w, float rs, 
     return pack_bf16(p0, p1);
 }
 
-// binary32 value of bf16(a), a >= 0 or NaN
-__device__ __forceinline__ float round_bf16(float a)
-{
-    return bf_lo(pack_bf16(a, a));
-}
-
 // Static per-tensor E4M3 epilogue: q = e4m3(clamp(y / s)) straight from the
 // row, 8 bytes per 16-byte slice.
 template <int WPR, int VPT, bool FAST>

@@ -43,12 +43,21 @@ struct Words<2> {
     typedef uint32_t Q;  // 4 E4M3 codes
 };
 
+// Running maxima of |y| over jobs, taken on the binary32 products a * u
+// before their bf16 rounding (the caller rounds the result once, round_bf16):
+// AMAX_DROP_NAN folds with fmaxf, which drops NaN (the per-token and
+// per-group scale rules); AMAX_KEEP_NAN with the NaN-propagating maximum (the
+// FP4 block rules, where a NaN marks the block).
+enum JobAmax : int { AMAX_NONE = 0, AMAX_DROP_NAN = 1, AMAX_KEEP_NAN = 2 };
+
 // 2W outputs of one job: a = bf16(silu(g)), y = bf16(a * u).  Returns the
 // bf16 results as W packed words.  Each word of the gate is turned into its
 // word of a at once (two SiLUs, one pack), so only the packed words stay
 // live; a lane with a flagged element redoes its words in the rare branch.
-template <int W>
-__device__ __forceinline__ typename Words<W>::T swiglu_job(typename Words<W>::T gv, typename Words<W>::T uv)
+// With AMAX, amax also takes the job's |a * u| (see JobAmax).
+template <int W, int AMAX = AMAX_NONE>
+__device__ __forceinline__ typename Words<W>::T swiglu_job(typename Words<W>::T gv, typename Words<W>::T uv,
+                                                          float &amax)
 {
     uint32_t a[W];
     // running extrema: smallest knife-edge key of the results, largest gate
@@ -81,8 +90,23 @@ __device__ __forceinline__ typename Words<W>::T swiglu_job(typename Words<W>::T 
     }
     typename Words<W>::T y;
 #pragma unroll
-    for (int e = 0; e < W; ++e) y[e] = pack_bf16(bf_lo(a[e]) * bf_lo(uv[e]), bf_hi(a[e]) * bf_hi(uv[e]));
+    for (int e = 0; e < W; ++e) {
+        const float p0 = bf_lo(a[e]) * bf_lo(uv[e]), p1 = bf_hi(a[e]) * bf_hi(uv[e]);
+        y[e] = pack_bf16(p0, p1);
+        if constexpr (AMAX == AMAX_DROP_NAN)
+            amax = fmaxf(amax, fmaxf(__builtin_fabsf(p0), __builtin_fabsf(p1)));
+        else if constexpr (AMAX == AMAX_KEEP_NAN)
+            amax = __builtin_elementwise_maximum(
+                amax, __builtin_elementwise_maximum(__builtin_fabsf(p0), __builtin_fabsf(p1)));
+    }
     return y;
+}
+
+template <int W>
+__device__ __forceinline__ typename Words<W>::T swiglu_job(typename Words<W>::T gv, typename Words<W>::T uv)
+{
+    float unused = 0.0f;
+    return swiglu_job<W, AMAX_NONE>(gv, uv, unused);
 }
 
 // MXFP4 block of 32 outputs = the jobs of 32 / (2W) adjacent lanes: the
@@ -127,12 +151,11 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t c = c0 + 256u * u;
-            const V y = swiglu_job<W>(gv[u], uv[u]);
-            uint32_t mag = 0;
-#pragma unroll
-            for (int e = 0; e < W; ++e)
-                mag = max(mag, max((y[e] << 16) & 0x7FFFFFFFu, y[e] & 0x7FFF0000u));
-            mag = mx_block_max<W>(mag);
+            float amax = 0.0f;
+            const V y = swiglu_job<W, AMAX_KEEP_NAN>(gv[u], uv[u], amax);
+            // magnitude bits of the job's largest |y| (a NaN or Inf gives bits
+            // at or above 0x7F800000: the NaN scale)
+            const uint32_t mag = mx_block_max<W>(__float_as_uint(round_bf16(amax)));
             if (c >= njobs) continue;
             const uint32_t sb = mx_scale_byte(mag);
             const float inv = __uint_as_float((254u - (sb == 0xFFu ? 127u : sb)) << 23);
@@ -171,14 +194,12 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t c = c0 + 256u * u;
-            const V y = swiglu_job<W>(gv[u], uv[u]);
-            uint32_t mag = 0;
+            float amax = 0.0f;
+            const V y = swiglu_job<W, AMAX_KEEP_NAN>(gv[u], uv[u], amax);
             uint32_t w[W];
 #pragma unroll
-            for (int e = 0; e < W; ++e) {
-                w[e] = y[e];
-                mag = max(mag, max((y[e] << 16) & 0x7FFFFFFFu, y[e] & 0x7FFF0000u));
-            }
+            for (int e = 0; e < W; ++e) w[e] = y[e];
+            uint32_t mag = __float_as_uint(round_bf16(amax));
             mag = max(mag, dpp_u32<DPP_XOR1>(mag));
             if constexpr (W == 2) mag = max(mag, dpp_u32<DPP_XOR2>(mag));
             if (c >= njobs) continue;
@@ -202,16 +223,15 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t c = c0 + 256u * u;
-            const V y = swiglu_job<W>(gv[u], uv[u]);
-            float yf[2 * W];
             float amax = 0.0f;
+            const V y = swiglu_job<W, AMAX_DROP_NAN>(gv[u], uv[u], amax);
+            float yf[2 * W];
 #pragma unroll
             for (int e = 0; e < W; ++e) {
                 yf[2 * e] = bf_lo(y[e]);
                 yf[2 * e + 1] = bf_hi(y[e]);
-                amax = fmaxf(amax, fmaxf(__builtin_fabsf(yf[2 * e]), __builtin_fabsf(yf[2 * e + 1])));
             }
-            amax = group_max<LANES>(amax);
+            amax = group_max<LANES>(round_bf16(amax));
             if (c >= njobs) continue;
             const float s = amax / 448.0f;
             if (c % LANES == 0) so[c / LANES] = s;
@@ -335,13 +355,8 @@ __global__ void __launch_bounds__(WPR == 1 ? 256 : WPR * 64) swiglu_rowq_kernel(
     // y = 0 there and the amax is unaffected
     float amax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < JPT; ++k) {
-        y[k] = swiglu_job<4>(y[k], uv[k]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf_lo(y[k][e])), __builtin_fabsf(bf_hi(y[k][e]))));
-    }
-    amax = wave_max(amax);
+    for (int k = 0; k < JPT; ++k) y[k] = swiglu_job<4, AMAX_DROP_NAN>(y[k], uv[k], amax);
+    amax = wave_max(round_bf16(amax));
     if constexpr (WPR > 1) {
         if ((lane & 63) == 0) pmax[lane >> 6] = amax;
         __syncthreads();
