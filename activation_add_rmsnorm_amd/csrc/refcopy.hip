@@ -61,11 +61,15 @@ hipError_t launch(const void *in0, const void *in1, void *out0, void *out1, uint
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // Copy designs, for a sweep of how a plain stream of a given read/write mix
-// is best issued on this device.  Per input vector pair (two 16-byte loads):
-// KIND 0 writes one 16-byte vector (the SwiGLU mix), KIND 1 two (the bf16
-// norm mix), KIND 2 one 16-byte and one 8-byte vector (the E4M3 norm mix).
-// U vectors of each input per lane; NT = streaming hints; the grid is either
-// one-shot (one block per 256 U vectors) or smaller, with a grid-stride loop.
+// is best issued on this device.  Per vector index i: KIND 0 reads in0[i]
+// and in1[i] and writes one 16-byte vector (the SwiGLU mix), KIND 1 two (the
+// bf16 norm mix), KIND 2 one 16-byte and one 8-byte vector (the E4M3 norm
+// mix), KIND 6 one 8-byte vector (the E4M3 SwiGLU mix); KIND 3 only reads
+// in0[i] and in1[i] (its store is guarded by a test no data passes in
+// practice, so the loads are not dead), KIND 4 only writes out0[i], KIND 5
+// reads in0[i] and writes out0[i].  U vectors per lane; NT = streaming
+// hints; the grid is either one-shot (one block per 256 U vectors) or
+// smaller, with a grid-stride loop.
 template <bool NT>
 __device__ __forceinline__ u32x4 ld(const u32x4 *p)
 {
@@ -91,18 +95,34 @@ copy_design_kernel(const u32x4 *__restrict__ in0, const u32x4 *__restrict__ in1,
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint64_t i = base + (uint64_t)u * 256u;
+            a[u] = b[u] = (u32x4)0u;
             if (i < n) {
-                a[u] = ld<NT>(in0 + i);
-                b[u] = ld<NT>(in1 + i);
+                if constexpr (KIND != 4) a[u] = ld<NT>(in0 + i);
+                if constexpr (KIND != 4 && KIND != 5) b[u] = ld<NT>(in1 + i);
             }
+        }
+        if constexpr (KIND == 3) {
+            u32x4 acc = (u32x4)0u;
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc ^= a[u] + b[u];
+            if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0x85EBCA6Bu && acc.w == 0xC2B2AE35u &&
+                base < n)
+                st<NT>(out0 + base, acc);
+            continue;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint64_t i = base + (uint64_t)u * 256u;
             if (i >= n) continue;
-            st<NT>(out0 + i, a[u] ^ b[u]);
-            if constexpr (KIND == 1) st<NT>((u32x4 *)out1 + i, a[u] + b[u]);
-            if constexpr (KIND == 2) st<NT>((u32x2 *)out1 + i, (u32x2){a[u].x ^ b[u].z, a[u].y ^ b[u].w});
+            if constexpr (KIND == 4) {
+                st<NT>(out0 + i, (u32x4)(uint32_t)i);
+            } else if constexpr (KIND == 6) {
+                st<NT>((u32x2 *)out0 + i, (u32x2){a[u].x ^ b[u].z, a[u].y ^ b[u].w});
+            } else {
+                st<NT>(out0 + i, a[u] ^ b[u]);
+                if constexpr (KIND == 1) st<NT>((u32x4 *)out1 + i, a[u] + b[u]);
+                if constexpr (KIND == 2) st<NT>((u32x2 *)out1 + i, (u32x2){a[u].x ^ b[u].z, a[u].y ^ b[u].w});
+            }
         }
     }
 }
@@ -153,34 +173,42 @@ extern "C" __attribute__((visibility("default"))) int aarms_reference_copy(void 
     return (int)e;
 }
 
-// One launch of a copy design (see copy_design_kernel): kind 0, 1 or 2;
+// One launch of a copy design (see copy_design_kernel): kind 0 to 6;
 // vecs_per_lane 1, 2 or 4; nt 0 or 1; grid_blocks 0 for the one-shot grid,
 // else that many 256-lane blocks looping over the data.  n 16-byte vectors
-// per input; out1 holds n 16-byte (kind 1) or 8-byte (kind 2) vectors.
+// per input; out0 holds n 16-byte vectors (n 8-byte ones for kind 6), out1
+// n 16-byte (kind 1) or 8-byte (kind 2) vectors and is ignored otherwise;
+// in1 is ignored by kinds 4 and 5, in0 by kind 4 (they may then be null).
 // Returns 0, -1 for bad arguments (nothing launched), or the HIP error.
 extern "C" __attribute__((visibility("default"))) int aarms_copy_design(int kind, int vecs_per_lane, int nt,
                                                                        int64_t grid_blocks, void *out0, void *out1,
                                                                        const void *in0, const void *in1, int64_t n,
                                                                        hipStream_t stream)
 {
-    if (kind < 0 || kind > 2 || (vecs_per_lane != 1 && vecs_per_lane != 2 && vecs_per_lane != 4) || n < 0 ||
+    if (kind < 0 || kind > 6 || (vecs_per_lane != 1 && vecs_per_lane != 2 && vecs_per_lane != 4) || n < 0 ||
         grid_blocks < 0)
         return -1;
     if (n == 0) return 0;
-    if (!in0 || !in1 || !out0 || (kind > 0 && !out1) || !aligned(in0, 16) || !aligned(in1, 16) ||
-        !aligned(out0, 16) || (kind > 0 && !aligned(out1, kind == 1 ? 16 : 8)))
+    const bool reads0 = kind != 4, reads1 = kind != 4 && kind != 5, has_out1 = kind == 1 || kind == 2;
+    if ((reads0 && (!in0 || !aligned(in0, 16))) || (reads1 && (!in1 || !aligned(in1, 16))) || !out0 ||
+        !aligned(out0, kind == 6 ? 8 : 16) || (has_out1 && (!out1 || !aligned(out1, kind == 1 ? 16 : 8))))
         return -1;
     const uint64_t m = (uint64_t)n;
     const uint64_t per_block = 256u * (uint64_t)vecs_per_lane;
     uint64_t grid = (m + per_block - 1) / per_block;
     if (grid_blocks > 0 && (uint64_t)grid_blocks < grid) grid = (uint64_t)grid_blocks;
     if (grid > (uint64_t)INT32_MAX) return -1;
-    hipError_t e;
-    if (kind == 0) e = nt ? design_u<0, true>(vecs_per_lane, in0, in1, out0, out1, m, grid, stream)
-                          : design_u<0, false>(vecs_per_lane, in0, in1, out0, out1, m, grid, stream);
-    else if (kind == 1) e = nt ? design_u<1, true>(vecs_per_lane, in0, in1, out0, out1, m, grid, stream)
-                               : design_u<1, false>(vecs_per_lane, in0, in1, out0, out1, m, grid, stream);
-    else e = nt ? design_u<2, true>(vecs_per_lane, in0, in1, out0, out1, m, grid, stream)
-                : design_u<2, false>(vecs_per_lane, in0, in1, out0, out1, m, grid, stream);
-    return (int)e;
+#define AARMS_DESIGN_KIND(K)                                                                     \
+    if (kind == K)                                                                               \
+        return (int)(nt ? design_u<K, true>(vecs_per_lane, in0, in1, out0, out1, m, grid, stream) \
+                        : design_u<K, false>(vecs_per_lane, in0, in1, out0, out1, m, grid, stream));
+    AARMS_DESIGN_KIND(0)
+    AARMS_DESIGN_KIND(1)
+    AARMS_DESIGN_KIND(2)
+    AARMS_DESIGN_KIND(3)
+    AARMS_DESIGN_KIND(4)
+    AARMS_DESIGN_KIND(5)
+    AARMS_DESIGN_KIND(6)
+#undef AARMS_DESIGN_KIND
+    return -1;
 }

@@ -17,7 +17,8 @@ that copy's time over the kernel's (above 1: the kernel is faster).  It is a
 reference, not a bound: the bound is the 8 TB/s HBM peak, and kernels that
 issue their accesses differently can beat the copy.  ``--copy-sweep`` times
 other designs of such copies instead (vectors per lane, grid-stride or
-one-shot grids, streaming hints) and prints them as the JSON line.
+one-shot grids, streaming hints), and pure reads, pure writes and a 1:1 copy
+of 1 GiB, and prints them as the JSON line.
 
 The same run also measures, as supplementary figures, the static-FP8 SwiGLU
 on Llama-70B's [8192, 57344] gate_up, the dynamic-FP8 norm on Llama-405B's
@@ -73,7 +74,8 @@ def parse():
     ap.add_argument("--copy-sweep", action="store_true",
                     help="instead of the workloads, time plain copy designs (vectors per lane, one-shot or "
                          "grid-stride grid, streaming hints) at the read/write mixes and sizes of the "
-                         "headline kernels and the Llama-405B norm; prints them as the JSON line")
+                         "headline kernels and the Llama norm and SwiGLU, and pure reads, pure writes "
+                         "and a 1:1 copy of 1 GiB; prints them as the JSON line")
     ap.add_argument("--phase-timeline", action="store_true",
                     help="instead of the workloads, record the per-wave phase timeline of the Llama-405B "
                          "per-token E4M3 norm (libaarms_stamps.so) and print its summary as the JSON line")
@@ -409,12 +411,19 @@ COPY_MIXES = [
     ("norm_mix_50MB", 1, 64, "fused_add_rmsnorm bf16 [4096,1536]: two inputs, two outputs", 50331648),
     ("norm_fp8_mix_235MB", 2, 56, "fused_add_rmsnorm_quant_fp8 [2048,16384]: two inputs, a bf16 and an e4m3 output",
      234881024),
+    ("swiglu_fp8_mix_1174MB", 6, 40,
+     "swiglu_quant_fp8 [8192,57344] -> e4m3 [8192,28672]: two inputs, an output of a quarter of their bytes",
+     1174405120),
+    ("read_only_1GB", 3, 32, "reads only (two inputs, no output)", 1 << 30),
+    ("write_only_1GB", 4, 16, "writes only (one output, no input)", 1 << 30),
+    ("copy_1GB", 5, 32, "one input, one output of the same bytes", 1 << 30),
 ]
 
 
 def copy_sweep(args, torch, clib, dev, sp, timer):
-    """Plain copies at the read/write mix and size of each headline kernel:
-    1, 2 or 4 vectors of each input per lane, a one-shot grid or a
+    """Plain copies at the read/write mix and size of each headline kernel,
+    and pure reads, pure writes and a 1:1 copy at 1 GiB (what the device's
+    HBM gives each direction alone): 1, 2 or 4 vectors per lane, a one-shot grid or a
     grid-stride loop over two 4-wave blocks per CU, with and without the streaming
     hints; rotated buffer sets (3x the last-level cache) as in the workload
     measurements.  Median of 5 timed regions per design, designs interleaved."""
@@ -430,7 +439,7 @@ def copy_sweep(args, torch, clib, dev, sp, timer):
             a = torch.empty(n * 16, dtype=torch.uint8, device=dev)
             b = torch.empty(n * 16, dtype=torch.uint8, device=dev)
             o0 = torch.empty(n * 16, dtype=torch.uint8, device=dev)
-            o1 = torch.empty(n * (16 if kind == 1 else 8), dtype=torch.uint8, device=dev) if kind else None
+            o1 = torch.empty(n * (16 if kind == 1 else 8), dtype=torch.uint8, device=dev) if kind in (1, 2) else None
             sets.append((a, b, o0, o1))
         designs = [(u, grid, nt) for u in (1, 2, 4) for grid in ("one-shot", "grid-stride") for nt in (1, 0)]
         times = {d: [] for d in designs}

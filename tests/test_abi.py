@@ -370,7 +370,11 @@ def test_reference_copy_library_rejects_bad_arguments():
     d = lib.aarms_copy_design
     d.argtypes = [i32, i32, i32, i64, vp, vp, vp, vp, i64, vp]
     assert d(0, 1, 1, 0, P, None, P + (1 << 30), P + (2 << 30), 0, None) == 0        # empty: no launch
-    assert d(3, 1, 1, 0, P, P, P, P, 8, None) == -1                                   # bad kind
+    assert d(7, 1, 1, 0, P, P, P, P, 8, None) == -1                                   # bad kind
+    assert d(-1, 1, 1, 0, P, P, P, P, 8, None) == -1
+    assert d(3, 1, 1, 0, P, None, P, None, 8, None) == -1                             # read-only: in1 missing
+    assert d(5, 1, 1, 0, P, None, None, None, 8, None) == -1                          # copy: in0 missing
+    assert d(6, 1, 1, 0, P + 4, None, P, P, 8, None) == -1                            # 8-byte out0 misaligned
     assert d(0, 3, 1, 0, P, None, P, P, 8, None) == -1                                # bad vectors per lane
     assert d(1, 1, 1, 0, P, None, P, P, 8, None) == -1                                # out1 missing
     assert d(2, 1, 1, 0, P, P + 4, P, P, 8, None) == -1                               # out1 misaligned
