@@ -222,12 +222,14 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
 constexpr int64_t kSwigluHalfJobOutputs = (int64_t)1 << 21;
 constexpr int64_t kSwigluFp8TwoJobOutputs = (int64_t)1 << 22;
 constexpr int64_t kSwigluNvfp4TwoJobOutputs = (int64_t)1 << 25;
+// the flat grid indexes jobs with 32 bits (larger launches take the row-chunked grid)
+constexpr int64_t kSwigluFlatMaxJobs = 0xFFFFFF00ll;
 
-static int swiglu_find(int jobs_per_lane, int job_outputs)
+static int swiglu_find(int jobs_per_lane, int job_outputs, int flat = 0)
 {
     for (int i = 0; i < swiglu_variant_count(); ++i) {
         const SwigluVariant *v = swiglu_variant(i);
-        if (v->jobs_per_lane == jobs_per_lane && v->job_outputs == job_outputs) return i;
+        if (v->jobs_per_lane == jobs_per_lane && v->job_outputs == job_outputs && v->flat == flat) return i;
     }
     return -1;
 }
@@ -248,8 +250,17 @@ int pick_swiglu(int64_t tokens, int64_t inter, int epi)
     // jobs) and one job per lane measured about 10% faster for the per-group
     // form at 8,960 and 14,336 wide, while two jobs measured 1-4% faster at
     // 28,672 wide from 2,048 tokens.
-    if (epi == SWIGLU_EPI_FP8 && tokens > kSwigluFp8TwoJobOutputs / inter)
+    // On rows that are not whole 512-job blocks, the two-job grid leaves the
+    // last block of every row partly idle (27% of its lanes at N = 8,960),
+    // and the flat grid (blocks of 256 jobs over the rows laid end to end)
+    // measured 2-17% faster from 512 tokens at N = 2,560-14,336; on whole
+    // 512-job rows (N = 28,672) and on rows of 256 jobs two jobs per lane
+    // are as fast or faster.
+    if (epi == SWIGLU_EPI_FP8 && tokens > kSwigluFp8TwoJobOutputs / inter) {
+        const int64_t njobs = inter / 8;
+        if (njobs % 512 != 0 && njobs > 256 && tokens <= kSwigluFlatMaxJobs / njobs) return swiglu_find(1, 8, 1);
         return swiglu_find(2, 8);
+    }
     if ((epi == SWIGLU_EPI_NVFP4 || epi == SWIGLU_EPI_FP8_GROUP) && tokens > kSwigluNvfp4TwoJobOutputs / inter &&
         (inter / 8) % 512 == 0)
         return swiglu_find(2, 8);
@@ -393,7 +404,7 @@ int swiglu_common(void *out, const void *gate_up, const float *scale, uint8_t *s
     const int partner[2] = {-1, -1};
     if ((st = check_outputs(outs, partner, n_out, ins, with_scale ? 2 : 1))) return st;
     if (variant == -1) variant = pick_swiglu(tokens, inter, epi);
-    SwigluParams p;
+    SwigluParams p{};
     p.out = out;
     p.gate_up = gate_up;
     p.scale = with_scale ? scale : nullptr;
@@ -422,7 +433,7 @@ int swiglu_rowq_common(void *out, float *scale_out, const void *gate_up, int64_t
     if (variant == -1) variant = pick_swiglu_rowq(tokens, inter);
     const SwigluRowVariant *v = swiglu_row_variant(variant);
     if (!v || rowq_capacity(v) < inter) return AARMS_ERR_BAD_VARIANT;
-    SwigluParams p;
+    SwigluParams p{};
     p.out = out;
     p.gate_up = gate_up;
     p.scale = nullptr;

@@ -65,6 +65,9 @@ struct SwigluParams {
     int64_t tokens;          // T
     int64_t inter;           // N
     uint32_t vecs_per_row;   // N / 8: one job = 8 adjacent outputs of a row
+    // Flat grid only: floor(n / jobs per row) for 32-bit n as
+    // (t + ((n - t) >> div_shift1)) >> div_shift2 with t = mulhi(n, div_magic)
+    uint32_t div_magic, div_shift1, div_shift2;
 };
 
 // Rows per launch along grid y; more rows go to grid z.
@@ -83,6 +86,8 @@ struct NormVariant {
 struct SwigluVariant {
     int jobs_per_lane;       // a block of 256 lanes covers 256 * jobs_per_lane jobs of one row
     int job_outputs;         // outputs per job: 8 (16-byte loads) or 4 (8-byte loads)
+    int flat;                // 1: blocks of 256 jobs over the rows laid end to end (one 8-output
+                             // job per lane; rows of at least 256 jobs, under 2^32 jobs per launch)
     const char *name;
 };
 

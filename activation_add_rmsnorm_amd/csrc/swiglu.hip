@@ -125,24 +125,53 @@ __device__ __forceinline__ uint32_t mx_block_max(uint32_t mag)
 // division; 3: MXFP4 (codes to out, E8M0 block scales to scale_out); 4:
 // NVFP4 (codes to out, E4M3 block scales to scale_out, tensor scale read
 // from scale); 5: E4M3 with an fp32 scale per 128 outputs (scale_out).
-template <int U, int W, int MODE>
+// FLAT: the grid is one dimension of 256-job blocks over the rows laid end
+// to end (U = 1, W = 4), so no lane idles at a row's end (a row of 1,120
+// jobs fills 4.375 blocks of the row-chunked grid).  With at least 256 jobs
+// per row a block spans at most two rows: the first is a per-block scalar
+// (a division by the row length with the host's magic numbers), and a lane
+// whose job lies past that row's end takes it from the next row.
+template <int U, int W, int MODE, bool FLAT = false>
 __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Scale &qs)
 {
     typedef typename Words<W>::T V;
-    const uint64_t row = (uint64_t)blockIdx.z * SWIGLU_ROWS_PER_Y + blockIdx.y;
-    if (row >= (uint64_t)p.tokens) return;
     const uint32_t njobs = p.vecs_per_row * (4 / W);
-    const uint32_t c0 = blockIdx.x * (256u * U) + threadIdx.x;
-    const V *gate = (const V *)((const uint16_t *)p.gate_up + row * 2u * (uint64_t)p.inter);
-    const V *up = gate + njobs;
-    const uint64_t job0 = row * njobs;
+    // per job slot: its index in the row-major [T, njobs] job space (outputs
+    // and block scales are indexed by it), whether it exists, and its gate
+    // vector (the up vector is njobs further)
+    uint64_t jout[U];
+    bool ok[U];
+    const V *gsrc[U];
+    if constexpr (FLAT) {
+        static_assert(U == 1 && W == 4, "flat grids take one 8-output job per lane");
+        const uint32_t j0 = blockIdx.x * 256u;
+        const uint32_t t1 = __umulhi(j0, p.div_magic);
+        const uint32_t row0 = (t1 + ((j0 - t1) >> p.div_shift1)) >> p.div_shift2;
+        const uint32_t c = j0 - row0 * njobs + threadIdx.x;
+        const bool next = c >= njobs;
+        // row (row0 + next), column c - (next ? njobs : 0): gate vector
+        // 2 njobs (row0 + next) + c - (next ? njobs : 0)
+        gsrc[0] = (const V *)p.gate_up + (uint64_t)row0 * 2u * njobs + (c + (next ? njobs : 0u));
+        jout[0] = (uint64_t)j0 + threadIdx.x;
+        ok[0] = (uint64_t)row0 + (next ? 1u : 0u) < (uint64_t)p.tokens;
+    } else {
+        const uint64_t row = (uint64_t)blockIdx.z * SWIGLU_ROWS_PER_Y + blockIdx.y;
+        if (row >= (uint64_t)p.tokens) return;
+        const uint32_t c0 = blockIdx.x * (256u * U) + threadIdx.x;
+        const V *gate = (const V *)((const uint16_t *)p.gate_up + row * 2u * (uint64_t)p.inter);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = c0 + 256u * u;
+            ok[u] = c < njobs;
+            jout[u] = row * njobs + c;
+            gsrc[u] = gate + c;
+        }
+    }
     V gv[U], uv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t c = c0 + 256u * u;
-        const bool ok = c < njobs;
-        gv[u] = ok ? ld_stream(gate + c) : (V)0u;
-        uv[u] = ok ? ld_stream(up + c) : (V)0u;
+        gv[u] = ok[u] ? ld_stream(gsrc[u]) : (V)0u;
+        uv[u] = ok[u] ? ld_stream(gsrc[u] + njobs) : (V)0u;
     }
     if constexpr (MODE == 3) {
         // every lane takes part in the block maxima (slots past the row end
@@ -150,28 +179,27 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
         constexpr uint32_t LANES = 16 / W;       // lanes per 32-output block
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t c = c0 + 256u * u;
             float amax = 0.0f;
             const V y = swiglu_job<W, AMAX_KEEP_NAN>(gv[u], uv[u], amax);
             // magnitude bits of the job's largest |y| (a NaN or Inf gives bits
             // at or above 0x7F800000: the NaN scale)
             const uint32_t mag = mx_block_max<W>(__float_as_uint(round_bf16(amax)));
-            if (c >= njobs) continue;
+            if (!ok[u]) continue;
             const uint32_t sb = mx_scale_byte(mag);
             const float inv = __uint_as_float((254u - (sb == 0xFFu ? 127u : sb)) << 23);
             if constexpr (W == 4) {
                 const uint32_t w4[4] = {y[0], y[1], y[2], y[3]};
                 const uint32_t q = (sb == 0xFFu) ? 0u : pack_e2m1x8(w4, inv);
-                st_stream((uint32_t *)p.out + job0 + c, q);
+                st_stream((uint32_t *)p.out + jout[u], q);
             } else {
                 uint32_t q = 0;
                 if (sb != 0xFFu) {
                     q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, bf_lo(y[0]) * inv, bf_hi(y[0]) * inv, 1.0f, 0);
                     q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, bf_lo(y[1]) * inv, bf_hi(y[1]) * inv, 1.0f, 1);
                 }
-                st_stream((uint16_t *)p.out + job0 + c, (uint16_t)q);
+                st_stream((uint16_t *)p.out + jout[u], (uint16_t)q);
             }
-            if (c % LANES == 0) ((uint8_t *)p.scale_out)[(job0 + c) / LANES] = (uint8_t)sb;
+            if (jout[u] % LANES == 0) ((uint8_t *)p.scale_out)[jout[u] / LANES] = (uint8_t)sb;
         }
         return;
     }
@@ -193,7 +221,6 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
         const Nvfp4Tensor nt = make_nvfp4_tensor(g, nv_inv[127]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t c = c0 + 256u * u;
             float amax = 0.0f;
             const V y = swiglu_job<W, AMAX_KEEP_NAN>(gv[u], uv[u], amax);
             uint32_t w[W];
@@ -202,14 +229,14 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
             uint32_t mag = __float_as_uint(round_bf16(amax));
             mag = max(mag, dpp_u32<DPP_XOR1>(mag));
             if constexpr (W == 2) mag = max(mag, dpp_u32<DPP_XOR2>(mag));
-            if (c >= njobs) continue;
+            if (!ok[u]) continue;
             const uint32_t sb = nv_scale_byte(mag, nt);
             const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<W>(w, sb, nt, nv_inv[sb]);
             if constexpr (W == 4)
-                st_stream((uint32_t *)p.out + job0 + c, q);
+                st_stream((uint32_t *)p.out + jout[u], q);
             else
-                st_stream((uint16_t *)p.out + job0 + c, (uint16_t)q);
-            if (c % LANES == 0) ((uint8_t *)p.scale_out)[(job0 + c) / LANES] = (uint8_t)sb;
+                st_stream((uint16_t *)p.out + jout[u], (uint16_t)q);
+            if (jout[u] % LANES == 0) ((uint8_t *)p.scale_out)[jout[u] / LANES] = (uint8_t)sb;
         }
         return;
     }
@@ -219,10 +246,8 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
         // takes part in the group maximum (slots past the row end hold zeros;
         // N is a multiple of 128, so a group is all in or all out)
         constexpr uint32_t LANES = FP8_GROUP / (2 * W);
-        float *so = p.scale_out + row * (uint64_t)(p.inter / FP8_GROUP);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t c = c0 + 256u * u;
             float amax = 0.0f;
             const V y = swiglu_job<W, AMAX_DROP_NAN>(gv[u], uv[u], amax);
             float yf[2 * W];
@@ -232,9 +257,10 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
                 yf[2 * e + 1] = bf_hi(y[e]);
             }
             amax = group_max<LANES>(round_bf16(amax));
-            if (c >= njobs) continue;
+            if (!ok[u]) continue;
             const float s = amax / 448.0f;
-            if (c % LANES == 0) so[c / LANES] = s;
+            // the scales are [T, N / 128] row-major: scale index = job index / LANES
+            if (jout[u] % LANES == 0) p.scale_out[jout[u] / LANES] = s;
             const E4m3Scale gs = make_e4m3_scale(s);
             float z[2 * W];
             // |y| <= amax, so |y / s| <= 448 (1 + 2^-24): no input clamp
@@ -252,17 +278,16 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
             } else {
                 q = pack_e4m3x4(z[0], z[1], z[2], z[3]);
             }
-            st_stream((typename Words<W>::Q *)p.out + job0 + c, q);
+            st_stream((typename Words<W>::Q *)p.out + jout[u], q);
         }
         return;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t c = c0 + 256u * u;
-        if (c >= njobs) continue;
+        if (!ok[u]) continue;
         const V y = swiglu_job<W>(gv[u], uv[u]);
         if constexpr (MODE == 0) {
-            st_stream((V *)p.out + job0 + c, y);
+            st_stream((V *)p.out + jout[u], y);
         } else {
             float z[2 * W];
 #pragma unroll
@@ -277,28 +302,28 @@ __device__ __forceinline__ void swiglu_block(const SwigluParams &p, const E4m3Sc
             } else {
                 q = pack_e4m3x4(z[0], z[1], z[2], z[3]);
             }
-            st_stream((typename Words<W>::Q *)p.out + job0 + c, q);
+            st_stream((typename Words<W>::Q *)p.out + jout[u], q);
         }
     }
 }
 
-template <int U, int W, int EPI>
+template <int U, int W, int EPI, bool FLAT = false>
 __global__ void __launch_bounds__(256) swiglu_kernel(SwigluParams p)
 {
     if constexpr (EPI == SWIGLU_EPI_FP8) {
         const E4m3Scale qs = make_e4m3_scale(*p.scale);
         if (e4m3_scale_is_fast(qs))
-            swiglu_block<U, W, 1>(p, qs);
+            swiglu_block<U, W, 1, FLAT>(p, qs);
         else
-            swiglu_block<U, W, 2>(p, qs);
+            swiglu_block<U, W, 2, FLAT>(p, qs);
     } else if constexpr (EPI == SWIGLU_EPI_MXFP4) {
-        swiglu_block<U, W, 3>(p, E4m3Scale{});
+        swiglu_block<U, W, 3, FLAT>(p, E4m3Scale{});
     } else if constexpr (EPI == SWIGLU_EPI_NVFP4) {
-        swiglu_block<U, W, 4>(p, E4m3Scale{});
+        swiglu_block<U, W, 4, FLAT>(p, E4m3Scale{});
     } else if constexpr (EPI == SWIGLU_EPI_FP8_GROUP) {
-        swiglu_block<U, W, 5>(p, E4m3Scale{});
+        swiglu_block<U, W, 5, FLAT>(p, E4m3Scale{});
     } else {
-        swiglu_block<U, W, 0>(p, E4m3Scale{});
+        swiglu_block<U, W, 0, FLAT>(p, E4m3Scale{});
     }
 }
 
@@ -424,10 +449,11 @@ hipError_t launch_swiglu_rowq(const SwigluParams &p, int variant, hipStream_t s)
 // ---------------------------------------------------------------- variants
 
 static const SwigluVariant kSwigluVariants[] = {
-    {1, 8, "1 job/lane"},
-    {2, 8, "2 jobs/lane"},
-    {4, 8, "4 jobs/lane"},
-    {1, 4, "1 half job/lane"},
+    {1, 8, 0, "1 job/lane"},
+    {2, 8, 0, "2 jobs/lane"},
+    {4, 8, 0, "4 jobs/lane"},
+    {1, 4, 0, "1 half job/lane"},
+    {1, 8, 1, "1 job/lane, flat rows"},
 };
 constexpr int kNumSwigluVariants = sizeof(kSwigluVariants) / sizeof(kSwigluVariants[0]);
 
@@ -451,11 +477,34 @@ static hipError_t launch_one(const SwigluParams &p, hipStream_t stream)
     return hipLaunchKernel((const void *)&swiglu_kernel<U, W, EPI>, grid, dim3(256), args, 0, stream);
 }
 
+// The flat grid (see swiglu_block): ceil(T * njobs / 256) blocks of 256
+// jobs.  Rows under 256 jobs, or a launch of 2^32 jobs or more, take the
+// row-chunked grid of one job per lane instead (same results).
+template <int EPI>
+static hipError_t launch_flat(const SwigluParams &p, hipStream_t stream)
+{
+    const uint32_t d = p.vecs_per_row;
+    const uint64_t jobs = (uint64_t)p.tokens * d;
+    if (d < 256u || jobs > 0xFFFFFF00ull) return launch_one<1, 4, EPI>(p, stream);
+    SwigluParams copy = p;
+    // floor(n / d) for every 32-bit n (Granlund and Montgomery's round-up
+    // method): l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1 < 2^32
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    copy.div_magic = (uint32_t)((((1ull << l) - d) << 32) / d + 1u);
+    copy.div_shift1 = l < 1u ? l : 1u;
+    copy.div_shift2 = l < 1u ? 0u : l - 1u;
+    void *args[] = {&copy};
+    return hipLaunchKernel((const void *)&swiglu_kernel<1, 4, EPI, true>, dim3((unsigned)((jobs + 255u) / 256u)),
+                           dim3(256), args, 0, stream);
+}
+
 template <int Q>
 static hipError_t dispatch(const SwigluParams &p, int variant, hipStream_t s)
 {
     const SwigluVariant *v = swiglu_variant(variant);
     if (!v) return hipErrorInvalidValue;
+    if (v->flat) return (v->jobs_per_lane == 1 && v->job_outputs == 8) ? launch_flat<Q>(p, s) : hipErrorInvalidValue;
     if (v->job_outputs == 8) {
         switch (v->jobs_per_lane) {
         case 1: return launch_one<1, 4, Q>(p, s);

@@ -247,7 +247,7 @@ def test_norm_fp8_ragged_and_tiny():
 
 # ------------------------------------------------------------------ swiglu
 
-@pytest.mark.parametrize("variant", [-1, 0, 1, 2, 3])
+@pytest.mark.parametrize("variant", [-1, 0, 1, 2, 3, 4])
 def test_swiglu_silu_table_exhaustive(variant):
     """One row: gate = every bf16 pattern, up = 1, so the output is the
     GPU's bf16(silu(g)) for all 65,536 gates: it must equal the oracle's
