@@ -109,6 +109,45 @@ def test_every_gate_block_scaled_every_variant():
         P.check_swiglu_fp8_group(gu, bits(q), bits(s))
 
 
+def _flat_variant():
+    return [v for v in _swiglu_variants() if A.variant_name(A.OP_SWIGLU, v) == "1 job/lane, flat rows"][0]
+
+
+def _every_gate_in_rows_of(N, up):
+    """All 65,536 gate patterns (then the first ones again to fill the last
+    row) in rows of N gates, up constant."""
+    T = -(-65536 // N)
+    g = np.resize(np.arange(65536, dtype=np.uint16), T * N).reshape(T, N)
+    return np.concatenate([g, np.full_like(g, oracle.bf16_from_f64(up))], axis=1)
+
+
+def test_flat_grid_every_form_straddling_rows():
+    """The flat grid's blocks of 256 jobs over rows of 257 jobs (N = 2,056:
+    every block spans two rows, the last block is partial) and of 272 jobs
+    (N = 2,176, the smallest width above 256 jobs that every block-scaled
+    form takes), every gate pattern, in every output form, bit-exact."""
+    v = _flat_variant()
+    gu = _every_gate_in_rows_of(2056, 1.5)
+    gt = bf16(gu)
+    announce("flat grid bf16 and static E4M3", gu.shape)
+    P.check_swiglu(gu, bits(A.swiglu(gt, variant=v)))
+    for scale in (0.05, 2.0 ** -10):
+        P.check_swiglu_fp8(gu, scale, bits(A.swiglu_quant_fp8(gt, f32(scale), variant=v)))
+    gu = _every_gate_in_rows_of(2176, 1.5)
+    gt = bf16(gu)
+    announce("flat grid block-scaled forms", gu.shape)
+    q, s = A.swiglu_quant_mxfp4(gt, variant=v)
+    P.check_swiglu_mxfp4(gu, bits(q), bits(s))
+    q, s = A.swiglu_quant_nvfp4(gt, f32(0.05), variant=v)
+    P.check_swiglu_nvfp4(gu, 0.05, bits(q), bits(s))
+    q, s = A.swiglu_quant_fp8_group(gt, variant=v)
+    P.check_swiglu_fp8_group(gu, bits(q), bits(s))
+    # the rows past the last one a block reaches are not written
+    out = torch.full((gu.shape[0] + 1, gu.shape[1] // 2), -1, dtype=torch.int16, device=DEV)
+    A.swiglu(gt, out=out[:-1].view(torch.bfloat16), variant=v)
+    assert bool((out[-1] == -1).all())
+
+
 def test_swiglu_fp8_dynamic_scales_every_significand():
     """The per-token and per-group scales are binary32(a / 448) for a bf16 a,
     and every such quotient goes through the corrected-quotient path: sweep
