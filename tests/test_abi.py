@@ -311,6 +311,10 @@ def test_pick_variant_ranges():
     assert name(4096, 8960, 1) == name(2048, 5632, 1) == name(8192, 3584, 1) == "1 job/lane, flat rows"
     assert name(8192, 28672, 1) == name(8192, 2048, 1) == "2 jobs/lane"
     assert name(256, 8960, 1) == "1 job/lane"
+    # rows of 257-511 jobs: the flat grid in every format (past the decode sizes)
+    for f in range(5):
+        assert name(8192, 3584, f) == name(4096, 2056, f) == "1 job/lane, flat rows", f
+    assert name(8192, 2048, 0) == name(8192, 4096, 0) == "1 job/lane"
     assert name(4096, 8960, 3) == "1 job/lane"
     assert name(8192, 28672, 3) == "2 jobs/lane" and name(512, 28672, 3) == "1 job/lane"
     assert name(4096, 8960, 4) == name(8192, 14336, 4) == "1 job/lane"
