@@ -1,14 +1,17 @@
 // norm.hip -- RMSNorm for gfx950, with or without the residual add in front,
-// and with a bf16 epilogue, a dynamic per-token E4M3 epilogue or a static
-// per-tensor E4M3 epilogue.
+// and with a bf16 epilogue or a quantised one: E4M3 with a per-token, a
+// per-tensor or a per-128-value scale, MXFP4 or NVFP4.
 //
 // One pass over HBM: x (and the residual) are read once with 16-byte
 // streaming loads, the updated residual and the output are written once, and
-// the row stays in registers between the reduction and the epilogue.  A row is handled by one
-// wave (narrow rows, four rows per 256-thread block) or by a whole block of
-// 2..16 waves (wide rows).  The sum of squares is accumulated per lane in
-// binary64, reduced with a wave butterfly and, across waves, through LDS in
-// a fixed order, so results are bitwise reproducible.
+// the row stays in registers between the reduction and the epilogue.  A row
+// is handled by one wave (narrow rows, four rows per 256-thread block) or by
+// a whole block of 2..16 waves (wide rows); a persistent, software-pipelined
+// form walks several rows per block.  The sum of squares is accumulated per
+// lane in binary64, reduced with a wave butterfly and, across waves, through
+// LDS in a fixed order, so results are bitwise reproducible.  One-generation
+// bf16 launches hold their stores until the launch's reads are served (see
+// hold_stores).
 //
 // The arithmetic follows the eight-operation RMSNorm with the residual add
 // in front ("TensorRT-LLM: Compiling Inference Engines Ahead of Time",

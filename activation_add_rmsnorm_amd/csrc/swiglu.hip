@@ -1,5 +1,6 @@
-// swiglu.hip -- silu(gate) * up over a concatenated gate_up row, with a bf16
-// epilogue or a static per-tensor E4M3 epilogue, for gfx950.
+// swiglu.hip -- silu(gate) * up over a concatenated gate_up row, for gfx950,
+// with a bf16 epilogue or a quantised one: E4M3 with a per-tensor, a
+// per-token or a per-128-output scale, MXFP4 or NVFP4.
 //
 // A job is 8 adjacent outputs of one row, fed by one 16-byte load of gate and
 // one of up from the same row of gate_up (gate first, up second:
@@ -11,7 +12,9 @@
 // the row is a per-block scalar, every load and store of a wave is one
 // contiguous stretch, and blocks are dispatched in memory order (one block
 // per chunk, no grid-stride loop: the blocks in flight then cover one
-// contiguous window of HBM).  Nothing is kept between jobs.
+// contiguous window of HBM).  Nothing is kept between jobs.  A flat form of
+// the grid takes blocks of 256 jobs over the rows laid end to end instead
+// (see swiglu_block), so that no lane idles at a row's end.
 //
 // The per-token (dynamic) E4M3 form needs the row's amax before any code is
 // written, so there a row belongs to one wave or one block (as in the norm),
