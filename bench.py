@@ -527,7 +527,7 @@ def phase_timeline(args, torch, np, W, dev, sp, timer):
     torch.cuda.synchronize()
     L.aarms_set_phase_stamps(None)
     a = stamps.cpu().numpy().reshape(T, wpr, 16).astype(np.float64)
-    t = (a[:, :, :8] - a[:, :, 0].min()) * 0.01          # us from the first wave's start
+    t = (a - a[:, :, 0].min()) * 0.01          # us from the first wave's start (slots 8, 9: IDs)
     bstart = t[:, :, 0].min(1)
     span = float(t[:, :, 7].max())
     pct = lambda v: {"p10": round(float(np.percentile(v, 10)), 2), "median": round(float(np.median(v)), 2),
@@ -546,6 +546,17 @@ def phase_timeline(args, torch, np, W, dev, sp, timer):
         "row amax -> wave maximum": pct((t[:, :, 5] - t[:, :, 4]).ravel()),
         "second barrier -> last store issued": pct((t[:, :, 7] - t[:, :, 6]).ravel()),
     }
+    if (a[:, :, 10:15] > 0).all():
+        # the sub-phases of the chain after the first barrier
+        per_wave.update({
+            "first barrier -> row sum combined": pct((t[:, :, 10] - t[:, :, 3]).ravel()),
+            "row sum -> mean and 1/sqrt": pct((t[:, :, 11] - t[:, :, 10]).ravel()),
+            "1/sqrt -> weight in registers": pct((t[:, :, 12] - t[:, :, 11]).ravel()),
+            "weight -> row amax computed": pct((t[:, :, 4] - t[:, :, 12]).ravel()),
+            "second barrier -> row amax combined": pct((t[:, :, 13] - t[:, :, 6]).ravel()),
+            "row amax -> scale and reciprocal": pct((t[:, :, 14] - t[:, :, 13]).ravel()),
+            "scale -> last store issued": pct((t[:, :, 7] - t[:, :, 14]).ravel()),
+        })
     order = np.argsort(bstart)
     octiles = []
     for g in range(8):
