@@ -144,8 +144,11 @@ constexpr int64_t kPipelinedMinTokens = 768, kPipelinedMaxTokens = 1536;
 // one wave per row: with the residual add 12-21% faster at 4,096-8,192
 // rows of 896-2,048 (22-50 MB of reads), with the best hold
 // near reads / 7-8 TB/s and falling off on both sides (a hold too short
-// gains little, one too long adds its excess); reads / 7.4 TB/s is within
-// 1-4% of the best hold at every measured shape.  Without the residual add
+// gains little, one too long adds its excess).  With the residual add,
+// reads / 7.8 TB/s measured 1.3% and 1.5% faster than 7.4 TB/s at
+// [4096, 1536] and [4096, 2048] and 0.3% slower at [8192, 1536]; without
+// it no single rate wins (7.0 TB/s: 0.5% and 1.8% faster at 4,096 rows,
+// 1.8% slower at [8192, 1536]), so that form keeps 7.4.  Without the residual add
 // (rmsnorm) the gain starts at about 12 MB of reads (4-18% at 12.6-18.9 MB,
 // 4,096-8,192 rows of 896-2,048).  No gain below 4,096 rows, below those
 // read sizes (16.8 MB with the add at [4096, 1024]; 7-8 MB without) or
@@ -153,7 +156,8 @@ constexpr int64_t kPipelinedMinTokens = 768, kPipelinedMaxTokens = 1536;
 // does not fit on the device at once.
 constexpr int64_t kHoldMinTokens = 4096;
 constexpr double kHoldMinReadBytesAdd = 20e6, kHoldMinReadBytesNoAdd = 12e6;
-constexpr double kHoldReadBytesPerTick = 74000.0;   // 7.4 TB/s in 10 ns ticks
+// read bytes served per 10 ns tick of the hold: 7.8 and 7.4 TB/s
+constexpr double kHoldReadBytesPerTickAdd = 78000.0, kHoldReadBytesPerTickNoAdd = 74000.0;
 
 uint32_t norm_hold_ticks(int64_t tokens, int64_t hidden, int epi, bool res, const NormVariant *v)
 {
@@ -161,7 +165,7 @@ uint32_t norm_hold_ticks(int64_t tokens, int64_t hidden, int epi, bool res, cons
         return 0;
     const double reads = (double)tokens * (double)hidden * (res ? 4.0 : 2.0);
     if (reads < (res ? kHoldMinReadBytesAdd : kHoldMinReadBytesNoAdd)) return 0;
-    const double ticks = reads / kHoldReadBytesPerTick;
+    const double ticks = reads / (res ? kHoldReadBytesPerTickAdd : kHoldReadBytesPerTickNoAdd);
     return ticks > (double)NORM_HOLD_MAX_TICKS ? 0u : (uint32_t)(ticks + 0.5);
 }
 
