@@ -159,6 +159,22 @@ constexpr double kHoldMinReadBytesAdd = 20e6, kHoldMinReadBytesNoAdd = 12e6;
 // read bytes served per 10 ns tick of the hold: 7.8 and 7.4 TB/s
 constexpr double kHoldReadBytesPerTickAdd = 78000.0, kHoldReadBytesPerTickNoAdd = 74000.0;
 
+// The quantised forms with the residual add store the updated residual in
+// the epilogue (after the row reduction) rather than right after the add in
+// launches of one generation of blocks from this many bytes of reads:
+// measured 3-16% faster at [256, 16384], [512, 16384] and [1024, 4096] in
+// every quantised form and 2-15% at [4096, 1536] (1% slower for per-token
+// E4M3 there); neutral to 3% slower at 8 MB and below.  Keeping the residual
+// live for the choice costs multi-generation launches 0-2.5% (0.6% faster
+// for the Llama-405B per-token E4M3 norm).
+constexpr double kResLastMinReadBytes = 12e6;
+
+uint32_t norm_res_last(int64_t tokens, int64_t hidden, int epi, bool res)
+{
+    if (!res || epi == NORM_EPI_BF16) return 0;
+    return (double)tokens * (double)hidden * 4.0 >= kResLastMinReadBytes ? 1u : 0u;
+}
+
 uint32_t norm_hold_ticks(int64_t tokens, int64_t hidden, int epi, bool res, const NormVariant *v)
 {
     if (epi != NORM_EPI_BF16 || v->waves_per_row != 1 || v->blocks_per_cu != 0 || tokens < kHoldMinTokens)
@@ -361,7 +377,7 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     if (variant == -1) variant = pick_norm(tokens, hidden, epi, res);
     const NormVariant *v = norm_variant(variant);
     if (!v || norm_capacity(v) < hidden) return AARMS_ERR_BAD_VARIANT;
-    NormParams p;
+    NormParams p{};
     p.out = out;
     p.residual_out = res ? residual_out : nullptr;
     p.x = x;
@@ -374,6 +390,7 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     p.eps = eps;
     p.inv_hidden = 1.0 / (double)hidden;
     p.hold_ticks = norm_hold_ticks(tokens, hidden, epi, res, v);
+    p.res_last = norm_res_last(tokens, hidden, epi, res);
 #ifdef AARMS_PHASE_STAMPS
     p.stamps = g_phase_stamps;
 #endif

@@ -38,6 +38,10 @@ struct NormParams {
     // clock: a row's stores wait until this long after its wave started (0:
     // none).  At most NORM_HOLD_MAX_TICKS.
     uint32_t hold_ticks;
+    // Quantised forms with the residual add: store the updated residual after
+    // the output rather than right after the add (1), if the launch turns out
+    // to be one generation of blocks (the launcher clears it otherwise).
+    uint32_t res_last;
 #ifdef AARMS_PHASE_STAMPS
     // Measurement build only (libaarms_stamps.so): per wave of each row,
     // 16 slots of real-time-clock stamps at the phases of norm_kernel.

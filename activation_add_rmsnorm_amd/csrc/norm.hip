@@ -86,9 +86,12 @@ __device__ __forceinline__ uint32_t norm_word(uint32_t r, uint32_t w, float rs, 
 
 // Static per-tensor E4M3 epilogue: q = e4m3(clamp(y / s)) straight from the
 // row, 8 bytes per 16-byte slice.
+// With late_ro, slice k of the updated residual is stored there once it has
+// been read (the late residual stores of finish_row).
 template <int WPR, int VPT, bool FAST>
 __device__ __forceinline__ void store_static_fp8(const u32x4 (&rv)[VPT], const u32x4 (&wv)[VPT], float rs,
-                                                 const E4m3Scale &qs, uint8_t *qo, int lane, int nvec)
+                                                 const E4m3Scale &qs, uint8_t *qo, int lane, int nvec,
+                                                 u32x4 *late_ro)
 {
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -101,6 +104,7 @@ __device__ __forceinline__ void store_static_fp8(const u32x4 (&rv)[VPT], const u
             z[2 * e] = e4m3_quotient<FAST, true>(bf_lo(y), qs);
             z[2 * e + 1] = e4m3_quotient<FAST, true>(bf_hi(y), qs);
         }
+        if (late_ro) st_stream(late_ro + v, rv[k]);
         u32x2 q;
         q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
         q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
@@ -188,10 +192,14 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
     // One counter tracks both loads and stores on gfx9, so a load waited on
     // after a store is issued (the weight) also waits for that store to
     // reach memory.  The bf16 form stores the updated residual last, with
-    // the output (1-2% faster); the quantised forms store it here, which
-    // spreads their writes better than one burst at the end (2-4% faster,
-    // the wait notwithstanding).
-    constexpr bool RES_LAST = EPI == NORM_EPI_BF16;
+    // the output (1-2% faster).  The quantised forms store each slice in the
+    // epilogue, once it has been read for the last time, when the launch is
+    // one generation of blocks (p.res_last: the writes then come after the
+    // row reduction, so after most of the launch's reads; 4-19% faster from
+    // 12 MB of reads); in longer launches they store it here, which spreads
+    // their writes between the generations.
+    const bool res_late = EPI != NORM_EPI_BF16 && RES && p.res_last != 0;
+    u32x4 *const late_ro = res_late ? ro : nullptr;
     // With few vectors per lane the FP8 form keeps h = f32(r) for the
     // epilogue (fewer instructions); otherwise the packed words are kept
     // (fewer registers, so more rows in flight) and widened again.
@@ -208,7 +216,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 r[e] = pack_bf16(bf_lo(xv[k][e]) + bf_lo(rv[k][e]), bf_hi(xv[k][e]) + bf_hi(rv[k][e]));
-            if (!RES_LAST && v < nvec) st_stream(ro + v, r);
+            if (EPI != NORM_EPI_BF16 && !res_late && v < nvec) st_stream(ro + v, r);
         } else {
             r = xv[k];
         }
@@ -290,6 +298,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
                 amax = __builtin_elementwise_maximum(
                     amax, __builtin_elementwise_maximum(__builtin_fabsf(p0), __builtin_fabsf(p1)));
             }
+            if (late_ro && v < nvec) st_stream(late_ro + v, rv[k]);
             uint32_t mag = __float_as_uint(round_bf16(amax));
             // the block's 4 slices sit in lanes 4j..4j+3 (all inside or all
             // past the row end, as H is a multiple of 32)
@@ -321,6 +330,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
                 amax = __builtin_elementwise_maximum(
                     amax, __builtin_elementwise_maximum(__builtin_fabsf(p0), __builtin_fabsf(p1)));
             }
+            if (late_ro && v < nvec) st_stream(late_ro + v, rv[k]);
             uint32_t mag = __float_as_uint(round_bf16(amax));
             mag = max(mag, dpp_u32<DPP_XOR1>(mag));
             if (v >= nvec) continue;
@@ -350,6 +360,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
                 yf[2 * e + 1] = bf_hi(y);
                 amax = fmaxf(amax, fmaxf(__builtin_fabsf(p0), __builtin_fabsf(p1)));
             }
+            if (late_ro && v < nvec) st_stream(late_ro + v, rv[k]);
             amax = group_max<16>(round_bf16(amax));
             if (v >= nvec) continue;
             const float s = amax / 448.0f;
@@ -374,9 +385,9 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         const E4m3Scale qs = make_e4m3_scale(*p.scale_in);
         uint8_t *qo = (uint8_t *)p.out + base;
         if (e4m3_scale_is_fast(qs))
-            store_static_fp8<WPR, VPT, true>(rv, wv, rs, qs, qo, lane, nvec);
+            store_static_fp8<WPR, VPT, true>(rv, wv, rs, qs, qo, lane, nvec, late_ro);
         else
-            store_static_fp8<WPR, VPT, false>(rv, wv, rs, qs, qo, lane, nvec);
+            store_static_fp8<WPR, VPT, false>(rv, wv, rs, qs, qo, lane, nvec, late_ro);
     } else {
         // ---- y as above, kept as binary32 values of bf16; row amax (from
         // the products, rounded once).  Slices past the row end hold w = 0,
@@ -395,6 +406,8 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
                 hf[k][2 * e + 1] = bf_hi(y);
                 amax = fmaxf(amax, fmaxf(__builtin_fabsf(p0), __builtin_fabsf(p1)));
             }
+            const int v = lane + k * WPR * 64;
+            if (late_ro && v < nvec) st_stream(late_ro + v, rv[k]);
         }
         amax = round_bf16(amax);
         AARMS_STAMP(4, amax);
@@ -420,7 +433,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
     }
 
     // ---- the updated residual, bf16 form
-    if constexpr (RES && RES_LAST) {
+    if constexpr (RES && EPI == NORM_EPI_BF16) {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int v = lane + k * WPR * 64;
@@ -606,11 +619,12 @@ static hipError_t launch_one(const NormParams &p, int blocks_per_cu, int num_cus
     void *args[] = {&copy};
     const void *fn = PIPE ? (const void *)&norm_kernel_pipelined<WPR, VPT, EPI, RES>
                           : (const void *)&norm_kernel<WPR, VPT, EPI, RES>;
-    // the store hold only orders the reads and writes of one generation of
-    // blocks: a grid that does not fit on the device at once runs without it
-    if (copy.hold_ticks != 0) {
+    // the store hold and the late residual stores of the quantised forms
+    // only order the reads and writes of one generation of blocks: a grid
+    // that does not fit on the device at once runs without them
+    if (copy.hold_ticks != 0 || copy.res_last != 0) {
         const int rb = PIPE ? 0 : resident_blocks_per_cu(fn, threads, slot);
-        if (rb <= 0 || blocks > (int64_t)rb * num_cus) copy.hold_ticks = 0;
+        if (rb <= 0 || blocks > (int64_t)rb * num_cus) copy.hold_ticks = copy.res_last = 0;
         if (copy.hold_ticks > NORM_HOLD_MAX_TICKS) copy.hold_ticks = NORM_HOLD_MAX_TICKS;
     }
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
