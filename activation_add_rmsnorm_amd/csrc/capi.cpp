@@ -16,9 +16,16 @@ using namespace aarms;
 // Measurement build only (libaarms_stamps.so): where the one-shot norm kernel
 // writes its phase stamps (16 uint64 per wave of each row; null: none).
 static uint64_t *g_phase_stamps = nullptr;
+static uint32_t g_stamp_detail = 0;
 extern "C" __attribute__((visibility("default"))) void aarms_set_phase_stamps(void *stamps)
 {
     g_phase_stamps = (uint64_t *)stamps;
+}
+// detail != 0: also stamp the sub-steps after the first barrier (more stores
+// and waits in the stamped kernel, so a separate pass)
+extern "C" __attribute__((visibility("default"))) void aarms_set_phase_stamp_detail(int detail)
+{
+    g_stamp_detail = detail ? 1u : 0u;
 }
 #endif
 
@@ -393,6 +400,7 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     p.res_last = norm_res_last(tokens, hidden, epi, res);
 #ifdef AARMS_PHASE_STAMPS
     p.stamps = g_phase_stamps;
+    p.stamp_detail = g_stamp_detail;
 #endif
     return launch_status(launch_norm(p, epi, res, variant, device_cus(), stream));
 }

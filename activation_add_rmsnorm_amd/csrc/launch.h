@@ -44,8 +44,10 @@ struct NormParams {
     uint32_t res_last;
 #ifdef AARMS_PHASE_STAMPS
     // Measurement build only (libaarms_stamps.so): per wave of each row,
-    // 16 slots of real-time-clock stamps at the phases of norm_kernel.
+    // 16 slots of real-time-clock stamps at the phases of norm_kernel;
+    // stamp_detail: also the sub-steps of the chain after the first barrier.
     uint64_t *stamps;
+    uint32_t stamp_detail;
 #endif
 };
 

@@ -129,9 +129,10 @@ __device__ __forceinline__ void load_weight(const NormParams &p, int lane, int n
 // 0 start, 1 row loads consumed, 2 wave sum, 3 first barrier passed, 4 row
 // amax (per-token E4M3) or outputs computed, 5 wave maximum, 6 second
 // barrier passed, 7 last store issued; 8 and 9 hold the HW_ID and XCC_ID
-// registers (which CU ran the wave); per-token E4M3 with several waves per
-// row also 10 row sum combined, 11 mean and 1/sqrt computed, 12 weight in
-// registers, 13 row amax combined, 14 scale and its reciprocal computed.
+// registers (which CU ran the wave); with stamp_detail, per-token E4M3 with
+// several waves per row also 10 row sum combined, 11 mean and 1/sqrt
+// computed, 12 weight in registers, 13 row amax combined, 14 scale and its
+// reciprocal computed.
 #ifdef AARMS_PHASE_STAMPS
 __device__ __forceinline__ uint64_t stamp_after(float dep)
 {
@@ -145,8 +146,13 @@ __device__ __forceinline__ uint64_t stamp_after(float dep)
             if ((lane & 63) == 0) p.stamps[((size_t)row * WPR + (size_t)(lane >> 6)) * 16 + (k)] = t_; \
         }                                                                                          \
     } while (0)
+#define AARMS_STAMP_DETAIL(k, dep)                                                                 \
+    do {                                                                                           \
+        if (p.stamp_detail) AARMS_STAMP(k, dep);                                                   \
+    } while (0)
 #else
 #define AARMS_STAMP(k, dep) do {} while (0)
+#define AARMS_STAMP_DETAIL(k, dep) do {} while (0)
 #endif
 
 // Store hold.  In a launch whose blocks are all resident at once, every
@@ -247,7 +253,7 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
         __syncthreads();
         AARMS_STAMP(3, (float)acc);
         acc = block_sum<WPR>(psum, lane & 63);
-        if constexpr (EPI == NORM_EPI_FP8_DYNAMIC) AARMS_STAMP(10, (float)acc);
+        if constexpr (EPI == NORM_EPI_FP8_DYNAMIC) AARMS_STAMP_DETAIL(10, (float)acc);
     }
 
     // ---- mean (rounded once to binary32), + eps, reciprocal square root;
@@ -264,8 +270,8 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
     else
         rs = (float)(1.0 / sqrt((double)var));
     if constexpr (EPI == NORM_EPI_FP8_DYNAMIC && WPR > 1) {
-        AARMS_STAMP(11, rs);
-        AARMS_STAMP(12, __uint_as_float(wv[0][0]));
+        AARMS_STAMP_DETAIL(11, rs);
+        AARMS_STAMP_DETAIL(12, __uint_as_float(wv[0][0]));
     }
 
     if constexpr (EPI == NORM_EPI_BF16) {
@@ -418,13 +424,13 @@ __device__ __forceinline__ void finish_row(const NormParams &p, int64_t row, int
             __syncthreads();
             AARMS_STAMP(6, amax);
             amax = block_max<WPR>(pmax, lane & 63);
-            AARMS_STAMP(13, amax);
+            AARMS_STAMP_DETAIL(13, amax);
         }
         // ---- per-token scale, then q = e4m3(clamp(y / s))
         const float s = amax / 448.0f;
         if (lane == 0) p.scale_out[row] = s;
         const E4m3Scale qs = make_e4m3_scale(s);
-        if constexpr (WPR > 1) AARMS_STAMP(14, qs.inv);
+        if constexpr (WPR > 1) AARMS_STAMP_DETAIL(14, qs.inv);
         uint8_t *qo = (uint8_t *)p.out + base;
         if (e4m3_scale_is_fast(qs))
             quantize_row<WPR, VPT, true, false>(hf, qs, qo, lane, nvec);

@@ -489,6 +489,8 @@ def phase_timeline(args, torch, np, W, dev, sp, timer):
     L.fused_add_rmsnorm_quant_fp8_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, vp]
     L.aarms_set_phase_stamps.argtypes = [vp]
     L.aarms_set_phase_stamps.restype = None
+    L.aarms_set_phase_stamp_detail.argtypes = [i32]
+    L.aarms_set_phase_stamp_detail.restype = None
     L.aarms_pick_variant.argtypes = [i32, i64, i64, i32]
     L.aarms_variant_name.argtypes = [i32, i32]
     L.aarms_variant_name.restype = C.c_char_p
@@ -546,17 +548,32 @@ def phase_timeline(args, torch, np, W, dev, sp, timer):
         "row amax -> wave maximum": pct((t[:, :, 5] - t[:, :, 4]).ravel()),
         "second barrier -> last store issued": pct((t[:, :, 7] - t[:, :, 6]).ravel()),
     }
-    if (a[:, :, 10:15] > 0).all():
-        # the sub-phases of the chain after the first barrier
-        per_wave.update({
-            "first barrier -> row sum combined": pct((t[:, :, 10] - t[:, :, 3]).ravel()),
-            "row sum -> mean and 1/sqrt": pct((t[:, :, 11] - t[:, :, 10]).ravel()),
-            "1/sqrt -> weight in registers": pct((t[:, :, 12] - t[:, :, 11]).ravel()),
-            "weight -> row amax computed": pct((t[:, :, 4] - t[:, :, 12]).ravel()),
-            "second barrier -> row amax combined": pct((t[:, :, 13] - t[:, :, 6]).ravel()),
-            "row amax -> scale and reciprocal": pct((t[:, :, 14] - t[:, :, 13]).ravel()),
-            "scale -> last store issued": pct((t[:, :, 7] - t[:, :, 14]).ravel()),
-        })
+    # a second pass with the sub-steps of the chain after the first barrier
+    # stamped too (more stores and waits in the kernel: its own pass)
+    L.aarms_set_phase_stamp_detail(1)
+    L.aarms_set_phase_stamps(stamps.data_ptr())
+    timer.warm(call)
+    us_detail = timer.region(call, reps) * 1e3
+    stamps.zero_()
+    torch.cuda.synchronize()
+    for i in range(2 * ns):
+        call(i)
+    torch.cuda.synchronize()
+    L.aarms_set_phase_stamps(None)
+    L.aarms_set_phase_stamp_detail(0)
+    ad = stamps.cpu().numpy().reshape(T, wpr, 16).astype(np.float64)
+    td = (ad - ad[:, :, 0].min()) * 0.01
+    per_wave_detail = {}
+    if (ad[:, :, 10:15] > 0).all():
+        per_wave_detail = {
+            "first barrier -> row sum combined": pct((td[:, :, 10] - td[:, :, 3]).ravel()),
+            "row sum -> mean and 1/sqrt": pct((td[:, :, 11] - td[:, :, 10]).ravel()),
+            "1/sqrt -> weight in registers": pct((td[:, :, 12] - td[:, :, 11]).ravel()),
+            "weight -> row amax computed": pct((td[:, :, 4] - td[:, :, 12]).ravel()),
+            "second barrier -> row amax combined": pct((td[:, :, 13] - td[:, :, 6]).ravel()),
+            "row amax -> scale and reciprocal": pct((td[:, :, 14] - td[:, :, 13]).ravel()),
+            "scale -> last store issued": pct((td[:, :, 7] - td[:, :, 14]).ravel()),
+        }
     order = np.argsort(bstart)
     octiles = []
     for g in range(8):
@@ -577,6 +594,7 @@ def phase_timeline(args, torch, np, W, dev, sp, timer):
             "variant": vname, "waves_per_row": wpr, "launch_us": round(us_plain, 2),
             "launch_us_with_stamps": round(us_stamped, 2), "span_us": round(span, 2),
             "per_block_from_block_start_us": phases, "per_wave_us": per_wave, "octiles_by_start": octiles,
+            "launch_us_with_detail_stamps": round(us_detail, 2), "per_wave_detail_us": per_wave_detail,
             "grid_us": [round(float(g), 2) for g in grid], "blocks_in_flight": in_flight,
             "waves_awaiting_row_loads": awaiting, "distinct_cus": int(len(per_cu)),
             "blocks_per_cu": {"min": int(per_cu.min()), "max": int(per_cu.max())},
