@@ -273,27 +273,24 @@ int pick_swiglu(int64_t tokens, int64_t inter, int epi)
     // 1-6% faster than the row-chunked one at N = 3,584 (4,096 and 8,192
     // tokens) in the bf16, MXFP4, NVFP4 and per-group forms.
     if (flat_fits && njobs < 512) return swiglu_find(1, 8, 1);
-    // bf16 and MXFP4 output: one job per lane (the most blocks, each
-    // short-lived, so the blocks in flight stay on one contiguous stretch of
-    // memory).  Per-tensor E4M3 output, from about four million outputs: two
-    // jobs per lane, which gives the longer per-job arithmetic two loads in
-    // flight to hide behind.  NVFP4 and per-group E4M3 output (the most
-    // arithmetic per output): two jobs per lane from about 32 million
-    // outputs, when a row is a whole number of 512-job blocks; otherwise the
-    // last block of every row is mostly idle (N = 8,960 rows have 1,120
-    // jobs) and one job per lane measured about 10% faster for the per-group
-    // form at 8,960 and 14,336 wide, while two jobs measured 1-4% faster at
-    // 28,672 wide from 2,048 tokens.
-    // On rows that are not whole 512-job blocks, the two-job grid leaves the
-    // last block of every row partly idle (27% of its lanes at N = 8,960),
-    // and the flat grid (blocks of 256 jobs over the rows laid end to end)
-    // measured 2-17% faster from 512 tokens at N = 2,560-14,336; on whole
-    // 512-job rows (N = 28,672) and on rows of 256 jobs two jobs per lane
-    // are as fast or faster.
+    // bf16, MXFP4 and per-group E4M3 output: one job per lane on the
+    // row-chunked grid (the most blocks, each short-lived, so the blocks in
+    // flight stay on one contiguous stretch of memory; per-group E4M3 with
+    // two jobs per lane on whole 512-job rows measured 1-2% slower from 8,192
+    // tokens of 28,672).  Per-tensor E4M3 output, from about four million
+    // outputs: the flat grid, one job per lane and no lane idle at a row's
+    // end.  Against two jobs per lane (which gives the longer per-job
+    // arithmetic two loads in flight) it measured 2-17% faster from 512
+    // tokens on rows that are not whole 512-job blocks (N = 2,560-14,336,
+    // where two jobs leave up to 27% of the last block's lanes idle), and
+    // on whole 512-job rows (N = 28,672) tied or won at 8,192 tokens on
+    // three boxes (up to 4.1%) and at 16,384 (5%), within 1.4% either way at
+    // 4,096; on rows of exactly 256 jobs two jobs per lane are faster.
+    // NVFP4 output (the most arithmetic per output): two jobs per lane from
+    // about 32 million outputs on rows of whole 512-job blocks.
     if (epi == SWIGLU_EPI_FP8 && tokens > kSwigluFp8TwoJobOutputs / inter)
-        return (flat_fits && njobs % 512 != 0) ? swiglu_find(1, 8, 1) : swiglu_find(2, 8);
-    if ((epi == SWIGLU_EPI_NVFP4 || epi == SWIGLU_EPI_FP8_GROUP) && tokens > kSwigluNvfp4TwoJobOutputs / inter &&
-        (inter / 8) % 512 == 0)
+        return flat_fits ? swiglu_find(1, 8, 1) : swiglu_find(2, 8);
+    if (epi == SWIGLU_EPI_NVFP4 && tokens > kSwigluNvfp4TwoJobOutputs / inter && (inter / 8) % 512 == 0)
         return swiglu_find(2, 8);
     return swiglu_find(1, 8);
 }
