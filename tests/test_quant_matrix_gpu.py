@@ -801,3 +801,26 @@ def test_large_random_shapes_every_swiglu_form(T, N):
         q, sc = A.swiglu_quant_fp8_group(gt)
         P.check_swiglu_fp8_group(gu, bits(q), bits(sc))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,H", [(256, 16384), (512, 16384), (1024, 4096)])
+def test_fused_quant_forms_one_generation_late_residual(T, H):
+    """Launches whose blocks are all resident at once and that read 12 MB or
+    more: there the quantised forms store the updated residual in the
+    epilogue, after its last use, instead of right after the add.  Every
+    quantised form with the residual add, default variant, against the
+    oracle (residual bit-exact, codes and scales to the usual bar)."""
+    x, r, w = norm_case(T, H, seed=T + H, outliers=0.001)
+    eps = 1e-5
+    announce("fused_add_rmsnorm_quant_fp8 one generation", (T, H))
+    q, s, ro = A.fused_add_rmsnorm_quant_fp8(bf16(x), bf16(r), bf16(w), eps)
+    torch.cuda.synchronize()
+    P.check_norm_fp8(x, r, w, eps, bits(q), bits(s), bits(ro))
+    q, ro = run_fused_static(x, r, w, eps, 0.02)
+    P.check_norm_fp8_static(x, r, w, eps, 0.02, q, ro)
+    q, s, ro = run_fused_mx(x, r, w, eps)
+    P.check_norm_mxfp4(x, r, w, eps, q, s, ro)
+    q, s, ro = run_fused_nv(x, r, w, eps, 0.02)
+    P.check_norm_nvfp4(x, r, w, eps, 0.02, q, s, ro)
+    q, s, ro = run_fused_grp(x, r, w, eps)
+    P.check_norm_fp8_group(x, r, w, eps, q, s, ro)
