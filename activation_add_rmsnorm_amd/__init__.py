@@ -25,7 +25,7 @@ __all__ = [
     "fused_add_rmsnorm_quant_mxfp4", "rmsnorm_quant_mxfp4",
     "fused_add_rmsnorm_quant_nvfp4", "rmsnorm_quant_nvfp4", "swiglu_quant_nvfp4",
     "swiglu", "swiglu_quant_fp8", "swiglu_quant_fp8_dynamic", "swiglu_quant_mxfp4",
-    "variant_count", "variant_name", "pick_variant",
+    "variant_count", "variant_name", "variant_fits", "pick_variant",
     "OP_NORM", "OP_SWIGLU", "OP_SWIGLU_DYNAMIC", "OP_RMSNORM",
 ]
 
@@ -117,6 +117,7 @@ def load():
             "swiglu_quant_fp8_group_ex": [vp, vp, vp, i64, i64, i32, vp],
             "aarms_variant_count": [i32],
             "aarms_pick_variant": [i32, i64, i64, i32],
+            "aarms_variant_fits": [i32, i32, i64],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -622,6 +623,12 @@ def variant_count(op: int) -> int:
 def variant_name(op: int, variant: int) -> str | None:
     s = load().aarms_variant_name(int(op), int(variant))
     return s.decode() if s else None
+
+
+def variant_fits(op: int, variant: int, width: int) -> bool:
+    """Whether the variant runs rows of `width` values (the library's own
+    check: capacity, and a multiple of 512 for the resident-row norms)."""
+    return bool(load().aarms_variant_fits(int(op), int(variant), int(width)))
 
 
 def pick_variant(op: int, tokens: int, width: int, quant: int | bool = False) -> int:

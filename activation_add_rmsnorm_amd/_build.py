@@ -32,7 +32,7 @@ REFCOPY_PATH = os.path.join(PKG, "libaarms_refcopy.so")
 STAMPS_PATH = os.path.join(PKG, "libaarms_stamps.so")
 ARCH = os.environ.get("AARMS_OFFLOAD_ARCH", "gfx950")
 
-HIP_SOURCES = ["norm.hip", "swiglu.hip"]
+HIP_SOURCES = ["norm.hip", "norm_resident.hip", "swiglu.hip"]
 HOST_SOURCES = ["capi.cpp"]
 REFCOPY_SOURCES = ["refcopy.hip"]
 
@@ -94,12 +94,14 @@ def build(verbose: bool = False) -> str:
     jobs = [[hipcc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, s), "-o", obj(s)]
             for s in HIP_SOURCES + REFCOPY_SOURCES]
     jobs += [[hipcc, *COMMON, "-c", os.path.join(CSRC, s), "-o", obj(s)] for s in HOST_SOURCES]
-    jobs += [[hipcc, *COMMON, *DEVICE, *stamps, "-c", os.path.join(CSRC, "norm.hip"), "-o", sobj("norm.hip")],
-             [hipcc, *COMMON, *stamps, "-c", os.path.join(CSRC, "capi.cpp"), "-o", sobj("capi.cpp")]]
+    jobs += [[hipcc, *COMMON, *DEVICE, *stamps, "-c", os.path.join(CSRC, s), "-o", sobj(s)]
+             for s in ("norm.hip", "norm_resident.hip")]
+    jobs += [[hipcc, *COMMON, *stamps, "-c", os.path.join(CSRC, "capi.cpp"), "-o", sobj("capi.cpp")]]
     _run(jobs, verbose)
     _link(hipcc, [obj(s) for s in HIP_SOURCES + HOST_SOURCES], LIB_PATH)
     _link(hipcc, [obj(s) for s in REFCOPY_SOURCES], REFCOPY_PATH)
-    _link(hipcc, [sobj("norm.hip"), obj("swiglu.hip"), sobj("capi.cpp")], STAMPS_PATH)
+    _link(hipcc, [sobj("norm.hip"), sobj("norm_resident.hip"), obj("swiglu.hip"), sobj("capi.cpp")],
+          STAMPS_PATH)
     return LIB_PATH
 
 

@@ -98,6 +98,15 @@ int device_cus()
 
 int norm_capacity(const NormVariant *v) { return v->waves_per_row * 64 * v->vecs_per_lane * 8; }
 
+// Whether variant v runs rows of `hidden` values: wide enough, and for the
+// resident-row kernels a width that is a multiple of 512 (whole 64-slice
+// chunks of the row, which the weight's LDS transfer moves per wave).
+bool norm_fits(const NormVariant *v, int64_t hidden)
+{
+    if (!v || hidden <= 0 || norm_capacity(v) < hidden) return false;
+    return v->blocks_per_cu >= 0 || hidden % NORM_RESIDENT_WIDTH_MULTIPLE == 0;
+}
+
 // One-shot variant with `waves` waves per row that fits the row with the
 // fewest vectors per lane, if that is at most max_vecs; else -1.
 static int norm_fit(int waves, int64_t hidden, int max_vecs)
@@ -217,6 +226,25 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
     if (!residual && hidden > 2048 && hidden <= 4096 && tokens < kNarrowMultiWaveTokens) {
         const int i = norm_fit(4, hidden, 2);
         if (i >= 0) return i;
+    }
+    // Per-token E4M3 with the residual add on rows of 12,289-16,384
+    // (multiples of 512) in batches whose four-row blocks fill 0.8-1 or
+    // 1.75-2 blocks per CU: the resident rows (one wave per row, the batch one
+    // generation of blocks) measured 3-11% faster at 832-1,024 tokens and
+    // 1.5-6% at 1,792-2,048 than the split rows below (16,384 wide, 256 CUs);
+    // between the two bands the CUs holding two blocks set the pace and the
+    // split rows win.
+    if (epi == NORM_EPI_FP8_DYNAMIC && residual && hidden > 12288 && hidden <= NORM_RESIDENT_MAX_HIDDEN &&
+        hidden % NORM_RESIDENT_WIDTH_MULTIPLE == 0) {
+        const int64_t blocks = (tokens + 3) / 4, cus = device_cus();
+        if (blocks * 5 >= cus * 4 && blocks <= cus) {
+            const int i = norm_find(1, 32, NORM_RESIDENT_Y_IN_PLACE);
+            if (i >= 0) return i;
+        }
+        if (blocks * 4 >= cus * 7 && blocks <= 2 * cus) {
+            const int i = norm_find(1, 32, NORM_RESIDENT);
+            if (i >= 0) return i;
+        }
     }
     if (epi == NORM_EPI_FP8_DYNAMIC && residual && hidden > 8192 && tokens <= kDynamicFp8FewWavesTokens) {
         const int i = norm_fit(8, hidden, 4);
@@ -380,7 +408,7 @@ int norm_common(void *out, float *scale_out, const float *scale_in, void *residu
     if ((st = check_outputs(outs, partner, n_out, ins, n_in))) return st;
     if (variant == -1) variant = pick_norm(tokens, hidden, epi, res);
     const NormVariant *v = norm_variant(variant);
-    if (!v || norm_capacity(v) < hidden) return AARMS_ERR_BAD_VARIANT;
+    if (!norm_fits(v, hidden)) return AARMS_ERR_BAD_VARIANT;
     NormParams p{};
     p.out = out;
     p.residual_out = res ? residual_out : nullptr;
@@ -789,6 +817,17 @@ int swiglu_quant_fp8_group_ex(void *out_fp8, float *scale_out, const void *gate_
 {
     return swiglu_common(out_fp8, gate_up, nullptr, (uint8_t *)scale_out, num_tokens, inter,
                          SWIGLU_EPI_FP8_GROUP, variant, stream);
+}
+
+int aarms_variant_fits(int op, int variant, int64_t width)
+{
+    if (op == 0 || op == 3) return norm_fits(norm_variant(variant), width) ? 1 : 0;
+    if (op == 1) return swiglu_variant(variant) && width > 0 && width % 8 == 0 ? 1 : 0;
+    if (op == 2) {
+        const SwigluRowVariant *v = swiglu_row_variant(variant);
+        return v && width > 0 && width % 8 == 0 && rowq_capacity(v) >= width ? 1 : 0;
+    }
+    return 0;
 }
 
 int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant)

@@ -84,10 +84,19 @@ constexpr uint32_t SWIGLU_ROWS_PER_Y = 65535;
 struct NormVariant {
     int waves_per_row;
     int vecs_per_lane;
-    int blocks_per_cu;       // 0: one block per row (or row quartet); else a persistent,
-                             // software-pipelined grid of this many blocks per CU
+    int blocks_per_cu;       // 0: one block per row (or row quartet); > 0: a persistent,
+                             // software-pipelined grid of this many blocks per CU; < 0: a
+                             // resident-row kernel (norm_resident.hip), NORM_RESIDENT_*
     const char *name;
 };
+
+// Resident-row kernels: one wave holds a row of up to 16,384 values in its
+// registers (rows a multiple of 512 wide).  Y_IN_PLACE: the per-token E4M3
+// form overwrites h with y in its amax pass (a narrower load window).
+constexpr int NORM_RESIDENT_Y_IN_PLACE = -1;
+constexpr int NORM_RESIDENT = -2;
+constexpr int NORM_RESIDENT_MAX_HIDDEN = 16384;
+constexpr int NORM_RESIDENT_WIDTH_MULTIPLE = 512;
 
 struct SwigluVariant {
     int jobs_per_lane;       // a block of 256 lanes covers 256 * jobs_per_lane jobs of one row
@@ -112,6 +121,7 @@ const SwigluVariant *swiglu_variant(int id);
 
 hipError_t launch_norm(const NormParams &p, int epi, bool residual, int variant, int num_cus,
                        hipStream_t stream);
+hipError_t launch_norm_resident(const NormParams &p, int epi, bool residual, int kind, hipStream_t stream);
 int swiglu_row_variant_count();
 const SwigluRowVariant *swiglu_row_variant(int id);
 hipError_t launch_swiglu(const SwigluParams &p, int epi, int variant, hipStream_t stream);

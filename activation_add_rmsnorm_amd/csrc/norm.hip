@@ -584,6 +584,9 @@ static const NormVariant kNormVariants[] = {
     {4, 4, 4, "4 waves/row x4 vec, pipelined 4 blocks/CU"},
     {16, 4, 1, "16 waves/row x4 vec, pipelined 1 block/CU"},
     {16, 8, 1, "16 waves/row x8 vec, pipelined 1 block/CU"},
+    // one wave holds the whole row (norm_resident.hip)
+    {1, 32, NORM_RESIDENT_Y_IN_PLACE, "wave/row x32 vec, resident, y in place"},
+    {1, 32, NORM_RESIDENT, "wave/row x32 vec, resident"},
 };
 constexpr int kNumNormVariants = sizeof(kNormVariants) / sizeof(kNormVariants[0]);
 static_assert(kNumNormVariants <= 64, "the occupancy cache holds 64 variants per form");
@@ -642,6 +645,7 @@ static hipError_t dispatch(const NormParams &p, int variant, int num_cus, hipStr
     const NormVariant *v = norm_variant(variant);
     if (!v) return hipErrorInvalidValue;
     const int b = v->blocks_per_cu;
+    if (b < 0) return launch_norm_resident(p, EPI, RES, b, s);
     const int slot = (EPI * 2 + (RES ? 1 : 0)) * 64 + variant;
 #define AARMS_NORM_CASE(W, V)                                                              \
     if (v->waves_per_row == W && v->vecs_per_lane == V)                                    \

@@ -1,0 +1,492 @@
+// norm_resident.hip -- RMSNorm (with or without the residual add in front)
+// and every output form of norm.hip, for wide rows whose whole batch fits on
+// the device at once: one wave holds one row in its registers from the first
+// load to the last store.
+//
+// A row of up to 16,384 bf16 values is 32 16-byte slices per lane (128
+// VGPRs), so with 256 VGPRs per wave two waves fit per SIMD and a 256-thread
+// block (four rows) fits twice per CU: 2,048 rows of 16,384 on 256 CUs are
+// one generation of blocks.  In the one-shot kernels of norm.hip a wide row
+// is split over 8-16 waves and a batch of that size is four generations,
+// whose end (the last blocks, each ~8 us long, draining with nothing to
+// replace them) costs ~10% of the launch.  Here every load is issued in the
+// first microseconds, rows finish loading between ~10 and ~25 us, and each
+// row's writes follow its own reductions.
+//
+// Per wave: the x (and residual) slices stream in through a window of WIN
+// slices in flight (a slice is consumed, its add and sum of squares done, and
+// the next one issued), so the row never needs more registers than the row
+// itself plus the window.  The weight (shared by the block's four rows) goes
+// straight from memory into LDS at the start (LDS DMA: no registers) and is
+// read back per slice after the row statistics.  The row sum needs no
+// barrier (one wave per row); the only block barrier makes the weight
+// visible.  Loads go through buffer resources (one per row and tensor: a
+// scalar base and length; the lane passes a 32-bit offset, so no vector
+// registers hold 64-bit addresses, and slices past the row end read zero).
+// Stores use a scalar base plus the lane's 32-bit offset (global_store with
+// saddr); buffer stores with an SGPR offset were not used, since the
+// compiler inserts no wait state between such a 16-byte store and a VALU
+// write of its data registers, and that lost data here.
+//
+// The arithmetic is the one of norm.hip (same roundings, same binary64 sum of
+// squares in four chains, the same epilogues), so the outputs are the same
+// bits; only the order of the row sum's partial sums differs, which the
+// binary64 accumulation makes immaterial for the binary32 mean.
+//
+// The eight-operation RMSNorm with the residual add in front follows
+// "TensorRT-LLM: Compiling Inference Engines Ahead of Time" (section
+// "Fusing operations, measured"); the FP8 epilogues follow vLLM's RMSNorm +
+// quant fusion ("Introduction to torch.compile and How It Works with vLLM",
+// section 4).
+
+#include "device.h"
+#include "launch.h"
+
+namespace aarms {
+
+namespace {
+
+constexpr int RES_VPT = 32;        // 16-byte slices per lane: rows up to 16,384
+constexpr int RES_ROWS = 4;        // rows (waves) per 256-thread block
+
+// Loads through a buffer resource of one row: base address and length in
+// bytes (0 for a wave past the last row: its loads read zero without
+// touching memory).  Word 3 selects raw 32-bit access on gfx9-family parts.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc row_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes at voff + soff, streaming (non-temporal) hint
+__device__ __forceinline__ u32x4 ld_slice(Rsrc r, uint32_t voff, int soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 2);
+}
+
+// Streaming store of v at base + byte_off (uniform: kept in scalar
+// registers) + lane_off (the lane's 32-bit byte offset).
+template <typename T>
+__device__ __forceinline__ void st_at(const void *base, uint32_t byte_off, uint32_t lane_off, T v)
+{
+    typedef __attribute__((address_space(1))) char gchar;
+    typedef __attribute__((address_space(1))) T gT;
+    const uint64_t b = (uint64_t)base + byte_off;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    gchar *u = (gchar *)(((uint64_t)hi << 32) | lo);
+    __builtin_nontemporal_store(v, (gT *)(u + lane_off));
+}
+
+// y = bf16(w * bf16(h * rs)) for the two bf16 of one word, with the binary32
+// products p0, p1 before their rounding (maxima are taken on them and
+// rounded once: rounding to nearest is monotone and symmetric).
+__device__ __forceinline__ uint32_t norm_pair(uint32_t h, uint32_t w, float rs, float &p0, float &p1)
+{
+    const uint32_t t = pack_bf16(bf_lo(h) * rs, bf_hi(h) * rs);
+    p0 = bf_lo(w) * bf_lo(t);
+    p1 = bf_hi(w) * bf_hi(t);
+    return pack_bf16(p0, p1);
+}
+__device__ __forceinline__ uint32_t norm_pair(uint32_t h, uint32_t w, float rs)
+{
+    float p0, p1;
+    return norm_pair(h, w, rs, p0, p1);
+}
+
+#ifdef AARMS_PHASE_STAMPS
+// Measurement build: lane 0 of the row's wave records the real-time clock at
+// slot k (0 start, 1 row loads consumed, 2 wave sum, 3 weight in LDS, 4 row
+// amax of the per-token form, 5 its wave maximum, 7 last store issued; 8 and
+// 9 the HW_ID and XCC_ID registers), the layout of norm.hip's one-shot kernel
+// with one wave per row.
+__device__ __forceinline__ uint64_t res_stamp_after(float dep)
+{
+    asm volatile("" : : "v"(dep));
+    return __builtin_amdgcn_s_memrealtime();
+}
+#define RES_STAMP(k, dep)                                                                          \
+    do {                                                                                           \
+        if (p.stamps) {                                                                            \
+            const uint64_t t_ = res_stamp_after(dep);                                              \
+            if (lane == 0) p.stamps[(size_t)row * 16 + (k)] = t_;                                  \
+        }                                                                                          \
+    } while (0)
+#else
+#define RES_STAMP(k, dep) do {} while (0)
+#endif
+
+// One row per wave, four rows per block.  WIN: residual slices in flight per
+// lane during the first pass.  Y_IN_PLACE (per-token E4M3 only): the amax
+// pass stores the updated residual and overwrites each slice of h with y, so
+// the quantizing pass has no normalization to redo (fewer instructions, but
+// the residual's writes start while other rows still load); otherwise the
+// quantizing pass recomputes y from h and the weight and stores the residual
+// with the codes.
+template <int EPI, bool RES, int WIN, bool Y_IN_PLACE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+norm_kernel_resident(NormParams p)
+{
+    constexpr int VPT = RES_VPT;
+    __shared__ u32x4 wl[VPT * 64];
+    __shared__ float nv_inv[EPI == NORM_EPI_NVFP4 ? 128 : 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int64_t row = (int64_t)blockIdx.x * RES_ROWS + __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool live = row < p.tokens;
+    const int nvec = p.hidden >> 3;                   // a multiple of 64 (hidden % 512 == 0)
+    const int nk = nvec >> 6;                         // slices per lane inside the row
+    const uint32_t rb = (uint32_t)p.hidden * 2u;      // bytes of a bf16 row
+    const uint32_t lo = (uint32_t)lane * 16u;         // the lane's offset in a 1 KB stripe
+    if (live) RES_STAMP(0, 0.0f);
+
+    // NVFP4: the table of block-scale reciprocals (it has its own barrier,
+    // which every thread reaches)
+    if constexpr (EPI == NORM_EPI_NVFP4) {
+        const float g = *p.scale_in;
+        if (tid < 127)
+            nv_inv[tid] = nv_block_inverse((uint32_t)tid, nv_tensor_scale(g));
+        else if (tid == 127)
+            nv_inv[127] = nv_six_inverse(g);
+        __syncthreads();
+    }
+
+    // the weight into LDS: each wave moves 64-slice chunks (slot c + lane)
+    {
+        typedef __attribute__((address_space(3))) void lds_void;
+        const u32x4 *wg = (const u32x4 *)p.weight;
+#pragma unroll
+        for (int i = 0; i < VPT / RES_ROWS; ++i) {
+            const int c = (tid & ~63) + 256 * i;
+            if (c < nvec)
+                __builtin_amdgcn_global_load_lds((const void *)(wg + c + lane), (lds_void *)(wl + c), 16, 0, 0);
+        }
+    }
+
+    // ---- first pass: x (+ residual) through a window of WIN slices in
+    // flight, the add, and the sum of squares in binary64
+    const size_t base = (size_t)(live ? row : 0) * (size_t)p.hidden;
+    const Rsrc rx = row_rsrc((const uint16_t *)p.x + base, live ? rb : 0u);
+    u32x4 h[VPT];
+    double acc4[4] = {0.0, 0.0, 0.0, 0.0};
+    const Rsrc rr = row_rsrc(RES ? (const uint16_t *)p.residual + base : nullptr, RES && live ? rb : 0u);
+    u32x4 rw[RES ? WIN : 1];
+#pragma unroll
+    for (int k = 0; k < WIN; ++k) {
+        h[k] = ld_slice(rx, lo, k * 1024);
+        if constexpr (RES) rw[k] = ld_slice(rr, lo, k * 1024);
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        if constexpr (RES) {
+            const u32x4 r = rw[k % WIN];
+            u32x4 s;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                s[e] = pack_bf16(bf_lo(h[k][e]) + bf_lo(r[e]), bf_hi(h[k][e]) + bf_hi(r[e]));
+            h[k] = s;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float h0 = bf_lo(h[k][e]), h1 = bf_hi(h[k][e]);
+            acc4[e] = __builtin_fma((double)h0, (double)h0, acc4[e]);
+            acc4[e] = __builtin_fma((double)h1, (double)h1, acc4[e]);
+        }
+        if (k + WIN < VPT) {
+            h[k + WIN] = ld_slice(rx, lo, (k + WIN) * 1024);
+            if constexpr (RES) rw[k % WIN] = ld_slice(rr, lo, (k + WIN) * 1024);
+        }
+        // keep the loads where they are: one slice (pair) issued per slice consumed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // the row as packed words from here on: the compiler must not keep the
+    // first pass's widened values alive into the epilogue (twice the registers)
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) asm volatile("" : "+v"(h[k]));
+    double acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    if (live) RES_STAMP(1, (float)acc);
+    acc = wave_sum(acc);
+    if (live) RES_STAMP(2, (float)acc);
+
+    // ---- mean (rounded once to binary32), + eps, reciprocal square root
+    float mean;
+    if (acc <= __DBL_MAX__)
+        mean = row_mean(acc, (double)p.hidden, p.inv_hidden);
+    else
+        mean = (float)(acc / (double)p.hidden);
+    const float var = mean + p.eps;
+    float rs;
+    if (row_rsqrt_in_range(var))
+        rs = row_rsqrt(var);
+    else
+        rs = (float)(1.0 / sqrt((double)var));
+
+    // the weight: this wave's LDS DMA is done (vmcnt 0: its row loads were
+    // consumed above, so nothing else is waited for); the barrier makes the
+    // other waves' chunks visible
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (!live) return;
+    RES_STAMP(3, rs);
+
+    const void *ro = RES ? (const void *)((uint16_t *)p.residual_out + base) : nullptr;
+
+    if constexpr (EPI == NORM_EPI_FP8_DYNAMIC) {
+        // ---- row amax (from the products, rounded once)
+        float amax = 0.0f;
+        u32x4 wn = wl[lane];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            if (k < nk) {
+                const u32x4 w = wn;
+                if (k + 1 < VPT) wn = wl[lane + 64 * (k + 1)];
+                u32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float p0, p1;
+                    y[e] = norm_pair(h[k][e], w[e], rs, p0, p1);
+                    amax = fmaxf(amax, fmaxf(__builtin_fabsf(p0), __builtin_fabsf(p1)));
+                }
+                if constexpr (Y_IN_PLACE) {
+                    if constexpr (RES) st_at(ro, k * 1024, lo, h[k]);
+                    h[k] = y;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if constexpr (Y_IN_PLACE) {
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) asm volatile("" : "+v"(h[k]));
+        }
+        amax = round_bf16(amax);
+        RES_STAMP(4, amax);
+        amax = wave_max(amax);
+        RES_STAMP(5, amax);
+        // ---- per-token scale, then q = e4m3(y / s); |y| <= amax, no clamp
+        const float s = amax / 448.0f;
+        if (lane == 0) p.scale_out[row] = s;
+        const E4m3Scale qs = make_e4m3_scale(s);
+        const bool fast = e4m3_scale_is_fast(qs);
+        const void *qo = (const uint8_t *)p.out + base;
+        const uint32_t qlo = (uint32_t)lane * 8u;
+        // a second pass over the row: the compiler must not carry the first
+        // pass's products across it (they would not fit in registers)
+        float rs2 = rs;
+        asm volatile("" : "+v"(rs2) : : "memory");
+        wn = wl[lane];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            if (k < nk) {
+                u32x4 y;
+                if constexpr (Y_IN_PLACE) {
+                    y = h[k];
+                } else {
+                    const u32x4 w = wn;
+                    if (k + 1 < VPT) wn = wl[lane + 64 * (k + 1)];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = norm_pair(h[k][e], w[e], rs2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                float z[8];
+                if (fast) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        z[2 * e] = e4m3_quotient<true, false>(bf_lo(y[e]), qs);
+                        z[2 * e + 1] = e4m3_quotient<true, false>(bf_hi(y[e]), qs);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        z[2 * e] = e4m3_quotient<false, false>(bf_lo(y[e]), qs);
+                        z[2 * e + 1] = e4m3_quotient<false, false>(bf_hi(y[e]), qs);
+                    }
+                }
+                if constexpr (RES && !Y_IN_PLACE) st_at(ro, k * 1024, lo, h[k]);
+                u32x2 q;
+                q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+                q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
+                st_at(qo, k * 512, qlo, q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+        // ---- one pass: y, the form's block maxima and codes, the stores
+        E4m3Scale qs_static{};
+        bool fast_static = false;
+        if constexpr (EPI == NORM_EPI_FP8_STATIC) {
+            qs_static = make_e4m3_scale(*p.scale_in);
+            fast_static = e4m3_scale_is_fast(qs_static);
+        }
+        Nvfp4Tensor nt{};
+        if constexpr (EPI == NORM_EPI_NVFP4) nt = make_nvfp4_tensor(*p.scale_in, nv_inv[127]);
+        u32x4 wn = wl[lane];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            if (k < nk) {
+                const u32x4 w = wn;
+                if (k + 1 < VPT) wn = wl[lane + 64 * (k + 1)];
+                if constexpr (EPI == NORM_EPI_BF16) {
+                    u32x4 y;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = norm_pair(h[k][e], w[e], rs);
+                    st_at((const uint16_t *)p.out + base, k * 1024, lo, y);
+                } else if constexpr (EPI == NORM_EPI_FP8_STATIC) {
+                    float z[8];
+                    if (fast_static) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t y = norm_pair(h[k][e], w[e], rs);
+                            z[2 * e] = e4m3_quotient<true, true>(bf_lo(y), qs_static);
+                            z[2 * e + 1] = e4m3_quotient<true, true>(bf_hi(y), qs_static);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t y = norm_pair(h[k][e], w[e], rs);
+                            z[2 * e] = e4m3_quotient<false, true>(bf_lo(y), qs_static);
+                            z[2 * e + 1] = e4m3_quotient<false, true>(bf_hi(y), qs_static);
+                        }
+                    }
+                    u32x2 q;
+                    q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+                    q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
+                    st_at((const uint8_t *)p.out + base, k * 512, (uint32_t)lane * 8u, q);
+                } else if constexpr (EPI == NORM_EPI_FP8_GROUP) {
+                    // a 128-value group is the slices of 16 adjacent lanes
+                    float yf[8];
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float p0, p1;
+                        const uint32_t y = norm_pair(h[k][e], w[e], rs, p0, p1);
+                        yf[2 * e] = bf_lo(y);
+                        yf[2 * e + 1] = bf_hi(y);
+                        amax = fmaxf(amax, fmaxf(__builtin_fabsf(p0), __builtin_fabsf(p1)));
+                    }
+                    amax = group_max<16>(round_bf16(amax));
+                    const float s = amax / 448.0f;
+                    if ((lane & 15) == 0)
+                        st_at(p.scale_out + (size_t)row * (size_t)(p.hidden / FP8_GROUP), k * 16,
+                              (uint32_t)(lane >> 4) * 4u, s);
+                    const E4m3Scale qs = make_e4m3_scale(s);
+                    float z[8];
+                    // |y| <= amax, so |y / s| <= 448 (1 + 2^-24): no input clamp
+                    if (e4m3_scale_is_fast(qs)) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) z[j] = e4m3_quotient<true, false>(yf[j], qs);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) z[j] = e4m3_quotient<false, false>(yf[j], qs);
+                    }
+                    u32x2 q;
+                    q[0] = pack_e4m3x4(z[0], z[1], z[2], z[3]);
+                    q[1] = pack_e4m3x4(z[4], z[5], z[6], z[7]);
+                    st_at((const uint8_t *)p.out + base, k * 512, (uint32_t)lane * 8u, q);
+                } else if constexpr (EPI == NORM_EPI_MXFP4) {
+                    // a 32-value block is the slices of 4 adjacent lanes; NaN-
+                    // propagating maxima, so a block holding a NaN gets the NaN scale
+                    uint32_t y[4];
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float p0, p1;
+                        y[e] = norm_pair(h[k][e], w[e], rs, p0, p1);
+                        amax = __builtin_elementwise_maximum(
+                            amax, __builtin_elementwise_maximum(__builtin_fabsf(p0), __builtin_fabsf(p1)));
+                    }
+                    uint32_t mag = __float_as_uint(round_bf16(amax));
+                    mag = max(mag, dpp_u32<DPP_XOR1>(mag));
+                    mag = max(mag, dpp_u32<DPP_XOR2>(mag));
+                    const uint32_t sb = mx_scale_byte(mag);
+                    const float inv = __uint_as_float((254u - (sb == 0xFFu ? 127u : sb)) << 23);
+                    const uint32_t q = (sb == 0xFFu) ? 0u : pack_e2m1x8(y, inv);
+                    const size_t qrow = (size_t)row * (size_t)(p.hidden / 2);
+                    st_at((const uint8_t *)p.out + qrow, k * 256, (uint32_t)lane * 4u, q);
+                    if ((lane & 3) == 0)
+                        st_at((const uint8_t *)p.scale_out + (size_t)row * (size_t)(p.hidden / 32), k * 16,
+                              (uint32_t)(lane >> 2), (uint8_t)sb);
+                } else if constexpr (EPI == NORM_EPI_NVFP4) {
+                    // a 16-value block is the slices of 2 adjacent lanes
+                    uint32_t y[4];
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float p0, p1;
+                        y[e] = norm_pair(h[k][e], w[e], rs, p0, p1);
+                        amax = __builtin_elementwise_maximum(
+                            amax, __builtin_elementwise_maximum(__builtin_fabsf(p0), __builtin_fabsf(p1)));
+                    }
+                    uint32_t mag = __float_as_uint(round_bf16(amax));
+                    mag = max(mag, dpp_u32<DPP_XOR1>(mag));
+                    const uint32_t sb = nv_scale_byte(mag, nt);
+                    const uint32_t q = (sb == 0x7Fu) ? 0u : pack_nvfp4<4>(y, sb, nt, nv_inv[sb]);
+                    const size_t qrow = (size_t)row * (size_t)(p.hidden / 2);
+                    st_at((const uint8_t *)p.out + qrow, k * 256, (uint32_t)lane * 4u, q);
+                    if ((lane & 1) == 0)
+                        st_at((const uint8_t *)p.scale_out + (size_t)row * (size_t)(p.hidden / 16), k * 32,
+                              (uint32_t)(lane >> 1), (uint8_t)sb);
+                }
+                if constexpr (RES) st_at(ro, k * 1024, lo, h[k]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    RES_STAMP(7, 0.0f);
+#ifdef AARMS_PHASE_STAMPS
+    if (p.stamps && lane == 0) {
+        uint64_t *st = p.stamps + (size_t)row * 16;
+        st[8] = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID
+        st[9] = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID
+    }
+#endif
+}
+
+template <int EPI, bool RES>
+hipError_t launch_kind(const NormParams &p, int kind, hipStream_t stream)
+{
+    NormParams copy = p;
+    void *args[] = {&copy};
+    // the per-token form with y kept in place takes a narrower window (the
+    // amax pass holds more registers); every other kind takes 10 slices
+    const void *fn = (const void *)&norm_kernel_resident<EPI, RES, 10, false>;
+    if (kind == NORM_RESIDENT_Y_IN_PLACE) {
+        if constexpr (EPI == NORM_EPI_FP8_DYNAMIC)
+            fn = (const void *)&norm_kernel_resident<EPI, RES, 6, true>;
+        else
+            fn = (const void *)&norm_kernel_resident<EPI, RES, 6, false>;
+    }
+    const int64_t blocks = (p.tokens + RES_ROWS - 1) / RES_ROWS;
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_norm_resident(const NormParams &p, int epi, bool residual, int kind, hipStream_t stream)
+{
+    if (p.hidden > RES_VPT * 512 || p.hidden % 512 != 0) return hipErrorInvalidValue;
+    switch (epi) {
+    case NORM_EPI_BF16:
+        return residual ? launch_kind<NORM_EPI_BF16, true>(p, kind, stream)
+                        : launch_kind<NORM_EPI_BF16, false>(p, kind, stream);
+    case NORM_EPI_FP8_DYNAMIC:
+        return residual ? launch_kind<NORM_EPI_FP8_DYNAMIC, true>(p, kind, stream)
+                        : launch_kind<NORM_EPI_FP8_DYNAMIC, false>(p, kind, stream);
+    case NORM_EPI_FP8_STATIC:
+        return residual ? launch_kind<NORM_EPI_FP8_STATIC, true>(p, kind, stream)
+                        : launch_kind<NORM_EPI_FP8_STATIC, false>(p, kind, stream);
+    case NORM_EPI_MXFP4:
+        return residual ? launch_kind<NORM_EPI_MXFP4, true>(p, kind, stream)
+                        : launch_kind<NORM_EPI_MXFP4, false>(p, kind, stream);
+    case NORM_EPI_NVFP4:
+        return residual ? launch_kind<NORM_EPI_NVFP4, true>(p, kind, stream)
+                        : launch_kind<NORM_EPI_NVFP4, false>(p, kind, stream);
+    case NORM_EPI_FP8_GROUP:
+        return residual ? launch_kind<NORM_EPI_FP8_GROUP, true>(p, kind, stream)
+                        : launch_kind<NORM_EPI_FP8_GROUP, false>(p, kind, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace aarms

@@ -92,17 +92,7 @@ def clear() -> None:
 
 def variants_fitting(form: str, width: int):
     op, _ = FORMS[form]
-    out = []
-    for v in range(A.variant_count(op)):
-        name = A.variant_name(op, v)
-        if op == A.OP_SWIGLU:
-            out.append(v)                       # any width that is a multiple of 8
-            continue
-        waves = 1 if name.startswith("wave/row") else int(name.split()[0])
-        per_lane = int(name.split("x")[-1].split()[0])
-        if waves * 64 * per_lane * 8 >= width:
-            out.append(v)
-    return out
+    return [v for v in range(A.variant_count(op)) if A.variant_fits(op, v, width)]
 
 
 def _buffers(form: str, tokens: int, width: int, device):

@@ -352,10 +352,15 @@ int swiglu_quant_fp8_group(void *out_fp8, float *scale_out, const void *gate_up,
  * is returned for a format code outside these.
  * aarms_pick_variant() returns the id the plain entry point would use, or -1
  * for an unsupported shape.  Variant -1 in an *_ex call means "pick".
+ * aarms_variant_fits() returns 1 if the variant runs rows of `width` values
+ * (hidden for the norms, inter for the SwiGLU ops), 0 if an *_ex call with it
+ * would return AARMS_ERR_BAD_VARIANT for that width (too narrow, or, for the
+ * norm variants named "resident", a width that is not a multiple of 512).
  */
 int aarms_variant_count(int op);
 const char *aarms_variant_name(int op, int variant);
 int aarms_pick_variant(int op, int64_t num_tokens, int64_t width, int quant);
+int aarms_variant_fits(int op, int variant, int64_t width);
 
 int fused_add_rmsnorm_ex(void *out, void *residual_out,
                          const void *x, const void *residual, const void *weight,

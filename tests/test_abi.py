@@ -156,6 +156,29 @@ def test_norm_variant_checks():
     narrow = [i for i in range(n) if "wave/row x1" in A.variant_name(A.OP_NORM, i)][0]
     assert lib.fused_add_rmsnorm_ex(*args, 4, 1536, 1e-6, narrow, None) == VARIANT
     assert A.variant_name(A.OP_NORM, n) is None
+    # the resident-row variants: rows up to 16,384 wide, multiples of 512
+    resident = [i for i in range(n) if "resident" in A.variant_name(A.OP_NORM, i)]
+    assert len(resident) == 2
+    for i in resident:
+        for H, ok in ((512, True), (1536, True), (16384, True), (12800, True), (1544, False),
+                      (16376, False), (16896, False), (8, False)):
+            assert A.variant_fits(A.OP_NORM, i, H) == ok, (i, H)
+            assert A.variant_fits(A.OP_RMSNORM, i, H) == ok, (i, H)
+        assert lib.fused_add_rmsnorm_ex(*args, 4, 1544, 1e-6, i, None) == VARIANT
+        assert lib.fused_add_rmsnorm_quant_fp8_ex(P, P + BIG, P + 2 * BIG, P + 3 * BIG, P + 4 * BIG,
+                                                  P + 5 * BIG, 4, 16376, 1e-6, i, None) == VARIANT
+    # the fit query agrees with the capacity rule everywhere else
+    for i in range(n):
+        name = A.variant_name(A.OP_NORM, i)
+        w = 1 if name.startswith("wave/row") else int(name.split()[0])
+        cap = w * 64 * int(name.split("x")[-1].split()[0]) * 8
+        for H in (8, 1536, 4096, 4104, 16384, 65536):
+            expect = cap >= H and ("resident" not in name or H % 512 == 0)
+            assert A.variant_fits(A.OP_NORM, i, H) == expect, (name, H)
+    assert not A.variant_fits(A.OP_NORM, n, 1536) and not A.variant_fits(A.OP_NORM, -1, 1536)
+    assert not A.variant_fits(7, 0, 1536)
+    for v in range(A.variant_count(A.OP_SWIGLU)):
+        assert A.variant_fits(A.OP_SWIGLU, v, 8960) and not A.variant_fits(A.OP_SWIGLU, v, 12)
 
 
 # ----------------------------------------------------------------- the other norm forms
@@ -326,8 +349,21 @@ def test_pick_variant_ranges():
         assert nname(A.OP_NORM, 256, 16384, f) == "16 waves/row x2 vec"
     assert nname(A.OP_NORM, 256, 16384, 1) == "8 waves/row x4 vec"
     assert nname(A.OP_NORM, 1, 12288, 1) == "8 waves/row x4 vec"
-    assert nname(A.OP_NORM, 1024, 16384, 1) == "8 waves/row x4 vec"
-    assert nname(A.OP_NORM, 2048, 16384, 1) == "16 waves/row x2 vec"   # the 405B workload
+    assert nname(A.OP_NORM, 768, 16384, 1) == "8 waves/row x4 vec"
+    # per-token E4M3 with the residual, 12,289-16,384 wide (multiples of 512):
+    # resident rows at 0.8-1 and 1.75-2 four-row blocks per CU (256 CUs
+    # without a device), the split rows between and around
+    for T in (832, 1000, 1024):
+        assert nname(A.OP_NORM, T, 16384, 1) == "wave/row x32 vec, resident, y in place", T
+    for T in (1792, 2040, 2048):
+        assert nname(A.OP_NORM, T, 16384, 1) == "wave/row x32 vec, resident", T   # 2,048: the 405B workload
+    assert nname(A.OP_NORM, 2048, 12800, 1) == "wave/row x32 vec, resident"
+    assert nname(A.OP_NORM, 1536, 16384, 1) == nname(A.OP_NORM, 2049, 16384, 1) == "16 waves/row x2 vec"
+    assert nname(A.OP_NORM, 2048, 12288, 1) == nname(A.OP_NORM, 2048, 16376, 1) == "16 waves/row x2 vec"
+    for f in (0, 2, 3, 4, 5):
+        assert "resident" not in nname(A.OP_NORM, 2048, 16384, f), f
+        assert "resident" not in nname(A.OP_RMSNORM, 2048, 16384, f), f
+    assert "resident" not in nname(A.OP_RMSNORM, 2048, 16384, 1)
     assert nname(A.OP_NORM, 256, 8192, 1) == nname(A.OP_NORM, 256, 8192, 0) == "8 waves/row x2 vec"
     assert nname(A.OP_RMSNORM, 256, 16384, 1) == nname(A.OP_RMSNORM, 256, 16384, 0)
     for f in (-1, 6):

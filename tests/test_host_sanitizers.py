@@ -20,7 +20,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ROCM = "/opt/rocm"
 CSRC = os.path.join(ROOT, "activation_add_rmsnorm_amd", "csrc")
-OBJS = [os.path.join(ROOT, "_build", s + ".o") for s in ("norm.hip", "swiglu.hip")]
+OBJS = [os.path.join(ROOT, "_build", s + ".o") for s in ("norm.hip", "norm_resident.hip", "swiglu.hip")]
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 
 

@@ -311,3 +311,42 @@ def test_pipelined_variant_walks_rows_every_epilogue(v, name, w, vec, bpc):
     wt = gen.normal_bf16((H,), v, 3, mean=1.0, std=0.1)
     announce("norm forms", name, (T, H))
     _all_norm_forms(x, r, wt, 1e-5, 0.02, v)
+
+
+def _resident_variants():
+    return [(v, A.variant_name(A.OP_NORM, v)) for v in range(A.variant_count(A.OP_NORM))
+            if "resident" in A.variant_name(A.OP_NORM, v)]
+
+
+@pytest.mark.parametrize("T,H", [(37, 512), (5, 16384), (130, 12800), (300, 16384)])
+def test_resident_variants_every_epilogue(T, H):
+    """The resident-row kernels (one wave holds a whole row; four rows per
+    block) in every output format, with and without the residual add: rows
+    narrower than the 32 slices a lane can hold (whole slices past the row
+    end, 512 and 12,800 wide), waves past the last row (T not a multiple of
+    4), and more blocks than one per CU."""
+    x = gen.normal_bf16((T, H), T, 1, outlier_frac=0.001)
+    r = gen.normal_bf16((T, H), T, 2)
+    wt = gen.normal_bf16((H,), T, 3, mean=1.0, std=0.1)
+    for v, name in _resident_variants():
+        announce("norm forms", name, (T, H))
+        _all_norm_forms(x, r, wt, 1e-5, 0.02, v)
+
+
+@pytest.mark.parametrize("T", [1024, 2040])
+def test_resident_default_pick_per_token(T):
+    """Per-token E4M3 with the residual add where the library picks the
+    resident rows (about one and about two four-row blocks per CU), against
+    the oracle, with the Llama-405B norm's input recipe."""
+    H = 16384
+    name = A.variant_name(A.OP_NORM, A.pick_variant(A.OP_NORM, T, H, 1))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus == 256:
+        assert "resident" in name, name
+    x = gen.normal_bf16((T, H), T, 1, outlier_frac=0.001, outlier_mult=50.0)
+    r = gen.normal_bf16((T, H), T, 2)
+    wt = gen.normal_bf16((H,), T, 3, mean=1.0, std=0.1)
+    announce("fused_add_rmsnorm_quant_fp8 default", name, (T, H))
+    q, s, ro = A.fused_add_rmsnorm_quant_fp8(bf16(x), bf16(r), bf16(wt), 1e-5)
+    torch.cuda.synchronize()
+    P.check_norm_fp8(x, r, wt, 1e-5, bits(q), bits(s), bits(ro))

@@ -74,15 +74,7 @@ def run_swiglu_fp8(gu, scale, variant=-1):
 
 
 def norm_variants_for(H):
-    n = A.variant_count(A.OP_NORM)
-    out = []
-    for v in range(n):
-        name = A.variant_name(A.OP_NORM, v)
-        w = 1 if name.startswith("wave/row") else int(name.split()[0])
-        vec = int(name.split("x")[-1].split()[0])
-        if w * 64 * vec * 8 >= H:
-            out.append(v)
-    return out
+    return [v for v in range(A.variant_count(A.OP_NORM)) if A.variant_fits(A.OP_NORM, v, H)]
 
 
 # ------------------------------------------------------------------ library

@@ -46,14 +46,7 @@ def norm_case(T, H, seed=0, outliers=0.0, std=1.0):
 
 
 def variants_for(op, width):
-    out = []
-    for v in range(A.variant_count(op)):
-        name = A.variant_name(op, v)
-        waves = 1 if name.startswith("wave/row") else int(name.split()[0])
-        per_lane = int(name.split("x")[-1].split()[0])
-        if waves * 64 * per_lane * 8 >= width:
-            out.append(v)
-    return out
+    return [v for v in range(A.variant_count(op)) if A.variant_fits(op, v, width)]
 
 
 def run_rms(x, w, eps, variant=-1):
