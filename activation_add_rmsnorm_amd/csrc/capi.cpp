@@ -205,6 +205,29 @@ uint32_t norm_hold_ticks(int64_t tokens, int64_t hidden, int epi, bool res, cons
 int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
 {
     if (hidden <= 0 || hidden > AARMS_MAX_HIDDEN) return -1;
+    // Resident rows (one wave holds the row, the batch one generation of
+    // four-row blocks) on rows of 12,289-16,384 (multiples of 512) in batches
+    // that fill 0.8-1 or 1.75-2 blocks per CU.  Measured on MI355X (256 CUs)
+    // against the split rows, 16,384 wide: per-token E4M3 with the residual
+    // add 3-11% faster at 832-1,024 tokens and 1.5-9% at 1,792-2,048; bf16
+    // with the add 13-20% and 7-8.5%; per-tensor E4M3 with the add 15-17% and
+    // 5-10%; bf16 without it 4-11% and 5-8%.  Between the bands the CUs that
+    // hold two blocks set the pace and the split rows win (1,536 tokens: up
+    // to 4% slower resident); NVFP4, MXFP4, per-group E4M3 and the quantised
+    // forms without the add were as fast or faster split (their epilogues
+    // need more instructions per byte than two waves per SIMD can hide).  In
+    // the first band every form takes the 6-slice window; in the second the
+    // forms with the add take 10 slices.
+    if (hidden > 12288 && hidden <= NORM_RESIDENT_MAX_HIDDEN && hidden % NORM_RESIDENT_WIDTH_MULTIPLE == 0 &&
+        (epi == NORM_EPI_BF16 || (residual && (epi == NORM_EPI_FP8_DYNAMIC || epi == NORM_EPI_FP8_STATIC)))) {
+        const int64_t blocks = (tokens + 3) / 4, cus = device_cus();
+        const bool one = blocks * 5 >= cus * 4 && blocks <= cus;
+        const bool two = blocks * 4 >= cus * 7 && blocks <= 2 * cus;
+        if (one || two) {
+            const int i = norm_find(1, 32, (two && residual) ? NORM_RESIDENT : NORM_RESIDENT_Y_IN_PLACE);
+            if (i >= 0) return i;
+        }
+    }
     if (epi == NORM_EPI_BF16 && residual && hidden > 4096 && hidden <= 8192 &&
         tokens >= kPipelinedMinTokens && tokens <= kPipelinedMaxTokens) {
         const int i = norm_find(8, 2, 2);
@@ -213,7 +236,8 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
     // The same band without the residual add, on rows of 8,193-16,384 (8
     // waves of 4 vectors): the pipelined 8 x 4 grid measured 5-25% faster
     // from 512 to 2,048 tokens at 16,384 wide (bf16 only: the per-token E4M3
-    // form is slower pipelined).
+    // form is slower pipelined); the resident rows above take the batches
+    // they fit better.
     if (epi == NORM_EPI_BF16 && !residual && hidden > 8192 && hidden <= 16384 && tokens >= 512 &&
         tokens <= 2048) {
         const int i = norm_find(8, 4, 2);
@@ -226,25 +250,6 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
     if (!residual && hidden > 2048 && hidden <= 4096 && tokens < kNarrowMultiWaveTokens) {
         const int i = norm_fit(4, hidden, 2);
         if (i >= 0) return i;
-    }
-    // Per-token E4M3 with the residual add on rows of 12,289-16,384
-    // (multiples of 512) in batches whose four-row blocks fill 0.8-1 or
-    // 1.75-2 blocks per CU: the resident rows (one wave per row, the batch one
-    // generation of blocks) measured 3-11% faster at 832-1,024 tokens and
-    // 1.5-6% at 1,792-2,048 than the split rows below (16,384 wide, 256 CUs);
-    // between the two bands the CUs holding two blocks set the pace and the
-    // split rows win.
-    if (epi == NORM_EPI_FP8_DYNAMIC && residual && hidden > 12288 && hidden <= NORM_RESIDENT_MAX_HIDDEN &&
-        hidden % NORM_RESIDENT_WIDTH_MULTIPLE == 0) {
-        const int64_t blocks = (tokens + 3) / 4, cus = device_cus();
-        if (blocks * 5 >= cus * 4 && blocks <= cus) {
-            const int i = norm_find(1, 32, NORM_RESIDENT_Y_IN_PLACE);
-            if (i >= 0) return i;
-        }
-        if (blocks * 4 >= cus * 7 && blocks <= 2 * cus) {
-            const int i = norm_find(1, 32, NORM_RESIDENT);
-            if (i >= 0) return i;
-        }
     }
     if (epi == NORM_EPI_FP8_DYNAMIC && residual && hidden > 8192 && tokens <= kDynamicFp8FewWavesTokens) {
         const int i = norm_fit(8, hidden, 4);

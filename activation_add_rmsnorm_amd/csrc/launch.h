@@ -91,8 +91,9 @@ struct NormVariant {
 };
 
 // Resident-row kernels: one wave holds a row of up to 16,384 values in its
-// registers (rows a multiple of 512 wide).  Y_IN_PLACE: the per-token E4M3
-// form overwrites h with y in its amax pass (a narrower load window).
+// registers (rows a multiple of 512 wide).  NORM_RESIDENT_Y_IN_PLACE: a
+// 6-slice load window, and the per-token E4M3 form overwrites h with y in its
+// amax pass; NORM_RESIDENT: a 10-slice window.
 constexpr int NORM_RESIDENT_Y_IN_PLACE = -1;
 constexpr int NORM_RESIDENT = -2;
 constexpr int NORM_RESIDENT_MAX_HIDDEN = 16384;

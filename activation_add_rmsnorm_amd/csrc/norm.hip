@@ -585,8 +585,8 @@ static const NormVariant kNormVariants[] = {
     {16, 4, 1, "16 waves/row x4 vec, pipelined 1 block/CU"},
     {16, 8, 1, "16 waves/row x8 vec, pipelined 1 block/CU"},
     // one wave holds the whole row (norm_resident.hip)
-    {1, 32, NORM_RESIDENT_Y_IN_PLACE, "wave/row x32 vec, resident, y in place"},
-    {1, 32, NORM_RESIDENT, "wave/row x32 vec, resident"},
+    {1, 32, NORM_RESIDENT_Y_IN_PLACE, "wave/row x32 vec, resident, 6-slice window"},
+    {1, 32, NORM_RESIDENT, "wave/row x32 vec, resident, 10-slice window"},
 };
 constexpr int kNumNormVariants = sizeof(kNormVariants) / sizeof(kNormVariants[0]);
 static_assert(kNumNormVariants <= 64, "the occupancy cache holds 64 variants per form");

@@ -474,12 +474,12 @@ def copy_sweep(args, torch, clib, dev, sp, timer):
 
 def phase_timeline(args, torch, np, W, dev, sp, timer):
     """Per-wave phase stamps of the Llama-405B per-token E4M3 norm
-    ([2048, 16384], the library's default variant) from the measurement build
-    libaarms_stamps.so (real-time clock, 100 MHz): one launch in the middle of
-    a back-to-back run over rotated buffer sets.  Reports the launch time with
-    and without the stamps, the per-block phase times, the same by start-time
-    octile, and the blocks in flight and waves still waiting for their row's
-    loads at 40 points across the launch."""
+    ([2048, 16384]) from the measurement build libaarms_stamps.so (real-time
+    clock, 100 MHz): one launch in the middle of a back-to-back run over
+    rotated buffer sets, for the library's default variant (resident rows:
+    one wave per row) and for the split rows (16 waves per row) it replaced.
+    Reports the launch time with and without the stamps, the per-row (per-
+    block) phase times, and over the launch the rows or blocks in flight."""
     import ctypes as C
     from activation_add_rmsnorm_amd import _build
     if not os.path.exists(_build.STAMPS_PATH):
@@ -494,111 +494,145 @@ def phase_timeline(args, torch, np, W, dev, sp, timer):
     L.aarms_pick_variant.argtypes = [i32, i64, i64, i32]
     L.aarms_variant_name.argtypes = [i32, i32]
     L.aarms_variant_name.restype = C.c_char_p
+    L.aarms_variant_count.argtypes = [i32]
     wl = W.NORM_FP8_LLAMA405B
     T, H = wl.tokens, wl.hidden
-    v = L.aarms_pick_variant(0, T, H, 1)
-    vname = L.aarms_variant_name(0, v).decode()
-    wpr = 1 if vname.startswith("wave/row") else int(vname.split()[0])
     d = W.norm_inputs(wl)
     to = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
     x0, r0, w0 = to(d["x"]), to(d["residual"]), to(d["weight"])
     ns = rotation_sets(norm_bytes(T, H, quant=True))
     sets = [dict(x=x0.clone(), r=r0.clone(), q=torch.empty((T, H), dtype=torch.uint8, device=dev),
                  s=torch.empty((T,), dtype=torch.float32, device=dev), ro=torch.empty_like(r0)) for _ in range(ns)]
-
-    def call(i):
-        z = sets[i % ns]
-        st = L.fused_add_rmsnorm_quant_fp8_ex(z["q"].data_ptr(), z["s"].data_ptr(), z["ro"].data_ptr(),
-                                               z["x"].data_ptr(), z["r"].data_ptr(), w0.data_ptr(), T, H, wl.eps, v, sp)
-        if st:
-            raise RuntimeError("fused_add_rmsnorm_quant_fp8_ex: %d" % st)
-
     reps = max(20, args.steps // 2)
-    stamps = torch.zeros(T * wpr * 16, dtype=torch.int64, device=dev)
-    L.aarms_set_phase_stamps(None)
-    timer.warm(call)
-    us_plain = timer.region(call, reps) * 1e3
-    L.aarms_set_phase_stamps(stamps.data_ptr())
-    timer.warm(call)
-    us_stamped = timer.region(call, reps) * 1e3
-    # the stamps of the last launch of a back-to-back run
-    stamps.zero_()
-    torch.cuda.synchronize()
-    for i in range(2 * ns):
-        call(i)
-    torch.cuda.synchronize()
-    L.aarms_set_phase_stamps(None)
-    a = stamps.cpu().numpy().reshape(T, wpr, 16).astype(np.float64)
-    t = (a - a[:, :, 0].min()) * 0.01          # us from the first wave's start (slots 8, 9: IDs)
-    bstart = t[:, :, 0].min(1)
-    span = float(t[:, :, 7].max())
     pct = lambda v: {"p10": round(float(np.percentile(v, 10)), 2), "median": round(float(np.median(v)), 2),
                      "p90": round(float(np.percentile(v, 90)), 2), "max": round(float(v.max()), 2)}
-    phases = {
-        "last wave's row loads consumed": pct(t[:, :, 1].max(1) - bstart),
-        "first wave's row loads consumed": pct(t[:, :, 1].min(1) - bstart),
-        "first barrier passed": pct(t[:, :, 3].min(1) - bstart),
-        "row amax computed (last wave)": pct(t[:, :, 4].max(1) - bstart),
-        "second barrier passed": pct(t[:, :, 6].min(1) - bstart),
-        "last store issued (last wave)": pct(t[:, :, 7].max(1) - bstart),
-    }
-    per_wave = {
-        "loads consumed -> wave sum": pct((t[:, :, 2] - t[:, :, 1]).ravel()),
-        "first barrier -> row amax computed": pct((t[:, :, 4] - t[:, :, 3]).ravel()),
-        "row amax -> wave maximum": pct((t[:, :, 5] - t[:, :, 4]).ravel()),
-        "second barrier -> last store issued": pct((t[:, :, 7] - t[:, :, 6]).ravel()),
-    }
-    # a second pass with the sub-steps of the chain after the first barrier
-    # stamped too (more stores and waits in the kernel: its own pass)
-    L.aarms_set_phase_stamp_detail(1)
-    L.aarms_set_phase_stamps(stamps.data_ptr())
-    timer.warm(call)
-    us_detail = timer.region(call, reps) * 1e3
-    stamps.zero_()
-    torch.cuda.synchronize()
-    for i in range(2 * ns):
-        call(i)
-    torch.cuda.synchronize()
-    L.aarms_set_phase_stamps(None)
-    L.aarms_set_phase_stamp_detail(0)
-    ad = stamps.cpu().numpy().reshape(T, wpr, 16).astype(np.float64)
-    td = (ad - ad[:, :, 0].min()) * 0.01
-    per_wave_detail = {}
-    if (ad[:, :, 10:15] > 0).all():
-        per_wave_detail = {
-            "first barrier -> row sum combined": pct((td[:, :, 10] - td[:, :, 3]).ravel()),
-            "row sum -> mean and 1/sqrt": pct((td[:, :, 11] - td[:, :, 10]).ravel()),
-            "1/sqrt -> weight in registers": pct((td[:, :, 12] - td[:, :, 11]).ravel()),
-            "weight -> row amax computed": pct((td[:, :, 4] - td[:, :, 12]).ravel()),
-            "second barrier -> row amax combined": pct((td[:, :, 13] - td[:, :, 6]).ravel()),
-            "row amax -> scale and reciprocal": pct((td[:, :, 14] - td[:, :, 13]).ravel()),
-            "scale -> last store issued": pct((td[:, :, 7] - td[:, :, 14]).ravel()),
+
+    def stamped_launch(v, wpr, detail):
+        """Plain and stamped launch times, and the stamps [T, wpr, 16] of one
+        launch in a back-to-back run."""
+        def call(i):
+            z = sets[i % ns]
+            st = L.fused_add_rmsnorm_quant_fp8_ex(z["q"].data_ptr(), z["s"].data_ptr(), z["ro"].data_ptr(),
+                                                   z["x"].data_ptr(), z["r"].data_ptr(), w0.data_ptr(), T, H,
+                                                   wl.eps, v, sp)
+            if st:
+                raise RuntimeError("fused_add_rmsnorm_quant_fp8_ex: %d" % st)
+        stamps = torch.zeros(T * wpr * 16, dtype=torch.int64, device=dev)
+        L.aarms_set_phase_stamp_detail(1 if detail else 0)
+        L.aarms_set_phase_stamps(None)
+        timer.warm(call)
+        us_plain = timer.region(call, reps) * 1e3
+        L.aarms_set_phase_stamps(stamps.data_ptr())
+        timer.warm(call)
+        us_stamped = timer.region(call, reps) * 1e3
+        stamps.zero_()
+        torch.cuda.synchronize()
+        for i in range(2 * ns):
+            call(i)
+        torch.cuda.synchronize()
+        L.aarms_set_phase_stamps(None)
+        L.aarms_set_phase_stamp_detail(0)
+        return us_plain, us_stamped, stamps.cpu().numpy().reshape(T, wpr, 16).astype(np.float64)
+
+    def cus_used(a):
+        hw, xcc = a[:, 0, 8].astype(np.int64), a[:, 0, 9].astype(np.int64) & 0xF
+        cu = ((xcc * 8 + ((hw >> 13) & 7)) * 2 + ((hw >> 12) & 1)) * 16 + ((hw >> 8) & 0xF)
+        _, per_cu = np.unique(cu, return_counts=True)
+        return int(len(per_cu)), {"min": int(per_cu.min()), "max": int(per_cu.max())}
+
+    def resident(v, vname):
+        us_plain, us_stamped, a = stamped_launch(v, 1, False)
+        t = (a[:, 0, :] - a[:, 0, 0].min()) * 0.01      # us from the first row's start
+        span = float(t[:, 7].max())
+        grid = np.linspace(0.0, span, 41)
+        ncu, per_cu = cus_used(a)
+        return {"variant": vname, "waves_per_row": 1, "launch_us": round(us_plain, 2),
+                "launch_us_with_stamps": round(us_stamped, 2), "span_us": round(span, 2),
+                "per_row_from_launch_start_us": {
+                    "row start": pct(t[:, 0]), "row loads consumed": pct(t[:, 1]),
+                    "weight in LDS (block barrier)": pct(t[:, 3]), "row amax computed": pct(t[:, 4]),
+                    "last store issued": pct(t[:, 7])},
+                "per_row_us": {
+                    "start -> row loads consumed": pct(t[:, 1] - t[:, 0]),
+                    "loads consumed -> wave sum": pct(t[:, 2] - t[:, 1]),
+                    "wave sum -> weight in LDS": pct(t[:, 3] - t[:, 2]),
+                    "weight -> row amax computed (amax pass)": pct(t[:, 4] - t[:, 3]),
+                    "row amax -> wave maximum": pct(t[:, 5] - t[:, 4]),
+                    "wave maximum -> last store issued (quantizing pass)": pct(t[:, 7] - t[:, 5])},
+                "grid_us": [round(float(g), 2) for g in grid],
+                "rows_loading": [int(((t[:, 0] <= g) & (t[:, 1] > g)).sum()) for g in grid],
+                "rows_in_epilogue": [int(((t[:, 1] <= g) & (t[:, 7] > g)).sum()) for g in grid],
+                "rows_done": [int((t[:, 7] <= g).sum()) for g in grid],
+                "distinct_cus": ncu, "rows_per_cu": per_cu}
+
+    def split(v, vname, wpr):
+        us_plain, us_stamped, a = stamped_launch(v, wpr, False)
+        t = (a - a[:, :, 0].min()) * 0.01          # us from the first wave's start (slots 8, 9: IDs)
+        bstart = t[:, :, 0].min(1)
+        span = float(t[:, :, 7].max())
+        phases = {
+            "last wave's row loads consumed": pct(t[:, :, 1].max(1) - bstart),
+            "first wave's row loads consumed": pct(t[:, :, 1].min(1) - bstart),
+            "first barrier passed": pct(t[:, :, 3].min(1) - bstart),
+            "row amax computed (last wave)": pct(t[:, :, 4].max(1) - bstart),
+            "second barrier passed": pct(t[:, :, 6].min(1) - bstart),
+            "last store issued (last wave)": pct(t[:, :, 7].max(1) - bstart),
         }
-    order = np.argsort(bstart)
-    octiles = []
-    for g in range(8):
-        sl = order[g * T // 8:(g + 1) * T // 8]
-        octiles.append({"start_us": round(float(np.median(bstart[sl])), 2),
-                        "loads_us": round(float(np.median(t[sl, :, 1].max(1) - bstart[sl])), 2),
-                        "barrier1_us": round(float(np.median(t[sl, :, 3].min(1) - bstart[sl])), 2),
-                        "barrier2_us": round(float(np.median(t[sl, :, 6].min(1) - bstart[sl])), 2),
-                        "end_us": round(float(np.median(t[sl, :, 7].max(1) - bstart[sl])), 2)})
-    grid = np.linspace(0.0, span, 41)
-    bend = t[:, :, 7].max(1)
-    in_flight = [int(((bstart <= g) & (bend > g)).sum()) for g in grid]
-    awaiting = [int(((t[:, :, 0] <= g) & (t[:, :, 1] > g)).sum()) for g in grid]
-    hw, xcc = a[:, 0, 8].astype(np.int64), a[:, 0, 9].astype(np.int64) & 0xF
-    cu = ((xcc * 8 + ((hw >> 13) & 7)) * 2 + ((hw >> 12) & 1)) * 16 + ((hw >> 8) & 0xF)
-    _, per_cu = np.unique(cu, return_counts=True)
-    return {"metric": "per-wave phase timeline, fused_add_rmsnorm_quant_fp8 [2048,16384] (Llama-405B)",
-            "variant": vname, "waves_per_row": wpr, "launch_us": round(us_plain, 2),
-            "launch_us_with_stamps": round(us_stamped, 2), "span_us": round(span, 2),
-            "per_block_from_block_start_us": phases, "per_wave_us": per_wave, "octiles_by_start": octiles,
-            "launch_us_with_detail_stamps": round(us_detail, 2), "per_wave_detail_us": per_wave_detail,
-            "grid_us": [round(float(g), 2) for g in grid], "blocks_in_flight": in_flight,
-            "waves_awaiting_row_loads": awaiting, "distinct_cus": int(len(per_cu)),
-            "blocks_per_cu": {"min": int(per_cu.min()), "max": int(per_cu.max())},
-            "buffer_sets_rotated": ns}
+        per_wave = {
+            "loads consumed -> wave sum": pct((t[:, :, 2] - t[:, :, 1]).ravel()),
+            "first barrier -> row amax computed": pct((t[:, :, 4] - t[:, :, 3]).ravel()),
+            "row amax -> wave maximum": pct((t[:, :, 5] - t[:, :, 4]).ravel()),
+            "second barrier -> last store issued": pct((t[:, :, 7] - t[:, :, 6]).ravel()),
+        }
+        # a second pass with the sub-steps of the chain after the first
+        # barrier stamped too (more stores and waits in the kernel)
+        us_detail, _, ad = stamped_launch(v, wpr, True)
+        td = (ad - ad[:, :, 0].min()) * 0.01
+        per_wave_detail = {}
+        if (ad[:, :, 10:15] > 0).all():
+            per_wave_detail = {
+                "first barrier -> row sum combined": pct((td[:, :, 10] - td[:, :, 3]).ravel()),
+                "row sum -> mean and 1/sqrt": pct((td[:, :, 11] - td[:, :, 10]).ravel()),
+                "1/sqrt -> weight in registers": pct((td[:, :, 12] - td[:, :, 11]).ravel()),
+                "weight -> row amax computed": pct((td[:, :, 4] - td[:, :, 12]).ravel()),
+                "second barrier -> row amax combined": pct((td[:, :, 13] - td[:, :, 6]).ravel()),
+                "row amax -> scale and reciprocal": pct((td[:, :, 14] - td[:, :, 13]).ravel()),
+                "scale -> last store issued": pct((td[:, :, 7] - td[:, :, 14]).ravel()),
+            }
+        order = np.argsort(bstart)
+        octiles = []
+        for g in range(8):
+            sl = order[g * T // 8:(g + 1) * T // 8]
+            octiles.append({"start_us": round(float(np.median(bstart[sl])), 2),
+                            "loads_us": round(float(np.median(t[sl, :, 1].max(1) - bstart[sl])), 2),
+                            "barrier1_us": round(float(np.median(t[sl, :, 3].min(1) - bstart[sl])), 2),
+                            "barrier2_us": round(float(np.median(t[sl, :, 6].min(1) - bstart[sl])), 2),
+                            "end_us": round(float(np.median(t[sl, :, 7].max(1) - bstart[sl])), 2)})
+        grid = np.linspace(0.0, span, 41)
+        bend = t[:, :, 7].max(1)
+        ncu, per_cu = cus_used(a)
+        return {"variant": vname, "waves_per_row": wpr, "launch_us": round(us_plain, 2),
+                "launch_us_with_stamps": round(us_stamped, 2), "span_us": round(span, 2),
+                "per_block_from_block_start_us": phases, "per_wave_us": per_wave, "octiles_by_start": octiles,
+                "launch_us_with_detail_stamps": round(us_detail, 2), "per_wave_detail_us": per_wave_detail,
+                "grid_us": [round(float(g), 2) for g in grid],
+                "blocks_in_flight": [int(((bstart <= g) & (bend > g)).sum()) for g in grid],
+                "waves_awaiting_row_loads": [int(((t[:, :, 0] <= g) & (t[:, :, 1] > g)).sum()) for g in grid],
+                "distinct_cus": ncu, "blocks_per_cu": per_cu}
+
+    out = {"metric": "per-wave phase timeline, fused_add_rmsnorm_quant_fp8 [2048,16384] (Llama-405B)",
+           "buffer_sets_rotated": ns}
+    v = L.aarms_pick_variant(0, T, H, 1)
+    vname = L.aarms_variant_name(0, v).decode()
+    names = {L.aarms_variant_name(0, i).decode(): i for i in range(L.aarms_variant_count(0))}
+    if "resident" in vname:
+        out["default"] = resident(v, vname)
+        progress("phase timeline: split rows")
+        out["split_rows"] = split(names["16 waves/row x2 vec"], "16 waves/row x2 vec", 16)
+    else:
+        wpr = 1 if vname.startswith("wave/row") else int(vname.split()[0])
+        out["default"] = split(v, vname, wpr)
+    return out
 
 
 # Supplementary entries and the keys of their traffic lines in profiles/.

@@ -350,20 +350,25 @@ def test_pick_variant_ranges():
     assert nname(A.OP_NORM, 256, 16384, 1) == "8 waves/row x4 vec"
     assert nname(A.OP_NORM, 1, 12288, 1) == "8 waves/row x4 vec"
     assert nname(A.OP_NORM, 768, 16384, 1) == "8 waves/row x4 vec"
-    # per-token E4M3 with the residual, 12,289-16,384 wide (multiples of 512):
-    # resident rows at 0.8-1 and 1.75-2 four-row blocks per CU (256 CUs
-    # without a device), the split rows between and around
-    for T in (832, 1000, 1024):
-        assert nname(A.OP_NORM, T, 16384, 1) == "wave/row x32 vec, resident, y in place", T
-    for T in (1792, 2040, 2048):
-        assert nname(A.OP_NORM, T, 16384, 1) == "wave/row x32 vec, resident", T   # 2,048: the 405B workload
-    assert nname(A.OP_NORM, 2048, 12800, 1) == "wave/row x32 vec, resident"
-    assert nname(A.OP_NORM, 1536, 16384, 1) == nname(A.OP_NORM, 2049, 16384, 1) == "16 waves/row x2 vec"
-    assert nname(A.OP_NORM, 2048, 12288, 1) == nname(A.OP_NORM, 2048, 16376, 1) == "16 waves/row x2 vec"
-    for f in (0, 2, 3, 4, 5):
+    # 12,289-16,384 wide (multiples of 512): resident rows at 0.8-1 and 1.75-2
+    # four-row blocks per CU (256 CUs without a device) for per-token and
+    # per-tensor E4M3 with the add and bf16 with and without it; the split
+    # rows between the bands, around them and for the other forms
+    W6, W10 = "wave/row x32 vec, resident, 6-slice window", "wave/row x32 vec, resident, 10-slice window"
+    for f in (0, 1, 2):
+        for T in (832, 1000, 1024):
+            assert nname(A.OP_NORM, T, 16384, f) == W6, (T, f)
+        for T in (1792, 2040, 2048):                     # 2,048 per-token: the 405B workload
+            assert nname(A.OP_NORM, T, 16384, f) == W10, (T, f)
+        assert nname(A.OP_NORM, 2048, 12800, f) == W10
+        assert nname(A.OP_NORM, 1536, 16384, f) == nname(A.OP_NORM, 2049, 16384, f) == "16 waves/row x2 vec"
+        assert nname(A.OP_NORM, 2048, 12288, f) == nname(A.OP_NORM, 2048, 16376, f) == "16 waves/row x2 vec"
+    assert nname(A.OP_RMSNORM, 1024, 16384, 0) == nname(A.OP_RMSNORM, 2048, 16384, 0) == W6
+    assert nname(A.OP_RMSNORM, 1536, 16384, 0) == "8 waves/row x4 vec, pipelined 2 blocks/CU"
+    for f in (3, 4, 5):
         assert "resident" not in nname(A.OP_NORM, 2048, 16384, f), f
+    for f in (1, 2, 3, 4, 5):
         assert "resident" not in nname(A.OP_RMSNORM, 2048, 16384, f), f
-    assert "resident" not in nname(A.OP_RMSNORM, 2048, 16384, 1)
     assert nname(A.OP_NORM, 256, 8192, 1) == nname(A.OP_NORM, 256, 8192, 0) == "8 waves/row x2 vec"
     assert nname(A.OP_RMSNORM, 256, 16384, 1) == nname(A.OP_RMSNORM, 256, 16384, 0)
     for f in (-1, 6):
@@ -383,7 +388,7 @@ def test_pick_variant_ranges():
     # pipelined 8 x 4 for bf16 at 8,193-16,384 wide from 512 to 2,048 tokens
     assert nname(A.OP_RMSNORM, 512, 4096, 0) == nname(A.OP_RMSNORM, 1, 4096, 1) == "4 waves/row x2 vec"
     assert nname(A.OP_RMSNORM, 1024, 4096, 0) == "2 waves/row x4 vec"
-    assert nname(A.OP_RMSNORM, 1024, 16384, 0) == "8 waves/row x4 vec, pipelined 2 blocks/CU"
+    assert nname(A.OP_RMSNORM, 768, 16384, 0) == "8 waves/row x4 vec, pipelined 2 blocks/CU"
     assert nname(A.OP_RMSNORM, 1024, 16384, 1) == nname(A.OP_RMSNORM, 4096, 16384, 0) == "8 waves/row x4 vec"
     # per-token SwiGLU: several waves per row take at most 3 jobs before 4
     rq = lambda N: A.variant_name(A.OP_SWIGLU_DYNAMIC, A.pick_variant(A.OP_SWIGLU_DYNAMIC, 64, N))
