@@ -142,6 +142,10 @@ def _check(status: int, what: str) -> None:
 
 
 def _require(t: torch.Tensor, name: str, dtypes, shape) -> None:
+    # the common case in one expression (a few attribute reads); the checks
+    # below name what is wrong
+    if isinstance(t, torch.Tensor) and t.is_cuda and t.dtype in dtypes and t.shape == shape and t.is_contiguous():
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.device.type != "cuda":
@@ -154,14 +158,22 @@ def _require(t: torch.Tensor, name: str, dtypes, shape) -> None:
         raise ValueError("%s must be contiguous" % name)
 
 
-def _stream(device: torch.device) -> int:
+# The current stream's raw handle without building a torch.cuda.Stream per
+# call (the same handle torch.cuda.current_stream(i).cuda_stream gives).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device: int) -> int:
+    """hipStream_t of the current stream on GPU `device` (an index)."""
+    if _raw_stream is not None:
+        return _raw_stream(device)
     return torch.cuda.current_stream(device).cuda_stream
 
 
 def _same_device(*ts: torch.Tensor) -> None:
-    d = ts[0].device
+    d = ts[0].get_device()
     for t in ts[1:]:
-        if t.device != d:
+        if t.get_device() != d:
             raise ValueError("all tensors must be on the same device")
 
 
@@ -189,7 +201,7 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Ten
     variant = _variant("fused_add_rmsnorm", T, H, variant)
     _check(lib.fused_add_rmsnorm_ex(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
                                     residual.data_ptr(), weight.data_ptr(), T, H, float(eps),
-                                    int(variant), _stream(x.device)), "fused_add_rmsnorm")
+                                    int(variant), _stream(x.get_device())), "fused_add_rmsnorm")
     return out, residual_out
 
 
@@ -220,7 +232,7 @@ def fused_add_rmsnorm_quant_fp8(x: torch.Tensor, residual: torch.Tensor, weight:
     _check(lib.fused_add_rmsnorm_quant_fp8_ex(out.data_ptr(), scale_out.data_ptr(),
                                               residual_out.data_ptr(), x.data_ptr(),
                                               residual.data_ptr(), weight.data_ptr(), T, H,
-                                              float(eps), int(variant), _stream(x.device)),
+                                              float(eps), int(variant), _stream(x.get_device())),
            "fused_add_rmsnorm_quant_fp8")
     return out, scale_out, residual_out
 
@@ -251,7 +263,7 @@ def fused_add_rmsnorm_quant_fp8_static(x: torch.Tensor, residual: torch.Tensor,
     _check(lib.fused_add_rmsnorm_quant_fp8_static_ex(out.data_ptr(), residual_out.data_ptr(),
                                                      x.data_ptr(), residual.data_ptr(),
                                                      weight.data_ptr(), scale.data_ptr(), T, H,
-                                                     float(eps), int(variant), _stream(x.device)),
+                                                     float(eps), int(variant), _stream(x.get_device())),
            "fused_add_rmsnorm_quant_fp8_static")
     return out, residual_out
 
@@ -271,7 +283,7 @@ def rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, out: torch.Tensor
     lib = load()
     variant = _variant("rmsnorm", T, H, variant)
     _check(lib.rmsnorm_ex(out.data_ptr(), x.data_ptr(), weight.data_ptr(), T, H, float(eps),
-                          int(variant), _stream(x.device)), "rmsnorm")
+                          int(variant), _stream(x.get_device())), "rmsnorm")
     return out
 
 
@@ -296,7 +308,7 @@ def rmsnorm_quant_fp8(x: torch.Tensor, weight: torch.Tensor, eps: float,
     variant = _variant("rmsnorm_quant_fp8", T, H, variant)
     _check(lib.rmsnorm_quant_fp8_ex(out.data_ptr(), scale_out.data_ptr(), x.data_ptr(),
                                     weight.data_ptr(), T, H, float(eps), int(variant),
-                                    _stream(x.device)), "rmsnorm_quant_fp8")
+                                    _stream(x.get_device())), "rmsnorm_quant_fp8")
     return out, scale_out
 
 
@@ -317,7 +329,7 @@ def rmsnorm_quant_fp8_static(x: torch.Tensor, weight: torch.Tensor, scale: torch
     variant = _variant("rmsnorm_quant_fp8_static", T, H, variant)
     _check(lib.rmsnorm_quant_fp8_static_ex(out.data_ptr(), x.data_ptr(), weight.data_ptr(),
                                            scale.data_ptr(), T, H, float(eps), int(variant),
-                                           _stream(x.device)), "rmsnorm_quant_fp8_static")
+                                           _stream(x.get_device())), "rmsnorm_quant_fp8_static")
     return out
 
 
@@ -355,7 +367,7 @@ def fused_add_rmsnorm_quant_mxfp4(x: torch.Tensor, residual: torch.Tensor, weigh
     _check(lib.fused_add_rmsnorm_quant_mxfp4_ex(out.data_ptr(), scale_out.data_ptr(),
                                                 residual_out.data_ptr(), x.data_ptr(),
                                                 residual.data_ptr(), weight.data_ptr(), T, H,
-                                                float(eps), int(variant), _stream(x.device)),
+                                                float(eps), int(variant), _stream(x.get_device())),
            "fused_add_rmsnorm_quant_mxfp4")
     return out, scale_out, residual_out
 
@@ -375,7 +387,7 @@ def rmsnorm_quant_mxfp4(x: torch.Tensor, weight: torch.Tensor, eps: float,
     variant = _variant("rmsnorm_quant_mxfp4", T, H, variant)
     _check(lib.rmsnorm_quant_mxfp4_ex(out.data_ptr(), scale_out.data_ptr(), x.data_ptr(),
                                       weight.data_ptr(), T, H, float(eps), int(variant),
-                                      _stream(x.device)), "rmsnorm_quant_mxfp4")
+                                      _stream(x.get_device())), "rmsnorm_quant_mxfp4")
     return out, scale_out
 
 
@@ -416,7 +428,7 @@ def fused_add_rmsnorm_quant_nvfp4(x: torch.Tensor, residual: torch.Tensor, weigh
                                                 residual_out.data_ptr(), x.data_ptr(),
                                                 residual.data_ptr(), weight.data_ptr(),
                                                 tensor_scale.data_ptr(), T, H, float(eps),
-                                                int(variant), _stream(x.device)),
+                                                int(variant), _stream(x.get_device())),
            "fused_add_rmsnorm_quant_nvfp4")
     return out, scale_out, residual_out
 
@@ -437,7 +449,7 @@ def rmsnorm_quant_nvfp4(x: torch.Tensor, weight: torch.Tensor, tensor_scale: tor
     variant = _variant("rmsnorm_quant_nvfp4", T, H, variant)
     _check(lib.rmsnorm_quant_nvfp4_ex(out.data_ptr(), scale_out.data_ptr(), x.data_ptr(),
                                       weight.data_ptr(), tensor_scale.data_ptr(), T, H, float(eps),
-                                      int(variant), _stream(x.device)), "rmsnorm_quant_nvfp4")
+                                      int(variant), _stream(x.get_device())), "rmsnorm_quant_nvfp4")
     return out, scale_out
 
 
@@ -454,7 +466,7 @@ def swiglu(gate_up: torch.Tensor, out: torch.Tensor | None = None, variant: int 
     lib = load()
     variant = _variant("swiglu", T, N, variant)
     _check(lib.swiglu_ex(out.data_ptr(), gate_up.data_ptr(), T, N, int(variant),
-                         _stream(gate_up.device)), "swiglu")
+                         _stream(gate_up.get_device())), "swiglu")
     return out
 
 
@@ -474,7 +486,7 @@ def swiglu_quant_fp8(gate_up: torch.Tensor, scale: torch.Tensor, out: torch.Tens
     lib = load()
     variant = _variant("swiglu_quant_fp8", T, N, variant)
     _check(lib.swiglu_quant_fp8_ex(out.data_ptr(), gate_up.data_ptr(), scale.data_ptr(), T, N,
-                                   int(variant), _stream(gate_up.device)), "swiglu_quant_fp8")
+                                   int(variant), _stream(gate_up.get_device())), "swiglu_quant_fp8")
     return out
 
 
@@ -515,7 +527,7 @@ def fused_add_rmsnorm_quant_fp8_group(x: torch.Tensor, residual: torch.Tensor, w
     _check(lib.fused_add_rmsnorm_quant_fp8_group_ex(out.data_ptr(), scale_out.data_ptr(),
                                                     residual_out.data_ptr(), x.data_ptr(),
                                                     residual.data_ptr(), weight.data_ptr(), T, H,
-                                                    float(eps), int(variant), _stream(x.device)),
+                                                    float(eps), int(variant), _stream(x.get_device())),
            "fused_add_rmsnorm_quant_fp8_group")
     return out, scale_out, residual_out
 
@@ -536,7 +548,7 @@ def rmsnorm_quant_fp8_group(x: torch.Tensor, weight: torch.Tensor, eps: float,
     variant = _variant("rmsnorm_quant_fp8_group", T, H, variant)
     _check(lib.rmsnorm_quant_fp8_group_ex(out.data_ptr(), scale_out.data_ptr(), x.data_ptr(),
                                           weight.data_ptr(), T, H, float(eps), int(variant),
-                                          _stream(x.device)), "rmsnorm_quant_fp8_group")
+                                          _stream(x.get_device())), "rmsnorm_quant_fp8_group")
     return out, scale_out
 
 
@@ -553,7 +565,7 @@ def swiglu_quant_fp8_group(gate_up: torch.Tensor, out: torch.Tensor | None = Non
     lib = load()
     variant = _variant("swiglu_quant_fp8_group", T, N, variant)
     _check(lib.swiglu_quant_fp8_group_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(),
-                                         T, N, int(variant), _stream(gate_up.device)),
+                                         T, N, int(variant), _stream(gate_up.get_device())),
            "swiglu_quant_fp8_group")
     return out, scale_out
 
@@ -576,7 +588,7 @@ def swiglu_quant_fp8_dynamic(gate_up: torch.Tensor, out: torch.Tensor | None = N
     lib = load()
     variant = _variant("swiglu_quant_fp8_dynamic", T, N, variant)
     _check(lib.swiglu_quant_fp8_dynamic_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(),
-                                           T, N, int(variant), _stream(gate_up.device)),
+                                           T, N, int(variant), _stream(gate_up.get_device())),
            "swiglu_quant_fp8_dynamic")
     return out, scale_out
 
@@ -594,7 +606,7 @@ def swiglu_quant_mxfp4(gate_up: torch.Tensor, out: torch.Tensor | None = None,
     lib = load()
     variant = _variant("swiglu_quant_mxfp4", T, N, variant)
     _check(lib.swiglu_quant_mxfp4_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(), T, N,
-                                     int(variant), _stream(gate_up.device)), "swiglu_quant_mxfp4")
+                                     int(variant), _stream(gate_up.get_device())), "swiglu_quant_mxfp4")
     return out, scale_out
 
 
@@ -611,7 +623,7 @@ def swiglu_quant_nvfp4(gate_up: torch.Tensor, tensor_scale: torch.Tensor, out: t
     lib = load()
     variant = _variant("swiglu_quant_nvfp4", T, N, variant)
     _check(lib.swiglu_quant_nvfp4_ex(out.data_ptr(), scale_out.data_ptr(), gate_up.data_ptr(),
-                                     tensor_scale.data_ptr(), T, N, int(variant), _stream(gate_up.device)),
+                                     tensor_scale.data_ptr(), T, N, int(variant), _stream(gate_up.get_device())),
            "swiglu_quant_nvfp4")
     return out, scale_out
 
