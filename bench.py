@@ -310,14 +310,17 @@ def main():
         timer.warm(step_heuristic, 0.02)
         ms_step_heuristic = timer.region(step_heuristic, K)
 
-    # per-kernel durations: each kernel alone, K back-to-back launches over
+    # per-kernel durations: each kernel alone, back-to-back launches over
     # the same rotation, HIP events on the launch stream at both ends
-    norm_us = timer.region(norm_call, K) * 1e3
-    swiglu_us = timer.region(swiglu_call, K) * 1e3
+    # (at least 200 launches each, whatever K: a region of a few launches
+    # carries the events' own overhead)
+    Kk = max(K, 200)
+    norm_us = timer.region(norm_call, Kk) * 1e3
+    swiglu_us = timer.region(swiglu_call, Kk) * 1e3
     timer.warm(norm_refcopy, 0.02)
-    norm_copy_us = timer.region(norm_refcopy, K) * 1e3
+    norm_copy_us = timer.region(norm_refcopy, Kk) * 1e3
     timer.warm(swiglu_refcopy, 0.02)
-    swiglu_copy_us = timer.region(swiglu_refcopy, K) * 1e3
+    swiglu_copy_us = timer.region(swiglu_refcopy, Kk) * 1e3
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     src_hash = kernel_sources_hash()
