@@ -350,3 +350,47 @@ def test_resident_default_pick_per_token(T):
     q, s, ro = A.fused_add_rmsnorm_quant_fp8(bf16(x), bf16(r), bf16(wt), 1e-5)
     torch.cuda.synchronize()
     P.check_norm_fp8(x, r, wt, 1e-5, bits(q), bits(s), bits(ro))
+
+
+def _special_rows(T, H, seed):
+    """Rows the resident kernels have to get right besides random ones (bf16
+    bit patterns): zero, constant, a NaN, an infinity, bf16 subnormals,
+    rows scaled by 1e30 and 1e-30, a lone outlier, x = -residual (a zero
+    sum), and a sum that overflows bf16; the rest random."""
+    x = gen.normal_bf16((T, H), seed, 1, outlier_frac=0.001)
+    r = gen.normal_bf16((T, H), seed, 2)
+    one = lambda v: np.uint16(oracle.bf16_from_f64(v))
+    x[0, :] = 0
+    r[0, :] = 0
+    x[1, :] = one(1.0)
+    r[1, :] = 0
+    x[2, 100] = 0x7FC0                                  # NaN
+    r[3, 7] = 0x7F80                                    # +inf
+    x[4, :] = (np.arange(H) % 127 + 1).astype(np.uint16)  # bf16 subnormals
+    r[4, :] = 0
+    x[5, :] = one(1e30)
+    x[5, ::3] = one(-1e30)
+    r[5, :] = 0
+    x[6, :] = one(1e-30)
+    r[6, ::5] = one(-2e-30)
+    x[7, :] = 0
+    r[7, :] = 0
+    x[7, H // 2 + 3] = one(3e4)
+    r[8, :] = x[8, :] ^ np.uint16(0x8000)               # x + residual = 0 exactly
+    x[9, :] = one(3e38)
+    r[9, :] = one(3e38)                                 # the sum rounds to +inf in bf16
+    return x, r
+
+
+@pytest.mark.parametrize("H", [1024, 16384])
+def test_resident_variants_special_rows(H):
+    """Zero, constant, non-finite, subnormal, extreme-scale and cancelling
+    rows through the resident-row kernels in every output format, with and
+    without the residual add (the library's default variant at this shape,
+    rows split over waves, runs the same rows as a control)."""
+    T = 12
+    x, r = _special_rows(T, H, 7)
+    wt = gen.normal_bf16((H,), 7, 3, mean=1.0, std=0.1)
+    for v, name in _resident_variants() + [(-1, "default")]:
+        announce("special rows", name, (T, H))
+        _all_norm_forms(x, r, wt, 1e-5, 0.02, v)
