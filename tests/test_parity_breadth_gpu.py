@@ -313,6 +313,27 @@ def test_pipelined_variant_walks_rows_every_epilogue(v, name, w, vec, bpc):
     _all_norm_forms(x, r, wt, 1e-5, 0.02, v)
 
 
+@pytest.mark.parametrize("v,name,w,vec,bpc", _pipelined_variants() if torch.cuda.is_available() else [])
+def test_pipelined_variant_special_rows_between_normal_ones(v, name, w, vec, bpc):
+    """The special rows (zero, NaN, Inf, subnormal, extreme scales,
+    cancelling, overflowing) as the first and the last rows of a batch the
+    persistent grid walks, so that blocks carry their registers, partial-sum
+    slot and reciprocal table from a special row into normal ones and from
+    normal rows into special ones: nothing may leak across rows."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows_per_block = 4 if w == 1 else 1
+    H = min(w * 64 * vec * 8, 16384) if w > 1 else 1536
+    T = 2 * cus * bpc * rows_per_block + 37
+    x = gen.normal_bf16((T, H), v + 100, 1, outlier_frac=0.001)
+    r = gen.normal_bf16((T, H), v + 100, 2)
+    sx, sr = _special_rows(12, H, v + 100)
+    x[:10], r[:10] = sx[:10], sr[:10]
+    x[-10:], r[-10:] = sx[:10], sr[:10]
+    wt = gen.normal_bf16((H,), v + 100, 3, mean=1.0, std=0.1)
+    announce("norm forms, special rows", name, (T, H))
+    _all_norm_forms(x, r, wt, 1e-5, 0.02, v)
+
+
 def _resident_variants():
     return [(v, A.variant_name(A.OP_NORM, v)) for v in range(A.variant_count(A.OP_NORM))
             if "resident" in A.variant_name(A.OP_NORM, v)]
