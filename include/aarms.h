@@ -41,8 +41,9 @@
  *   - SiLU: a = bf16(silu(gate)) correctly rounded (silu(g) = g/(1+e^-g));
  *     y = bf16(f32(a) * f32(up)).
  *   - FP8: q = e4m3(clamp(f32(y) / scale, -448, 448)), the quotient rounded
- *     once to binary32, then round-to-nearest-even to E4M3.  NaN stays NaN,
- *     infinities saturate.  A scale of exactly zero is treated as one.
+ *     once to binary32, then round-to-nearest-even to E4M3.  NaN stays NaN
+ *     (0x7F or 0xFF: the sign of a NaN is not specified), infinities
+ *     saturate.  A scale of exactly zero is treated as one.
  */
 #ifndef AARMS_H
 #define AARMS_H
