@@ -54,6 +54,23 @@ def test_library_exports_only_declared_symbols():
     assert exported == set(declared_functions()), exported ^ set(declared_functions())
 
 
+def test_library_imports_no_allocation_or_synchronization():
+    """The header's promise that the library never allocates, frees or
+    synchronizes, checked on the built library: everything it imports is
+    kernel registration, the current device and its attributes, the
+    occupancy calculator, the launch, and the C++ runtime's start-up hooks.
+    No hipMalloc, hipFree, *Synchronize, blocking copy or host heap."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", A.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    imported = {l.split()[-1].split("@")[0] for l in out.splitlines() if l.strip()}
+    allowed = {"__hipRegisterFatBinary", "__hipUnregisterFatBinary", "__hipRegisterFunction",
+               "__hipPopCallConfiguration", "__hipPushCallConfiguration", "hipLaunchKernel", "hipGetDevice",
+               "hipDeviceGetAttribute", "hipOccupancyMaxActiveBlocksPerMultiprocessor",
+               "__cxa_atexit", "__cxa_finalize", "__deregister_frame_info", "__register_frame_info",
+               "__gmon_start__", "_ITM_deregisterTMCloneTable", "_ITM_registerTMCloneTable"}
+    assert imported <= allowed, sorted(imported - allowed)
+
+
 def test_status_strings():
     lib = A.load()
     for s in range(9):
