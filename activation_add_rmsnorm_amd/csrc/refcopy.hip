@@ -145,6 +145,42 @@ hipError_t design_u(int u, const void *in0, const void *in1, void *out0, void *o
     return launch_design<KIND, 4, NT>(in0, in1, out0, out1, n, grid, s);
 }
 
+// A copy in the one-wave-per-row layout of the norm's store hold: rows of
+// V * 64 16-byte vectors, four rows (waves) per 256-thread block, every lane
+// loading its V vectors of each input, then waiting until hold_ticks of the
+// 100 MHz real-time clock have passed since the wave started (bounded; 0: no
+// wait), then writing out0 = a ^ b and out1 = a + b.  All of a launch's rows
+// are resident at once for the sizes it is used at.
+template <int V>
+__global__ void __launch_bounds__(256) held_copy_kernel(const u32x4 *__restrict__ in0, const u32x4 *__restrict__ in1,
+                                                        u32x4 *__restrict__ out0, u32x4 *__restrict__ out1,
+                                                        uint64_t rows, uint32_t hold_ticks)
+{
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t row = (uint64_t)blockIdx.x * 4u + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const uint64_t base = row * (uint64_t)(V * 64) + (threadIdx.x & 63u);
+    u32x4 a[V], b[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        a[v] = __builtin_nontemporal_load(in0 + base + v * 64);
+        b[v] = __builtin_nontemporal_load(in1 + base + v * 64);
+    }
+    if (hold_ticks) {
+        asm volatile("" : : "v"(a[0]), "v"(b[V - 1]));
+        while (true) {
+            const uint64_t now = __builtin_amdgcn_s_memrealtime();
+            if (now < t0 || now - t0 >= hold_ticks) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        __builtin_nontemporal_store(a[v] ^ b[v], out0 + base + v * 64);
+        __builtin_nontemporal_store(a[v] + b[v], out1 + base + v * 64);
+    }
+}
+
 }  // namespace
 
 // Returns 0 on success, -1 for bad arguments (nothing launched), or the HIP
@@ -211,4 +247,32 @@ extern "C" __attribute__((visibility("default"))) int aarms_copy_design(int kind
     AARMS_DESIGN_KIND(6)
 #undef AARMS_DESIGN_KIND
     return -1;
+}
+
+// The held copy (held_copy_kernel): rows of row_vecs 16-byte vectors (64,
+// 128, 192 or 256) in each of in0, in1, out0 and out1 (16-byte aligned),
+// hold_ticks at most 4,000 (40 us).  Returns 0, -1 for bad arguments
+// (nothing launched), or the HIP error.
+extern "C" __attribute__((visibility("default"))) int aarms_copy_held(int64_t rows, int row_vecs, int hold_ticks,
+                                                                     void *out0, void *out1, const void *in0,
+                                                                     const void *in1, hipStream_t stream)
+{
+    if (rows < 0 || rows > (int64_t)INT32_MAX * 4 || hold_ticks < 0 || hold_ticks > 4000) return -1;
+    if (row_vecs != 64 && row_vecs != 128 && row_vecs != 192 && row_vecs != 256) return -1;
+    if (rows == 0) return 0;
+    if (!in0 || !in1 || !out0 || !out1 || !aligned(in0, 16) || !aligned(in1, 16) || !aligned(out0, 16) ||
+        !aligned(out1, 16))
+        return -1;
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    const u32x4 *a = (const u32x4 *)in0, *b = (const u32x4 *)in1;
+    u32x4 *o0 = (u32x4 *)out0, *o1 = (u32x4 *)out1;
+    const uint64_t r = (uint64_t)rows;
+    const uint32_t h = (uint32_t)hold_ticks;
+    switch (row_vecs / 64) {
+    case 1: hipLaunchKernelGGL(held_copy_kernel<1>, grid, block, 0, stream, a, b, o0, o1, r, h); break;
+    case 2: hipLaunchKernelGGL(held_copy_kernel<2>, grid, block, 0, stream, a, b, o0, o1, r, h); break;
+    case 3: hipLaunchKernelGGL(held_copy_kernel<3>, grid, block, 0, stream, a, b, o0, o1, r, h); break;
+    default: hipLaunchKernelGGL(held_copy_kernel<4>, grid, block, 0, stream, a, b, o0, o1, r, h); break;
+    }
+    return (int)hipGetLastError();
 }

@@ -168,6 +168,7 @@ def load_refcopy():
     vp, i32, i64 = C.c_void_p, C.c_int, C.c_int64
     lib.aarms_reference_copy.argtypes = [vp, i32, vp, i32, vp, vp, i64, vp]
     lib.aarms_copy_design.argtypes = [i32, i32, i32, i64, vp, vp, vp, vp, i64, vp]
+    lib.aarms_copy_held.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
     return lib
 
 
@@ -426,6 +427,10 @@ COPY_MIXES = [
      "swiglu_quant_fp8 [8192,57344] -> e4m3 [8192,28672]: two inputs, an output of a quarter of their bytes",
      1174405120),
     ("read_only_1GB", 3, 32, "reads only (two inputs, no output)", 1 << 30),
+    ("read_only_134MB", 3, 32, "reads only: the inputs of fused_add_rmsnorm_quant_fp8 [2048,16384]", 134217728),
+    ("write_only_101MB", 4, 16, "writes only: the outputs of fused_add_rmsnorm_quant_fp8 [2048,16384]", 100663296),
+    ("read_only_25MB", 3, 32, "reads only: the inputs of fused_add_rmsnorm [4096,1536]", 25165824),
+    ("write_only_25MB", 4, 16, "writes only: the outputs of fused_add_rmsnorm [4096,1536]", 25165824),
     ("write_only_1GB", 4, 16, "writes only (one output, no input)", 1 << 30),
     ("copy_1GB", 5, 32, "one input, one output of the same bytes", 1 << 30),
 ]
@@ -433,8 +438,10 @@ COPY_MIXES = [
 
 def copy_sweep(args, torch, clib, dev, sp, timer):
     """Plain copies at the read/write mix and size of each headline kernel,
-    and pure reads, pure writes and a 1:1 copy at 1 GiB (what the device's
-    HBM gives each direction alone): 1, 2 or 4 vectors per lane, a one-shot grid or a
+    pure reads, pure writes and a 1:1 copy at 1 GiB (what the device's HBM
+    gives each direction alone), pure reads and pure writes of the Llama-405B
+    and headline norms' inputs and outputs, and a copy of the headline norm's
+    bytes in its layout with its stores held for a range of holds: 1, 2 or 4 vectors per lane, a one-shot grid or a
     grid-stride loop over two 4-wave blocks per CU, with and without the streaming
     hints; rotated buffer sets (3x the last-level cache) as in the workload
     measurements.  Median of 5 timed regions per design, designs interleaved."""
@@ -476,6 +483,31 @@ def copy_sweep(args, torch, clib, dev, sp, timer):
         out["mixes"][name] = {"what": what, "bytes": n * pair_bytes, "buffer_sets_rotated": ns, "designs": rows}
         del sets
         torch.cuda.empty_cache()
+    # the headline norm's layout (one wave per 1,536-wide row, 4,096 rows, all
+    # resident), its stores held on the real-time clock for a range of holds
+    T, row_vecs = 4096, 1536 // 8
+    nb = T * row_vecs * 16
+    ns = rotation_sets(4 * nb)
+    sets = [tuple(torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(4)) for _ in range(ns)]
+    holds = [0, 250, 280, 300, 320, 340, 360, 400]
+    times = {h: [] for h in holds}
+    for _ in range(5):
+        for h in holds:
+            def call(i, h=h):
+                a, b, o0, o1 = sets[i % ns]
+                st = clib.aarms_copy_held(T, row_vecs, h, o0.data_ptr(), o1.data_ptr(), a.data_ptr(), b.data_ptr(), sp)
+                if st:
+                    raise RuntimeError("aarms_copy_held: %d" % st)
+            timer.warm(call, 0.02)
+            times[h].append(timer.region(call, max(reps, 200)) * 1e3)
+    out["norm_layout_held_copy_50MB"] = {
+        "what": "fused_add_rmsnorm [4096,1536]'s bytes in its layout (one wave per row, 3 vectors per lane), "
+                "stores held until hold_ticks (10 ns) after each wave's start",
+        "bytes": 4 * nb, "buffer_sets_rotated": ns,
+        "holds": [{"hold_ticks": h, "us": round(sorted(times[h])[2], 2),
+                   "GB/s": round(4 * nb / (sorted(times[h])[2] * 1e-6) / 1e9, 1)} for h in holds]}
+    del sets
+    torch.cuda.empty_cache()
     return out
 
 
