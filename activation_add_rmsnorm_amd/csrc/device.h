@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace aarms {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -19,6 +21,12 @@ template <typename T>
 __device__ __forceinline__ T ld_stream(const T *p) { return __builtin_nontemporal_load(p); }
 template <typename T>
 __device__ __forceinline__ void st_stream(T *p, T v) { __builtin_nontemporal_store(v, p); }
+
+// The block's index in the launch's row of blocks (linear_grid): a scalar.
+__device__ __forceinline__ int64_t linear_block()
+{
+    return ((int64_t)blockIdx.y << LINEAR_GRID_SHIFT) + (int64_t)blockIdx.x;
+}
 
 // A 16-byte vector holds 8 bf16 values: element 2e is the low half of word
 // e, element 2e+1 the high half.  Widening bf16 -> binary32 is exact.

@@ -7,6 +7,21 @@
 
 namespace aarms {
 
+// A dispatch counts its work-items per grid dimension in 32 bits.  The
+// kernels of one block per row (or row quartet) are launched on a 1-D grid
+// while it fits; past that, on rows of 2^LINEAR_GRID_SHIFT blocks (grid y =
+// the number of such rows), and they number their blocks (blockIdx.y <<
+// LINEAR_GRID_SHIFT) + blockIdx.x -- blockIdx.x itself on a 1-D grid.  With
+// at most 1,024 threads a block, 2^21 blocks are 2^31 work-items.
+constexpr int LINEAR_GRID_SHIFT = 21;
+
+inline dim3 linear_grid(int64_t blocks, int threads)
+{
+    if ((uint64_t)blocks * (uint64_t)threads <= 0xFFFFFFFFull) return dim3((unsigned)blocks);
+    const int64_t x = (int64_t)1 << LINEAR_GRID_SHIFT;
+    return dim3((unsigned)x, (unsigned)((blocks + x - 1) / x));
+}
+
 // Norm epilogues.
 enum NormEpilogue : int {
     NORM_EPI_BF16 = 0,        // bf16 out

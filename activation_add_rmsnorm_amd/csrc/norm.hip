@@ -490,7 +490,7 @@ norm_kernel(NormParams p)
     const int lane = tid % ROW_THREADS;
     // the row is uniform over the wave (WPR == 1) or the block, and is made a
     // scalar so that row addresses are scalar bases plus one lane offset
-    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK +
+    const int64_t row = linear_block() * ROWS_PER_BLOCK +
                         (WPR == 1 ? __builtin_amdgcn_readfirstlane(tid / ROW_THREADS) : 0);
     // WPR == 1: the test is per wave (no block barrier follows); WPR > 1:
     // one row per block, so the whole block leaves together.
@@ -636,7 +636,7 @@ static hipError_t launch_one(const NormParams &p, int blocks_per_cu, int num_cus
         if (rb <= 0 || blocks > (int64_t)rb * num_cus) copy.hold_ticks = copy.res_last = 0;
         if (copy.hold_ticks > NORM_HOLD_MAX_TICKS) copy.hold_ticks = NORM_HOLD_MAX_TICKS;
     }
-    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, stream);
+    return hipLaunchKernel(fn, linear_grid(blocks, threads), dim3(threads), args, 0, stream);
 }
 
 template <int EPI, bool RES>

@@ -132,7 +132,7 @@ norm_kernel_resident(NormParams p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int64_t row = (int64_t)blockIdx.x * RES_ROWS + __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t row = linear_block() * RES_ROWS + __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool live = row < p.tokens;
     const int nvec = p.hidden >> 3;                   // a multiple of 64 (hidden % 512 == 0)
     const int nk = nvec >> 6;                         // slices per lane inside the row
@@ -457,7 +457,7 @@ hipError_t launch_kind(const NormParams &p, int kind, hipStream_t stream)
             fn = (const void *)&norm_kernel_resident<EPI, RES, 6, false>;
     }
     const int64_t blocks = (p.tokens + RES_ROWS - 1) / RES_ROWS;
-    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, stream);
+    return hipLaunchKernel(fn, linear_grid(blocks, 256), dim3(256), args, 0, stream);
 }
 
 }  // namespace

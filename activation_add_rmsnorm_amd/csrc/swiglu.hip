@@ -363,7 +363,7 @@ __global__ void __launch_bounds__(WPR == 1 ? 256 : WPR * 64) swiglu_rowq_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid % ROW_THREADS;
-    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK +
+    const int64_t row = linear_block() * ROWS_PER_BLOCK +
                         (WPR == 1 ? __builtin_amdgcn_readfirstlane(tid / ROW_THREADS) : 0);
     // uniform per wave (WPR == 1: no block barrier follows) or per block
     if (row >= p.tokens) return;
@@ -423,7 +423,7 @@ static hipError_t launch_rowq(const SwigluParams &p, hipStream_t stream)
     const int64_t blocks = (p.tokens + rows_per_block - 1) / rows_per_block;
     SwigluParams copy = p;
     void *args[] = {&copy};
-    return hipLaunchKernel((const void *)&swiglu_rowq_kernel<WPR, JPT>, dim3((unsigned)blocks),
+    return hipLaunchKernel((const void *)&swiglu_rowq_kernel<WPR, JPT>, linear_grid(blocks, threads),
                            dim3(threads), args, 0, stream);
 }
 
