@@ -10,6 +10,7 @@ These launches reach the limits the header states and the places where
   slices deep in z there.
 * Norms of 16,384-wide rows past 2^32 elements per tensor, and forced
   variants (16 waves a row, the resident rows) past the 1-D grid's reach.
+* SwiGLU rows of 2^33 outputs (the width limit) in every static form.
 * The per-tensor E4M3 SwiGLU of 28,672-wide rows at the flat grid's last
   launch under 2^32 jobs and at the first launch past it (the row-chunked
   grid then takes over), with the job index crossing 2^31 inside.
@@ -321,3 +322,71 @@ def test_swiglu_past_2_32_outputs_qwen_rows():
     _all_written(s, "scales")
     sel = torch.from_numpy(rows).to(DEV)
     P.check_swiglu_fp8_dynamic(gus, _take(q, rows), P.from_gpu_bits(s.index_select(0, sel)))
+
+
+# ------------------------------------------------------------------ SwiGLU at the row-width limit
+
+def test_swiglu_widest_rows_every_static_form():
+    """[2, 2 x 2^33] -> [2, 2^33] (AARMS_MAX_INTER): one row holds 2^33
+    outputs, so output, scale and `up` offsets pass 2^31 and 2^32 within a
+    row; bf16, per-tensor E4M3 (the flat grid, 2^31 jobs), MXFP4, NVFP4 and
+    per-128 E4M3.  Sampled: aligned 128-output blocks (whole scale blocks of
+    every form) at both ends of each row and around 2^31 and 2^32."""
+    T, N = 2, 1 << 33
+    _need(T * 2 * N * 2 + T * N * 2)
+    gu = _randn((T, 2 * N), 2.0, 22)
+    rng = np.random.default_rng(23)
+    starts = [0, 1 << 30, (1 << 31) - 128, 1 << 31, (1 << 32) - 128, 1 << 32, N - 256, N - 128]
+    starts += (rng.integers(0, N // 128, 6) * 128).tolist()
+    cols = np.unique(np.concatenate([np.arange(c, c + 128) for c in starts]))
+    blocks = lambda per: torch.from_numpy(np.unique(cols // per)).to(DEV)
+    idx = torch.from_numpy(cols).to(DEV)
+    gus = P.from_gpu_bits(torch.cat([gu.index_select(1, idx), gu.index_select(1, idx + N)], dim=1))
+    take_cols = lambda t, ix: P.from_gpu_bits(t.index_select(1, ix))
+    name = lambda q: A.variant_name(A.OP_SWIGLU, A.pick_variant(A.OP_SWIGLU, T, N, q))
+
+    announce("widest rows: swiglu bf16, variant", name(0))
+    y = _poisoned((T, N), torch.bfloat16)
+    A.swiglu(gu, out=y)
+    torch.cuda.synchronize()
+    _all_written(y, "y")
+    P.check_swiglu(gus, take_cols(y, idx))
+    del y
+
+    announce("widest rows: swiglu_quant_fp8, variant", name(1))
+    scale = torch.tensor([0.05], dtype=torch.float32, device=DEV)
+    q = _poisoned((T, N), torch.float8_e4m3fn)
+    A.swiglu_quant_fp8(gu, scale, out=q)
+    torch.cuda.synchronize()
+    _all_written(q, "codes")
+    P.check_swiglu_fp8(gus, 0.05, take_cols(q, idx))
+
+    announce("widest rows: swiglu_quant_fp8_group, variant", name(4))
+    q.view(torch.uint8).fill_(0x7F)
+    s = _poisoned((T, N // 128), torch.float32)
+    A.swiglu_quant_fp8_group(gu, out=q, scale_out=s)
+    torch.cuda.synchronize()
+    _all_written(q, "codes")
+    _all_written(s, "scales")
+    P.check_swiglu_fp8_group(gus, take_cols(q, idx), take_cols(s, blocks(128)))
+    del q, s
+
+    # E2M1 codes have no unused pattern; the scale bytes are checked written
+    # (0xFF is the E8M0 NaN scale, 0x7F the E4M3 NaN: neither comes from
+    # finite inputs)
+    half = torch.from_numpy(np.unique(cols // 2)).to(DEV)
+    announce("widest rows: swiglu_quant_mxfp4, variant", name(2))
+    q4 = torch.empty((T, N // 2), dtype=torch.uint8, device=DEV)
+    s4 = torch.full((T, N // 32), 0xFF, dtype=torch.uint8, device=DEV)
+    A.swiglu_quant_mxfp4(gu, out=q4, scale_out=s4)
+    torch.cuda.synchronize()
+    assert not bool((s4 == 0xFF).any()), "MXFP4 scales: a block was not written"
+    P.check_swiglu_mxfp4(gus, take_cols(q4, half), take_cols(s4, blocks(32)))
+
+    announce("widest rows: swiglu_quant_nvfp4, variant", name(3))
+    g = torch.tensor([0.05], dtype=torch.float32, device=DEV)
+    s16 = torch.full((T, N // 16), 0x7F, dtype=torch.uint8, device=DEV)
+    A.swiglu_quant_nvfp4(gu, g, out=q4, scale_out=s16)
+    torch.cuda.synchronize()
+    assert not bool(((s16 & 0x7F) == 0x7F).any()), "NVFP4 scales: a block was not written"
+    P.check_swiglu_nvfp4(gus, 0.05, take_cols(q4, half), take_cols(s16, blocks(16)))
