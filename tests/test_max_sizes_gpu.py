@@ -163,9 +163,10 @@ def test_norms_at_the_row_limit_narrow_rows():
 
 
 def test_forced_wide_variants_past_the_one_dimensional_grid():
-    """16 waves a row (1,024-thread blocks) on 5,000,000 rows, and the resident
-    rows (four 512-wide rows a block) on 2^26 + 12 rows: both grids are more
-    than 2^32 work-items along one dimension."""
+    """16 waves a row (1,024-thread blocks) on 5,000,000 rows, the norm and
+    the per-token SwiGLU, and the resident rows (four 512-wide rows a block)
+    on 2^26 + 12 rows: every grid is more than 2^32 work-items along one
+    dimension."""
     eps = 1e-6
     T, H = 5_000_000, 8
     v16 = next(i for i in range(A.variant_count(A.OP_NORM)) if A.variant_name(A.OP_NORM, i) == "16 waves/row x1 vec")
@@ -181,6 +182,22 @@ def test_forced_wide_variants_past_the_one_dimensional_grid():
     _all_written(res, "residual_out")
     P.check_norm(_take(x, rows), _take(r, rows), P.from_gpu_bits(w), eps, _take(out, rows), _take(res, rows))
     del x, r, out, res
+
+    # the per-token SwiGLU on 16-wave rows: [5,000,000, 2 x 8]
+    N = 8
+    vq = next(i for i in range(A.variant_count(A.OP_SWIGLU_DYNAMIC))
+              if A.variant_name(A.OP_SWIGLU_DYNAMIC, i) == "16 waves/row x2 jobs")
+    announce("swiglu_quant_fp8_dynamic, 16 waves a row, on [%d, %d]" % (T, 2 * N))
+    gu = _randn((T, 2 * N), 1.0, 24)
+    q = _poisoned((T, N), torch.float8_e4m3fn)
+    s = _poisoned((T,), torch.float32)
+    A.swiglu_quant_fp8_dynamic(gu, out=q, scale_out=s, variant=vq)
+    torch.cuda.synchronize()
+    _all_written(q, "codes")
+    _all_written(s, "scales")
+    sel = torch.from_numpy(rows).to(DEV)
+    P.check_swiglu_fp8_dynamic(_take(gu, rows), _take(q, rows), P.from_gpu_bits(s.index_select(0, sel)))
+    del gu, q, s
 
     T, H = (1 << 26) + 12, 512
     _need(2 * T * H * 2)
