@@ -392,6 +392,19 @@ def test_pick_variant_ranges():
     for f in (1, 2, 3, 4, 5):
         assert "resident" not in nname(A.OP_RMSNORM, 2048, 16384, f), f
     assert nname(A.OP_NORM, 256, 8192, 1) == nname(A.OP_NORM, 256, 8192, 0) == "8 waves/row x2 vec"
+    # narrow rows: four waves per row for small batches, up to 2,047 tokens
+    # (1,535 at 1,024 wide) for bf16 with the residual add, 1,023 otherwise
+    for H in (1536, 2048):
+        assert nname(A.OP_NORM, 2047, H, 0) == "4 waves/row x1 vec", H
+        assert nname(A.OP_NORM, 2048, H, 0).startswith("wave/row"), H
+    assert nname(A.OP_NORM, 1535, 1024, 0) == "4 waves/row x1 vec"
+    assert nname(A.OP_NORM, 1536, 1024, 0) == "wave/row x2 vec"
+    assert nname(A.OP_NORM, 4096, 1536, 0) == "wave/row x3 vec"                # the headline norm
+    for f in (1, 2, 3, 4, 5):
+        assert nname(A.OP_NORM, 1023, 1536, f) == "4 waves/row x1 vec", f
+        assert nname(A.OP_NORM, 1024, 1536, f) == "wave/row x3 vec", f
+    assert nname(A.OP_RMSNORM, 1023, 1536, 0) == "4 waves/row x1 vec"
+    assert nname(A.OP_RMSNORM, 1024, 1536, 0) == "wave/row x3 vec"
     assert nname(A.OP_RMSNORM, 256, 16384, 1) == nname(A.OP_RMSNORM, 256, 16384, 0)
     for f in (-1, 6):
         assert A.pick_variant(A.OP_NORM, 16, 1536, f) == -1            # unknown output format
