@@ -136,15 +136,21 @@ static int norm_find(int waves, int vecs, int blocks_per_cu)
 // dependent chain of loads and reductions; from here on one wave per row
 // wins (measured on MI355X, 256 CUs, rows of 1,536).
 constexpr int64_t kNarrowMultiWaveTokens = 1024;
-// The bf16 form with the residual add keeps four waves per row longer: one
-// wave per row holds at most two rows per SIMD there, and timed by graph
-// replay four waves of one vector beat it by 2-5% at 1,024-1,280 tokens of
-// 1,024, by 5-21% at 1,024-2,047 tokens of 1,536 and by 7-15% at
-// 1,024-1,536 tokens of 2,048; one wave per row is ahead again from 1,536
-// tokens of 1,024 (3.5% at 2,048) and at 2,048 tokens of 2,048 (5.5%).  The
-// other forms stay at kNarrowMultiWaveTokens (within a few percent either
-// way in the same sweep).
-constexpr int64_t kNarrowMultiWaveTokensAdd = 2048, kNarrowMultiWaveTokensAdd1024 = 1536;
+// With the residual add, four waves per row stay ahead longer: one wave per
+// row holds at most two rows per SIMD there.  Timed by graph replay, four
+// waves of one vector beat one wave per row for bf16 by 2-5% at 1,024-1,280
+// tokens of 1,024, by 5-21% at 1,024-2,047 tokens of 1,536 and by 4-15% at
+// 1,024-1,792 tokens of 2,048 (one wave per row ahead again from 1,536
+// tokens of 1,024); for the per-tensor E4M3, MXFP4, NVFP4 and per-group
+// E4M3 forms by 4-32% at 1,024-1,536 tokens of 1,536 and 2,048, and at
+// 1,792 tokens of 2,048 (2-11%).  On rows of 1,537-2,048 (four vectors per
+// lane in one wave) one wave per row is ahead again at 2,047 tokens (up to
+// 10%), on rows of 1,025-1,536 from 2,048.  Per-token E4M3 (two row
+// reductions) was not consistently faster either way, and on rows of 1,024
+// the quantised forms were within a few percent: those keep
+// kNarrowMultiWaveTokens.
+constexpr int64_t kNarrowMultiWaveTokensAdd = 2048, kNarrowMultiWaveTokensAdd2048 = 1800,
+                  kNarrowMultiWaveTokensAdd1024 = 1536;
 
 // Per-token E4M3 with the residual add reduces each row twice (sum of
 // squares, then amax), so the cost of a cross-wave barrier weighs more: for
@@ -274,9 +280,11 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
     // and 4 vectors per lane (half the waves per row, twice the rows in
     // flight) come first.
     if (hidden <= 2048) {
-        const int64_t multi = (epi == NORM_EPI_BF16 && residual)
-                                  ? (hidden > 1024 ? kNarrowMultiWaveTokensAdd : kNarrowMultiWaveTokensAdd1024)
-                                  : kNarrowMultiWaveTokens;
+        int64_t multi = kNarrowMultiWaveTokens;
+        if (residual && epi != NORM_EPI_FP8_DYNAMIC && hidden > 1024)
+            multi = hidden > 1536 ? kNarrowMultiWaveTokensAdd2048 : kNarrowMultiWaveTokensAdd;
+        else if (residual && epi == NORM_EPI_BF16)
+            multi = kNarrowMultiWaveTokensAdd1024;
         const int i = norm_fit(tokens < multi ? 4 : 1, hidden, 4);
         if (i >= 0) return i;
     }

@@ -392,19 +392,25 @@ def test_pick_variant_ranges():
     for f in (1, 2, 3, 4, 5):
         assert "resident" not in nname(A.OP_RMSNORM, 2048, 16384, f), f
     assert nname(A.OP_NORM, 256, 8192, 1) == nname(A.OP_NORM, 256, 8192, 0) == "8 waves/row x2 vec"
-    # narrow rows: four waves per row for small batches, up to 2,047 tokens
-    # (1,535 at 1,024 wide) for bf16 with the residual add, 1,023 otherwise
-    for H in (1536, 2048):
-        assert nname(A.OP_NORM, 2047, H, 0) == "4 waves/row x1 vec", H
-        assert nname(A.OP_NORM, 2048, H, 0).startswith("wave/row"), H
+    # narrow rows: four waves per row for small batches; with the residual
+    # add (every form but per-token E4M3) up to 2,047 tokens on rows of
+    # 1,025-1,536 and 1,799 on rows of 1,537-2,048, up to 1,535 tokens of
+    # 1,024 or less (bf16), else up to 1,023
+    for f in (0, 2, 3, 4, 5):
+        for H, last in ((1536, 2047), (1544, 1799), (2048, 1799)):
+            assert nname(A.OP_NORM, last, H, f) == "4 waves/row x1 vec", (H, f)
+            assert nname(A.OP_NORM, last + 1, H, f).startswith("wave/row"), (H, f)
+        assert nname(A.OP_NORM, 1023, 1024, f) == "4 waves/row x1 vec", f
     assert nname(A.OP_NORM, 1535, 1024, 0) == "4 waves/row x1 vec"
     assert nname(A.OP_NORM, 1536, 1024, 0) == "wave/row x2 vec"
+    for f in (2, 3, 4, 5):
+        assert nname(A.OP_NORM, 1024, 1024, f) == "wave/row x2 vec", f
     assert nname(A.OP_NORM, 4096, 1536, 0) == "wave/row x3 vec"                # the headline norm
-    for f in (1, 2, 3, 4, 5):
-        assert nname(A.OP_NORM, 1023, 1536, f) == "4 waves/row x1 vec", f
-        assert nname(A.OP_NORM, 1024, 1536, f) == "wave/row x3 vec", f
-    assert nname(A.OP_RMSNORM, 1023, 1536, 0) == "4 waves/row x1 vec"
-    assert nname(A.OP_RMSNORM, 1024, 1536, 0) == "wave/row x3 vec"
+    assert nname(A.OP_NORM, 1023, 1536, 1) == "4 waves/row x1 vec"
+    assert nname(A.OP_NORM, 1024, 1536, 1) == "wave/row x3 vec"
+    for f in (0, 1, 2, 3, 4, 5):
+        assert nname(A.OP_RMSNORM, 1023, 1536, f) == "4 waves/row x1 vec", f
+        assert nname(A.OP_RMSNORM, 1024, 1536, f) == "wave/row x3 vec", f
     assert nname(A.OP_RMSNORM, 256, 16384, 1) == nname(A.OP_RMSNORM, 256, 16384, 0)
     for f in (-1, 6):
         assert A.pick_variant(A.OP_NORM, 16, 1536, f) == -1            # unknown output format
