@@ -354,7 +354,14 @@ def test_pick_variant_ranges():
     assert name(4096, 8960, 0) == name(4096, 8960, 2) == "1 job/lane"
     assert name(4096, 8960, 1) == name(2048, 5632, 1) == name(8192, 3584, 1) == "1 job/lane, flat rows"
     assert name(8192, 28672, 1) == "1 job/lane, flat rows" and name(8192, 2048, 1) == "2 jobs/lane"
-    assert name(256, 8960, 1) == "1 job/lane"
+    assert name(256, 8960, 1) == "1 job/lane, flat rows"                      # E4M3 from ~2 M outputs
+    # rows ending in a partial block over an even number of blocks (whose
+    # partial blocks would land on half the XCDs): the flat grid
+    for f in (0, 2, 3, 4):
+        for N in (7168, 11008, 18944):
+            assert name(4096, N, f) == "1 job/lane, flat rows", (N, f)
+        for N in (5632, 8960, 9728, 13824, 14336):                            # odd counts, whole blocks
+            assert name(4096, N, f) == "1 job/lane", (N, f)
     # rows of 257-511 jobs: the flat grid in every format (past the decode sizes)
     for f in range(5):
         assert name(8192, 3584, f) == name(4096, 2056, f) == "1 job/lane, flat rows", f
