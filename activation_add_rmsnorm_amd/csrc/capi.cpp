@@ -160,13 +160,24 @@ constexpr int64_t kNarrowMultiWaveTokensAdd = 2048, kNarrowMultiWaveTokensAdd204
 // forms, with one reduction, keep 16 x 2.
 constexpr int64_t kDynamicFp8FewWavesTokens = 1024;
 
-// bf16 with the residual add on rows of 4,097-8,192: from 768 to 1,536
-// tokens a one-shot grid of 8-wave blocks runs about 0.75-1.5 generations
-// and leaves a partial one; the persistent, software-pipelined 8 x 2 variant
-// (two blocks per CU, each walking rows and loading the next during the
-// current one's reductions) measured 0-19% faster there at 5,120-8,192 wide,
-// and no faster below 768 or from 2,048 tokens.
-constexpr int64_t kPipelinedMinTokens = 768, kPipelinedMaxTokens = 1536;
+// bf16 with the residual add on rows of 4,097-8,192: from 1,024 to 1,536
+// tokens a one-shot grid of 8-wave blocks runs about 1-1.5 generations
+// and leaves a partial one.  Fewer waves per row (fewer, longer-lived
+// blocks) fit such a batch into one generation: timed by graph replay on
+// three boxes at 5,120, 6,144 and 8,192 wide, 4 waves of 4 vectors were the
+// fastest or within 3% at 1,024-1,280 tokens (up to 14% ahead of 8 x 2, and
+// of the persistent, software-pipelined 8 x 2 variant chosen here before)
+// and 2 waves of 8 the fastest at 1,536 (6-17% ahead).  Below 1,024 tokens
+// the general rule's 8 x 2 is as fast or faster (6% at 768 x 5,120).
+constexpr int64_t kWideFewWavesMinTokens = 1024, kWideFourWavesMaxTokens = 1280, kWideFewWavesMaxTokens = 1536;
+
+// bf16 with the residual add on rows of 2,049-4,096 (4 waves of 2 vectors
+// by default): batches of 2,049-2,560 tokens spill the 4-wave blocks into a
+// thin second generation, and 2 waves of 4 vectors keep them in one: 3-9%
+// faster at 2,049 tokens and 18-25% at 2,304-2,560 of 2,560-4,096 (graph
+// replay, two boxes; from 3,072 tokens mixed).  Per-token E4M3 was within
+// 3.6% either way there and keeps 4 x 2.
+constexpr int64_t kMidTwoWavesMinTokens = 2049, kMidTwoWavesMaxTokens = 2560;
 
 // Store hold of the one-shot kernel (norm.hip, hold_stores): each row's
 // stores wait until about the time the launch's reads take after its wave
@@ -244,8 +255,13 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
         }
     }
     if (epi == NORM_EPI_BF16 && residual && hidden > 4096 && hidden <= 8192 &&
-        tokens >= kPipelinedMinTokens && tokens <= kPipelinedMaxTokens) {
-        const int i = norm_find(8, 2, 2);
+        tokens >= kWideFewWavesMinTokens && tokens <= kWideFewWavesMaxTokens) {
+        const int i = tokens <= kWideFourWavesMaxTokens ? norm_find(4, 4, 0) : norm_find(2, 8, 0);
+        if (i >= 0) return i;
+    }
+    if (residual && epi == NORM_EPI_BF16 && hidden > 2048 && hidden <= 4096 &&
+        tokens >= kMidTwoWavesMinTokens && tokens <= kMidTwoWavesMaxTokens) {
+        const int i = norm_find(2, 4, 0);
         if (i >= 0) return i;
     }
     // The same band without the residual add, on rows of 8,193-16,384 (8

@@ -425,13 +425,23 @@ def test_pick_variant_ranges():
         assert A.pick_variant(op, -1, 1536) == -1                      # what the entry points reject
         assert A.pick_variant(op, 16, 1540) == -1
         assert A.pick_variant(op, 0, 1536) >= 0                        # zero tokens is a valid call
-    # bf16 with the residual, 4,097-8,192 wide, 768-1,536 tokens: the pipelined 8 x 2
-    for T, H in ((768, 5120), (1024, 8192), (1536, 6144)):
-        assert nname(A.OP_NORM, T, H, 0) == "8 waves/row x2 vec, pipelined 2 blocks/CU"
-    for T, H in ((512, 8192), (2048, 8192), (1024, 4096), (1024, 12288)):
-        assert "pipelined" not in nname(A.OP_NORM, T, H, 0)
-    assert "pipelined" not in nname(A.OP_NORM, 1024, 8192, 1)           # not the quantised forms
+    # bf16 with the residual, 4,097-8,192 wide: 4 waves x 4 at 1,024-1,280
+    # tokens and 2 waves x 8 at 1,281-1,536 (one generation of blocks)
+    for T, H in ((1024, 5120), (1024, 8192), (1280, 6144), (1024, 4104)):
+        assert nname(A.OP_NORM, T, H, 0) == "4 waves/row x4 vec", (T, H)
+    for T, H in ((1281, 5120), (1536, 6144), (1536, 8192)):
+        assert nname(A.OP_NORM, T, H, 0) == "2 waves/row x8 vec", (T, H)
+    for T, H in ((768, 5120), (1023, 8192), (1537, 8192), (2048, 8192), (1024, 12288)):
+        assert nname(A.OP_NORM, T, H, 0) == nname(A.OP_NORM, T, H, 2), (T, H)   # the general rule
+    assert nname(A.OP_NORM, 1024, 8192, 1) == "8 waves/row x2 vec"      # not the quantised forms
     assert "pipelined" not in nname(A.OP_RMSNORM, 1024, 8192, 0)        # nor without the add at 8,192
+    # bf16 with the add on rows of 2,049-4,096: 2 waves x 4 at 2,049-2,560
+    # tokens, else 4 waves x 2
+    for H in (2560, 3584, 4096):
+        assert nname(A.OP_NORM, 2049, H, 0) == nname(A.OP_NORM, 2560, H, 0) == "2 waves/row x4 vec", H
+        assert nname(A.OP_NORM, 2048, H, 0) == nname(A.OP_NORM, 2561, H, 0) == "4 waves/row x2 vec", H
+    for f in (1, 2):
+        assert nname(A.OP_NORM, 2304, 4096, f) == "4 waves/row x2 vec", f    # E4M3 forms: unchanged
     # without the add: 4 waves x 2 below 1,024 tokens up to 4,096 wide; the
     # pipelined 8 x 4 for bf16 at 8,193-16,384 wide from 512 to 2,048 tokens
     assert nname(A.OP_RMSNORM, 512, 4096, 0) == nname(A.OP_RMSNORM, 1, 4096, 1) == "4 waves/row x2 vec"
