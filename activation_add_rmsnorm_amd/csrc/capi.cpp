@@ -244,13 +244,23 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
     // need more instructions per byte than two waves per SIMD can hide).  In
     // the first band every form takes the 6-slice window; in the second the
     // forms with the add take 10 slices.
-    if (hidden > 12288 && hidden <= NORM_RESIDENT_MAX_HIDDEN && hidden % NORM_RESIDENT_WIDTH_MULTIPLE == 0 &&
+    // With the residual add the resident rows also pay on narrower rows
+    // (graph replay, 832-2,048 tokens): on rows of 10,240-12,288 in both
+    // bands, bf16 3-8%, per-token E4M3 2-13% and per-tensor E4M3 7-24%
+    // faster than the split rows; on rows of 6,144-9,728 bf16 only, in the
+    // second band (5-14%; in the first band and for the E4M3 forms the split
+    // rows were as fast or faster).  On these rows the 6-slice window was
+    // the faster or within 1.3% in both bands.
+    const bool res_wide = hidden > 12288 && hidden <= NORM_RESIDENT_MAX_HIDDEN;
+    const bool res_mid = residual && hidden >= 10240 && hidden <= 12288;
+    const bool res_mid_bf16 = residual && epi == NORM_EPI_BF16 && hidden >= 6144 && hidden < 10240;
+    if ((res_wide || res_mid || res_mid_bf16) && hidden % NORM_RESIDENT_WIDTH_MULTIPLE == 0 &&
         (epi == NORM_EPI_BF16 || (residual && (epi == NORM_EPI_FP8_DYNAMIC || epi == NORM_EPI_FP8_STATIC)))) {
         const int64_t blocks = (tokens + 3) / 4, cus = device_cus();
         const bool one = blocks * 5 >= cus * 4 && blocks <= cus;
         const bool two = blocks * 4 >= cus * 7 && blocks <= 2 * cus;
-        if (one || two) {
-            const int i = norm_find(1, 32, (two && residual) ? NORM_RESIDENT : NORM_RESIDENT_Y_IN_PLACE);
+        if (res_mid_bf16 ? two : (one || two)) {
+            const int i = norm_find(1, 32, (res_wide && two && residual) ? NORM_RESIDENT : NORM_RESIDENT_Y_IN_PLACE);
             if (i >= 0) return i;
         }
     }

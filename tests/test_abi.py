@@ -391,7 +391,7 @@ def test_pick_variant_ranges():
             assert nname(A.OP_NORM, T, 16384, f) == W10, (T, f)
         assert nname(A.OP_NORM, 2048, 12800, f) == W10
         assert nname(A.OP_NORM, 1536, 16384, f) == nname(A.OP_NORM, 2049, 16384, f) == "16 waves/row x2 vec"
-        assert nname(A.OP_NORM, 2048, 12288, f) == nname(A.OP_NORM, 2048, 16376, f) == "16 waves/row x2 vec"
+        assert nname(A.OP_NORM, 2048, 16376, f) == "16 waves/row x2 vec"
     assert nname(A.OP_RMSNORM, 1024, 16384, 0) == nname(A.OP_RMSNORM, 2048, 16384, 0) == W6
     assert nname(A.OP_RMSNORM, 1536, 16384, 0) == "8 waves/row x4 vec, pipelined 2 blocks/CU"
     for f in (3, 4, 5):
@@ -399,6 +399,22 @@ def test_pick_variant_ranges():
     for f in (1, 2, 3, 4, 5):
         assert "resident" not in nname(A.OP_RMSNORM, 2048, 16384, f), f
     assert nname(A.OP_NORM, 256, 8192, 1) == nname(A.OP_NORM, 256, 8192, 0) == "8 waves/row x2 vec"
+    # with the add, the resident rows (6-slice window) also on rows of
+    # 10,240-12,288 in both bands, and for bf16 on 6,144-9,728 in the second
+    for f in (0, 1, 2):
+        for H in (10240, 12288):
+            for T in (832, 1024, 1792, 2048):
+                assert nname(A.OP_NORM, T, H, f) == W6, (T, H, f)
+            assert "resident" not in nname(A.OP_NORM, 1536, H, f)
+            assert "resident" not in nname(A.OP_NORM, 2049, H, f)
+            assert "resident" not in nname(A.OP_RMSNORM, 1024, H, f)          # not without the add
+        assert "resident" not in nname(A.OP_NORM, 2048, 10248, f)             # a multiple of 512 only
+    for H in (6144, 8192, 9728):
+        assert nname(A.OP_NORM, 1792, H, 0) == nname(A.OP_NORM, 2048, H, 0) == W6, H
+        assert "resident" not in nname(A.OP_NORM, 1024, H, 0), H
+        for f in (1, 2):
+            assert "resident" not in nname(A.OP_NORM, 2048, H, f), (H, f)
+    assert "resident" not in nname(A.OP_NORM, 2048, 5632, 0)
     # narrow rows: four waves per row for small batches; with the residual
     # add (every form but per-token E4M3) up to 2,047 tokens on rows of
     # 1,025-1,536 and 1,799 on rows of 1,537-2,048, up to 1,535 tokens of
@@ -431,7 +447,7 @@ def test_pick_variant_ranges():
         assert nname(A.OP_NORM, T, H, 0) == "4 waves/row x4 vec", (T, H)
     for T, H in ((1281, 5120), (1536, 6144), (1536, 8192)):
         assert nname(A.OP_NORM, T, H, 0) == "2 waves/row x8 vec", (T, H)
-    for T, H in ((768, 5120), (1023, 8192), (1537, 8192), (2048, 8192), (1024, 12288)):
+    for T, H in ((768, 5120), (1023, 8192), (1537, 8192), (1024, 12800)):
         assert nname(A.OP_NORM, T, H, 0) == nname(A.OP_NORM, T, H, 2), (T, H)   # the general rule
     assert nname(A.OP_NORM, 1024, 8192, 1) == "8 waves/row x2 vec"      # not the quantised forms
     assert "pipelined" not in nname(A.OP_RMSNORM, 1024, 8192, 0)        # nor without the add at 8,192

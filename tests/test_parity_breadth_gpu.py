@@ -373,6 +373,33 @@ def test_resident_default_pick_per_token(T):
     P.check_norm_fp8(x, r, wt, 1e-5, bits(q), bits(s), bits(ro))
 
 
+@pytest.mark.parametrize("T,H,f", [(1792, 8192, 0), (2048, 6144, 0), (832, 10240, 1), (1024, 12288, 2),
+                                   (2048, 10240, 2), (1920, 12288, 1)])
+def test_resident_default_pick_mid_widths(T, H, f):
+    """The forms with the residual add where the library picks the resident
+    rows on rows of 6,144-12,288 (bf16 in the second band from 6,144, every
+    E4M3 form in both bands from 10,240), against the oracle."""
+    name = A.variant_name(A.OP_NORM, A.pick_variant(A.OP_NORM, T, H, f))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert "resident" in name, name
+    x = gen.normal_bf16((T, H), T + H, 1, outlier_frac=0.001, outlier_mult=50.0)
+    r = gen.normal_bf16((T, H), T + H, 2)
+    wt = gen.normal_bf16((H,), T + H, 3, mean=1.0, std=0.1)
+    announce("norm form", f, "default", name, (T, H))
+    if f == 0:
+        o, ro = A.fused_add_rmsnorm(bf16(x), bf16(r), bf16(wt), 1e-6)
+        torch.cuda.synchronize()
+        P.check_norm(x, r, wt, 1e-6, bits(o), bits(ro))
+    elif f == 1:
+        q, s, ro = A.fused_add_rmsnorm_quant_fp8(bf16(x), bf16(r), bf16(wt), 1e-5)
+        torch.cuda.synchronize()
+        P.check_norm_fp8(x, r, wt, 1e-5, bits(q), bits(s), bits(ro))
+    else:
+        q, ro = A.fused_add_rmsnorm_quant_fp8_static(bf16(x), bf16(r), bf16(wt), f32(0.02), 1e-5)
+        torch.cuda.synchronize()
+        P.check_norm_fp8_static(x, r, wt, 1e-5, 0.02, bits(q), bits(ro))
+
+
 def _special_rows(T, H, seed):
     """Rows the resident kernels have to get right besides random ones (bf16
     bit patterns): zero, constant, a NaN, an infinity, bf16 subnormals,
