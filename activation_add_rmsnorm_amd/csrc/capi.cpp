@@ -159,6 +159,7 @@ constexpr int64_t kNarrowMultiWaveTokensAdd = 2048, kNarrowMultiWaveTokensAdd204
 // 16,384; from 2,048 tokens 16 x 2 is as fast or faster).  The block-scaled
 // forms, with one reduction, keep 16 x 2.
 constexpr int64_t kDynamicFp8FewWavesTokens = 1024;
+constexpr int64_t kWideOneVecTokensBf16 = 512, kWideOneVecTokensFp8 = 64;
 
 // bf16 with the residual add on rows of 4,097-8,192: from 1,024 to 1,536
 // tokens a one-shot grid of 8-wave blocks runs about 1-1.5 generations
@@ -290,6 +291,19 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
     // from 1,024 tokens 2 x 4 is as fast or faster.
     if (!residual && hidden > 2048 && hidden <= 4096 && tokens < kNarrowMultiWaveTokens) {
         const int i = norm_fit(4, hidden, 2);
+        if (i >= 0) return i;
+    }
+    // Small batches with the residual add on rows of 2,049-8,192: one vector
+    // per lane over twice the waves (8 up to 4,096 wide, else 16) shortens
+    // every row's chain while the launch is latency-bound.  Graph replay:
+    // bf16 5-10% faster at 1-64 tokens and 2.4-3.9% at 512 (level at 512 x
+    // 8,192); per-token E4M3 3.5-5.4% at 1-64 tokens of 3,072-4,096 (level
+    // at 512, and at any batch from 5,120 wide, where its two row
+    // reductions favour fewer waves).
+    if (residual && hidden > 2048 && hidden <= 8192 &&
+        ((epi == NORM_EPI_BF16 && tokens <= kWideOneVecTokensBf16) ||
+         (epi == NORM_EPI_FP8_DYNAMIC && hidden <= 4096 && tokens <= kWideOneVecTokensFp8))) {
+        const int i = norm_find(hidden <= 4096 ? 8 : 16, 1, 0);
         if (i >= 0) return i;
     }
     if (epi == NORM_EPI_FP8_DYNAMIC && residual && hidden > 8192 && tokens <= kDynamicFp8FewWavesTokens) {

@@ -398,7 +398,7 @@ def test_pick_variant_ranges():
         assert "resident" not in nname(A.OP_NORM, 2048, 16384, f), f
     for f in (1, 2, 3, 4, 5):
         assert "resident" not in nname(A.OP_RMSNORM, 2048, 16384, f), f
-    assert nname(A.OP_NORM, 256, 8192, 1) == nname(A.OP_NORM, 256, 8192, 0) == "8 waves/row x2 vec"
+    assert nname(A.OP_NORM, 256, 8192, 1) == nname(A.OP_NORM, 768, 8192, 0) == "8 waves/row x2 vec"
     # with the add, the resident rows (6-slice window) also on rows of
     # 10,240-12,288 in both bands, and for bf16 on 6,144-9,728 in the second
     for f in (0, 1, 2):
@@ -451,6 +451,16 @@ def test_pick_variant_ranges():
         assert nname(A.OP_NORM, T, H, 0) == nname(A.OP_NORM, T, H, 2), (T, H)   # the general rule
     assert nname(A.OP_NORM, 1024, 8192, 1) == "8 waves/row x2 vec"      # not the quantised forms
     assert "pipelined" not in nname(A.OP_RMSNORM, 1024, 8192, 0)        # nor without the add at 8,192
+    # small batches with the add on rows of 2,049-8,192: one vector per lane
+    # (bf16 up to 512 tokens; per-token E4M3 up to 64 tokens of 2,049-4,096)
+    for T in (1, 64, 512):
+        assert nname(A.OP_NORM, T, 3072, 0) == nname(A.OP_NORM, T, 4096, 0) == "8 waves/row x1 vec", T
+        assert nname(A.OP_NORM, T, 5120, 0) == nname(A.OP_NORM, T, 8192, 0) == "16 waves/row x1 vec", T
+    assert nname(A.OP_NORM, 513, 4096, 0) == "4 waves/row x2 vec"
+    assert nname(A.OP_NORM, 513, 8192, 0) == "8 waves/row x2 vec"
+    assert nname(A.OP_NORM, 64, 4096, 1) == "8 waves/row x1 vec"
+    assert nname(A.OP_NORM, 65, 4096, 1) == nname(A.OP_NORM, 64, 4096, 2) == "4 waves/row x2 vec"
+    assert nname(A.OP_NORM, 1, 8192, 1) == "8 waves/row x2 vec"
     # bf16 with the add on rows of 2,049-4,096: 2 waves x 4 at 2,049-2,560
     # tokens, else 4 waves x 2
     for H in (2560, 3584, 4096):
