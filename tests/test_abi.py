@@ -461,11 +461,19 @@ def test_pick_variant_ranges():
     assert nname(A.OP_NORM, 64, 4096, 1) == "8 waves/row x1 vec"
     assert nname(A.OP_NORM, 65, 4096, 1) == nname(A.OP_NORM, 64, 4096, 2) == "4 waves/row x2 vec"
     assert nname(A.OP_NORM, 1, 8192, 1) == "8 waves/row x2 vec"
+    # with the add on rows of 2,049-4,096 at 1,792-2,048 tokens (one
+    # generation of two waves per SIMD): one wave per row, bf16 and per-token E4M3
+    for f in (0, 1):
+        assert nname(A.OP_NORM, 1792, 3072, f) == nname(A.OP_NORM, 2048, 3072, f) == "wave/row x6 vec", f
+        assert nname(A.OP_NORM, 2048, 4096, f) == nname(A.OP_NORM, 1800, 2560, f).replace("x6", "x8"), f
+        assert nname(A.OP_NORM, 1787, 4096, f) == "4 waves/row x2 vec", f     # 447 blocks: below the band
+    assert nname(A.OP_NORM, 2048, 4096, 2) == "4 waves/row x2 vec"      # not the per-tensor form
     # bf16 with the add on rows of 2,049-4,096: 2 waves x 4 at 2,049-2,560
-    # tokens, else 4 waves x 2
+    # tokens (one wave per row just below, 4 waves x 2 above)
     for H in (2560, 3584, 4096):
         assert nname(A.OP_NORM, 2049, H, 0) == nname(A.OP_NORM, 2560, H, 0) == "2 waves/row x4 vec", H
-        assert nname(A.OP_NORM, 2048, H, 0) == nname(A.OP_NORM, 2561, H, 0) == "4 waves/row x2 vec", H
+        assert nname(A.OP_NORM, 2048, H, 0).startswith("wave/row"), H
+        assert nname(A.OP_NORM, 2561, H, 0) == "4 waves/row x2 vec", H
     for f in (1, 2):
         assert nname(A.OP_NORM, 2304, 4096, f) == "4 waves/row x2 vec", f    # E4M3 forms: unchanged
     # without the add: 4 waves x 2 below 1,024 tokens up to 4,096 wide; the
