@@ -160,6 +160,7 @@ constexpr int64_t kNarrowMultiWaveTokensAdd = 2048, kNarrowMultiWaveTokensAdd204
 // forms, with one reduction, keep 16 x 2.
 constexpr int64_t kDynamicFp8FewWavesTokens = 1024;
 constexpr int64_t kWideOneVecTokensBf16 = 512, kWideOneVecTokensFp8 = 64;
+constexpr int64_t kNoAddOneWaveMaxTokensBf16 = 3072, kNoAddOneWaveMaxTokensFp8 = 4096;
 
 // bf16 with the residual add on rows of 4,097-8,192: from 1,024 to 1,536
 // tokens a one-shot grid of 8-wave blocks runs about 1-1.5 generations
@@ -301,6 +302,26 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
     // tokens: 4 waves of 2 vectors per lane beat 2 waves of 4 by 9-18% (the
     // shorter per-lane chain matters while the launch is latency-bound);
     // from 1,024 tokens 2 x 4 is as fast or faster.
+    // Without the residual add, rows of 2,049-4,096 once a batch fills the
+    // device: one wave per row (6 or 8 vectors) keeps 1,792-3,072 tokens in
+    // one generation of up to three waves per SIMD, and a batch of four per
+    // SIMD (4,096 tokens on 256 CUs) both fits one generation and takes the
+    // store hold.  Graph replay on two boxes: bf16 level at 1,792 tokens,
+    // 6-23% faster than 2 x 4 at 2,048-3,072 and 15-28% at 4,096 (between
+    // 3,072 and 4,096, without the hold, 1-9% slower: not taken); per-token
+    // E4M3 on rows up to 3,072 wide 1-13% faster at 1,792-4,096 tokens
+    // (mixed from 6,144, and at 3,584-4,096 wide).
+    if (!residual && hidden > 2048 && tokens >= 1792) {
+        const int64_t cus = device_cus();
+        const bool bf16_band = epi == NORM_EPI_BF16 && hidden <= 4096 &&
+                               (tokens <= kNoAddOneWaveMaxTokensBf16 ||
+                                (tokens >= kHoldMinTokens && tokens <= 16 * cus));
+        const bool fp8_band = epi == NORM_EPI_FP8_DYNAMIC && hidden <= 3072 && tokens <= kNoAddOneWaveMaxTokensFp8;
+        if (bf16_band || fp8_band) {
+            const int i = norm_fit(1, hidden, 8);
+            if (i >= 0) return i;
+        }
+    }
     if (!residual && hidden > 2048 && hidden <= 4096 && tokens < kNarrowMultiWaveTokens) {
         const int i = norm_fit(4, hidden, 2);
         if (i >= 0) return i;

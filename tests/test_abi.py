@@ -451,6 +451,15 @@ def test_pick_variant_ranges():
         assert nname(A.OP_NORM, T, H, 0) == nname(A.OP_NORM, T, H, 2), (T, H)   # the general rule
     assert nname(A.OP_NORM, 1024, 8192, 1) == "8 waves/row x2 vec"      # not the quantised forms
     assert "pipelined" not in nname(A.OP_RMSNORM, 1024, 8192, 0)        # nor without the add at 8,192
+    # without the add, rows of 2,049-4,096: one wave per row in bf16 at
+    # 1,792-3,072 tokens and at 4,096 (256 CUs), per-token E4M3 on rows up
+    # to 3,072 at 1,792-4,096 tokens
+    for T in (1792, 3072, 4096):
+        assert nname(A.OP_RMSNORM, T, 3072, 0) == nname(A.OP_RMSNORM, T, 3072, 1) == "wave/row x6 vec", T
+        assert nname(A.OP_RMSNORM, T, 4096, 0) == "wave/row x8 vec", T
+    for T in (1791, 3073, 4095, 4097):
+        assert nname(A.OP_RMSNORM, T, 4096, 0) == "2 waves/row x4 vec", T
+    assert nname(A.OP_RMSNORM, 2048, 4096, 1) == nname(A.OP_RMSNORM, 4097, 3072, 1) == "2 waves/row x4 vec"
     # small batches with the add on rows of 2,049-8,192: one vector per lane
     # (bf16 up to 512 tokens; per-token E4M3 up to 64 tokens of 2,049-4,096)
     for T in (1, 64, 512):
