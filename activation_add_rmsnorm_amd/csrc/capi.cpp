@@ -283,6 +283,20 @@ int pick_norm(int64_t tokens, int64_t hidden, int epi, bool residual)
             if (i >= 0) return i;
         }
     }
+    // Past that band, on rows of 2,049-3,072: one wave per row again.  At
+    // 2,561-3,072 tokens (one generation of three waves per SIMD) 8 vectors
+    // per lane, 1-15% faster than 4 x 2 by graph replay (6 vectors lost 4% at
+    // 2,600 x 3,072); at four waves per SIMD (4,096 tokens on 256 CUs, where
+    // the store hold applies) the fewest vectors that fit, whose registers
+    // let the whole batch be resident: 11-20% faster (8 vectors do not fit).
+    if (residual && epi == NORM_EPI_BF16 && hidden > 2048 && hidden <= 3072) {
+        int i = -1;
+        if (tokens > kMidTwoWavesMaxTokens && tokens <= 3072)
+            i = norm_find(1, 8, 0);
+        else if (tokens >= kHoldMinTokens && tokens <= 16 * device_cus())
+            i = norm_fit(1, hidden, 8);
+        if (i >= 0) return i;
+    }
     if (residual && epi == NORM_EPI_BF16 && hidden > 2048 && hidden <= 4096 &&
         tokens >= kMidTwoWavesMinTokens && tokens <= kMidTwoWavesMaxTokens) {
         const int i = norm_find(2, 4, 0);

@@ -482,7 +482,15 @@ def test_pick_variant_ranges():
     for H in (2560, 3584, 4096):
         assert nname(A.OP_NORM, 2049, H, 0) == nname(A.OP_NORM, 2560, H, 0) == "2 waves/row x4 vec", H
         assert nname(A.OP_NORM, 2048, H, 0).startswith("wave/row"), H
-        assert nname(A.OP_NORM, 2561, H, 0) == "4 waves/row x2 vec", H
+        assert nname(A.OP_NORM, 2561, H, 0) == ("wave/row x8 vec" if H <= 3072 else "4 waves/row x2 vec"), H
+    # and one wave per row on rows of 2,049-3,072: 8 vectors at 2,561-3,072
+    # tokens, the fewest that fit at 4,096
+    for T in (2561, 3072):
+        assert nname(A.OP_NORM, T, 3072, 0) == nname(A.OP_NORM, T, 2560, 0) == "wave/row x8 vec", T
+    assert nname(A.OP_NORM, 4096, 3072, 0) == nname(A.OP_NORM, 4096, 2560, 0) == "wave/row x6 vec"
+    for T in (3073, 4095, 4097):
+        assert nname(A.OP_NORM, T, 3072, 0) == "4 waves/row x2 vec", T
+    assert nname(A.OP_NORM, 3072, 3072, 1) == "4 waves/row x2 vec"
     for f in (1, 2):
         assert nname(A.OP_NORM, 2304, 4096, f) == "4 waves/row x2 vec", f    # E4M3 forms: unchanged
     # without the add: 4 waves x 2 below 1,024 tokens up to 4,096 wide; the
